@@ -1,0 +1,388 @@
+"""Benchmark of the per-layer mixed-precision Adam update on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c1|c0|c2|c3|c4] [--gpus 1]
+
+A step is one pass of the whole update over every block of the workload
+(host constants, one ragged multi-tensor launch, the fused kernel) with
+that step's BF16 gradients already resident in HBM.  W untimed steps, then
+K timed steps between two device synchronisations; one JSON line on stdout.
+
+Workloads (shapes from the pages, values synthetic, see
+layer_streamed_optimizer_amd/configs.py):
+  c0  one 1024x1024 block                                  (resident)
+  c1  TinyLlama-1.1B shape, 25 blocks, 1,100,048,384 params (resident, default)
+  c2  LoRA r=8 on TinyLlama, 308 ragged tensors, 6,307,840  (resident)
+  c3  LLaMA-7B shape, 35 blocks, 6,738,415,616 params       (resident, ~108 GB)
+  c4  70B-shaped slice, 16 layers of 855,654,400 params, streamed from
+      ~164 GB of pinned host memory                          (streamed)
+
+Roofline: the fused kernel moves 28 algorithmic bytes per parameter (reads
+2 g + 4 master + 4 m + 4 v, writes 4 + 4 + 4 + 2 w); its average launch
+duration is measured with HIP events on the launch stream.  The CPU
+baseline is the oracle (plain scalar FP64 C, all host cores) timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gparams/s Adam step; % HBM peak (resident) / % host-link peak (streamed)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BYTES_PER_PARAM = 28            # algorithmic, resident kernel
+LINK_BYTES_PER_PARAM = 12       # streamed: [master | m | v] each way
+KERNEL_SOURCE = os.path.join(ROOT, "layer_streamed_optimizer_amd", "csrc", "lso_adam.hip")
+
+
+def progress(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("lso_adam.hip", "lso_internal.h", "lso_bf16.h"):
+        with open(os.path.join(ROOT, "layer_streamed_optimizer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fused_adam_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+# ------------------------------------------------------------ resident path
+
+def resident(args, w):
+    import torch
+
+    import layer_streamed_optimizer_amd as lso
+    import synth
+    from layer_streamed_optimizer_amd import configs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sid = configs.STREAM_ID[w.key]
+    sizes = [b.n for b in w.blocks]
+    lay = configs.ResidentLayout(sizes)
+    params = w.params
+    total_steps = args.warmup + args.steps
+    free, _total = torch.cuda.mem_get_info()
+    budget = free - lay.state_bytes - lay.weight_bytes - (8 << 30)
+    n_sets = max(1, min(total_steps, budget // max(lay.grad_bytes, 1)))
+    progress(f"{w.key}: {len(sizes)} blocks, {params:,} params, state {lay.state_bytes / 1e9:.1f} GB, "
+             f"{n_sets} gradient sets of {lay.grad_bytes / 1e9:.2f} GB")
+    stream = torch.cuda.current_stream()
+    hs = int(stream.cuda_stream)
+    state = torch.empty(lay.state_bytes, dtype=torch.uint8, device=dev)
+    weight = torch.empty(lay.weight_bytes, dtype=torch.uint8, device=dev)
+    grads = [torch.empty(lay.grad_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    sb, wb = int(state.data_ptr()), int(weight.data_ptr())
+
+    def init_state():
+        for b, spec in enumerate(w.blocks):
+            n = spec.n
+            if spec.init == "zero":
+                synth.device_fill_zero(sb + lay.off_master[b], 4 * n, hs)
+            else:
+                lora = spec.init == "lora_a"
+                synth.device_fill_normal_f32(
+                    sb + lay.off_master[b], n, stream=sid, block=b,
+                    purpose=synth.PURPOSE_LORA_A if lora else synth.PURPOSE_MASTER, step=0,
+                    sigma=configs.LORA_A_SIGMA if lora else configs.MASTER_SIGMA, hip_stream=hs)
+            synth.device_fill_zero(sb + lay.off_m[b], 4 * n, hs)
+            synth.device_fill_zero(sb + lay.off_v[b], 4 * n, hs)
+
+    init_state()
+    for r in range(n_sets):
+        gb = int(grads[r].data_ptr())
+        for b, n in enumerate(sizes):
+            synth.device_fill_normal_bf16(gb + lay.off_grad[b], n, stream=sid, block=b,
+                                          purpose=synth.PURPOSE_GRAD, step=r + 1,
+                                          sigma=configs.GRAD_SIGMA, hip_stream=hs)
+    tables = []
+    for r in range(n_sets):
+        gb = int(grads[r].data_ptr())
+        rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
+                     grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], t=1,
+                     lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2, eps=configs.EPS)
+                for b, n in enumerate(sizes)]
+        tables.append(lso.BlockTable.from_rows(rows))
+    # Upload every table once outside the timed region: an lr = 0 step
+    # leaves the weights bit-exact; the moments are re-zeroed afterwards.
+    for tab in tables:
+        tab.arr["lr"] = 0.0
+        lso.adam_step(tab, hs)
+        tab.arr["lr"] = configs.LR
+    init_state()
+    torch.cuda.synchronize()
+    progress("inputs resident; warming up")
+
+    def step(j):          # j = 1-based global step; grads of set (j-1) % n_sets
+        tab = tables[(j - 1) % n_sets]
+        tab.set_step(j)
+        lso.adam_step(tab, hs)
+
+    for j in range(1, args.warmup + 1):
+        step(j)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        step(args.warmup + 1 + k)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(kernel_ms) / len(kernel_ms)
+    achieved = BYTES_PER_PARAM * params / (avg_ms * 1e-3) / 1e9
+    ceiling = copy_ceiling(torch, dev)
+    progress(f"steps: wall {wall * 1e3:.3f} ms for {args.steps}; kernel avg {avg_ms * 1e3:.1f} us; "
+             f"{achieved:.0f} GB/s; copy ceiling {ceiling:.0f} GB/s")
+    traffic = measured_traffic(w.key)
+    result = dict(
+        metric=METRIC, value=params * args.steps / wall / 1e9, unit="Gparams/s",
+        ms_per_step=wall * 1e3 / args.steps,
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBPS, traffic=traffic),
+        kernel_avg_us=avg_ms * 1e3, kernel_min_us=min(kernel_ms) * 1e3,
+        hbm_copy_ceiling_GBps=ceiling,
+        config=dict(workload=f"{w.key}: {w.title}", blocks=len(sizes), params=params,
+                    bytes_per_param=BYTES_PER_PARAM, gradient_sets=n_sets,
+                    hyper=dict(lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2,
+                               eps=configs.EPS)),
+    )
+    del state, weight, grads
+    return result
+
+
+def copy_ceiling(torch, dev, nbytes=8 << 30) -> float:
+    """GB/s (read + write) of a plain device copy: the measured HBM ceiling
+    for a 1:1 read/write stream."""
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    hs = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert P.lso_probe_copy(a.data_ptr(), b.data_ptr(), nbytes, 0, hs) == 0
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    reps = 5
+    for _ in range(reps):
+        assert P.lso_probe_copy(a.data_ptr(), b.data_ptr(), nbytes, 0, hs) == 0
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------ streamed path
+
+def link_peak(torch, nbytes=4 << 30):
+    """Host-link GB/s with pinned buffers: H2D alone, D2H alone, and each
+    direction while both run concurrently on two streams."""
+    import layer_streamed_optimizer_amd as lso
+    h1, h2 = lso.host_alloc(nbytes), lso.host_alloc(nbytes)
+    d1 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn, reps=3):
+        best = 1e30
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            best = min(best, time.perf_counter() - t0)
+        return best
+
+    h2d = lambda: hip.hipMemcpyAsync(d1.data_ptr(), h1.ptr, nbytes, 1, s1.cuda_stream)
+    d2h = lambda: hip.hipMemcpyAsync(h2.ptr, d2.data_ptr(), nbytes, 2, s2.cuda_stream)
+    t_h2d = timed(h2d)
+    t_d2h = timed(d2h)
+    t_both = timed(lambda: (h2d(), d2h()))
+    del d1, d2
+    h1.close()
+    h2.close()
+    return dict(h2d=nbytes / t_h2d / 1e9, d2h=nbytes / t_d2h / 1e9,
+                bidir_each=nbytes / t_both / 1e9, bidir_total=2 * nbytes / t_both / 1e9)
+
+
+def streamed(args, w):
+    import numpy as np
+    import torch
+
+    import layer_streamed_optimizer_amd as lso
+    import synth
+    from layer_streamed_optimizer_amd import configs
+
+    torch.cuda.set_device(0)
+    sid = configs.STREAM_ID[w.key]
+    n_layers = len(w.blocks)
+    n = w.blocks[0].n
+    om, omm, ov, nbytes = configs.host_layer_layout(n)
+    peak = link_peak(torch)
+    progress(f"link: {peak}")
+    progress(f"{w.key}: pinning {n_layers} x {nbytes / 1e9:.2f} GB host blocks")
+    hosts = []
+    hs = torch.cuda.current_stream().cuda_stream
+    stage = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for b in range(n_layers):
+        hb = lso.host_alloc(nbytes)
+        # initial state made on the device and copied down (untimed)
+        synth.device_fill_zero(int(stage.data_ptr()), nbytes, hs)
+        synth.device_fill_normal_f32(int(stage.data_ptr()) + om, n, stream=sid, block=b,
+                                     purpose=synth.PURPOSE_MASTER, step=0,
+                                     sigma=configs.MASTER_SIGMA, hip_stream=hs)
+        torch.cuda.synchronize()
+        ctypes.memmove(hb.ptr, 0, 0)  # touch nothing; keep the handle
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        assert hip.hipMemcpy(hb.ptr, int(stage.data_ptr()), nbytes, 2) == 0
+        hosts.append(hb)
+        progress(f"layer {b} ready")
+    del stage
+    fn, Params = synth.grad_callback()
+    prm = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
+                 scale=synth.scale_for(configs.GRAD_SIGMA), block_base=0)
+    ls = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
+    L = lso.LayerStream.layers(n_layers)
+    for b in range(n_layers):
+        L[b]["host_base"], L[b]["bytes"], L[b]["n"] = hosts[b].ptr, nbytes, n
+        L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
+        L[b]["opt"] = lso.LSO_OPT_ADAM
+        L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = (configs.LR, configs.BETA1,
+                                                                 configs.BETA2, configs.EPS)
+    step_s = []
+    for j in range(1, args.warmup + args.steps + 1):
+        prm.step = j
+        L["t"] = j
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ls.stream_layers(L)
+        dt = time.perf_counter() - t0
+        progress(f"step {j}: {dt:.3f} s")
+        if j > args.warmup:
+            step_s.append(dt)
+    ls.close()
+    wall = sum(step_s)
+    params = w.params
+    link_each = LINK_BYTES_PER_PARAM * params / (wall / len(step_s)) / 1e9
+    result = dict(
+        metric=METRIC, value=params * len(step_s) / wall / 1e9, unit="Gparams/s",
+        ms_per_step=wall * 1e3 / len(step_s),
+        roofline=dict(bound="host-link", achieved=link_each, peak=peak["bidir_each"],
+                      unit="GB/s per direction", frac=link_each / peak["bidir_each"], traffic=None),
+        link_peak_GBps=peak,
+        config=dict(workload=f"{w.key}: {w.title}", layers=n_layers, params=params,
+                    host_bytes=nbytes * n_layers, link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
+    )
+    for hb in hosts:
+        hb.close()
+    return result
+
+
+# -------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle as it stands, on the host's cores, on a bounded sample:
+    the first blocks of the workload (up to 64M params), repeated steps
+    until budget_s of CPU time has passed."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from layer_streamed_optimizer_amd import configs
+
+    sid = configs.STREAM_ID[w.key]
+    take, blocks = 0, []
+    for b, spec in enumerate(w.blocks):
+        if take >= (64 << 20):
+            break
+        n = min(spec.n, (64 << 20) - take)
+        blocks.append((b, n))
+        take += n
+    arrays = []
+    for b, n in blocks:
+        master = synth.normal_f32(n, stream=sid, block=b, purpose=0, step=0, sigma=0.02)
+        g = synth.normal_bf16(n, stream=sid, block=b, purpose=2, step=1, sigma=1e-3)
+        arrays.append((master, np.zeros(n, np.float32), np.zeros(n, np.float32), g,
+                       np.zeros(n, np.uint16)))
+    steps, threads = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        steps += 1
+        for master, m, v, g, wb in arrays:
+            threads = oracle.adam_step(master, m, v, g, wb, steps, 1e-3, 0.9, 0.999, 1e-8)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=take * steps / dt / 1e9, unit="Gparams/s", cores=threads, kind="oracle",
+                sample=f"first {take:,} params of {w.key} ({len(blocks)} block(s)), {steps} steps, "
+                       f"{dt:.1f} s, inputs in host RAM")
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the update is elementwise and would shard by "
+              "contiguous 1/N ranges with no exchange inside the step; multi-GPU runs are not "
+              "part of this build.", file=sys.stderr)
+        sys.exit(2)
+    from layer_streamed_optimizer_amd import configs
+    w = configs.get(args.config)
+    defaults = {"c0": (3, 10), "c1": (2, 10), "c2": (5, 100), "c3": (1, 4), "c4": (1, 2)}
+    dw, dk = defaults[args.config]
+    args.warmup = dw if args.warmup is None else args.warmup
+    args.steps = dk if args.steps is None else args.steps
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+    res = streamed(args, w) if w.streamed else resident(args, w)
+    out = dict(metric=res.pop("metric"), value=res.pop("value"), unit=res.pop("unit"), n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=res.pop("ms_per_step"),
+               higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+               data="synthetic", config=res.pop("config"), roofline=res.pop("roofline"))
+    if not args.no_cpu_baseline:
+        progress("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(w)
+    out.update(res)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * lso.h -- C ABI of the layer-streamed mixed-precision Adam library (gfx950).
+ *
+ * One operation, two ways of feeding it:
+ *   lso_adam_step      updates blocks that already live in device memory
+ *                      (HBM-resident state), one kernel launch per call;
+ *   lso_stream_layers  updates layers whose authoritative state lives in
+ *                      pinned host memory, streaming each layer in, updating
+ *                      it on the GPU and writing it back, double-buffered.
+ *
+ * The update, per element i of a block (all arithmetic below is what the
+ * library computes; the pages define it in exact arithmetic):
+ *   g      = BF16 gradient widened to FP32 (exact)
+ *   m'     = beta1*m + (1-beta1)*g
+ *   v'     = beta2*v + (1-beta2)*g^2
+ *   delta  = -lr * (m'/(1-beta1^t)) / (sqrt(v'/(1-beta2^t)) + eps)
+ *   master'= master + delta            (the additive write-back, W += delta)
+ *   w      = BF16 round-to-nearest-even of master'
+ * Sources: "Training 70B Models on Consumer Hardware (If You're Willing to
+ * Wait)" (bombadil.systems), section "The Math" for the moments, the bias
+ * correction with a global step t and the additive form of the update;
+ * section "The Assumption Everyone Makes" for the SGD rewrite
+ * W + (-lr*g) used by LSO_OPT_SGD; the Cloudera community training-memory
+ * article, line item "Optimizer states", for the FP32 master copy that is
+ * updated and cast back down; the MegaTrain summary on blog.hotdry.top for
+ * BF16 weights/gradients with FP32 moments (section on the memory
+ * bottleneck), layer-contiguous 4 KB-aligned host blocks, double buffering
+ * and three streams joined by weights-ready / backward-done / buffer-free
+ * events (section on streaming execution and the double-buffered pipeline).
+ *
+ * Precision: the per-block constants 1-beta, lr/(1-beta1^t),
+ * 1/sqrt(1-beta2^t) are computed in FP64 on the host and rounded once to
+ * FP32; the per-element arithmetic is FP32 with correctly rounded sqrt and
+ * division.  Results match an FP64 evaluation to ~1e-6 relative after 10
+ * steps; the BF16 weight is always exactly bf16_rne(master').
+ *
+ * Conventions for every call:
+ *  - Return value: an lso_status.  Nothing throws across the ABI.  On an
+ *    error, lso_last_error() returns a message for the calling thread.
+ *  - Validation errors are detected before anything is enqueued; memory is
+ *    then untouched.
+ *  - Device faults from earlier asynchronous work surface as LSO_E_HIP from
+ *    the next call that synchronises.
+ *  - Streams are hipStream_t values passed as void* (NULL = the default
+ *    stream of the current device).  All streams the library creates have
+ *    the default priority.
+ */
+#ifndef LSO_H
+#define LSO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lso_status {
+    LSO_OK = 0,
+    LSO_E_INVALID = 1,   /* bad argument: NULL, n, t, hyper-parameters, sizes */
+    LSO_E_ALIGN = 2,     /* an array is not 16-byte aligned */
+    LSO_E_DTYPE = 3,     /* unsupported dtype / optimizer combination */
+    LSO_E_OVERLAP = 4,   /* a written array overlaps another array of the call */
+    LSO_E_NOMEM = 5,     /* device or pinned host allocation failed */
+    LSO_E_HIP = 6,       /* a HIP runtime call failed */
+    LSO_E_CALLBACK = 7   /* the gradient producer of lso_stream_layers failed */
+} lso_status;
+
+typedef enum lso_dtype { LSO_DT_NONE = 0, LSO_DT_F32 = 1, LSO_DT_BF16 = 2 } lso_dtype;
+typedef enum lso_opt { LSO_OPT_ADAM = 0, LSO_OPT_SGD = 1 } lso_opt;
+
+/*
+ * One block: a layer, or any tensor, whose arrays are updated together.
+ * The address of each array is (uintptr_t)base + off_*; base may be NULL
+ * with absolute addresses in the offsets.  Layout: planar, element i of
+ * every array belongs to parameter i.
+ *   master  FP32, read and written           (always)
+ *   m, v    FP32, read and written           (LSO_OPT_ADAM; ignored for SGD)
+ *   grad    BF16, read                       (grad_dtype must be LSO_DT_BF16)
+ *   weight  BF16, written                    (weight_dtype BF16; NONE skips it)
+ * Every used array must be 16-byte aligned.  No written array may overlap
+ * any other array of the same call (across blocks too); gradients may
+ * alias one another.  n == 0 makes the block a no-op.
+ * t is the step being applied (t >= 1; the first update is t = 1); the
+ * caller owns it and increments it per step -- it is the resume point of a
+ * checkpoint.  Per-block t lets blocks advance independently.
+ * lr finite; 0 <= beta1 < 1; 0 <= beta2 < 1; eps finite and >= 0 (Adam).
+ * For SGD only lr is used: master' = master + (-(fl32(lr) * g)), each
+ * operation rounded once in FP32.
+ */
+typedef struct lso_block {
+    void*    base;
+    uint64_t n;
+    uint64_t off_master;
+    uint64_t off_m;
+    uint64_t off_v;
+    uint64_t off_grad;
+    uint64_t off_weight;
+    uint32_t grad_dtype;     /* lso_dtype */
+    uint32_t weight_dtype;   /* lso_dtype */
+    uint32_t opt;            /* lso_opt */
+    uint32_t reserved;       /* must be 0 */
+    uint64_t t;
+    double   lr, beta1, beta2, eps;
+} lso_block;
+
+/*
+ * lso_adam_step: one update of n device-resident blocks, enqueued on
+ * stream as ONE kernel launch (a ragged multi-tensor launch: hundreds of
+ * small tensors cost one launch).  More than 16 distinct
+ * (opt, t, lr, beta1, beta2, eps) sets in one call split it into one launch
+ * per 16 sets.
+ * blocks: host array, read before return; the caller may reuse it at once.
+ * Arrays: device memory owned by the caller; they must stay untouched until
+ * stream passes the step.  Asynchronous: returns after enqueueing.
+ * n == 0 is a no-op.  Errors: INVALID, ALIGN, DTYPE, OVERLAP (nothing
+ * enqueued), NOMEM, HIP.
+ */
+lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream);
+
+/*
+ * Host-only helpers (no device work, callable without a GPU).
+ * lso_validate_blocks: the checks lso_adam_step runs, without enqueueing.
+ * lso_block_constants: the FP32 constants the kernel uses for one block,
+ *   out[0..7] = {beta1, 1-beta1, beta2, 1-beta2, lr/(1-beta1^t),
+ *                1/sqrt(1-beta2^t), eps, 0}, each computed in FP64 and
+ *   rounded once (SGD: {0,0,0,0, lr, 0, 0, 0}).
+ */
+lso_status lso_validate_blocks(const lso_block* blocks, size_t n);
+lso_status lso_block_constants(const lso_block* block, float out[8]);
+
+/* ---------------------------------------------------------------------
+ * Layer streaming.  The authoritative state of each layer lives in pinned
+ * host memory as one contiguous block [master | m | v] (FP32, each
+ * sub-array 4 KB aligned inside the block).  For each layer the library
+ * copies the block into a device slot (one DMA burst), lets the caller's
+ * gradient producer write that layer's BF16 gradients into the slot, runs
+ * the fused update on the slot, and copies the block back over the host
+ * copy -- so the host holds master + delta afterwards.  Two slots alternate
+ * (double buffering) on three streams: H2D waits buffer-free[slot], copies,
+ * records weights-ready[slot]; compute waits weights-ready, runs producer
+ * and update, records step-done[slot]; D2H waits step-done, copies back,
+ * records buffer-free[slot].  No host barrier inside the layer loop.
+ * ------------------------------------------------------------------- */
+
+typedef struct lso_host_layer {
+    void*    host_base;      /* pinned host block (lso_host_alloc), 4 KB aligned */
+    uint64_t bytes;          /* bytes copied each way: covers all three arrays */
+    uint64_t n;              /* parameters in the layer */
+    uint64_t off_master;     /* byte offsets inside the block, 16-byte aligned */
+    uint64_t off_m;
+    uint64_t off_v;
+    void*    dev_weight;     /* device BF16 output for the re-cast weight, or
+                                NULL: it then stays in the slot's own buffer
+                                until the slot is reused */
+    uint32_t opt;            /* lso_opt (SGD: m and v are not touched) */
+    uint32_t reserved;       /* must be 0 */
+    uint64_t t;
+    double   lr, beta1, beta2, eps;
+} lso_host_layer;
+
+/* Gradient producer: enqueue (never synchronise) work on compute_stream
+ * that writes n BF16 gradients of layer `layer` into dev_grad_bf16.  A
+ * nonzero return stops the stream (lso_stream_layers returns
+ * LSO_E_CALLBACK). */
+typedef int (*lso_grad_fn)(void* user, size_t layer, void* dev_grad_bf16, uint64_t n,
+                           void* compute_stream);
+
+typedef struct lso_stream_ctx lso_stream_ctx;
+
+/* Create a streaming context on `device`: three streams, two device slots
+ * of max_layer_bytes of state plus max_layer_params BF16 gradients and
+ * BF16 weights each, and the events.  fn/user: the gradient producer.
+ * Errors: INVALID, NOMEM, HIP.  *out is NULL on error. */
+lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params,
+                             lso_grad_fn fn, void* user, int device, lso_stream_ctx** out);
+
+/* Stream n_layers layers through the pipeline, in order.  Synchronous with
+ * respect to host memory: on LSO_OK every host block holds its updated
+ * state.  On LSO_E_CALLBACK at layer k, layers < k are fully written back
+ * and layers >= k are untouched on the host.  Validation (bytes, alignment,
+ * hyper-parameters) covers all layers before anything is enqueued. */
+lso_status lso_stream_layers(lso_stream_ctx* ctx, const lso_host_layer* host_blocks,
+                             size_t n_layers);
+
+/* Device address of slot s's BF16 weight buffer (s = layer index % 2 of
+ * the most recent lso_stream_layers call), or NULL. */
+void* lso_stream_slot_weight(lso_stream_ctx* ctx, int slot);
+
+/* Waits for outstanding work, frees slots, events and streams. */
+lso_status lso_stream_destroy(lso_stream_ctx* ctx);
+
+/* Pinned host memory for layer blocks (page aligned, so 4 KB aligned).
+ * Errors: INVALID (bytes == 0 or out NULL), NOMEM. */
+lso_status lso_host_alloc(uint64_t bytes, void** out);
+lso_status lso_host_free(void* p);
+
+/* Static text of a status, and the detail of the calling thread's last
+ * error ("" if none). */
+const char* lso_status_string(lso_status s);
+const char* lso_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSO_H */

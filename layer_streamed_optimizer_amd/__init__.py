@@ -1,0 +1,207 @@
+"""Per-layer mixed-precision Adam on MI355X (gfx950), HBM-resident or
+layer-streamed from pinned host memory.
+
+A thin binding over liblso.so (include/lso.h): it marshals descriptor tables
+and stream handles; every step of the update runs in the HIP library.
+PyTorch, where used, only provides device memory and streams.
+
+    table = BlockTable.from_arrays([...])     # one row per block
+    table.set_step(t)                         # the caller owns t
+    adam_step(table, stream)                  # one kernel launch
+
+    ls = LayerStream(max_layer_bytes, max_layer_params, grad_fn, user)
+    ls.stream_layers(host_layers)             # H2D / update / D2H, double-buffered
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Iterable
+
+import numpy as np
+
+from . import _native
+from ._native import (LSO_DT_BF16, LSO_DT_F32, LSO_DT_NONE, LSO_OPT_ADAM, LSO_OPT_SGD, LsoBlock,
+                      LsoError, LsoHostLayer)
+
+BLOCK_DTYPE = np.dtype(LsoBlock)
+HOST_LAYER_DTYPE = np.dtype(LsoHostLayer)
+
+__all__ = ["BlockTable", "adam_step", "validate", "block_constants", "LayerStream", "HostBuffer",
+           "host_alloc", "LsoError", "LSO_OPT_ADAM", "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE",
+           "LSO_DT_F32", "BLOCK_DTYPE", "HOST_LAYER_DTYPE", "stream_handle"]
+
+
+def stream_handle(stream=None) -> int:
+    """hipStream_t of a torch stream, an int handle, or torch's current stream."""
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+class BlockTable:
+    """A reusable lso_block table (numpy structured array in the C layout)."""
+
+    def __init__(self, n: int):
+        self.arr = np.zeros(n, BLOCK_DTYPE)
+
+    def __len__(self) -> int:
+        return len(self.arr)
+
+    @classmethod
+    def from_rows(cls, rows: Iterable[dict]) -> "BlockTable":
+        rows = list(rows)
+        tab = cls(len(rows))
+        for i, r in enumerate(rows):
+            tab.set_row(i, **r)
+        return tab
+
+    def set_row(self, i: int, *, n: int, master, grad, m=None, v=None, weight=None, t: int = 1,
+                lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                opt: int = LSO_OPT_ADAM, base: int = 0) -> None:
+        """Arrays are torch tensors (their data_ptr) or integer device
+        addresses; with base != 0 the integers are offsets from base."""
+        row = self.arr[i]
+        row["base"] = base
+        row["n"] = n
+        row["off_master"] = _addr(master)
+        row["off_m"] = _addr(m)
+        row["off_v"] = _addr(v)
+        row["off_grad"] = _addr(grad)
+        row["off_weight"] = _addr(weight)
+        row["grad_dtype"] = LSO_DT_BF16
+        row["weight_dtype"] = LSO_DT_BF16 if weight is not None else LSO_DT_NONE
+        row["opt"] = opt
+        row["reserved"] = 0
+        row["t"] = t
+        row["lr"], row["beta1"], row["beta2"], row["eps"] = lr, beta1, beta2, eps
+
+    def set_step(self, t: int) -> None:
+        self.arr["t"] = t
+
+    @property
+    def ptr(self) -> int:
+        return self.arr.ctypes.data
+
+
+def adam_step(table: BlockTable, stream=None) -> None:
+    """One fused update of every block in the table, enqueued on stream
+    (one kernel launch).  Asynchronous."""
+    st = _native.lib().lso_adam_step(table.ptr, len(table), stream_handle(stream))
+    _native.check(st, "lso_adam_step")
+
+
+def validate(table: BlockTable) -> int:
+    """The host-side checks of lso_adam_step; returns the status (0 = ok)."""
+    return _native.lib().lso_validate_blocks(table.ptr, len(table))
+
+
+def last_error() -> str:
+    return _native.lib().lso_last_error().decode(errors="replace")
+
+
+def block_constants(*, t: int, lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
+                    eps: float = 1e-8, opt: int = LSO_OPT_ADAM) -> np.ndarray:
+    """The FP32 constants the kernel uses for one block (host computation)."""
+    b = LsoBlock()
+    b.n, b.grad_dtype, b.weight_dtype, b.opt, b.t = 1, LSO_DT_BF16, LSO_DT_NONE, opt, t
+    b.lr, b.beta1, b.beta2, b.eps = lr, beta1, beta2, eps
+    out = (ctypes.c_float * 8)()
+    _native.check(_native.lib().lso_block_constants(ctypes.byref(b), out), "lso_block_constants")
+    return np.array(out, dtype=np.float32)
+
+
+class HostBuffer:
+    """Pinned host memory from lso_host_alloc (page aligned)."""
+
+    def __init__(self, nbytes: int):
+        p = ctypes.c_void_p()
+        _native.check(_native.lib().lso_host_alloc(nbytes, ctypes.byref(p)), "lso_host_alloc")
+        self.ptr = int(p.value)
+        self.nbytes = nbytes
+        self._closed = False
+
+    def view(self, dtype=np.uint8, offset: int = 0, count: int | None = None) -> np.ndarray:
+        dt = np.dtype(dtype)
+        if count is None:
+            count = (self.nbytes - offset) // dt.itemsize
+        if offset + count * dt.itemsize > self.nbytes:
+            raise ValueError("view past the end of the buffer")
+        raw = (ctypes.c_char * (count * dt.itemsize)).from_address(self.ptr + offset)
+        return np.frombuffer(raw, dtype=dt, count=count)
+
+    def close(self) -> None:
+        if not self._closed:
+            _native.check(_native.lib().lso_host_free(self.ptr), "lso_host_free")
+            self._closed = True
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def host_alloc(nbytes: int) -> HostBuffer:
+    return HostBuffer(nbytes)
+
+
+class LayerStream:
+    """lso_stream_create / lso_stream_layers / lso_stream_destroy.
+
+    grad_fn: a C function pointer (int) with the lso_grad_fn signature, or a
+    Python callable (layer, dev_grad_ptr, n, stream_handle) -> int that only
+    enqueues work on the given stream."""
+
+    def __init__(self, max_layer_bytes: int, max_layer_params: int, grad_fn, user: int = 0,
+                 device: int = 0):
+        if callable(grad_fn):
+            py = grad_fn
+            self._cb = _native.GRAD_FN(lambda u, layer, g, n, s: int(py(layer, g, n, s)))
+            fn_ptr = ctypes.cast(self._cb, ctypes.c_void_p).value
+        else:
+            self._cb = None
+            fn_ptr = int(grad_fn)
+        self._user = user
+        ctx = ctypes.c_void_p()
+        st = _native.lib().lso_stream_create(max_layer_bytes, max_layer_params, fn_ptr, user,
+                                              device, ctypes.byref(ctx))
+        _native.check(st, "lso_stream_create")
+        self.ctx = int(ctx.value)
+
+    @staticmethod
+    def layers(n: int) -> np.ndarray:
+        return np.zeros(n, HOST_LAYER_DTYPE)
+
+    def stream_layers(self, host_layers: np.ndarray) -> None:
+        if host_layers.dtype != HOST_LAYER_DTYPE or not host_layers.flags.c_contiguous:
+            raise TypeError("host_layers must be a contiguous HOST_LAYER_DTYPE array")
+        st = _native.lib().lso_stream_layers(self.ctx, host_layers.ctypes.data, len(host_layers))
+        _native.check(st, "lso_stream_layers")
+
+    def stream_layers_status(self, host_layers: np.ndarray) -> int:
+        return _native.lib().lso_stream_layers(self.ctx, host_layers.ctypes.data, len(host_layers))
+
+    def slot_weight(self, slot: int) -> int:
+        return int(_native.lib().lso_stream_slot_weight(self.ctx, slot) or 0)
+
+    def close(self) -> None:
+        if self.ctx:
+            _native.lib().lso_stream_destroy(self.ctx)
+            self.ctx = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,132 @@
+"""ctypes view of include/lso.h (argument marshalling only).
+
+Every step of the update runs in liblso.so.  If the library is missing the
+import still works (so host-side code can be inspected), but every call
+raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+LSO_OK, LSO_E_INVALID, LSO_E_ALIGN, LSO_E_DTYPE, LSO_E_OVERLAP = 0, 1, 2, 3, 4
+LSO_E_NOMEM, LSO_E_HIP, LSO_E_CALLBACK = 5, 6, 7
+LSO_DT_NONE, LSO_DT_F32, LSO_DT_BF16 = 0, 1, 2
+LSO_OPT_ADAM, LSO_OPT_SGD = 0, 1
+
+STATUS_NAMES = {0: "LSO_OK", 1: "LSO_E_INVALID", 2: "LSO_E_ALIGN", 3: "LSO_E_DTYPE",
+                4: "LSO_E_OVERLAP", 5: "LSO_E_NOMEM", 6: "LSO_E_HIP", 7: "LSO_E_CALLBACK"}
+
+
+class LsoBlock(ctypes.Structure):
+    _fields_ = [
+        ("base", ctypes.c_void_p),
+        ("n", ctypes.c_uint64),
+        ("off_master", ctypes.c_uint64),
+        ("off_m", ctypes.c_uint64),
+        ("off_v", ctypes.c_uint64),
+        ("off_grad", ctypes.c_uint64),
+        ("off_weight", ctypes.c_uint64),
+        ("grad_dtype", ctypes.c_uint32),
+        ("weight_dtype", ctypes.c_uint32),
+        ("opt", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("t", ctypes.c_uint64),
+        ("lr", ctypes.c_double),
+        ("beta1", ctypes.c_double),
+        ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double),
+    ]
+
+
+class LsoHostLayer(ctypes.Structure):
+    _fields_ = [
+        ("host_base", ctypes.c_void_p),
+        ("bytes", ctypes.c_uint64),
+        ("n", ctypes.c_uint64),
+        ("off_master", ctypes.c_uint64),
+        ("off_m", ctypes.c_uint64),
+        ("off_v", ctypes.c_uint64),
+        ("dev_weight", ctypes.c_void_p),
+        ("opt", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("t", ctypes.c_uint64),
+        ("lr", ctypes.c_double),
+        ("beta1", ctypes.c_double),
+        ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double),
+    ]
+
+
+GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                           ctypes.c_uint64, ctypes.c_void_p)
+
+# every symbol include/lso.h declares
+EXPORTS = ("lso_adam_step", "lso_validate_blocks", "lso_block_constants", "lso_stream_create",
+           "lso_stream_layers", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc",
+           "lso_host_free", "lso_status_string", "lso_last_error")
+
+_lib = None
+_probes = None
+
+
+class LsoError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {detail}")
+
+
+def lib():
+    """The loaded liblso.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        path = _build.lib_path("liblso.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "(no CPU fallback exists)")
+        L = ctypes.CDLL(path)
+        vp, sz, u64, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint64, ctypes.c_int
+        L.lso_adam_step.argtypes = [vp, sz, vp]
+        L.lso_validate_blocks.argtypes = [vp, sz]
+        L.lso_block_constants.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
+        L.lso_stream_create.argtypes = [u64, u64, vp, vp, i32, ctypes.POINTER(vp)]
+        L.lso_stream_layers.argtypes = [vp, vp, sz]
+        L.lso_stream_slot_weight.argtypes = [vp, i32]
+        L.lso_stream_slot_weight.restype = vp
+        L.lso_stream_destroy.argtypes = [vp]
+        L.lso_host_alloc.argtypes = [u64, ctypes.POINTER(vp)]
+        L.lso_host_free.argtypes = [vp]
+        L.lso_status_string.argtypes = [i32]
+        L.lso_status_string.restype = ctypes.c_char_p
+        L.lso_last_error.argtypes = []
+        L.lso_last_error.restype = ctypes.c_char_p
+        for name in ("lso_adam_step", "lso_validate_blocks", "lso_block_constants",
+                     "lso_stream_create", "lso_stream_layers", "lso_stream_destroy",
+                     "lso_host_alloc", "lso_host_free"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def probes():
+    global _probes
+    if _probes is None:
+        path = _build.lib_path("liblso_probes.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        P = ctypes.CDLL(path)
+        vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
+        P.lso_probe_copy.argtypes = [vp, vp, u64, ctypes.c_uint, vp]
+        P.lso_probe_copy.restype = ctypes.c_int
+        P.lso_probe_bf16_rne.argtypes = [u32, u64, vp, vp]
+        P.lso_probe_bf16_rne.restype = ctypes.c_int
+        _probes = P
+    return _probes
+
+
+def check(status: int, where: str) -> None:
+    if status != LSO_OK:
+        detail = lib().lso_last_error().decode(errors="replace")
+        raise LsoError(status, where, detail)

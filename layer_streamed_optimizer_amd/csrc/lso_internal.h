@@ -1,0 +1,66 @@
+// Internal types shared by the host runtime and the fused kernel.
+#pragma once
+
+#include <cstdint>
+
+#include "lso.h"
+
+namespace lso {
+
+// Work decomposition of the fused kernel.  A workgroup of kThreads lanes
+// handles one chunk of kChunk consecutive elements of one block per
+// iteration; each lane owns kUnroll groups of kVec consecutive elements
+// (one 16-byte BF16 vector, two 16-byte FP32 vectors per state array).
+constexpr int kThreads = 256;
+constexpr int kVec = 8;
+constexpr int kUnroll = 2;
+constexpr uint64_t kChunk = static_cast<uint64_t>(kThreads) * kVec * kUnroll;
+
+// At most this many distinct constant sets travel by value in one launch.
+constexpr int kMaxGroups = 16;
+
+enum : uint32_t { kFlagSgd = 1u, kFlagWeight = 2u };
+
+// One block as the kernel sees it (64 bytes, lives in a device table).
+struct DevBlock {
+    float* master;
+    float* m;
+    float* v;
+    const uint16_t* g;
+    uint16_t* w;
+    uint64_t n;
+    uint64_t chunk0;     // first global chunk index of this block
+    uint32_t group;      // index into KernelArgs::coef
+    uint32_t flags;      // kFlagSgd | kFlagWeight
+};
+static_assert(sizeof(DevBlock) == 64, "DevBlock layout");
+
+// FP32 constants of one (opt, t, lr, beta1, beta2, eps) set.
+struct Coef {
+    float b1, c1, b2, c2;   // beta1, 1-beta1, beta2, 1-beta2
+    float s;                // Adam: lr/(1-beta1^t); SGD: lr
+    float r;                // 1/sqrt(1-beta2^t)
+    float e;                // eps
+    float pad;
+};
+static_assert(sizeof(Coef) == 32, "Coef layout");
+
+// Up to this many blocks travel by value in the kernel arguments (no
+// device table, no upload, no dependent table load).
+constexpr int kInline = 4;
+
+struct KernelArgs {
+    const DevBlock* blocks;   // device table, or nullptr: use inl[]
+    uint64_t total_chunks;
+    uint32_t nblocks;
+    uint32_t pad;
+    Coef coef[kMaxGroups];
+    DevBlock inl[kInline];
+};
+
+// Enqueue the fused kernel (defined in lso_adam.hip).  grid == 0 picks the
+// default grid for the work.  Returns the hipError_t of the launch as int.
+int launch_fused_adam(const KernelArgs& args, unsigned grid, void* stream);
+unsigned default_grid(uint64_t total_chunks);
+
+}  // namespace lso

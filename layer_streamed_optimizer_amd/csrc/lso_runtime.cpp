@@ -1,0 +1,443 @@
+// Host runtime of the C ABI: validation, FP64 -> FP32 constants, the
+// multi-tensor launch plan, the device-table cache and lso_adam_step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "lso_internal.h"
+#include "lso_runtime.h"
+
+namespace lso {
+
+// ------------------------------------------------------------------ errors
+
+static thread_local char t_last_error[512] = "";
+
+lso_status fail(lso_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(t_last_error, sizeof t_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+void clear_error() { t_last_error[0] = '\0'; }
+
+lso_status hip_fail(int err, const char* what)
+{
+    return fail(LSO_E_HIP, "%s: %s", what, hipGetErrorString(static_cast<hipError_t>(err)));
+}
+
+// ------------------------------------------------------------- validation
+// Field checks (dtypes, optimizer, hyper-parameters) run on every call;
+// address checks (NULL, alignment, overlap) run when a block table is new.
+
+lso_status check_hyper(uint32_t opt, uint64_t t, double lr, double beta1, double beta2, double eps,
+                       size_t index)
+{
+    if (opt != LSO_OPT_ADAM && opt != LSO_OPT_SGD)
+        return fail(LSO_E_DTYPE, "block %zu: unknown optimizer %u", index, opt);
+    if (!std::isfinite(lr)) return fail(LSO_E_INVALID, "block %zu: lr is not finite", index);
+    if (opt == LSO_OPT_SGD) return LSO_OK;
+    if (t < 1) return fail(LSO_E_INVALID, "block %zu: t must be >= 1 (got %llu)", index,
+                           static_cast<unsigned long long>(t));
+    if (!(beta1 >= 0.0 && beta1 < 1.0))
+        return fail(LSO_E_INVALID, "block %zu: beta1 must be in [0, 1)", index);
+    if (!(beta2 >= 0.0 && beta2 < 1.0))
+        return fail(LSO_E_INVALID, "block %zu: beta2 must be in [0, 1)", index);
+    if (!(std::isfinite(eps) && eps >= 0.0))
+        return fail(LSO_E_INVALID, "block %zu: eps must be finite and >= 0", index);
+    return LSO_OK;
+}
+
+namespace {
+
+struct Interval {
+    uintptr_t lo, hi;   // [lo, hi)
+    bool written;
+    size_t block;
+};
+
+lso_status check_overlap(std::vector<Interval>& iv)
+{
+    std::sort(iv.begin(), iv.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
+    uintptr_t end_all = 0, end_written = 0;
+    size_t blk_all = 0, blk_written = 0;
+    for (const Interval& x : iv) {
+        if (x.lo < end_written)
+            return fail(LSO_E_OVERLAP, "block %zu: an array overlaps a written array of block %zu",
+                        x.block, blk_written);
+        if (x.written && x.lo < end_all)
+            return fail(LSO_E_OVERLAP, "block %zu: a written array overlaps an array of block %zu",
+                        x.block, blk_all);
+        if (x.hi > end_all) { end_all = x.hi; blk_all = x.block; }
+        if (x.written && x.hi > end_written) { end_written = x.hi; blk_written = x.block; }
+    }
+    return LSO_OK;
+}
+
+bool add_array(std::vector<Interval>& iv, uintptr_t addr, uint64_t bytes, bool written, size_t block)
+{
+    if (addr + bytes < addr) return false;   // wraps
+    iv.push_back({addr, addr + bytes, written, block});
+    return true;
+}
+
+}  // namespace
+
+lso_status validate_geometry(const lso_block* blocks, size_t n)
+{
+    std::vector<Interval> iv;
+    iv.reserve(n * 5);
+    for (size_t i = 0; i < n; ++i) {
+        const lso_block& b = blocks[i];
+        if (b.n == 0) continue;
+        if (b.n > (UINT64_MAX / 8)) return fail(LSO_E_INVALID, "block %zu: n too large", i);
+        const uintptr_t base = reinterpret_cast<uintptr_t>(b.base);
+        const bool adam = b.opt == LSO_OPT_ADAM;
+        struct A { uint64_t off; uint64_t esize; bool used; bool written; const char* name; } arr[5] = {
+            {b.off_master, 4, true, true, "master"},
+            {b.off_m, 4, adam, true, "m"},
+            {b.off_v, 4, adam, true, "v"},
+            {b.off_grad, 2, true, false, "grad"},
+            {b.off_weight, 2, b.weight_dtype == LSO_DT_BF16, true, "weight"},
+        };
+        for (const A& a : arr) {
+            if (!a.used) continue;
+            const uintptr_t addr = base + a.off;
+            if (addr == 0) return fail(LSO_E_INVALID, "block %zu: %s address is NULL", i, a.name);
+            if (addr % 16 != 0)
+                return fail(LSO_E_ALIGN, "block %zu: %s address %#llx is not 16-byte aligned", i, a.name,
+                            static_cast<unsigned long long>(addr));
+            if (!add_array(iv, addr, a.esize * b.n, a.written, i))
+                return fail(LSO_E_INVALID, "block %zu: %s range wraps the address space", i, a.name);
+        }
+    }
+    return check_overlap(iv);
+}
+
+lso_status check_fields(const lso_block& b, size_t i)
+{
+    if (b.reserved != 0) return fail(LSO_E_INVALID, "block %zu: reserved field must be 0", i);
+    if (b.grad_dtype != LSO_DT_BF16)
+        return fail(LSO_E_DTYPE, "block %zu: gradient dtype must be BF16", i);
+    if (b.weight_dtype != LSO_DT_BF16 && b.weight_dtype != LSO_DT_NONE)
+        return fail(LSO_E_DTYPE, "block %zu: weight dtype must be BF16 or NONE", i);
+    return check_hyper(b.opt, b.t, b.lr, b.beta1, b.beta2, b.eps, i);
+}
+
+lso_status validate_all(const lso_block* blocks, size_t n)
+{
+    if (n > 0 && !blocks) return fail(LSO_E_INVALID, "blocks is NULL");
+    for (size_t i = 0; i < n; ++i) {
+        lso_status s = check_fields(blocks[i], i);
+        if (s != LSO_OK) return s;
+    }
+    return validate_geometry(blocks, n);
+}
+
+// --------------------------------------------------------------- constants
+
+Coef make_coef(uint32_t opt, uint64_t t, double lr, double beta1, double beta2, double eps)
+{
+    Coef c{};
+    if (opt == LSO_OPT_SGD) {
+        c.s = static_cast<float>(lr);
+        return c;
+    }
+    // Everything in FP64, rounded once to FP32: 1 - beta in FP32 would be
+    // off by ~1e-5 relative for beta2 = 0.999.
+    const double td = static_cast<double>(t);
+    c.b1 = static_cast<float>(beta1);
+    c.c1 = static_cast<float>(1.0 - beta1);
+    c.b2 = static_cast<float>(beta2);
+    c.c2 = static_cast<float>(1.0 - beta2);
+    c.s = static_cast<float>(lr / (1.0 - std::pow(beta1, td)));
+    c.r = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(beta2, td)));
+    c.e = static_cast<float>(eps);
+    return c;
+}
+
+// ------------------------------------------------------------------- plan
+
+namespace {
+
+struct HyperKey {
+    uint32_t opt;
+    uint64_t t;
+    double lr, beta1, beta2, eps;
+    bool operator==(const HyperKey& o) const
+    {
+        return opt == o.opt && t == o.t && lr == o.lr && beta1 == o.beta1 && beta2 == o.beta2 && eps == o.eps;
+    }
+};
+
+HyperKey key_of(const lso_block& b)
+{
+    if (b.opt == LSO_OPT_SGD) return {b.opt, 0, b.lr, 0, 0, 0};
+    return {b.opt, b.t, b.lr, b.beta1, b.beta2, b.eps};
+}
+
+// Device tables of more than kInline blocks, cached by content so a
+// training loop that passes the same blocks every step uploads its table
+// once.  Per device; at most kCacheCap entries, least recently used evicted
+// after a device synchronisation (the entry may still be read by queued
+// kernels on any stream).
+struct TableEntry {
+    std::vector<DevBlock> key;
+    DevBlock* dev = nullptr;
+    DevBlock* pinned = nullptr;
+    hipEvent_t ready = nullptr;
+    bool ready_seen = false;
+    void* upload_stream = nullptr;
+    uint64_t tick = 0;
+};
+
+constexpr size_t kCacheCap = 64;
+
+struct DeviceTables {
+    std::vector<TableEntry> entries;
+    uint64_t tick = 0;
+};
+
+std::mutex g_mu;
+std::unordered_map<int, DeviceTables> g_tables;
+
+void free_entry(TableEntry& e)
+{
+    if (e.dev) (void)hipFree(e.dev);
+    if (e.pinned) (void)hipHostFree(e.pinned);
+    if (e.ready) (void)hipEventDestroy(e.ready);
+    e = TableEntry{};
+}
+
+lso_status device_table(const std::vector<DevBlock>& tab, void* stream, const DevBlock** out)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceTables& dt = g_tables[dev];
+    ++dt.tick;
+    const size_t bytes = tab.size() * sizeof(DevBlock);
+    for (TableEntry& e : dt.entries) {
+        if (e.key.size() == tab.size() && std::memcmp(e.key.data(), tab.data(), bytes) == 0) {
+            e.tick = dt.tick;
+            if (!e.ready_seen) {
+                if (hipEventQuery(e.ready) == hipSuccess) {
+                    e.ready_seen = true;
+                } else if (stream != e.upload_stream) {
+                    err = hipStreamWaitEvent(static_cast<hipStream_t>(stream), e.ready, 0);
+                    if (err != hipSuccess) return hip_fail(err, "hipStreamWaitEvent");
+                }
+            }
+            *out = e.dev;
+            return LSO_OK;
+        }
+    }
+    if (dt.entries.size() >= kCacheCap) {
+        auto lru = std::min_element(dt.entries.begin(), dt.entries.end(),
+                                    [](const TableEntry& a, const TableEntry& b) { return a.tick < b.tick; });
+        err = hipDeviceSynchronize();
+        if (err != hipSuccess) return hip_fail(err, "hipDeviceSynchronize (table eviction)");
+        free_entry(*lru);
+        dt.entries.erase(lru);
+    }
+    TableEntry e;
+    e.key = tab;
+    e.tick = dt.tick;
+    e.upload_stream = stream;
+    if (hipMalloc(reinterpret_cast<void**>(&e.dev), bytes) != hipSuccess) {
+        free_entry(e);
+        return fail(LSO_E_NOMEM, "hipMalloc of a %zu-byte block table failed", bytes);
+    }
+    if (hipHostMalloc(reinterpret_cast<void**>(&e.pinned), bytes, hipHostMallocDefault) != hipSuccess) {
+        free_entry(e);
+        return fail(LSO_E_NOMEM, "hipHostMalloc of a %zu-byte block table failed", bytes);
+    }
+    std::memcpy(e.pinned, tab.data(), bytes);
+    err = hipEventCreateWithFlags(&e.ready, hipEventDisableTiming);
+    if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipEventCreateWithFlags"); }
+    err = hipMemcpyAsync(e.dev, e.pinned, bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipMemcpyAsync (block table)"); }
+    err = hipEventRecord(e.ready, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipEventRecord"); }
+    *out = e.dev;
+    dt.entries.push_back(std::move(e));
+    return LSO_OK;
+}
+
+}  // namespace
+
+lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked)
+{
+    if (n == 0) return LSO_OK;
+    if (!blocks) return fail(LSO_E_INVALID, "blocks is NULL");
+    for (size_t i = 0; i < n; ++i) {
+        lso_status s = check_fields(blocks[i], i);
+        if (s != LSO_OK) return s;
+    }
+    // distinct constant sets, in order of first appearance
+    std::vector<HyperKey> sets;
+    std::vector<uint32_t> set_of(n);
+    for (size_t i = 0; i < n; ++i) {
+        const HyperKey k = key_of(blocks[i]);
+        size_t j = 0;
+        while (j < sets.size() && !(sets[j] == k)) ++j;
+        if (j == sets.size()) sets.push_back(k);
+        set_of[i] = static_cast<uint32_t>(j);
+    }
+    const size_t launches = (sets.size() + kMaxGroups - 1) / kMaxGroups;
+    bool checked = geometry_checked;
+    for (size_t L = 0; L < launches; ++L) {
+        KernelArgs args{};
+        std::vector<DevBlock> tab;
+        uint64_t chunks = 0;
+        for (size_t i = 0; i < n; ++i) {
+            if (set_of[i] / kMaxGroups != L) continue;
+            const lso_block& b = blocks[i];
+            if (b.n == 0) continue;
+            const uintptr_t base = reinterpret_cast<uintptr_t>(b.base);
+            DevBlock d{};
+            d.master = reinterpret_cast<float*>(base + b.off_master);
+            if (b.opt == LSO_OPT_ADAM) {
+                d.m = reinterpret_cast<float*>(base + b.off_m);
+                d.v = reinterpret_cast<float*>(base + b.off_v);
+            }
+            d.g = reinterpret_cast<const uint16_t*>(base + b.off_grad);
+            d.w = b.weight_dtype == LSO_DT_BF16 ? reinterpret_cast<uint16_t*>(base + b.off_weight) : nullptr;
+            d.n = b.n;
+            d.chunk0 = chunks;
+            d.group = set_of[i] % kMaxGroups;
+            d.flags = (b.opt == LSO_OPT_SGD ? kFlagSgd : 0u) | (d.w ? kFlagWeight : 0u);
+            chunks += (b.n + kChunk - 1) / kChunk;
+            tab.push_back(d);
+        }
+        for (size_t j = L * kMaxGroups; j < sets.size() && j < (L + 1) * kMaxGroups; ++j) {
+            const HyperKey& k = sets[j];
+            args.coef[j % kMaxGroups] = make_coef(k.opt, k.t, k.lr, k.beta1, k.beta2, k.eps);
+        }
+        if (tab.empty()) continue;
+        args.total_chunks = chunks;
+        args.nblocks = static_cast<uint32_t>(tab.size());
+        if (tab.size() <= static_cast<size_t>(kInline)) {
+            if (!checked) {
+                lso_status s = validate_geometry(blocks, n);
+                if (s != LSO_OK) return s;
+                checked = true;
+            }
+            for (size_t j = 0; j < tab.size(); ++j) args.inl[j] = tab[j];
+            args.blocks = nullptr;
+        } else {
+            // a table seen before was validated when it entered the cache
+            const DevBlock* dev_tab = nullptr;
+            bool cached = false;
+            {
+                int dev = 0;
+                (void)hipGetDevice(&dev);
+                std::lock_guard<std::mutex> lock(g_mu);
+                auto it = g_tables.find(dev);
+                if (it != g_tables.end()) {
+                    const size_t bytes = tab.size() * sizeof(DevBlock);
+                    for (const TableEntry& e : it->second.entries)
+                        if (e.key.size() == tab.size() && std::memcmp(e.key.data(), tab.data(), bytes) == 0) {
+                            cached = true;
+                            break;
+                        }
+                }
+            }
+            if (!cached && !checked) {
+                lso_status s = validate_geometry(blocks, n);
+                if (s != LSO_OK) return s;
+                checked = true;
+            }
+            lso_status s = device_table(tab, stream, &dev_tab);
+            if (s != LSO_OK) return s;
+            args.blocks = dev_tab;
+        }
+        int err = launch_fused_adam(args, 0, stream);
+        if (err != 0) return hip_fail(err, "fused Adam launch");
+    }
+    return LSO_OK;
+}
+
+}  // namespace lso
+
+// ================================================================== C ABI
+
+extern "C" {
+
+lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream)
+{
+    lso::clear_error();
+    return lso::enqueue_update(blocks, n, stream, false);
+}
+
+lso_status lso_validate_blocks(const lso_block* blocks, size_t n)
+{
+    lso::clear_error();
+    return lso::validate_all(blocks, n);
+}
+
+lso_status lso_block_constants(const lso_block* block, float out[8])
+{
+    lso::clear_error();
+    if (!block || !out) return lso::fail(LSO_E_INVALID, "NULL argument");
+    lso_status s = lso::check_hyper(block->opt, block->t, block->lr, block->beta1, block->beta2,
+                                    block->eps, 0);
+    if (s != LSO_OK) return s;
+    const lso::Coef c = lso::make_coef(block->opt, block->t, block->lr, block->beta1, block->beta2,
+                                       block->eps);
+    const float v[8] = {c.b1, c.c1, c.b2, c.c2, c.s, c.r, c.e, 0.0f};
+    std::memcpy(out, v, sizeof v);
+    return LSO_OK;
+}
+
+lso_status lso_host_alloc(uint64_t bytes, void** out)
+{
+    lso::clear_error();
+    if (!out || bytes == 0) return lso::fail(LSO_E_INVALID, "bytes must be > 0 and out non-NULL");
+    *out = nullptr;
+    void* p = nullptr;
+    hipError_t err = hipHostMalloc(&p, bytes, hipHostMallocDefault);
+    if (err != hipSuccess || !p)
+        return lso::fail(LSO_E_NOMEM, "hipHostMalloc(%llu) failed: %s", static_cast<unsigned long long>(bytes),
+                         hipGetErrorString(err));
+    *out = p;
+    return LSO_OK;
+}
+
+lso_status lso_host_free(void* p)
+{
+    lso::clear_error();
+    if (!p) return LSO_OK;
+    hipError_t err = hipHostFree(p);
+    return err == hipSuccess ? LSO_OK : lso::hip_fail(err, "hipHostFree");
+}
+
+const char* lso_status_string(lso_status s)
+{
+    switch (s) {
+    case LSO_OK: return "ok";
+    case LSO_E_INVALID: return "invalid argument";
+    case LSO_E_ALIGN: return "misaligned array";
+    case LSO_E_DTYPE: return "unsupported dtype or optimizer";
+    case LSO_E_OVERLAP: return "overlapping arrays";
+    case LSO_E_NOMEM: return "out of memory";
+    case LSO_E_HIP: return "HIP runtime error";
+    case LSO_E_CALLBACK: return "gradient producer failed";
+    }
+    return "unknown status";
+}
+
+const char* lso_last_error(void) { return lso::t_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+"""Helpers for the GPU tests: device arenas with canary bands, transfers,
+and the parity measures.  Test infrastructure only."""
+from __future__ import annotations
+
+import ctypes
+import sys
+
+import numpy as np
+
+import layer_streamed_optimizer_amd as lso
+
+CANARY = 0xA5
+GUARD = 256
+
+
+def log(*a):
+    """Name the case before each GPU step (flushed, so a crash still shows it)."""
+    print("[gpu-test]", *a, file=sys.stderr, flush=True)
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def to_dev(a: np.ndarray):
+    t = torch()
+    a = np.ascontiguousarray(a)
+    return t.from_numpy(a.view(np.uint8).copy()).to("cuda")
+
+
+class Arena:
+    """Blocks' arrays in one device buffer, each array surrounded by canary
+    bytes (every byte of the buffer outside an array is CANARY)."""
+
+    def __init__(self, sizes, adam=True, weight=True, extra_align=0):
+        t = torch()
+        self.sizes = list(sizes)
+        self.adam, self.weight = adam, weight
+        self.off = []
+        pos = GUARD
+        names = ["master", "grad"] + (["m", "v"] if adam else []) + (["weight"] if weight else [])
+        self.names = names
+        for n in self.sizes:
+            d = {}
+            for name in names:
+                esize = 2 if name in ("grad", "weight") else 4
+                d[name] = pos + extra_align
+                pos += extra_align + esize * n
+                pos = (pos + GUARD - 1) // GUARD * GUARD + GUARD
+            self.off.append(d)
+        self.total = pos
+        self.buf = t.full((self.total,), CANARY, dtype=t.uint8, device="cuda")
+        self.base = int(self.buf.data_ptr())
+
+    def esize(self, name):
+        return 2 if name in ("grad", "weight") else 4
+
+    def put(self, i, name, arr):
+        t = torch()
+        n = self.sizes[i]
+        dt = np.uint16 if self.esize(name) == 2 else np.float32
+        a = np.ascontiguousarray(arr, dtype=dt)
+        assert a.size == n
+        o = self.off[i][name]
+        self.buf[o:o + a.nbytes].copy_(t.from_numpy(a.view(np.uint8).copy()))
+
+    def get(self, i, name):
+        n = self.sizes[i]
+        o = self.off[i][name]
+        es = self.esize(name)
+        raw = self.buf[o:o + es * n].cpu().numpy()
+        return raw.view(np.uint16 if es == 2 else np.float32).copy()
+
+    def addr(self, i, name):
+        return self.base + self.off[i][name]
+
+    def rows(self, t=1, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, opt=lso.LSO_OPT_ADAM):
+        out = []
+        for i, n in enumerate(self.sizes):
+            out.append(dict(n=n, master=self.addr(i, "master"), grad=self.addr(i, "grad"),
+                            m=self.addr(i, "m") if self.adam else None,
+                            v=self.addr(i, "v") if self.adam else None,
+                            weight=self.addr(i, "weight") if self.weight else None,
+                            t=t, lr=lr, beta1=beta1, beta2=beta2, eps=eps, opt=opt))
+        return out
+
+    def table(self, **kw):
+        return lso.BlockTable.from_rows(self.rows(**kw))
+
+    def canaries_intact(self) -> bool:
+        host = self.buf.cpu().numpy()
+        mask = np.ones(self.total, bool)
+        for i, n in enumerate(self.sizes):
+            for name, o in self.off[i].items():
+                mask[o:o + self.esize(name) * n] = False
+        return bool(np.all(host[mask] == CANARY))
+
+
+# ----------------------------------------------------------- parity measures
+
+def rms(x) -> float:
+    x = np.asarray(x, np.float64)
+    return float(np.sqrt(np.mean(x * x))) if x.size else 0.0
+
+
+def rel_err_rms_floor(got, ref, floor=None) -> float:
+    """max_i |got - ref| / max(|ref_i|, floor), floor = rms(ref) unless
+    given: relative error with an RMS floor, so a moment that cancels to ~0
+    (m is an exponential average of signed gradients) is judged at the scale
+    of its quantity rather than at its own vanishing magnitude.  Callers with
+    tiny blocks pass the RMS of the quantity over the whole call."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    if floor is None:
+        floor = rms(ref)
+    den = np.maximum(np.abs(ref), floor)
+    den[den == 0] = 1.0
+    return float(np.max(np.abs(got - ref) / den))
+
+
+def bf16_value(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+
+def bf16_ulp(ref_bits):
+    """Spacing of BF16 numbers at each reference value."""
+    v = np.abs(bf16_value(ref_bits)).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -133)))
+    return 2.0 ** (np.maximum(e, -126) - 7)
+
+
+def call_scale(refs: list) -> dict:
+    """RMS of each FP32 quantity over every block of a call."""
+    out = {}
+    for q in ("master", "m", "v"):
+        parts = [np.asarray(r[q], np.float64) for r in refs if q in r]
+        if parts:
+            out[q] = rms(np.concatenate(parts))
+    return out
+
+
+def assert_parity(got: dict, ref: dict, tol: float, what: str = "", scale: dict | None = None):
+    """FP32 state within tol (RMS-floored relative; scale gives the floors,
+    default the block's own RMS); BF16 weight within one BF16 ulp (or tol at
+    the master's RMS) and equal to the RNE of the GPU's own master bit for
+    bit."""
+    import oracle
+    for q in ("master", "m", "v"):
+        if q in got and q in ref:
+            fl = None if scale is None else max(scale.get(q, 0.0), rms(ref[q]))
+            e = rel_err_rms_floor(got[q], ref[q], fl)
+            assert e <= tol, f"{what}: {q} relative error {e:.3g} > {tol:g}"
+    if "weight" in got and "weight" in ref:
+        gw, rw = got["weight"], ref["weight"]
+        assert np.array_equal(gw, oracle.bf16_rne(got["master"])), f"{what}: w != bf16_rne(master)"
+        diff = np.abs(bf16_value(gw).astype(np.float64) - bf16_value(rw))
+        bound = np.maximum(bf16_ulp(rw), tol * rms(ref["master"]))
+        bad = diff > bound
+        assert not np.any(bad), f"{what}: {int(bad.sum())} BF16 weights beyond one ulp"
+
+
+def max_errors(got: dict, ref: dict, scale: dict | None = None) -> dict:
+    out = {q: rel_err_rms_floor(got[q], ref[q],
+                                None if scale is None else max(scale.get(q, 0.0), rms(ref[q])))
+           for q in ("master", "m", "v") if q in got and q in ref}
+    if "weight" in got and "weight" in ref:
+        d = np.abs(bf16_value(got["weight"]).astype(np.float64) - bf16_value(ref["weight"]))
+        out["weight_ulps"] = float(np.max(d / bf16_ulp(ref["weight"]))) if d.size else 0.0
+    return out
+
+
+# ----------------------------------------------------------------- raw HIP
+
+_hip = None
+
+
+def hip():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_void_p]
+        _hip.hipMemcpyAsync.restype = ctypes.c_int
+    return _hip
+
+
+HIP_D2D = 3

@@ -1,0 +1,401 @@
+"""GPU parity: the fused kernel against the oracle, element by element, on
+seeded inputs (host generator), through the C ABI.  Sizes span several
+chunks with ragged tails; tolerances are stated per test."""
+import numpy as np
+import pytest
+
+import layer_streamed_optimizer_amd as lso
+import oracle
+import synth
+from layer_streamed_optimizer_amd import configs
+
+from gpu_util import Arena, assert_parity, bf16_value, call_scale, log, max_errors, torch
+
+pytestmark = pytest.mark.gpu
+
+TOL10 = 1e-6          # FP32 state after 10 steps (RMS-floored relative)
+LR, B1, B2, EPS = configs.LR, configs.BETA1, configs.BETA2, configs.EPS
+
+
+def host_inputs(sizes, stream, master_sigma=0.02, init=None):
+    """Initial master per block (host generator), m = v = 0."""
+    out = []
+    for b, n in enumerate(sizes):
+        kind = init[b] if init else "normal"
+        if kind == "zero":
+            master = np.zeros(n, np.float32)
+        else:
+            sig = configs.LORA_A_SIGMA if kind == "lora_a" else master_sigma
+            purpose = synth.PURPOSE_LORA_A if kind == "lora_a" else synth.PURPOSE_MASTER
+            master = synth.normal_f32(n, stream=stream, block=b, purpose=purpose, step=0, sigma=sig)
+        out.append(dict(master=master, m=np.zeros(n, np.float32), v=np.zeros(n, np.float32),
+                        weight=np.zeros(n, np.uint16)))
+    return out
+
+
+def grads(sizes, stream, step, sigma=1e-3):
+    return [synth.normal_bf16(n, stream=stream, block=b, purpose=synth.PURPOSE_GRAD, step=step,
+                              sigma=sigma) for b, n in enumerate(sizes)]
+
+
+def oracle_step(state, gs, t, lr=LR, b1=B1, b2=B2, eps=EPS):
+    for s, g in zip(state, gs):
+        oracle.adam_step(s["master"], s["m"], s["v"], g, s["weight"], t, lr, b1, b2, eps)
+
+
+def load_arena(arena, state):
+    for i, s in enumerate(state):
+        arena.put(i, "master", s["master"])
+        if arena.adam:
+            arena.put(i, "m", s["m"])
+            arena.put(i, "v", s["v"])
+
+
+def read_arena(arena, i):
+    d = {"master": arena.get(i, "master")}
+    if arena.adam:
+        d["m"] = arena.get(i, "m")
+        d["v"] = arena.get(i, "v")
+    if arena.weight:
+        d["weight"] = arena.get(i, "weight")
+    return d
+
+
+def run_parity(sizes, steps, stream_id, check_every=False, tol=TOL10, init=None):
+    log("parity", f"sizes={sizes[:6]}{'...' if len(sizes) > 6 else ''} blocks={len(sizes)} steps={steps}")
+    T = torch()
+    ref = host_inputs(sizes, stream_id, init=init)
+    arena = Arena(sizes)
+    load_arena(arena, ref)
+    table = arena.table()
+    errs = {}
+    for t in range(1, steps + 1):
+        gs = grads(sizes, stream_id, t)
+        for i, g in enumerate(gs):
+            arena.put(i, "grad", g)
+        table.set_step(t)
+        lso.adam_step(table, T.cuda.current_stream())
+        oracle_step(ref, gs, t)
+        if check_every or t == steps:
+            T.cuda.synchronize()
+            scale = call_scale(ref)
+            for i in range(len(sizes)):
+                got = read_arena(arena, i)
+                assert_parity(got, ref[i], tol, f"block {i} (n={sizes[i]}) step {t}", scale)
+                for k, v in max_errors(got, ref[i], scale).items():
+                    errs[k] = max(errs.get(k, 0.0), v)
+    assert arena.canaries_intact(), "a write landed outside its array"
+    return errs
+
+
+def test_c0_flat_block_10_steps():
+    errs = run_parity([1 << 20], 10, configs.STREAM_ID["c0"], check_every=True)
+    log("c0 max errors", errs)
+
+
+def test_ragged_sizes_inline_path():
+    """<= 4 blocks travel by value; tails of 1..7 elements, partial chunks."""
+    run_parity([1, 7, 4097, 8 * 4096 + 5], 10, 90, check_every=True)
+
+
+def test_ragged_sizes_table_path():
+    """> 4 blocks use the device table and the binary search."""
+    sizes = [1, 2, 3, 7, 8, 9, 15, 16, 17, 4095, 4096, 4097, 8191, 8192, 8193, 12345, 100003]
+    run_parity(sizes, 10, 91)
+
+
+def test_c2_lora_308_tensors_one_launch_per_step():
+    """308 ragged tensors (A ~ N(0, 1/8), B = 0); step 10 at 1e-6; step 100
+    at the stated looser 5e-6 (FP32 rounding accumulates with the steps)."""
+    w = configs.get("c2")
+    sizes = [b.n for b in w.blocks]
+    init = [b.init for b in w.blocks]
+    T = torch()
+    sid = configs.STREAM_ID["c2"]
+    ref = host_inputs(sizes, sid, init=init)
+    arena = Arena(sizes)
+    load_arena(arena, ref)
+    table = arena.table()
+    log("c2 lora 100 steps")
+    for t in range(1, 101):
+        gs = grads(sizes, sid, t)
+        for i, g in enumerate(gs):
+            arena.put(i, "grad", g)
+        table.set_step(t)
+        lso.adam_step(table, T.cuda.current_stream())
+        oracle_step(ref, gs, t)
+        if t in (10, 100):
+            T.cuda.synchronize()
+            tol = TOL10 if t == 10 else 5e-6
+            worst = {}
+            scale = call_scale(ref)
+            for i in range(len(sizes)):
+                got = read_arena(arena, i)
+                assert_parity(got, ref[i], tol, f"lora tensor {i} step {t}", scale)
+                for k, v in max_errors(got, ref[i], scale).items():
+                    worst[k] = max(worst.get(k, 0.0), v)
+            log(f"c2 step {t} max errors", worst)
+    assert arena.canaries_intact()
+
+
+def test_multi_tensor_equals_per_block_launches_bitwise():
+    sizes = [2048, 16384, 45056, 7, 100003, 16384]
+    T = torch()
+    ref = host_inputs(sizes, 92)
+    a1, a2 = Arena(sizes), Arena(sizes)
+    load_arena(a1, ref)
+    load_arena(a2, ref)
+    t1, t2 = a1.table(), a2.table()
+    for t in range(1, 4):
+        gs = grads(sizes, 92, t)
+        for i, g in enumerate(gs):
+            a1.put(i, "grad", g)
+            a2.put(i, "grad", g)
+        t1.set_step(t)
+        t2.set_step(t)
+        lso.adam_step(t1)
+        for i in range(len(sizes)):
+            one = lso.BlockTable(1)
+            one.arr[0] = t2.arr[i]
+            lso.adam_step(one)
+    T.cuda.synchronize()
+    for i in range(len(sizes)):
+        for q in ("master", "m", "v", "weight"):
+            assert np.array_equal(a1.get(i, q).view(np.uint8), a2.get(i, q).view(np.uint8)), (i, q)
+
+
+def test_run_to_run_determinism_and_checkpoint_resume():
+    """10 steps == 5 steps + copy the state out and back in + 5 steps, bit
+    for bit (t is the resume point), and two runs agree bit for bit."""
+    sizes = [5000, 70001]
+    T = torch()
+    ref = host_inputs(sizes, 93)
+
+    def run(arena, t0, t1):
+        tab = arena.table()
+        for t in range(t0, t1 + 1):
+            for i, g in enumerate(grads(sizes, 93, t)):
+                arena.put(i, "grad", g)
+            tab.set_step(t)
+            lso.adam_step(tab)
+        T.cuda.synchronize()
+
+    a = Arena(sizes)
+    load_arena(a, ref)
+    run(a, 1, 10)
+    b = Arena(sizes)
+    load_arena(b, ref)
+    run(b, 1, 5)
+    ckpt = [read_arena(b, i) for i in range(len(sizes))]
+    c = Arena(sizes)
+    load_arena(c, ckpt)
+    run(c, 6, 10)
+    d = Arena(sizes)
+    load_arena(d, ref)
+    run(d, 1, 10)
+    for i in range(len(sizes)):
+        for q in ("master", "m", "v", "weight"):
+            x = a.get(i, q).view(np.uint8)
+            assert np.array_equal(x, c.get(i, q).view(np.uint8)), ("resume", i, q)
+            assert np.array_equal(x, d.get(i, q).view(np.uint8)), ("determinism", i, q)
+
+
+def test_more_than_16_hyper_sets_split_launches():
+    """20 blocks with distinct (t, lr): per-block t as under progressive layer
+    locking; the call splits into two launches and every block matches."""
+    T = torch()
+    sizes = [3000 + 17 * i for i in range(20)]
+    ref = host_inputs(sizes, 94)
+    arena = Arena(sizes)
+    load_arena(arena, ref)
+    rows = arena.rows()
+    ts = [1 + (i % 7) for i in range(20)]
+    lrs = [1e-3 * (1 + i) for i in range(20)]
+    for i, r in enumerate(rows):
+        r["t"], r["lr"] = ts[i], lrs[i]
+    tab = lso.BlockTable.from_rows(rows)
+    gs = grads(sizes, 94, 1)
+    for i, g in enumerate(gs):
+        arena.put(i, "grad", g)
+    lso.adam_step(tab)
+    T.cuda.synchronize()
+    for i, s in enumerate(ref):
+        oracle.adam_step(s["master"], s["m"], s["v"], gs[i], s["weight"], ts[i], lrs[i], B1, B2, EPS)
+    scale = call_scale(ref)
+    for i, s in enumerate(ref):
+        assert_parity(read_arena(arena, i), s, TOL10, f"block {i}", scale)
+
+
+# ------------------------------------------------- closed forms on the GPU
+
+def test_gpu_constant_gradient_closed_form():
+    T = torch()
+    n = 10000
+    g = synth.normal_bf16(n, stream=95, block=0, purpose=2, step=1, sigma=1e-3)
+    arena = Arena([n])
+    arena.put(0, "master", np.zeros(n, np.float32))
+    arena.put(0, "m", np.zeros(n, np.float32))
+    arena.put(0, "v", np.zeros(n, np.float32))
+    arena.put(0, "grad", g)
+    tab = arena.table()
+    gv = bf16_value(g).astype(np.float64)
+    for t in range(1, 11):
+        tab.set_step(t)
+        lso.adam_step(tab)
+        T.cuda.synchronize()
+        exact = -t * LR * gv / (np.abs(gv) + EPS)
+        got = arena.get(0, "master")
+        assert np.max(np.abs(got - exact) / np.abs(exact)) < 2e-6, t
+
+
+def test_gpu_lr_zero_and_zero_gradient_invariants():
+    T = torch()
+    n = 9999
+    master0 = synth.normal_f32(n, stream=96, block=0, purpose=0, step=0, sigma=0.02)
+    arena = Arena([n])
+    arena.put(0, "master", master0)
+    m0 = (np.arange(n) % 511 - 255).astype(np.float32) * np.float32(2.0 ** -12)
+    v0 = (np.arange(n) % 255 + 1).astype(np.float32) * np.float32(2.0 ** -20)
+    arena.put(0, "m", m0)
+    arena.put(0, "v", v0)
+    # lr = 0: the weight never moves, bit for bit
+    tab = arena.table(lr=0.0)
+    for t in range(1, 11):
+        arena.put(0, "grad", synth.normal_bf16(n, stream=96, block=0, purpose=2, step=t, sigma=1e-3))
+        tab.set_step(t)
+        lso.adam_step(tab)
+    T.cuda.synchronize()
+    assert np.array_equal(arena.get(0, "master").view(np.uint32), master0.view(np.uint32))
+    assert np.array_equal(arena.get(0, "weight"), oracle.bf16_rne(master0))
+    # zero gradient, dyadic betas: moments decay by beta^t exactly
+    arena.put(0, "m", m0)
+    arena.put(0, "v", v0)
+    arena.put(0, "grad", np.zeros(n, np.uint16))
+    tab = arena.table(beta1=0.5, beta2=0.75)
+    for t in range(1, 11):
+        tab.set_step(t)
+        lso.adam_step(tab)
+    T.cuda.synchronize()
+    assert np.array_equal(arena.get(0, "m"), (m0.astype(np.float64) * 0.5 ** 10).astype(np.float32))
+    assert np.array_equal(arena.get(0, "v"), (v0.astype(np.float64) * 0.75 ** 10).astype(np.float32))
+
+
+def test_gpu_beta_zero_sign_descent():
+    T = torch()
+    n = 4099
+    master = synth.normal_f32(n, stream=97, block=0, purpose=0, step=0, sigma=0.02)
+    arena = Arena([n])
+    arena.put(0, "master", master)
+    arena.put(0, "m", np.zeros(n, np.float32))
+    arena.put(0, "v", np.zeros(n, np.float32))
+    tab = arena.table(beta1=0.0, beta2=0.0)
+    prev = master.astype(np.float64)
+    for t in range(1, 6):
+        g = synth.normal_bf16(n, stream=97, block=0, purpose=2, step=t, sigma=1e-3)
+        arena.put(0, "grad", g)
+        tab.set_step(t)
+        lso.adam_step(tab)
+        T.cuda.synchronize()
+        got = arena.get(0, "master")
+        gv = bf16_value(g).astype(np.float64)
+        delta = -LR * gv / (np.abs(gv) + EPS)
+        expect = prev + delta
+        # FP32 delta (fl32(lr), product, |g|+eps, quotient: <= 4 roundings)
+        # plus the rounding of the sum; master + delta can cancel, so the
+        # bound is in ulps of both, not of the result alone
+        sp = lambda x: np.spacing(np.abs(x).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - expect) <= sp(expect) + 4 * sp(delta)), t
+        prev = got.astype(np.float64)
+
+
+def test_gpu_sgd_matches_oracle_bitwise_and_page_test1():
+    T = torch()
+    # the page's three-element example: W - 0.015 * W
+    w0 = np.array([1.0, 2.0, 3.0], np.float32)
+    arena = Arena([3], adam=False)
+    arena.put(0, "master", w0)
+    arena.put(0, "grad", (w0.view(np.uint32) >> 16).astype(np.uint16))
+    lso.adam_step(arena.table(opt=lso.LSO_OPT_SGD, lr=0.015))
+    T.cuda.synchronize()
+    ref = w0.copy()
+    oracle.sgd_step(ref, (w0.view(np.uint32) >> 16).astype(np.uint16), None, 0.015)
+    got = arena.get(0, "master")
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    np.testing.assert_allclose(got, [0.985, 1.970, 2.955], rtol=2e-7)
+    # random data, many steps: bit for bit
+    n = 50001
+    master = synth.normal_f32(n, stream=98, block=0, purpose=0, step=0, sigma=0.02)
+    arena = Arena([n], adam=False)
+    arena.put(0, "master", master)
+    ref, refw = master.copy(), np.zeros(n, np.uint16)
+    tab = arena.table(opt=lso.LSO_OPT_SGD, lr=0.05)
+    for t in range(1, 6):
+        g = synth.normal_bf16(n, stream=98, block=0, purpose=2, step=t, sigma=0.1)
+        arena.put(0, "grad", g)
+        lso.adam_step(tab)
+        oracle.sgd_step(ref, g, refw, 0.05)
+    T.cuda.synchronize()
+    assert np.array_equal(arena.get(0, "master").view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(arena.get(0, "weight"), refw)
+    assert arena.canaries_intact()
+
+
+def test_gpu_nonfinite_gradients_stay_local():
+    T = torch()
+    n = 64
+    arena = Arena([n])
+    master = np.linspace(-1, 1, n).astype(np.float32)
+    arena.put(0, "master", master)
+    arena.put(0, "m", np.zeros(n, np.float32))
+    arena.put(0, "v", np.zeros(n, np.float32))
+    g = synth.normal_bf16(n, stream=99, block=0, purpose=2, step=1, sigma=1e-3)
+    g[5] = 0x7FC0   # NaN
+    g[9] = 0x7F80   # +Inf
+    g[13] = 0xFF80  # -Inf
+    arena.put(0, "grad", g)
+    lso.adam_step(arena.table())
+    T.cuda.synchronize()
+    ref = dict(master=master.copy(), m=np.zeros(n, np.float32), v=np.zeros(n, np.float32),
+               weight=np.zeros(n, np.uint16))
+    oracle.adam_step(ref["master"], ref["m"], ref["v"], g, ref["weight"], 1, LR, B1, B2, EPS)
+    got = read_arena(arena, 0)
+    for q in ("master", "m", "v"):
+        assert np.array_equal(np.isnan(got[q]), np.isnan(ref[q])), q
+    fin = ~np.isnan(ref["master"])
+    assert np.max(np.abs(got["master"][fin] - ref["master"][fin])) < 1e-6
+    assert np.array_equal(got["weight"], oracle.bf16_rne(got["master"]))
+
+
+def test_weight_output_can_be_skipped():
+    T = torch()
+    n = 10000
+    arena = Arena([n], weight=False)
+    ref = host_inputs([n], 100)
+    load_arena(arena, ref)
+    g = grads([n], 100, 1)[0]
+    arena.put(0, "grad", g)
+    lso.adam_step(arena.table())
+    T.cuda.synchronize()
+    oracle.adam_step(ref[0]["master"], ref[0]["m"], ref[0]["v"], g, None, 1, LR, B1, B2, EPS)
+    got = read_arena(arena, 0)
+    assert_parity(got, {k: ref[0][k] for k in ("master", "m", "v")}, TOL10)
+    assert arena.canaries_intact()
+
+
+def test_bf16_cast_exhaustive_all_fp32_patterns():
+    """The kernel's BF16 rounding over all 2^32 FP32 patterns equals the
+    oracle's definition bit for bit (NaNs included)."""
+    T = torch()
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    seg = 1 << 28
+    out = T.empty(seg, dtype=T.int16, device="cuda")
+    for s in range(16):
+        log("bf16 exhaustive segment", s)
+        rc = P.lso_probe_bf16_rne(s * seg, seg, out.data_ptr(), T.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        got = out.cpu().numpy().view(np.uint16)
+        bits = np.arange(s * seg, (s + 1) * seg, dtype=np.uint64).astype(np.uint32)
+        ref = oracle.bf16_rne(bits.view(np.float32))
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, f"segment {s}: {bad.size} mismatches, first {hex(int(bits[bad[0]]))}"

@@ -1,0 +1,203 @@
+"""GPU tests of layer streaming (lso_stream_layers): parity with the oracle,
+bitwise agreement with the resident path, failure handling and the
+persistence example, through the C ABI."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import layer_streamed_optimizer_amd as lso
+import oracle
+import synth
+from layer_streamed_optimizer_amd import configs
+
+from gpu_util import HIP_D2D, assert_parity, call_scale, hip, log, torch
+
+pytestmark = pytest.mark.gpu
+
+LR, B1, B2, EPS = configs.LR, configs.BETA1, configs.BETA2, configs.EPS
+
+
+class HostLayers:
+    """Authoritative pinned host blocks [master | m | v], one per layer."""
+
+    def __init__(self, sizes, sid):
+        self.sizes = sizes
+        self.bufs, self.lay = [], []
+        for b, n in enumerate(sizes):
+            om, omm, ov, nbytes = configs.host_layer_layout(n)
+            hb = lso.host_alloc(nbytes)
+            hb.view(np.uint8)[:] = 0
+            hb.view(np.float32, om, n)[:] = synth.normal_f32(n, stream=sid, block=b, purpose=0,
+                                                             step=0, sigma=0.02)
+            self.bufs.append(hb)
+            self.lay.append((om, omm, ov, nbytes))
+
+    def get(self, b, q):
+        om, omm, ov, _ = self.lay[b]
+        off = {"master": om, "m": omm, "v": ov}[q]
+        return self.bufs[b].view(np.float32, off, self.sizes[b]).copy()
+
+    def table(self, t, opt=lso.LSO_OPT_ADAM, lr=LR, dev_weight=None):
+        L = lso.LayerStream.layers(len(self.sizes))
+        for b, n in enumerate(self.sizes):
+            om, omm, ov, nbytes = self.lay[b]
+            L[b]["host_base"] = self.bufs[b].ptr
+            L[b]["bytes"] = nbytes
+            L[b]["n"] = n
+            L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
+            L[b]["dev_weight"] = dev_weight[b] if dev_weight else 0
+            L[b]["opt"] = opt
+            L[b]["t"] = t
+            L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = lr, B1, B2, EPS
+        return L
+
+
+def synth_stream(sizes, sid, max_bytes=None):
+    fn, Params = synth.grad_callback()
+    params = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
+                    scale=synth.scale_for(1e-3), block_base=0)
+    mb = max_bytes or max(configs.host_layer_layout(n)[3] for n in sizes)
+    ls = lso.LayerStream(mb, max(sizes), fn, ctypes.addressof(params))
+    return ls, params
+
+
+def test_stream_layers_matches_oracle():
+    T = torch()
+    sizes = [100003, 4096 * 3 + 7, 65536, 1]
+    sid = 40
+    log("stream parity", sizes)
+    host = HostLayers(sizes, sid)
+    ref = [dict(master=host.get(b, "master"), m=np.zeros(n, np.float32), v=np.zeros(n, np.float32),
+                weight=np.zeros(n, np.uint16)) for b, n in enumerate(sizes)]
+    dev_w = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
+    ls, params = synth_stream(sizes, sid)
+    for t in range(1, 4):
+        params.step = t
+        ls.stream_layers(host.table(t, dev_weight=[int(w.data_ptr()) for w in dev_w]))
+        for b, n in enumerate(sizes):
+            g = synth.normal_bf16(n, stream=sid, block=b, purpose=2, step=t, sigma=1e-3)
+            oracle.adam_step(ref[b]["master"], ref[b]["m"], ref[b]["v"], g, ref[b]["weight"], t,
+                             LR, B1, B2, EPS)
+    T.cuda.synchronize()
+    scale = call_scale(ref)
+    for b in range(len(sizes)):
+        got = dict(master=host.get(b, "master"), m=host.get(b, "m"), v=host.get(b, "v"),
+                   weight=dev_w[b].cpu().numpy().view(np.uint16))
+        assert_parity(got, ref[b], 1e-6, f"streamed layer {b}", scale)
+    ls.close()
+
+
+def test_streamed_equals_resident_bitwise():
+    """The same layers through lso_stream_layers and through lso_adam_step on
+    HBM-resident copies, with the same device-generated gradients: bit for
+    bit (the slot reuse must never let a copy overtake the update)."""
+    T = torch()
+    sizes = [300007, 262144, 5, 131072 + 3, 77777]
+    sid = 41
+    host = HostLayers(sizes, sid)
+    res = []
+    for b, n in enumerate(sizes):
+        res.append(dict(master=T.from_numpy(host.get(b, "master")).cuda(),
+                        m=T.zeros(n, dtype=T.float32, device="cuda"),
+                        v=T.zeros(n, dtype=T.float32, device="cuda"),
+                        g=T.empty(n, dtype=T.int16, device="cuda"),
+                        w=T.empty(n, dtype=T.int16, device="cuda")))
+    ls, params = synth_stream(sizes, sid)
+    for t in range(1, 4):
+        params.step = t
+        log("streamed vs resident step", t)
+        ls.stream_layers(host.table(t))
+        rows = []
+        for b, n in enumerate(sizes):
+            synth.device_fill_normal_bf16(res[b]["g"].data_ptr(), n, stream=sid, block=b,
+                                          purpose=2, step=t, sigma=1e-3,
+                                          hip_stream=T.cuda.current_stream().cuda_stream)
+            rows.append(dict(n=n, master=res[b]["master"], m=res[b]["m"], v=res[b]["v"],
+                             grad=res[b]["g"], weight=res[b]["w"], t=t))
+        lso.adam_step(lso.BlockTable.from_rows(rows))
+    T.cuda.synchronize()
+    for b in range(len(sizes)):
+        for q in ("master", "m", "v"):
+            assert np.array_equal(host.get(b, q).view(np.uint32),
+                                  res[b][q].cpu().numpy().view(np.uint32)), (b, q)
+    # the last layer's BF16 weight is still in its slot
+    last = len(sizes) - 1
+    n = sizes[last]
+    slot = T.empty(n, dtype=T.int16, device="cuda")
+    assert hip().hipMemcpyAsync(slot.data_ptr(), ls.slot_weight(last % 2), 2 * n, HIP_D2D,
+                                T.cuda.current_stream().cuda_stream) == 0
+    T.cuda.synchronize()
+    assert np.array_equal(slot.cpu().numpy(), res[last]["w"].cpu().numpy())
+    ls.close()
+
+
+def test_grad_producer_failure_leaves_later_layers_untouched():
+    """The producer fails at layer 2: layers 0 and 1 are fully written back,
+    layers 2 and 3 keep their old host state, and the call reports
+    LSO_E_CALLBACK (failure forced from the host; every kernel completes)."""
+    T = torch()
+    sizes = [50000, 50000, 50000, 50000]
+    sid = 42
+    host = HostLayers(sizes, sid)
+    before = [host.get(b, "master") for b in range(4)]
+    fill = synth._dev_lib().synth_fill_normal_bf16
+
+    def producer(layer, dev_grad, n, stream):
+        if layer == 2:
+            return 5
+        return fill(dev_grad, n, 0, synth.SEED, sid, layer, 2, 1, synth.scale_for(1e-3), stream)
+
+    ls = lso.LayerStream(max(configs.host_layer_layout(n)[3] for n in sizes), max(sizes), producer)
+    st = ls.stream_layers_status(host.table(1))
+    assert st == lso._native.LSO_E_CALLBACK
+    assert "layer 2" in lso.last_error()
+    for b in range(4):
+        now = host.get(b, "master")
+        if b < 2:
+            assert not np.array_equal(now, before[b]), b
+            assert np.any(host.get(b, "v") != 0), b
+        else:
+            assert np.array_equal(now.view(np.uint32), before[b].view(np.uint32)), b
+            assert not np.any(host.get(b, "m")), b
+    ls.close()
+
+
+def test_persistence_sgd_accumulates_in_host_block():
+    """The page's persistence check on the streamed path: two streamed SGD
+    steps whose deltas are BF16-exact add up in the authoritative host block
+    bit for bit: [1, 2] -> [1.5, 2.25] -> [2.0, 2.5]."""
+    T = torch()
+    host = HostLayers([2], 43)
+    host.bufs[0].view(np.float32, 0, 2)[:] = [1.0, 2.0]
+    gbits = (np.array([0.5, 0.25], np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    gsrc = T.from_numpy(gbits.view(np.int16)).cuda()
+
+    def producer(layer, dev_grad, n, stream):
+        return hip().hipMemcpyAsync(dev_grad, gsrc.data_ptr(), 2 * n, HIP_D2D, stream)
+
+    T.cuda.synchronize()
+    ls = lso.LayerStream(configs.host_layer_layout(2)[3], 2, producer)
+    # SGD: master + (-(lr * g)) with lr = -1 adds g
+    ls.stream_layers(host.table(1, opt=lso.LSO_OPT_SGD, lr=-1.0))
+    assert host.get(0, "master").tolist() == [1.5, 2.25]
+    ls.stream_layers(host.table(2, opt=lso.LSO_OPT_SGD, lr=-1.0))
+    assert host.get(0, "master").tolist() == [2.0, 2.5]
+    ls.close()
+
+
+def test_device_generator_matches_host_generator():
+    """The two implementations of the input generator agree bit for bit."""
+    T = torch()
+    n = 1 << 20
+    buf = T.empty(n, dtype=T.float32, device="cuda")
+    synth.device_fill_normal_f32(buf.data_ptr(), n, stream=7, block=3, purpose=0, step=0,
+                                 sigma=0.02, start=12345)
+    g = T.empty(n, dtype=T.int16, device="cuda")
+    synth.device_fill_normal_bf16(g.data_ptr(), n, stream=7, block=3, purpose=2, step=9, sigma=1e-3)
+    T.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(),
+                          synth.normal_f32(n, stream=7, block=3, purpose=0, step=0, sigma=0.02,
+                                           start=12345))
+    assert np.array_equal(g.cpu().numpy().view(np.uint16),
+                          synth.normal_bf16(n, stream=7, block=3, purpose=2, step=9, sigma=1e-3))
