@@ -54,6 +54,7 @@ class BlockTable:
 
     def __init__(self, n: int):
         self.arr = np.zeros(n, BLOCK_DTYPE)
+        self._ptr = self.arr.ctypes.data      # the array is never reallocated
 
     def __len__(self) -> int:
         return len(self.arr)
@@ -91,14 +92,15 @@ class BlockTable:
 
     @property
     def ptr(self) -> int:
-        return self.arr.ctypes.data
+        return self._ptr
 
 
 def adam_step(table: BlockTable, stream=None) -> None:
     """One fused update of every block in the table, enqueued on stream
     (one kernel launch).  Asynchronous."""
-    st = _native.lib().lso_adam_step(table.ptr, len(table), stream_handle(stream))
-    _native.check(st, "lso_adam_step")
+    st = _native.lib().lso_adam_step(table._ptr, len(table.arr), stream_handle(stream))
+    if st:
+        _native.check(st, "lso_adam_step")
 
 
 def validate(table: BlockTable) -> int:

@@ -8,11 +8,19 @@
 // 14 bytes read + 14 bytes written per parameter and nothing else: no
 // scratch, no second pass.
 //
-// Ragged multi-tensor launch: one grid walks the concatenated chunk space of
-// every block of the call; a workgroup finds the block that owns its chunk by
-// a uniform (scalar) binary search over the table's chunk starts.
+// Memory access: a lane owns groups of four consecutive elements, so every
+// FP32 access is one 128-bit load or store and every BF16 access one 64-bit
+// access, and each wave instruction covers one contiguous run (1 KB of FP32,
+// 512 B of BF16).  All state is touched exactly once, so loads and stores
+// are non-temporal (streamed past the caches).
 //
-// Built with -ffp-contract=off: every FMA below is an explicit fmaf, every
+// Ragged multi-tensor launch: one grid covers the concatenated chunk space
+// of every block of the call, one chunk per workgroup.  A workgroup finds
+// its block through a per-chunk block index (one scalar load), through a
+// binary search over the table when the call has too many chunks for an
+// index, or among the few blocks passed by value in the kernel arguments.
+//
+// Built with -ffp-contract=off: every FMA below is an explicit fmaf and every
 // other operator rounds once, so the SGD path is exactly fl(W + fl(-(lr*g))).
 #include <hip/hip_runtime.h>
 
@@ -25,13 +33,25 @@ namespace lso {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Explicit address spaces: state arrays are global memory (so the compiler
-// emits global_* rather than flat_* accesses), and the block table is
-// read-only for the kernel's lifetime (constant space, scalar loads).
+// State arrays are global memory (global_* rather than flat_* accesses);
+// the block table and chunk index are read-only while the kernel runs
+// (constant space: scalar loads).
 #define LSO_GLOBAL __attribute__((address_space(1)))
 #define LSO_CONST __attribute__((address_space(4)))
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const LSO_GLOBAL T*>(reinterpret_cast<uintptr_t>(p)));
+}
+
+template <typename T>
+__device__ __forceinline__ void st_nt(void* p, T v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<LSO_GLOBAL T*>(reinterpret_cast<uintptr_t>(p)));
+}
 
 template <typename T>
 __device__ __forceinline__ T ld(const void* p)
@@ -40,7 +60,7 @@ __device__ __forceinline__ T ld(const void* p)
 }
 
 template <typename T>
-__device__ __forceinline__ void st(void* p, const T& v)
+__device__ __forceinline__ void st(void* p, T v)
 {
     *reinterpret_cast<LSO_GLOBAL T*>(reinterpret_cast<uintptr_t>(p)) = v;
 }
@@ -62,81 +82,66 @@ __device__ __forceinline__ void sgd_elem(const Coef& c, float g, float& master)
     master = master + delta;
 }
 
-// Eight consecutive elements held by one lane.
-struct Group {
-    u32x4 g;          // 8 BF16
-    f32x4 p0, p1;     // master
-    f32x4 m0, m1;
-    f32x4 v0, v1;
+// Four consecutive elements held by one lane.
+struct Quad {
+    u32x2 g;     // 4 BF16
+    f32x4 p;     // master
+    f32x4 m;
+    f32x4 v;
 };
 
 template <bool kSgd>
-__device__ __forceinline__ void load_group(const DevBlock& b, uint64_t e, Group& x)
+__device__ __forceinline__ void load_quad(const DevBlock& b, uint64_t e, Quad& x)
 {
-    x.g = ld<u32x4>(b.g + e);
-    x.p0 = ld<f32x4>(b.master + e);
-    x.p1 = ld<f32x4>(b.master + e + 4);
+    x.g = ld_nt<u32x2>(b.g + e);
+    x.p = ld_nt<f32x4>(b.master + e);
     if (!kSgd) {
-        x.m0 = ld<f32x4>(b.m + e);
-        x.m1 = ld<f32x4>(b.m + e + 4);
-        x.v0 = ld<f32x4>(b.v + e);
-        x.v1 = ld<f32x4>(b.v + e + 4);
+        x.m = ld_nt<f32x4>(b.m + e);
+        x.v = ld_nt<f32x4>(b.v + e);
     }
 }
 
 template <bool kSgd>
-__device__ __forceinline__ void compute_group(const Coef& c, Group& x, u32x4& wout)
+__device__ __forceinline__ u32x2 compute_quad(const Coef& c, Quad& x)
 {
-    float gs[8], ps[8], ms[8], vs[8];
+    u32x2 w;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t word = x.g[k];
-        gs[2 * k] = bf16_widen(word & 0xFFFFu);
-        gs[2 * k + 1] = bf16_widen(word >> 16);
-        ps[k] = x.p0[k];
-        ps[k + 4] = x.p1[k];
-        if (!kSgd) {
-            ms[k] = x.m0[k];
-            ms[k + 4] = x.m1[k];
-            vs[k] = x.v0[k];
-            vs[k + 4] = x.v1[k];
+    for (int k = 0; k < 2; ++k) {
+        const float g0 = bf16_widen(x.g[k] & 0xFFFFu);
+        const float g1 = bf16_widen(x.g[k] >> 16);
+        float p0 = x.p[2 * k], p1 = x.p[2 * k + 1];
+        if (kSgd) {
+            sgd_elem(c, g0, p0);
+            sgd_elem(c, g1, p1);
+        } else {
+            float m0 = x.m[2 * k], m1 = x.m[2 * k + 1];
+            float v0 = x.v[2 * k], v1 = x.v[2 * k + 1];
+            adam_elem(c, g0, p0, m0, v0);
+            adam_elem(c, g1, p1, m1, v1);
+            x.m[2 * k] = m0;
+            x.m[2 * k + 1] = m1;
+            x.v[2 * k] = v0;
+            x.v[2 * k + 1] = v1;
         }
+        x.p[2 * k] = p0;
+        x.p[2 * k + 1] = p1;
+        w[k] = bf16_rne(p0) | (bf16_rne(p1) << 16);
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        if (kSgd) sgd_elem(c, gs[k], ps[k]);
-        else adam_elem(c, gs[k], ps[k], ms[k], vs[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        x.p0[k] = ps[k];
-        x.p1[k] = ps[k + 4];
-        if (!kSgd) {
-            x.m0[k] = ms[k];
-            x.m1[k] = ms[k + 4];
-            x.v0[k] = vs[k];
-            x.v1[k] = vs[k + 4];
-        }
-        wout[k] = bf16_rne(ps[2 * k]) | (bf16_rne(ps[2 * k + 1]) << 16);
-    }
+    return w;
 }
 
 template <bool kSgd>
-__device__ __forceinline__ void store_group(const DevBlock& b, uint64_t e, const Group& x,
-                                            const u32x4& wout, bool has_w)
+__device__ __forceinline__ void store_quad(const DevBlock& b, uint64_t e, const Quad& x, u32x2 w, bool has_w)
 {
-    st<f32x4>(b.master + e, x.p0);
-    st<f32x4>(b.master + e + 4, x.p1);
+    st_nt<f32x4>(b.master + e, x.p);
     if (!kSgd) {
-        st<f32x4>(b.m + e, x.m0);
-        st<f32x4>(b.m + e + 4, x.m1);
-        st<f32x4>(b.v + e, x.v0);
-        st<f32x4>(b.v + e + 4, x.v1);
+        st_nt<f32x4>(b.m + e, x.m);
+        st_nt<f32x4>(b.v + e, x.v);
     }
-    if (has_w) st<u32x4>(b.w + e, wout);
+    if (has_w) st_nt<u32x2>(b.w + e, w);
 }
 
-// Elements [e, n) of a block, fewer than eight: scalar accesses.
+// Elements [e, n) of a block, fewer than four: scalar accesses.
 template <bool kSgd>
 __device__ void tail_elems(const DevBlock& b, const Coef& c, uint64_t e, uint64_t n, bool has_w)
 {
@@ -156,53 +161,42 @@ __device__ void tail_elems(const DevBlock& b, const Coef& c, uint64_t e, uint64_
     }
 }
 
-template <bool kSgd>
+// One chunk of kThreads * kQuad * U elements starting at element e0 of b.
+template <int U, bool kSgd>
 __device__ __forceinline__ void run_chunk(const DevBlock& b, const Coef& c, uint64_t e0)
 {
+    constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
     const bool has_w = (b.flags & kFlagWeight) != 0;
     const uint64_t n = b.n;
-    if (e0 + kChunk <= n) {
-        // full chunk: all loads first, then arithmetic, then stores
-        Group x[kUnroll];
+    if (e0 + kChunkU <= n) {
+        // full chunk: every load of the lane first, then arithmetic and stores
+        Quad x[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            load_group<kSgd>(b, e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kVec, x[u]);
+        for (int u = 0; u < U; ++u)
+            load_quad<kSgd>(b, e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kQuad, x[u]);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            u32x4 w;
-            compute_group<kSgd>(c, x[u], w);
-            store_group<kSgd>(b, e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kVec, x[u], w, has_w);
+        for (int u = 0; u < U; ++u) {
+            const u32x2 w = compute_quad<kSgd>(c, x[u]);
+            store_quad<kSgd>(b, e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kQuad, x[u], w, has_w);
         }
         return;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t e = e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kVec;
-        if (e + kVec <= n) {
-            Group x;
-            u32x4 w;
-            load_group<kSgd>(b, e, x);
-            compute_group<kSgd>(c, x, w);
-            store_group<kSgd>(b, e, x, w, has_w);
+    for (int u = 0; u < U; ++u) {
+        const uint64_t e = e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kQuad;
+        if (e + kQuad <= n) {
+            Quad x;
+            load_quad<kSgd>(b, e, x);
+            const u32x2 w = compute_quad<kSgd>(c, x);
+            store_quad<kSgd>(b, e, x, w, has_w);
         } else if (e < n) {
             tail_elems<kSgd>(b, c, e, n, has_w);
         }
     }
 }
 
-// The block owning global chunk `chunk`: the last block whose chunk0 <=
-// chunk.  Uniform across the workgroup; the table lives in constant space
-// so the search and the block fields are scalar loads.
-__device__ __forceinline__ DevBlock find_block(const LSO_CONST DevBlock* blocks, uint32_t nblocks,
-                                               uint64_t chunk)
+__device__ __forceinline__ DevBlock load_block(const LSO_CONST DevBlock* p)
 {
-    uint32_t lo = 0, hi = nblocks;   // blocks[lo].chunk0 <= chunk < blocks[hi].chunk0
-    while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (blocks[mid].chunk0 <= chunk) lo = mid;
-        else hi = mid;
-    }
-    const LSO_CONST DevBlock* p = blocks + lo;
     DevBlock b;
     b.master = p->master;
     b.m = p->m;
@@ -216,6 +210,19 @@ __device__ __forceinline__ DevBlock find_block(const LSO_CONST DevBlock* blocks,
     return b;
 }
 
+// The last block whose chunk0 <= chunk (uniform across the workgroup).
+__device__ __forceinline__ uint32_t search_block(const LSO_CONST DevBlock* blocks, uint32_t nblocks,
+                                                 uint64_t chunk)
+{
+    uint32_t lo = 0, hi = nblocks;   // blocks[lo].chunk0 <= chunk < blocks[hi].chunk0
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (blocks[mid].chunk0 <= chunk) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
 // Same for the few blocks passed by value: fully unrolled selects.
 __device__ __forceinline__ DevBlock find_inline(const KernelArgs& a, uint64_t chunk)
 {
@@ -226,43 +233,46 @@ __device__ __forceinline__ DevBlock find_inline(const KernelArgs& a, uint64_t ch
     return b;
 }
 
+template <int U>
 __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const DevBlock& b, uint64_t chunk)
 {
+    constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
     const Coef c = args.coef[b.group];
-    const uint64_t e0 = (chunk - b.chunk0) * kChunk;
-    if (b.flags & kFlagSgd) run_chunk<true>(b, c, e0);
-    else run_chunk<false>(b, c, e0);
+    const uint64_t e0 = (chunk - b.chunk0) * kChunkU;
+    if (b.flags & kFlagSgd) run_chunk<U, true>(b, c, e0);
+    else run_chunk<U, false>(b, c, e0);
 }
 
+template <int U>
 __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs args)
 {
     if (args.blocks) {
         const LSO_CONST DevBlock* table =
             reinterpret_cast<const LSO_CONST DevBlock*>(reinterpret_cast<uintptr_t>(args.blocks));
-        for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x)
-            run_block_chunk(args, find_block(table, args.nblocks, chunk), chunk);
+        const LSO_CONST uint32_t* index =
+            reinterpret_cast<const LSO_CONST uint32_t*>(reinterpret_cast<uintptr_t>(args.chunk_block));
+        for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x) {
+            const uint32_t bi = index ? index[chunk] : search_block(table, args.nblocks, chunk);
+            run_block_chunk<U>(args, load_block(table + bi), chunk);
+        }
     } else {
         for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x)
-            run_block_chunk(args, find_inline(args, chunk), chunk);
+            run_block_chunk<U>(args, find_inline(args, chunk), chunk);
     }
 }
 
 }  // namespace
 
-unsigned default_grid(uint64_t total_chunks)
-{
-    // 256 CUs; eight resident workgroups of 256 lanes per CU keeps enough
-    // 16-byte requests in flight to cover HBM latency.
-    const uint64_t cap = 256ull * 8ull;
-    return static_cast<unsigned>(total_chunks < cap ? total_chunks : cap);
-}
-
-int launch_fused_adam(const KernelArgs& args, unsigned grid, void* stream)
+int launch_fused_adam(const KernelArgs& args, int unroll, void* stream)
 {
     if (args.total_chunks == 0) return 0;
-    if (grid == 0) grid = default_grid(args.total_chunks);
-    hipLaunchKernelGGL(fused_adam_kernel, dim3(grid), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), args);
+    // one chunk per workgroup; a call too large for one grid loops
+    const uint64_t grid = args.total_chunks < kMaxGrid ? args.total_chunks : kMaxGrid;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (unroll == kUnrollLarge)
+        hipLaunchKernelGGL(fused_adam_kernel<kUnrollLarge>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, args);
+    else
+        hipLaunchKernelGGL(fused_adam_kernel<kUnrollSmall>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, args);
     return static_cast<int>(hipGetLastError());
 }
 

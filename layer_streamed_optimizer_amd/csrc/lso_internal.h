@@ -8,13 +8,19 @@
 namespace lso {
 
 // Work decomposition of the fused kernel.  A workgroup of kThreads lanes
-// handles one chunk of kChunk consecutive elements of one block per
-// iteration; each lane owns kUnroll groups of kVec consecutive elements
-// (one 16-byte BF16 vector, two 16-byte FP32 vectors per state array).
+// handles one chunk of consecutive elements of one block; each lane owns U
+// groups of kQuad consecutive elements (U = kUnrollLarge for big calls,
+// kUnrollSmall for small ones, where more, smaller chunks spread the work
+// over all 256 CUs).
 constexpr int kThreads = 256;
-constexpr int kVec = 8;
-constexpr int kUnroll = 2;
-constexpr uint64_t kChunk = static_cast<uint64_t>(kThreads) * kVec * kUnroll;
+constexpr int kQuad = 4;
+constexpr int kUnrollLarge = 4;
+constexpr int kUnrollSmall = 1;
+constexpr uint64_t kSmallCallElems = 32ull << 20;   // below this, kUnrollSmall
+constexpr uint64_t kMaxGrid = 1ull << 24;            // workgroups per launch
+constexpr uint64_t kMaxIndexChunks = 1ull << 22;     // per-chunk block index up to this
+
+constexpr uint64_t chunk_elems(int unroll) { return static_cast<uint64_t>(kThreads) * kQuad * unroll; }
 
 // At most this many distinct constant sets travel by value in one launch.
 constexpr int kMaxGroups = 16;
@@ -50,7 +56,8 @@ static_assert(sizeof(Coef) == 32, "Coef layout");
 constexpr int kInline = 4;
 
 struct KernelArgs {
-    const DevBlock* blocks;   // device table, or nullptr: use inl[]
+    const DevBlock* blocks;        // device table, or nullptr: use inl[]
+    const uint32_t* chunk_block;   // block index per chunk, or nullptr: search
     uint64_t total_chunks;
     uint32_t nblocks;
     uint32_t pad;
@@ -58,9 +65,8 @@ struct KernelArgs {
     DevBlock inl[kInline];
 };
 
-// Enqueue the fused kernel (defined in lso_adam.hip).  grid == 0 picks the
-// default grid for the work.  Returns the hipError_t of the launch as int.
-int launch_fused_adam(const KernelArgs& args, unsigned grid, void* stream);
-unsigned default_grid(uint64_t total_chunks);
+// Enqueue the fused kernel (defined in lso_adam.hip) with chunks of
+// chunk_elems(unroll) elements.  Returns the hipError_t of the launch.
+int launch_fused_adam(const KernelArgs& args, int unroll, void* stream);
 
 }  // namespace lso

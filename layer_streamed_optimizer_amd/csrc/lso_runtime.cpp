@@ -186,22 +186,26 @@ HyperKey key_of(const lso_block& b)
     return {b.opt, b.t, b.lr, b.beta1, b.beta2, b.eps};
 }
 
-// Device tables of more than kInline blocks, cached by content so a
-// training loop that passes the same blocks every step uploads its table
-// once.  Per device; at most kCacheCap entries, least recently used evicted
-// after a device synchronisation (the entry may still be read by queued
-// kernels on any stream).
+// Device copies of block tables of more than kInline blocks (plus their
+// per-chunk block index), cached by content so a training loop that passes
+// the same blocks every step uploads its table once.  Per device; at most
+// kCacheCap entries.  The least recently used entry is evicted after a
+// device synchronisation, because queued kernels on any stream may still
+// read it; a loop that cycles through more than kCacheCap distinct tables
+// pays that synchronisation on every new one.
 struct TableEntry {
     std::vector<DevBlock> key;
-    DevBlock* dev = nullptr;
-    DevBlock* pinned = nullptr;
-    hipEvent_t ready = nullptr;
+    int unroll = 0;
+    void* dev = nullptr;          // [DevBlock x n | uint32 index x chunks]
+    void* pinned = nullptr;       // host staging of the upload
+    hipEvent_t ready = nullptr;   // recorded after the upload
     bool ready_seen = false;
     void* upload_stream = nullptr;
     uint64_t tick = 0;
+    bool has_index = false;
 };
 
-constexpr size_t kCacheCap = 64;
+constexpr size_t kCacheCap = 256;
 
 struct DeviceTables {
     std::vector<TableEntry> entries;
@@ -219,7 +223,17 @@ void free_entry(TableEntry& e)
     e = TableEntry{};
 }
 
-lso_status device_table(const std::vector<DevBlock>& tab, void* stream, const DevBlock** out)
+bool same_table(const TableEntry& e, const std::vector<DevBlock>& tab, int unroll)
+{
+    return e.unroll == unroll && e.key.size() == tab.size() &&
+           std::memcmp(e.key.data(), tab.data(), tab.size() * sizeof(DevBlock)) == 0;
+}
+
+// Find the cached device table for tab, or validate the call's addresses,
+// upload tab (and its chunk index) on stream and cache it.
+lso_status device_table(const lso_block* blocks, size_t n, bool geometry_checked,
+                        const std::vector<DevBlock>& tab, uint64_t total_chunks, int unroll,
+                        void* stream, KernelArgs& args)
 {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -227,21 +241,27 @@ lso_status device_table(const std::vector<DevBlock>& tab, void* stream, const De
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceTables& dt = g_tables[dev];
     ++dt.tick;
-    const size_t bytes = tab.size() * sizeof(DevBlock);
     for (TableEntry& e : dt.entries) {
-        if (e.key.size() == tab.size() && std::memcmp(e.key.data(), tab.data(), bytes) == 0) {
-            e.tick = dt.tick;
-            if (!e.ready_seen) {
-                if (hipEventQuery(e.ready) == hipSuccess) {
-                    e.ready_seen = true;
-                } else if (stream != e.upload_stream) {
-                    err = hipStreamWaitEvent(static_cast<hipStream_t>(stream), e.ready, 0);
-                    if (err != hipSuccess) return hip_fail(err, "hipStreamWaitEvent");
-                }
+        if (!same_table(e, tab, unroll)) continue;
+        e.tick = dt.tick;
+        if (!e.ready_seen) {
+            if (hipEventQuery(e.ready) == hipSuccess) {
+                e.ready_seen = true;
+            } else if (stream != e.upload_stream) {
+                err = hipStreamWaitEvent(static_cast<hipStream_t>(stream), e.ready, 0);
+                if (err != hipSuccess) return hip_fail(err, "hipStreamWaitEvent");
             }
-            *out = e.dev;
-            return LSO_OK;
         }
+        args.blocks = static_cast<const DevBlock*>(e.dev);
+        args.chunk_block = e.has_index
+            ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(e.dev) + tab.size() * sizeof(DevBlock))
+            : nullptr;
+        return LSO_OK;
+    }
+    // a new table: its addresses are checked once, here
+    if (!geometry_checked) {
+        lso_status s = validate_geometry(blocks, n);
+        if (s != LSO_OK) return s;
     }
     if (dt.entries.size() >= kCacheCap) {
         auto lru = std::min_element(dt.entries.begin(), dt.entries.end(),
@@ -253,24 +273,38 @@ lso_status device_table(const std::vector<DevBlock>& tab, void* stream, const De
     }
     TableEntry e;
     e.key = tab;
+    e.unroll = unroll;
     e.tick = dt.tick;
     e.upload_stream = stream;
-    if (hipMalloc(reinterpret_cast<void**>(&e.dev), bytes) != hipSuccess) {
+    e.has_index = total_chunks <= kMaxIndexChunks;
+    const size_t tab_bytes = tab.size() * sizeof(DevBlock);
+    const size_t bytes = tab_bytes + (e.has_index ? total_chunks * sizeof(uint32_t) : 0);
+    if (hipMalloc(&e.dev, bytes) != hipSuccess) {
         free_entry(e);
         return fail(LSO_E_NOMEM, "hipMalloc of a %zu-byte block table failed", bytes);
     }
-    if (hipHostMalloc(reinterpret_cast<void**>(&e.pinned), bytes, hipHostMallocDefault) != hipSuccess) {
+    if (hipHostMalloc(&e.pinned, bytes, hipHostMallocDefault) != hipSuccess) {
         free_entry(e);
         return fail(LSO_E_NOMEM, "hipHostMalloc of a %zu-byte block table failed", bytes);
     }
-    std::memcpy(e.pinned, tab.data(), bytes);
+    std::memcpy(e.pinned, tab.data(), tab_bytes);
+    if (e.has_index) {
+        uint32_t* idx = reinterpret_cast<uint32_t*>(static_cast<char*>(e.pinned) + tab_bytes);
+        for (size_t k = 0; k < tab.size(); ++k) {
+            const uint64_t end = k + 1 < tab.size() ? tab[k + 1].chunk0 : total_chunks;
+            for (uint64_t c = tab[k].chunk0; c < end; ++c) idx[c] = static_cast<uint32_t>(k);
+        }
+    }
     err = hipEventCreateWithFlags(&e.ready, hipEventDisableTiming);
     if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipEventCreateWithFlags"); }
     err = hipMemcpyAsync(e.dev, e.pinned, bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipMemcpyAsync (block table)"); }
     err = hipEventRecord(e.ready, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipEventRecord"); }
-    *out = e.dev;
+    args.blocks = static_cast<const DevBlock*>(e.dev);
+    args.chunk_block = e.has_index
+        ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(e.dev) + tab_bytes)
+        : nullptr;
     dt.entries.push_back(std::move(e));
     return LSO_OK;
 }
@@ -281,25 +315,37 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
 {
     if (n == 0) return LSO_OK;
     if (!blocks) return fail(LSO_E_INVALID, "blocks is NULL");
+    // per-thread scratch, reused across calls (no allocation in steady state)
+    thread_local std::vector<HyperKey> sets;
+    thread_local std::vector<uint32_t> set_of;
+    thread_local std::vector<DevBlock> tab;
+    sets.clear();
+    set_of.resize(n);
+    uint64_t total_elems = 0;
     for (size_t i = 0; i < n; ++i) {
         lso_status s = check_fields(blocks[i], i);
         if (s != LSO_OK) return s;
-    }
-    // distinct constant sets, in order of first appearance
-    std::vector<HyperKey> sets;
-    std::vector<uint32_t> set_of(n);
-    for (size_t i = 0; i < n; ++i) {
         const HyperKey k = key_of(blocks[i]);
         size_t j = 0;
         while (j < sets.size() && !(sets[j] == k)) ++j;
         if (j == sets.size()) sets.push_back(k);
         set_of[i] = static_cast<uint32_t>(j);
+        total_elems += blocks[i].n;
     }
+    const int unroll = total_elems < kSmallCallElems ? kUnrollSmall : kUnrollLarge;
+    const uint64_t chunk = chunk_elems(unroll);
     const size_t launches = (sets.size() + kMaxGroups - 1) / kMaxGroups;
     bool checked = geometry_checked;
+    if (launches > 1 && !checked) {
+        // overlaps across the launches of one call are checked up front, so
+        // an error never follows a launch already enqueued
+        lso_status s = validate_geometry(blocks, n);
+        if (s != LSO_OK) return s;
+        checked = true;
+    }
     for (size_t L = 0; L < launches; ++L) {
         KernelArgs args{};
-        std::vector<DevBlock> tab;
+        tab.clear();
         uint64_t chunks = 0;
         for (size_t i = 0; i < n; ++i) {
             if (set_of[i] / kMaxGroups != L) continue;
@@ -318,7 +364,7 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
             d.chunk0 = chunks;
             d.group = set_of[i] % kMaxGroups;
             d.flags = (b.opt == LSO_OPT_SGD ? kFlagSgd : 0u) | (d.w ? kFlagWeight : 0u);
-            chunks += (b.n + kChunk - 1) / kChunk;
+            chunks += (b.n + chunk - 1) / chunk;
             tab.push_back(d);
         }
         for (size_t j = L * kMaxGroups; j < sets.size() && j < (L + 1) * kMaxGroups; ++j) {
@@ -335,35 +381,11 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
                 checked = true;
             }
             for (size_t j = 0; j < tab.size(); ++j) args.inl[j] = tab[j];
-            args.blocks = nullptr;
         } else {
-            // a table seen before was validated when it entered the cache
-            const DevBlock* dev_tab = nullptr;
-            bool cached = false;
-            {
-                int dev = 0;
-                (void)hipGetDevice(&dev);
-                std::lock_guard<std::mutex> lock(g_mu);
-                auto it = g_tables.find(dev);
-                if (it != g_tables.end()) {
-                    const size_t bytes = tab.size() * sizeof(DevBlock);
-                    for (const TableEntry& e : it->second.entries)
-                        if (e.key.size() == tab.size() && std::memcmp(e.key.data(), tab.data(), bytes) == 0) {
-                            cached = true;
-                            break;
-                        }
-                }
-            }
-            if (!cached && !checked) {
-                lso_status s = validate_geometry(blocks, n);
-                if (s != LSO_OK) return s;
-                checked = true;
-            }
-            lso_status s = device_table(tab, stream, &dev_tab);
+            lso_status s = device_table(blocks, n, checked, tab, chunks, unroll, stream, args);
             if (s != LSO_OK) return s;
-            args.blocks = dev_tab;
         }
-        int err = launch_fused_adam(args, 0, stream);
+        int err = launch_fused_adam(args, unroll, stream);
         if (err != 0) return hip_fail(err, "fused Adam launch");
     }
     return LSO_OK;
