@@ -201,38 +201,24 @@ def copy_ceiling(torch, dev, nbytes=8 << 30) -> float:
 
 # ------------------------------------------------------------ streamed path
 
-def link_peak(torch, nbytes=4 << 30):
-    """Host-link GB/s with pinned buffers: H2D alone, D2H alone, and each
-    direction while both run concurrently on two streams."""
-    import layer_streamed_optimizer_amd as lso
-    h1, h2 = lso.host_alloc(nbytes), lso.host_alloc(nbytes)
-    d1 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    d2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                   ctypes.c_void_p]
-    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-
-    def timed(fn, reps=3):
-        best = 1e30
-        for _ in range(reps):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            fn()
-            torch.cuda.synchronize()
-            best = min(best, time.perf_counter() - t0)
-        return best
-
-    h2d = lambda: hip.hipMemcpyAsync(d1.data_ptr(), h1.ptr, nbytes, 1, s1.cuda_stream)
-    d2h = lambda: hip.hipMemcpyAsync(h2.ptr, d2.data_ptr(), nbytes, 2, s2.cuda_stream)
-    t_h2d = timed(h2d)
-    t_d2h = timed(d2h)
-    t_both = timed(lambda: (h2d(), d2h()))
-    del d1, d2
-    h1.close()
-    h2.close()
-    return dict(h2d=nbytes / t_h2d / 1e9, d2h=nbytes / t_d2h / 1e9,
-                bidir_each=nbytes / t_both / 1e9, bidir_total=2 * nbytes / t_both / 1e9)
+def link_peak(nbytes=4 << 30):
+    """Host-link GB/s with page-locked buffers, measured by the probe
+    library on its own two streams: each direction alone, and each direction
+    while both run at once -- with the DMA engines and with copy kernels
+    (the engine the layer stream uses).  The streamed roofline takes the
+    best concurrent figure, per direction."""
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    res = {}
+    for name, mode in (("dma", 0), ("kernel", 3)):
+        out = (ctypes.c_double * 4)()
+        rc = P.lso_probe_link_mode(nbytes, 3, mode, 128, out)
+        if rc != 0:
+            raise RuntimeError(f"lso_probe_link_mode failed ({rc})")
+        res[name] = dict(h2d=out[0], d2h=out[1], bidir_h2d=out[2], bidir_d2h=out[3])
+    res["bidir_per_direction"] = max(min(r["bidir_h2d"], r["bidir_d2h"])
+                                     for r in (res["dma"], res["kernel"]))
+    return res
 
 
 def streamed(args, w):
@@ -245,28 +231,35 @@ def streamed(args, w):
 
     torch.cuda.set_device(0)
     sid = configs.STREAM_ID[w.key]
-    n_layers = len(w.blocks)
+    n_layers = args.layers or len(w.blocks)
     n = w.blocks[0].n
     om, omm, ov, nbytes = configs.host_layer_layout(n)
-    peak = link_peak(torch)
+    peak = link_peak()
     progress(f"link: {peak}")
-    progress(f"{w.key}: pinning {n_layers} x {nbytes / 1e9:.2f} GB host blocks")
-    hosts = []
+    pinned = args.host_memory == "pinned"
+    progress(f"{w.key}: {n_layers} x {nbytes / 1e9:.2f} GB host blocks, "
+             f"{'pinned' if pinned else 'pageable (staged through two pinned buffers)'}")
+    hosts, ptrs = [], []
     hs = torch.cuda.current_stream().cuda_stream
     stage = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
     for b in range(n_layers):
-        hb = lso.host_alloc(nbytes)
+        if pinned:
+            hb = lso.host_alloc(nbytes)
+            ptr = hb.ptr
+        else:
+            hb = np.empty(nbytes, dtype=np.uint8)
+            ptr = hb.ctypes.data
         # initial state made on the device and copied down (untimed)
         synth.device_fill_zero(int(stage.data_ptr()), nbytes, hs)
         synth.device_fill_normal_f32(int(stage.data_ptr()) + om, n, stream=sid, block=b,
                                      purpose=synth.PURPOSE_MASTER, step=0,
                                      sigma=configs.MASTER_SIGMA, hip_stream=hs)
         torch.cuda.synchronize()
-        ctypes.memmove(hb.ptr, 0, 0)  # touch nothing; keep the handle
-        hip = ctypes.CDLL("libamdhip64.so")
-        hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
-        assert hip.hipMemcpy(hb.ptr, int(stage.data_ptr()), nbytes, 2) == 0
+        assert hip.hipMemcpy(ptr, int(stage.data_ptr()), nbytes, 2) == 0
         hosts.append(hb)
+        ptrs.append(ptr)
         progress(f"layer {b} ready")
     del stage
     fn, Params = synth.grad_callback()
@@ -275,7 +268,7 @@ def streamed(args, w):
     ls = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
     L = lso.LayerStream.layers(n_layers)
     for b in range(n_layers):
-        L[b]["host_base"], L[b]["bytes"], L[b]["n"] = hosts[b].ptr, nbytes, n
+        L[b]["host_base"], L[b]["bytes"], L[b]["n"] = ptrs[b], nbytes, n
         L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
         L[b]["opt"] = lso.LSO_OPT_ADAM
         L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = (configs.LR, configs.BETA1,
@@ -293,19 +286,23 @@ def streamed(args, w):
             step_s.append(dt)
     ls.close()
     wall = sum(step_s)
-    params = w.params
-    link_each = LINK_BYTES_PER_PARAM * params / (wall / len(step_s)) / 1e9
+    params = n * n_layers
+    per_dir = LINK_BYTES_PER_PARAM * params / (wall / len(step_s)) / 1e9
+    bidir_peak = peak["bidir_per_direction"]
     result = dict(
         metric=METRIC, value=params * len(step_s) / wall / 1e9, unit="Gparams/s",
         ms_per_step=wall * 1e3 / len(step_s),
-        roofline=dict(bound="host-link", achieved=link_each, peak=peak["bidir_each"],
-                      unit="GB/s per direction", frac=link_each / peak["bidir_each"], traffic=None),
+        roofline=dict(bound="host-link", achieved=per_dir, peak=bidir_peak,
+                      unit="GB/s per direction", frac=per_dir / bidir_peak, traffic=None),
         link_peak_GBps=peak,
-        config=dict(workload=f"{w.key}: {w.title}", layers=n_layers, params=params,
-                    host_bytes=nbytes * n_layers, link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
+        config=dict(workload=f"{w.key}: {w.title}", layers=n_layers, layers_in_config=len(w.blocks),
+                    params=params, host_memory="pinned" if pinned else "pageable+staged",
+                    host_bytes=nbytes * n_layers,
+                    link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
     )
     for hb in hosts:
-        hb.close()
+        if pinned:
+            hb.close()
     return result
 
 
@@ -358,6 +355,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-memory", choices=["pageable", "pinned"], default="pageable",
+                    help="c4: authoritative host blocks in pageable memory (staged through two "
+                         "pinned buffers) or page-locked (direct DMA; limited by the host's "
+                         "page-locked budget)")
+    ap.add_argument("--layers", type=int, default=0, help="c4: layers to stream (0 = all 16)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the update is elementwise and would shard by "

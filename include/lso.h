@@ -5,8 +5,8 @@
  *   lso_adam_step      updates blocks that already live in device memory
  *                      (HBM-resident state), one kernel launch per call;
  *   lso_stream_layers  updates layers whose authoritative state lives in
- *                      pinned host memory, streaming each layer in, updating
- *                      it on the GPU and writing it back, double-buffered.
+ *                      host memory, streaming each layer in, updating it on
+ *                      the GPU and writing it back, double-buffered.
  *
  * The update, per element i of a block (all arithmetic below is what the
  * library computes; the pages define it in exact arithmetic):
@@ -130,21 +130,28 @@ lso_status lso_validate_blocks(const lso_block* blocks, size_t n);
 lso_status lso_block_constants(const lso_block* block, float out[8]);
 
 /* ---------------------------------------------------------------------
- * Layer streaming.  The authoritative state of each layer lives in pinned
- * host memory as one contiguous block [master | m | v] (FP32, each
- * sub-array 4 KB aligned inside the block).  For each layer the library
- * copies the block into a device slot (one DMA burst), lets the caller's
- * gradient producer write that layer's BF16 gradients into the slot, runs
- * the fused update on the slot, and copies the block back over the host
- * copy -- so the host holds master + delta afterwards.  Two slots alternate
- * (double buffering) on three streams: H2D waits buffer-free[slot], copies,
+ * Layer streaming.  The authoritative state of each layer lives in host
+ * memory as one contiguous block [master | m | v] (FP32, each sub-array
+ * 4 KB aligned inside the block).  For each layer the library copies the
+ * block into a device slot (one DMA burst), lets the caller's gradient
+ * producer write that layer's BF16 gradients into the slot, runs the fused
+ * update on the slot, and copies the block back over the host copy -- so
+ * the host holds master + delta afterwards.  Two slots alternate (double
+ * buffering) on three streams: H2D waits buffer-free[slot], copies,
  * records weights-ready[slot]; compute waits weights-ready, runs producer
  * and update, records step-done[slot]; D2H waits step-done, copies back,
- * records buffer-free[slot].  No host barrier inside the layer loop.
+ * records buffer-free[slot].
+ * Host blocks may be pinned (lso_host_alloc, or any page-locked HIP host
+ * allocation): the DMA engines then read and write them directly and the
+ * host thread never waits inside the layer loop.  Or they may be ordinary
+ * pageable memory (for state larger than the page-locked budget): each then
+ * passes through one of two pinned CPU-side staging buffers of the context,
+ * copied in by worker threads before its H2D and out after its D2H.
  * ------------------------------------------------------------------- */
 
 typedef struct lso_host_layer {
-    void*    host_base;      /* pinned host block (lso_host_alloc), 4 KB aligned */
+    void*    host_base;      /* host block, pinned or pageable, 16-byte aligned
+                                (lso_host_alloc gives 4 KB-aligned pinned memory) */
     uint64_t bytes;          /* bytes copied each way: covers all three arrays */
     uint64_t n;              /* parameters in the layer */
     uint64_t off_master;     /* byte offsets inside the block, 16-byte aligned */
@@ -170,8 +177,9 @@ typedef struct lso_stream_ctx lso_stream_ctx;
 
 /* Create a streaming context on `device`: three streams, two device slots
  * of max_layer_bytes of state plus max_layer_params BF16 gradients and
- * BF16 weights each, and the events.  fn/user: the gradient producer.
- * Errors: INVALID, NOMEM, HIP.  *out is NULL on error. */
+ * BF16 weights each, and the events (the two pinned staging buffers of
+ * max_layer_bytes are added on the first pageable layer).  fn/user: the
+ * gradient producer.  Errors: INVALID, NOMEM, HIP.  *out is NULL on error. */
 lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params,
                              lso_grad_fn fn, void* user, int device, lso_stream_ctx** out);
 
@@ -179,7 +187,8 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
  * respect to host memory: on LSO_OK every host block holds its updated
  * state.  On LSO_E_CALLBACK at layer k, layers < k are fully written back
  * and layers >= k are untouched on the host.  Validation (bytes, alignment,
- * hyper-parameters) covers all layers before anything is enqueued. */
+ * hyper-parameters) covers all layers before anything is enqueued.  Calls
+ * on one context must not overlap (one caller thread at a time). */
 lso_status lso_stream_layers(lso_stream_ctx* ctx, const lso_host_layer* host_blocks,
                              size_t n_layers);
 

@@ -8,6 +8,7 @@
 //                      the host definition over all 2^32 patterns.
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cstdint>
 
 #include "lso_bf16.h"
@@ -29,6 +30,16 @@ copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16
             reinterpret_cast<const LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(src + i)));
         __builtin_nontemporal_store(x, reinterpret_cast<LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(dst + i)));
     }
+}
+
+// Copy between page-locked host memory and device memory by the shader
+// cores (PCIe reads or writes issued by the kernel itself).
+__global__ void __launch_bounds__(256)
+link_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n16)
+{
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
 }
 
 __global__ void __launch_bounds__(256)
@@ -73,6 +84,101 @@ int lso_probe_bf16_rne(uint32_t first, uint64_t count, uint16_t* out, void* stre
     hipLaunchKernelGGL(bf16_probe_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
                        first, count, out);
     return static_cast<int>(hipGetLastError());
+}
+
+// Host-link rates with page-locked buffers of `bytes` each: out[0] H2D
+// alone, out[1] D2H alone, out[2] H2D and out[3] D2H while both run at once
+// on two streams (best of `reps`), in GB/s.  mode selects the copy engine
+// per direction: bit 0 set = H2D by a copy kernel (else DMA engine), bit 1
+// set = D2H by a copy kernel; grid = workgroups of such a kernel.
+// Returns a hipError_t.
+int lso_probe_link_mode(uint64_t bytes, int reps, int mode, unsigned grid, double out[4]);
+
+int lso_probe_link(uint64_t bytes, int reps, double out[4])
+{
+    return lso_probe_link_mode(bytes, reps, 0, 0, out);
+}
+
+int lso_probe_link_mode(uint64_t bytes, int reps, int mode, unsigned grid, double out[4])
+{
+    if (bytes % 16 != 0 || bytes == 0) return static_cast<int>(hipErrorInvalidValue);
+    if (grid == 0) grid = 256;
+    void *h1 = nullptr, *h2 = nullptr, *d1 = nullptr, *d2 = nullptr;
+    hipStream_t s1 = nullptr, s2 = nullptr;
+    hipError_t err = hipSuccess;
+    auto now = [] { return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count(); };
+    auto best = [&](auto fn) {
+        double b = 1e30;
+        for (int r = 0; r < reps && err == hipSuccess; ++r) {
+            if ((err = hipDeviceSynchronize()) != hipSuccess) break;
+            const double t0 = now();
+            fn();
+            if ((err = hipDeviceSynchronize()) != hipSuccess) break;
+            const double dt = now() - t0;
+            b = dt < b ? dt : b;
+        }
+        return b;
+    };
+    if ((err = hipHostMalloc(&h1, bytes, hipHostMallocDefault)) != hipSuccess) goto done;
+    if ((err = hipHostMalloc(&h2, bytes, hipHostMallocDefault)) != hipSuccess) goto done;
+    if ((err = hipMalloc(&d1, bytes)) != hipSuccess) goto done;
+    if ((err = hipMalloc(&d2, bytes)) != hipSuccess) goto done;
+    if ((err = hipStreamCreateWithFlags(&s1, hipStreamNonBlocking)) != hipSuccess) goto done;
+    if ((err = hipStreamCreateWithFlags(&s2, hipStreamNonBlocking)) != hipSuccess) goto done;
+    {
+        auto h2d = [&] {
+            if (mode & 1) {
+                hipLaunchKernelGGL(link_copy_kernel, dim3(grid), dim3(256), 0, s1,
+                                   static_cast<const u32x4*>(h1), static_cast<u32x4*>(d1), bytes / 16);
+                err = hipGetLastError();
+            } else {
+                err = hipMemcpyAsync(d1, h1, bytes, hipMemcpyHostToDevice, s1);
+            }
+        };
+        auto d2h = [&] {
+            if (mode & 2) {
+                hipLaunchKernelGGL(link_copy_kernel, dim3(grid), dim3(256), 0, s2,
+                                   static_cast<const u32x4*>(d2), static_cast<u32x4*>(h2), bytes / 16);
+                err = hipGetLastError();
+            } else {
+                err = hipMemcpyAsync(h2, d2, bytes, hipMemcpyDeviceToHost, s2);
+            }
+        };
+        const double th = best(h2d);
+        const double td = best(d2h);
+        // concurrent: time each direction by its own stream's completion
+        double bh = 1e30, bd = 1e30;
+        for (int r = 0; r < reps && err == hipSuccess; ++r) {
+            if ((err = hipDeviceSynchronize()) != hipSuccess) break;
+            const double t0 = now();
+            h2d();
+            if (err != hipSuccess) break;
+            d2h();
+            if (err != hipSuccess) break;
+            double t1 = 0, t2 = 0;
+            bool f1 = false, f2 = false;
+            while (!(f1 && f2)) {
+                if (!f1 && hipStreamQuery(s1) == hipSuccess) { f1 = true; t1 = now() - t0; }
+                if (!f2 && hipStreamQuery(s2) == hipSuccess) { f2 = true; t2 = now() - t0; }
+            }
+            bh = t1 < bh ? t1 : bh;
+            bd = t2 < bd ? t2 : bd;
+        }
+        if (err == hipSuccess) {
+            out[0] = bytes / th / 1e9;
+            out[1] = bytes / td / 1e9;
+            out[2] = bytes / bh / 1e9;
+            out[3] = bytes / bd / 1e9;
+        }
+    }
+done:
+    if (s1) (void)hipStreamDestroy(s1);
+    if (s2) (void)hipStreamDestroy(s2);
+    if (d1) (void)hipFree(d1);
+    if (d2) (void)hipFree(d2);
+    if (h1) (void)hipHostFree(h1);
+    if (h2) (void)hipHostFree(h2);
+    return static_cast<int>(err);
 }
 
 }  // extern "C"

@@ -1,0 +1,189 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times, on sampled outputs.
+
+The state of the 1.1B / 6.7B-parameter workloads is initialised and its
+gradients drawn on the device (device input generator); the oracle rebuilds
+just the sampled elements from the host input generator (same counter-based
+generator, bit-identical -- checked by test_gpu_stream) and runs the same
+steps on them.  Samples per block: 65,536 elements at offset 0, the last
+65,536 (ragged end), and six seeded 16-aligned offsets.
+"""
+import numpy as np
+import pytest
+
+import layer_streamed_optimizer_amd as lso
+import oracle
+import synth
+from layer_streamed_optimizer_amd import configs
+
+from gpu_util import assert_parity, call_scale, log, max_errors, torch
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 65536
+
+
+def sample_offsets(n, seed):
+    if n <= SAMPLE:
+        return [(0, n)]
+    rng = np.random.default_rng(seed)
+    offs = {0, n - SAMPLE}
+    while len(offs) < 8:
+        offs.add(int(rng.integers(0, (n - SAMPLE) // 16)) * 16)
+    return [(o, SAMPLE) for o in sorted(offs)]
+
+
+def init_kind(spec):
+    if spec.init == "zero":
+        return None
+    if spec.init == "lora_a":
+        return synth.PURPOSE_LORA_A, configs.LORA_A_SIGMA
+    return synth.PURPOSE_MASTER, configs.MASTER_SIGMA
+
+
+def run_resident_sampled(key, steps):
+    T = torch()
+    w = configs.get(key)
+    sid = configs.STREAM_ID[key]
+    sizes = [b.n for b in w.blocks]
+    lay = configs.ResidentLayout(sizes)
+    log(f"{key}: {w.params:,} params, {len(sizes)} blocks, {steps} steps")
+    hs = T.cuda.current_stream().cuda_stream
+    state = T.empty(lay.state_bytes, dtype=T.uint8, device="cuda")
+    grad = T.empty(lay.grad_bytes, dtype=T.uint8, device="cuda")
+    weight = T.empty(lay.weight_bytes, dtype=T.uint8, device="cuda")
+    sb, gb, wb = int(state.data_ptr()), int(grad.data_ptr()), int(weight.data_ptr())
+    for b, spec in enumerate(w.blocks):
+        kind = init_kind(spec)
+        if kind is None:
+            synth.device_fill_zero(sb + lay.off_master[b], 4 * spec.n, hs)
+        else:
+            synth.device_fill_normal_f32(sb + lay.off_master[b], spec.n, stream=sid, block=b,
+                                         purpose=kind[0], step=0, sigma=kind[1], hip_stream=hs)
+        synth.device_fill_zero(sb + lay.off_m[b], 4 * spec.n, hs)
+        synth.device_fill_zero(sb + lay.off_v[b], 4 * spec.n, hs)
+    rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
+                 grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b])
+            for b, n in enumerate(sizes)]
+    table = lso.BlockTable.from_rows(rows)
+    for t in range(1, steps + 1):
+        for b, n in enumerate(sizes):
+            synth.device_fill_normal_bf16(gb + lay.off_grad[b], n, stream=sid, block=b,
+                                          purpose=synth.PURPOSE_GRAD, step=t,
+                                          sigma=configs.GRAD_SIGMA, hip_stream=hs)
+        table.set_step(t)
+        lso.adam_step(table, hs)
+    T.cuda.synchronize()
+    # oracle on the samples
+    refs, gots, where = [], [], []
+    for b, spec in enumerate(w.blocks):
+        for off, ln in sample_offsets(spec.n, 1000 + b):
+            kind = init_kind(spec)
+            if kind is None:
+                master = np.zeros(ln, np.float32)
+            else:
+                master = synth.normal_f32(ln, stream=sid, block=b, purpose=kind[0], step=0,
+                                          sigma=kind[1], start=off)
+            ref = dict(master=master, m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32),
+                       weight=np.zeros(ln, np.uint16))
+            for t in range(1, steps + 1):
+                g = synth.normal_bf16(ln, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=t,
+                                      sigma=configs.GRAD_SIGMA, start=off)
+                oracle.adam_step(ref["master"], ref["m"], ref["v"], g, ref["weight"], t,
+                                 configs.LR, configs.BETA1, configs.BETA2, configs.EPS)
+
+            def rd(buf, byte_off, es, dt):
+                return buf[byte_off: byte_off + es * ln].cpu().numpy().view(dt)
+
+            got = dict(master=rd(state, lay.off_master[b] + 4 * off, 4, np.float32),
+                       m=rd(state, lay.off_m[b] + 4 * off, 4, np.float32),
+                       v=rd(state, lay.off_v[b] + 4 * off, 4, np.float32),
+                       weight=rd(weight, lay.off_weight[b] + 2 * off, 2, np.uint16))
+            refs.append(ref)
+            gots.append(got)
+            where.append((b, off))
+    scale = call_scale(refs)
+    worst = {}
+    for ref, got, (b, off) in zip(refs, gots, where):
+        assert_parity(got, ref, 1e-6, f"{key} block {b} offset {off}", scale)
+        for k, v in max_errors(got, ref, scale).items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    log(f"{key} sampled max errors after {steps} steps", worst)
+    del state, grad, weight
+    T.cuda.empty_cache()
+
+
+def test_c1_tinyllama_full_size_sampled():
+    run_resident_sampled("c1", 10)
+
+
+def test_c3_llama7b_full_size_sampled():
+    T = torch()
+    free, _ = T.cuda.mem_get_info()
+    if free < 130e9:
+        pytest.skip("needs ~125 GB of free device memory")
+    run_resident_sampled("c3", 5)
+
+
+def test_c4_layer_shape_streamed_sampled():
+    """Three full 70B-shaped layers (855,654,400 params each, 10.27 GB host
+    blocks) streamed for three steps through the same two-slot pipeline the
+    benchmark times; sampled parity of the authoritative host state."""
+    import ctypes
+    T = torch()
+    sid = configs.STREAM_ID["c4"]
+    n = configs.layer_params(**configs.LLAMA70B)
+    om, omm, ov, nbytes = configs.host_layer_layout(n)
+    n_layers, steps = 3, 3
+    log(f"c4 layer shape: {n_layers} x {n:,} params, {nbytes / 1e9:.2f} GB host blocks")
+    hs = T.cuda.current_stream().cuda_stream
+    hosts = []
+    stage = T.empty(nbytes, dtype=T.uint8, device="cuda")
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    for b in range(n_layers):
+        hb = lso.host_alloc(nbytes)
+        synth.device_fill_zero(int(stage.data_ptr()), nbytes, hs)
+        synth.device_fill_normal_f32(int(stage.data_ptr()) + om, n, stream=sid, block=b,
+                                     purpose=synth.PURPOSE_MASTER, step=0,
+                                     sigma=configs.MASTER_SIGMA, hip_stream=hs)
+        T.cuda.synchronize()
+        assert hip.hipMemcpy(hb.ptr, int(stage.data_ptr()), nbytes, 2) == 0
+        hosts.append(hb)
+    del stage
+    fn, Params = synth.grad_callback()
+    prm = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
+                 scale=synth.scale_for(configs.GRAD_SIGMA), block_base=0)
+    ls = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
+    L = lso.LayerStream.layers(n_layers)
+    for b in range(n_layers):
+        L[b]["host_base"], L[b]["bytes"], L[b]["n"] = hosts[b].ptr, nbytes, n
+        L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
+        L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = (configs.LR, configs.BETA1,
+                                                                 configs.BETA2, configs.EPS)
+    for t in range(1, steps + 1):
+        prm.step = t
+        L["t"] = t
+        log(f"c4 streamed step {t}")
+        ls.stream_layers(L)
+    ls.close()
+    refs, gots = [], []
+    for b in range(n_layers):
+        for off, ln in sample_offsets(n, 2000 + b):
+            ref = dict(master=synth.normal_f32(ln, stream=sid, block=b, purpose=synth.PURPOSE_MASTER,
+                                               step=0, sigma=configs.MASTER_SIGMA, start=off),
+                       m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32))
+            for t in range(1, steps + 1):
+                g = synth.normal_bf16(ln, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=t,
+                                      sigma=configs.GRAD_SIGMA, start=off)
+                oracle.adam_step(ref["master"], ref["m"], ref["v"], g, None, t, configs.LR,
+                                 configs.BETA1, configs.BETA2, configs.EPS)
+            got = {q: hosts[b].view(np.float32, o + 4 * off, ln).copy()
+                   for q, o in (("master", om), ("m", omm), ("v", ov))}
+            refs.append(ref)
+            gots.append(got)
+    scale = call_scale(refs)
+    for i, (ref, got) in enumerate(zip(refs, gots)):
+        assert_parity(got, ref, 1e-6, f"c4 sample {i}", scale)
+    for hb in hosts:
+        hb.close()

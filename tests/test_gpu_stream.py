@@ -18,15 +18,34 @@ pytestmark = pytest.mark.gpu
 LR, B1, B2, EPS = configs.LR, configs.BETA1, configs.BETA2, configs.EPS
 
 
-class HostLayers:
-    """Authoritative pinned host blocks [master | m | v], one per layer."""
+class _Pageable:
+    """Ordinary (pageable) host memory with the HostBuffer interface."""
 
-    def __init__(self, sizes, sid):
+    def __init__(self, nbytes):
+        self.arr = np.empty(nbytes + 64, np.uint8)
+        shift = (-self.arr.ctypes.data) % 64
+        self.ptr = self.arr.ctypes.data + shift
+        self.nbytes = nbytes
+        self._shift = shift
+
+    def view(self, dtype=np.uint8, offset=0, count=None):
+        dt = np.dtype(dtype)
+        if count is None:
+            count = (self.nbytes - offset) // dt.itemsize
+        return self.arr[self._shift + offset:self._shift + offset + count * dt.itemsize].view(dt)
+
+
+class HostLayers:
+    """Authoritative host blocks [master | m | v], one per layer: pinned
+    (lso_host_alloc) or pageable, per layer."""
+
+    def __init__(self, sizes, sid, pageable=False):
         self.sizes = sizes
         self.bufs, self.lay = [], []
         for b, n in enumerate(sizes):
             om, omm, ov, nbytes = configs.host_layer_layout(n)
-            hb = lso.host_alloc(nbytes)
+            pg = pageable(b) if callable(pageable) else pageable
+            hb = _Pageable(nbytes) if pg else lso.host_alloc(nbytes)
             hb.view(np.uint8)[:] = 0
             hb.view(np.float32, om, n)[:] = synth.normal_f32(n, stream=sid, block=b, purpose=0,
                                                              step=0, sigma=0.02)
@@ -201,3 +220,54 @@ def test_device_generator_matches_host_generator():
                                            start=12345))
     assert np.array_equal(g.cpu().numpy().view(np.uint16),
                           synth.normal_bf16(n, stream=7, block=3, purpose=2, step=9, sigma=1e-3))
+
+
+def test_pageable_and_mixed_host_blocks_equal_pinned_bitwise():
+    """Pageable authoritative blocks go through the pinned staging buffers;
+    the result is bit-identical to pinned blocks (all pageable, and
+    alternating pinned / pageable layers)."""
+    T = torch()
+    sizes = [300007, 262144, 5, 131072 + 3, 77777]
+    sid = 44
+    ref = HostLayers(sizes, sid)
+    pag = HostLayers(sizes, sid, pageable=True)
+    mix = HostLayers(sizes, sid, pageable=lambda b: b % 2 == 1)
+    ls, params = synth_stream(sizes, sid)
+    for t in range(1, 4):
+        params.step = t
+        log("pinned / pageable / mixed step", t)
+        for h in (ref, pag, mix):
+            ls.stream_layers(h.table(t))
+    T.cuda.synchronize()
+    for b in range(len(sizes)):
+        for q in ("master", "m", "v"):
+            x = ref.get(b, q).view(np.uint32)
+            assert np.array_equal(x, pag.get(b, q).view(np.uint32)), ("pageable", b, q)
+            assert np.array_equal(x, mix.get(b, q).view(np.uint32)), ("mixed", b, q)
+    ls.close()
+
+
+def test_pageable_producer_failure_leaves_later_layers_untouched():
+    T = torch()
+    sizes = [40000] * 5
+    sid = 45
+    host = HostLayers(sizes, sid, pageable=True)
+    before = [host.get(b, "master") for b in range(5)]
+    fill = synth._dev_lib().synth_fill_normal_bf16
+
+    def producer(layer, dev_grad, n, stream):
+        if layer == 3:
+            return 9
+        return fill(dev_grad, n, 0, synth.SEED, sid, layer, 2, 1, synth.scale_for(1e-3), stream)
+
+    ls = lso.LayerStream(configs.host_layer_layout(40000)[3], 40000, producer)
+    assert ls.stream_layers_status(host.table(1)) == lso._native.LSO_E_CALLBACK
+    for b in range(5):
+        now = host.get(b, "master")
+        if b < 3:
+            assert not np.array_equal(now, before[b]), b
+            assert np.any(host.get(b, "v") != 0), b
+        else:
+            assert np.array_equal(now.view(np.uint32), before[b].view(np.uint32)), b
+            assert not np.any(host.get(b, "m")), b
+    ls.close()
