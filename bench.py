@@ -26,7 +26,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import re
@@ -40,7 +39,6 @@ METRIC = "Gparams/s Adam step; % HBM peak (resident) / % host-link peak (streame
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BYTES_PER_PARAM = 28            # algorithmic, resident kernel
 LINK_BYTES_PER_PARAM = 12       # streamed: [master | m | v] each way
-KERNEL_SOURCE = os.path.join(ROOT, "layer_streamed_optimizer_amd", "csrc", "lso_adam.hip")
 
 
 def progress(*a):
@@ -48,11 +46,8 @@ def progress(*a):
 
 
 def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for name in ("lso_adam.hip", "lso_internal.h", "lso_bf16.h"):
-        with open(os.path.join(ROOT, "layer_streamed_optimizer_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from layer_streamed_optimizer_amd.rocprof_summary import kernel_hash as kh
+    return kh()
 
 
 def measured_traffic(workload: str):

@@ -13,7 +13,7 @@
 
 #include <cstdint>
 
-#include "lso_internal.h"
+#include "lso_copy.h"
 
 namespace lso {
 namespace {

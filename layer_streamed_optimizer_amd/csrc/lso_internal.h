@@ -65,11 +65,6 @@ struct KernelArgs {
     DevBlock inl[kInline];
 };
 
-// Copy bytes between page-locked host memory and device memory with a
-// copy kernel on stream (lso_copy.hip); both pointers 16-byte aligned.
-constexpr unsigned kCopyGrid = 128;
-int launch_block_copy(void* dst, const void* src, uint64_t bytes, unsigned max_grid, void* stream);
-
 // Enqueue the fused kernel (defined in lso_adam.hip) with chunks of
 // chunk_elems(unroll) elements.  Returns the hipError_t of the launch.
 int launch_fused_adam(const KernelArgs& args, int unroll, void* stream);

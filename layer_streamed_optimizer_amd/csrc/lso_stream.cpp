@@ -42,7 +42,7 @@
 #include <thread>
 #include <vector>
 
-#include "lso_internal.h"
+#include "lso_copy.h"
 #include "lso_runtime.h"
 
 namespace {
