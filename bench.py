@@ -77,34 +77,45 @@ def resident(args, w):
     torch.cuda.set_device(dev)
     sid = configs.STREAM_ID[w.key]
     sizes = [b.n for b in w.blocks]
-    lay = configs.ResidentLayout(sizes)
+    tiled = args.layout == "tiled"
+    lay = configs.ResidentLayout(sizes, tiled=tiled)
     params = w.params
     total_steps = args.warmup + args.steps
     free, _total = torch.cuda.mem_get_info()
     budget = free - lay.state_bytes - lay.weight_bytes - (8 << 30)
     n_sets = max(1, min(total_steps, budget // max(lay.grad_bytes, 1)))
-    progress(f"{w.key}: {len(sizes)} blocks, {params:,} params, state {lay.state_bytes / 1e9:.1f} GB, "
-             f"{n_sets} gradient sets of {lay.grad_bytes / 1e9:.2f} GB")
+    progress(f"{w.key}: {len(sizes)} blocks, {params:,} params, {args.layout} state "
+             f"{lay.state_bytes / 1e9:.1f} GB, {n_sets} gradient sets of {lay.grad_bytes / 1e9:.2f} GB")
     stream = torch.cuda.current_stream()
     hs = int(stream.cuda_stream)
     state = torch.empty(lay.state_bytes, dtype=torch.uint8, device=dev)
     weight = torch.empty(lay.weight_bytes, dtype=torch.uint8, device=dev)
     grads = [torch.empty(lay.grad_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
     sb, wb = int(state.data_ptr()), int(weight.data_ptr())
+    scratch = torch.empty(max(sizes), dtype=torch.float32, device=dev) if tiled else None
+
+    def fill_master(dst, b, spec):
+        n = spec.n
+        if spec.init == "zero":
+            synth.device_fill_zero(dst, 4 * n, hs)
+        else:
+            lora = spec.init == "lora_a"
+            synth.device_fill_normal_f32(
+                dst, n, stream=sid, block=b,
+                purpose=synth.PURPOSE_LORA_A if lora else synth.PURPOSE_MASTER, step=0,
+                sigma=configs.LORA_A_SIGMA if lora else configs.MASTER_SIGMA, hip_stream=hs)
 
     def init_state():
         for b, spec in enumerate(w.blocks):
-            n = spec.n
-            if spec.init == "zero":
-                synth.device_fill_zero(sb + lay.off_master[b], 4 * n, hs)
+            if tiled:
+                # master drawn planar, packed with m = v = 0 into the tiled region
+                fill_master(int(scratch.data_ptr()), b, spec)
+                lso.tiled_pack(sb + lay.off_master[b], int(scratch.data_ptr()), None, None,
+                               n=spec.n, stream=hs)
             else:
-                lora = spec.init == "lora_a"
-                synth.device_fill_normal_f32(
-                    sb + lay.off_master[b], n, stream=sid, block=b,
-                    purpose=synth.PURPOSE_LORA_A if lora else synth.PURPOSE_MASTER, step=0,
-                    sigma=configs.LORA_A_SIGMA if lora else configs.MASTER_SIGMA, hip_stream=hs)
-            synth.device_fill_zero(sb + lay.off_m[b], 4 * n, hs)
-            synth.device_fill_zero(sb + lay.off_v[b], 4 * n, hs)
+                fill_master(sb + lay.off_master[b], b, spec)
+                synth.device_fill_zero(sb + lay.off_m[b], 4 * spec.n, hs)
+                synth.device_fill_zero(sb + lay.off_v[b], 4 * spec.n, hs)
 
     init_state()
     for r in range(n_sets):
@@ -118,7 +129,8 @@ def resident(args, w):
         gb = int(grads[r].data_ptr())
         rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
                      grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], t=1,
-                     lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2, eps=configs.EPS)
+                     lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2, eps=configs.EPS,
+                     layout=lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR)
                 for b, n in enumerate(sizes)]
         tables.append(lso.BlockTable.from_rows(rows))
     # Upload every table once outside the timed region: an lr = 0 step
@@ -164,11 +176,11 @@ def resident(args, w):
         kernel_avg_us=avg_ms * 1e3, kernel_min_us=min(kernel_ms) * 1e3,
         hbm_copy_ceiling_GBps=ceiling,
         config=dict(workload=f"{w.key}: {w.title}", blocks=len(sizes), params=params,
-                    bytes_per_param=BYTES_PER_PARAM, gradient_sets=n_sets,
+                    state_layout=args.layout, bytes_per_param=BYTES_PER_PARAM, gradient_sets=n_sets,
                     hyper=dict(lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2,
                                eps=configs.EPS)),
     )
-    del state, weight, grads
+    del state, weight, grads, scratch
     return result
 
 
@@ -228,7 +240,8 @@ def streamed(args, w):
     sid = configs.STREAM_ID[w.key]
     n_layers = args.layers or len(w.blocks)
     n = w.blocks[0].n
-    om, omm, ov, nbytes = configs.host_layer_layout(n)
+    tiled = args.layout == "tiled"
+    om, omm, ov, nbytes = configs.host_layer_layout(n, tiled=tiled)
     peak = link_peak()
     progress(f"link: {peak}")
     pinned = args.host_memory == "pinned"
@@ -237,6 +250,7 @@ def streamed(args, w):
     hosts, ptrs = [], []
     hs = torch.cuda.current_stream().cuda_stream
     stage = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(n, dtype=torch.float32, device="cuda") if tiled else None
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
     for b in range(n_layers):
@@ -248,15 +262,22 @@ def streamed(args, w):
             ptr = hb.ctypes.data
         # initial state made on the device and copied down (untimed)
         synth.device_fill_zero(int(stage.data_ptr()), nbytes, hs)
-        synth.device_fill_normal_f32(int(stage.data_ptr()) + om, n, stream=sid, block=b,
-                                     purpose=synth.PURPOSE_MASTER, step=0,
-                                     sigma=configs.MASTER_SIGMA, hip_stream=hs)
+        if tiled:
+            synth.device_fill_normal_f32(int(scratch.data_ptr()), n, stream=sid, block=b,
+                                         purpose=synth.PURPOSE_MASTER, step=0,
+                                         sigma=configs.MASTER_SIGMA, hip_stream=hs)
+            lso.tiled_pack(int(stage.data_ptr()) + om, int(scratch.data_ptr()), None, None, n=n,
+                           stream=hs)
+        else:
+            synth.device_fill_normal_f32(int(stage.data_ptr()) + om, n, stream=sid, block=b,
+                                         purpose=synth.PURPOSE_MASTER, step=0,
+                                         sigma=configs.MASTER_SIGMA, hip_stream=hs)
         torch.cuda.synchronize()
         assert hip.hipMemcpy(ptr, int(stage.data_ptr()), nbytes, 2) == 0
         hosts.append(hb)
         ptrs.append(ptr)
         progress(f"layer {b} ready")
-    del stage
+    del stage, scratch
     fn, Params = synth.grad_callback()
     prm = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
                  scale=synth.scale_for(configs.GRAD_SIGMA), block_base=0)
@@ -266,6 +287,7 @@ def streamed(args, w):
         L[b]["host_base"], L[b]["bytes"], L[b]["n"] = ptrs[b], nbytes, n
         L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
         L[b]["opt"] = lso.LSO_OPT_ADAM
+        L[b]["layout"] = lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR
         L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = (configs.LR, configs.BETA1,
                                                                  configs.BETA2, configs.EPS)
     step_s = []
@@ -292,6 +314,7 @@ def streamed(args, w):
         link_peak_GBps=peak,
         config=dict(workload=f"{w.key}: {w.title}", layers=n_layers, layers_in_config=len(w.blocks),
                     params=params, host_memory="pinned" if pinned else "pageable+staged",
+                    state_layout=args.layout,
                     host_bytes=nbytes * n_layers,
                     link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
     )
@@ -355,6 +378,8 @@ def main():
                          "pinned buffers) or page-locked (direct DMA; limited by the host's "
                          "page-locked budget)")
     ap.add_argument("--layers", type=int, default=0, help="c4: layers to stream (0 = all 16)")
+    ap.add_argument("--layout", choices=["tiled", "planar"], default=None,
+                    help="FP32 state layout (default: tiled for c1, c3, c4; planar for c0, c2)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the update is elementwise and would shard by "
@@ -365,6 +390,8 @@ def main():
     w = configs.get(args.config)
     defaults = {"c0": (3, 10), "c1": (2, 10), "c2": (5, 100), "c3": (1, 4), "c4": (1, 2)}
     dw, dk = defaults[args.config]
+    if args.layout is None:
+        args.layout = "planar" if args.config in ("c0", "c2") else "tiled"
     args.warmup = dw if args.warmup is None else args.warmup
     args.steps = dk if args.steps is None else args.steps
     if args.steps < 1:

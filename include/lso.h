@@ -69,18 +69,39 @@ typedef enum lso_status {
 typedef enum lso_dtype { LSO_DT_NONE = 0, LSO_DT_F32 = 1, LSO_DT_BF16 = 2 } lso_dtype;
 typedef enum lso_opt { LSO_OPT_ADAM = 0, LSO_OPT_SGD = 1 } lso_opt;
 
+/* How a block's FP32 optimizer state (master, m, v) is laid out.
+ *   PLANAR: three separate arrays at off_master, off_m, off_v.
+ *   TILED:  one region at off_master holding master, m and v interleaved
+ *           in tiles of LSO_TILE_ELEMS elements: tile k (elements
+ *           [k*T, k*T + T), T = LSO_TILE_ELEMS) is 12*T bytes at region
+ *           offset 12*T*k -- master of its elements at +0, m at +4*T, v at
+ *           +8*T, element j of the tile at index j of each.  The region is
+ *           lso_tiled_state_bytes(n) = 12*T*ceil(n/T) bytes; the padding
+ *           after element n-1 is never read or written.  Adam only.
+ * The state is private to the optimizer, so its layout is free; the tiled
+ * one keeps every workgroup of the update inside one contiguous run of
+ * memory, which the HBM serves markedly faster than three separate
+ * streams.  Gradients and weights are planar in both layouts (they are
+ * shared with the forward and backward passes).  lso_tiled_pack and
+ * lso_tiled_unpack convert between the two. */
+typedef enum lso_layout { LSO_LAYOUT_PLANAR = 0, LSO_LAYOUT_TILED = 1 } lso_layout;
+#define LSO_TILE_ELEMS 8192u
+
 /*
  * One block: a layer, or any tensor, whose arrays are updated together.
  * The address of each array is (uintptr_t)base + off_*; base may be NULL
- * with absolute addresses in the offsets.  Layout: planar, element i of
- * every array belongs to parameter i.
+ * with absolute addresses in the offsets.  Element i of every array belongs
+ * to parameter i.
  *   master  FP32, read and written           (always)
  *   m, v    FP32, read and written           (LSO_OPT_ADAM; ignored for SGD)
  *   grad    BF16, read                       (grad_dtype must be LSO_DT_BF16)
  *   weight  BF16, written                    (weight_dtype BF16; NONE skips it)
- * Every used array must be 16-byte aligned.  No written array may overlap
- * any other array of the same call (across blocks too); gradients may
- * alias one another.  n == 0 makes the block a no-op.
+ * layout (lso_layout): PLANAR, or TILED with master, m and v interleaved in
+ * one region at off_master (off_m and off_v are then ignored).
+ * Every used array (and a tiled region) must be 16-byte aligned.  No
+ * written array may overlap any other array of the same call (across
+ * blocks too); gradients may alias one another.  n == 0 makes the block a
+ * no-op.
  * t is the step being applied (t >= 1; the first update is t = 1); the
  * caller owns it and increments it per step -- it is the resume point of a
  * checkpoint.  Per-block t lets blocks advance independently.
@@ -99,7 +120,7 @@ typedef struct lso_block {
     uint32_t grad_dtype;     /* lso_dtype */
     uint32_t weight_dtype;   /* lso_dtype */
     uint32_t opt;            /* lso_opt */
-    uint32_t reserved;       /* must be 0 */
+    uint32_t layout;         /* lso_layout of master, m, v */
     uint64_t t;
     double   lr, beta1, beta2, eps;
 } lso_block;
@@ -108,8 +129,9 @@ typedef struct lso_block {
  * lso_adam_step: one update of n device-resident blocks, enqueued on
  * stream as ONE kernel launch (a ragged multi-tensor launch: hundreds of
  * small tensors cost one launch).  More than 16 distinct
- * (opt, t, lr, beta1, beta2, eps) sets in one call split it into one launch
- * per 16 sets.
+ * (opt, t, lr, beta1, beta2, eps) sets in one call, or planar and tiled
+ * blocks mixed in one call, split it into one launch per layout and per 16
+ * sets.
  * blocks: host array, read before return; the caller may reuse it at once.
  * Arrays: device memory owned by the caller; they must stay untouched until
  * stream passes the step.  Asynchronous: returns after enqueueing.
@@ -128,6 +150,20 @@ lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream);
  */
 lso_status lso_validate_blocks(const lso_block* blocks, size_t n);
 lso_status lso_block_constants(const lso_block* block, float out[8]);
+
+/* Bytes of the tiled state region of n parameters: 12 * T * ceil(n / T),
+ * T = LSO_TILE_ELEMS (0 for n == 0). */
+uint64_t lso_tiled_state_bytes(uint64_t n);
+
+/* Convert n parameters between planar FP32 arrays and a tiled state region
+ * (all device memory, 16-byte aligned, not overlapping), enqueued on
+ * stream.  pack: m or v may be NULL, which writes zeros.  unpack: master,
+ * m or v may be NULL, which skips that array.  Errors: INVALID, ALIGN,
+ * HIP. */
+lso_status lso_tiled_pack(void* state, const float* master, const float* m, const float* v,
+                          uint64_t n, void* stream);
+lso_status lso_tiled_unpack(const void* state, float* master, float* m, float* v, uint64_t n,
+                            void* stream);
 
 /* ---------------------------------------------------------------------
  * Layer streaming.  The authoritative state of each layer lives in host
@@ -152,16 +188,17 @@ lso_status lso_block_constants(const lso_block* block, float out[8]);
 typedef struct lso_host_layer {
     void*    host_base;      /* host block, pinned or pageable, 16-byte aligned
                                 (lso_host_alloc gives 4 KB-aligned pinned memory) */
-    uint64_t bytes;          /* bytes copied each way: covers all three arrays */
+    uint64_t bytes;          /* bytes copied each way: covers the state */
     uint64_t n;              /* parameters in the layer */
-    uint64_t off_master;     /* byte offsets inside the block, 16-byte aligned */
-    uint64_t off_m;
-    uint64_t off_v;
+    uint64_t off_master;     /* byte offsets inside the block, 16-byte aligned;
+                                TILED: offset of the tiled state region */
+    uint64_t off_m;          /* PLANAR only */
+    uint64_t off_v;          /* PLANAR only */
     void*    dev_weight;     /* device BF16 output for the re-cast weight, or
                                 NULL: it then stays in the slot's own buffer
                                 until the slot is reused */
     uint32_t opt;            /* lso_opt (SGD: m and v are not touched) */
-    uint32_t reserved;       /* must be 0 */
+    uint32_t layout;         /* lso_layout of the state inside the block */
     uint64_t t;
     double   lr, beta1, beta2, eps;
 } lso_host_layer;

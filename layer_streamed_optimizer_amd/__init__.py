@@ -20,15 +20,16 @@ from typing import Iterable
 import numpy as np
 
 from . import _native
-from ._native import (LSO_DT_BF16, LSO_DT_F32, LSO_DT_NONE, LSO_OPT_ADAM, LSO_OPT_SGD, LsoBlock,
-                      LsoError, LsoHostLayer)
+from ._native import (LSO_DT_BF16, LSO_DT_F32, LSO_DT_NONE, LSO_LAYOUT_PLANAR, LSO_LAYOUT_TILED,
+                      LSO_OPT_ADAM, LSO_OPT_SGD, LSO_TILE_ELEMS, LsoBlock, LsoError, LsoHostLayer)
 
 BLOCK_DTYPE = np.dtype(LsoBlock)
 HOST_LAYER_DTYPE = np.dtype(LsoHostLayer)
 
 __all__ = ["BlockTable", "adam_step", "validate", "block_constants", "LayerStream", "HostBuffer",
            "host_alloc", "LsoError", "LSO_OPT_ADAM", "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE",
-           "LSO_DT_F32", "BLOCK_DTYPE", "HOST_LAYER_DTYPE", "stream_handle"]
+           "LSO_DT_F32", "LSO_LAYOUT_PLANAR", "LSO_LAYOUT_TILED", "LSO_TILE_ELEMS", "BLOCK_DTYPE",
+           "HOST_LAYER_DTYPE", "stream_handle", "tiled_state_bytes", "tiled_pack", "tiled_unpack"]
 
 
 def stream_handle(stream=None) -> int:
@@ -69,9 +70,11 @@ class BlockTable:
 
     def set_row(self, i: int, *, n: int, master, grad, m=None, v=None, weight=None, t: int = 1,
                 lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
-                opt: int = LSO_OPT_ADAM, base: int = 0) -> None:
+                opt: int = LSO_OPT_ADAM, base: int = 0, layout: int = LSO_LAYOUT_PLANAR) -> None:
         """Arrays are torch tensors (their data_ptr) or integer device
-        addresses; with base != 0 the integers are offsets from base."""
+        addresses; with base != 0 the integers are offsets from base.  With
+        layout = LSO_LAYOUT_TILED, master is the tiled state region and m, v
+        are not used."""
         row = self.arr[i]
         row["base"] = base
         row["n"] = n
@@ -83,7 +86,7 @@ class BlockTable:
         row["grad_dtype"] = LSO_DT_BF16
         row["weight_dtype"] = LSO_DT_BF16 if weight is not None else LSO_DT_NONE
         row["opt"] = opt
-        row["reserved"] = 0
+        row["layout"] = layout
         row["t"] = t
         row["lr"], row["beta1"], row["beta2"], row["eps"] = lr, beta1, beta2, eps
 
@@ -106,6 +109,26 @@ def adam_step(table: BlockTable, stream=None) -> None:
 def validate(table: BlockTable) -> int:
     """The host-side checks of lso_adam_step; returns the status (0 = ok)."""
     return _native.lib().lso_validate_blocks(table.ptr, len(table))
+
+
+def tiled_state_bytes(n: int) -> int:
+    """Bytes of the tiled [master | m | v] state region of n parameters."""
+    return int(_native.lib().lso_tiled_state_bytes(n))
+
+
+def tiled_pack(state, master, m=None, v=None, *, n: int, stream=None) -> None:
+    """Planar FP32 master (and m, v, else zeros) -> tiled state region
+    (device addresses or tensors); asynchronous on stream."""
+    st = _native.lib().lso_tiled_pack(_addr(state), _addr(master), _addr(m) or None,
+                                      _addr(v) or None, n, stream_handle(stream))
+    _native.check(st, "lso_tiled_pack")
+
+
+def tiled_unpack(state, master=None, m=None, v=None, *, n: int, stream=None) -> None:
+    """Tiled state region -> planar FP32 arrays (None skips one)."""
+    st = _native.lib().lso_tiled_unpack(_addr(state), _addr(master) or None, _addr(m) or None,
+                                        _addr(v) or None, n, stream_handle(stream))
+    _native.check(st, "lso_tiled_unpack")
 
 
 def last_error() -> str:

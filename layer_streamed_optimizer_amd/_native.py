@@ -15,6 +15,8 @@ LSO_OK, LSO_E_INVALID, LSO_E_ALIGN, LSO_E_DTYPE, LSO_E_OVERLAP = 0, 1, 2, 3, 4
 LSO_E_NOMEM, LSO_E_HIP, LSO_E_CALLBACK = 5, 6, 7
 LSO_DT_NONE, LSO_DT_F32, LSO_DT_BF16 = 0, 1, 2
 LSO_OPT_ADAM, LSO_OPT_SGD = 0, 1
+LSO_LAYOUT_PLANAR, LSO_LAYOUT_TILED = 0, 1
+LSO_TILE_ELEMS = 8192
 
 STATUS_NAMES = {0: "LSO_OK", 1: "LSO_E_INVALID", 2: "LSO_E_ALIGN", 3: "LSO_E_DTYPE",
                 4: "LSO_E_OVERLAP", 5: "LSO_E_NOMEM", 6: "LSO_E_HIP", 7: "LSO_E_CALLBACK"}
@@ -32,7 +34,7 @@ class LsoBlock(ctypes.Structure):
         ("grad_dtype", ctypes.c_uint32),
         ("weight_dtype", ctypes.c_uint32),
         ("opt", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("layout", ctypes.c_uint32),
         ("t", ctypes.c_uint64),
         ("lr", ctypes.c_double),
         ("beta1", ctypes.c_double),
@@ -51,7 +53,7 @@ class LsoHostLayer(ctypes.Structure):
         ("off_v", ctypes.c_uint64),
         ("dev_weight", ctypes.c_void_p),
         ("opt", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("layout", ctypes.c_uint32),
         ("t", ctypes.c_uint64),
         ("lr", ctypes.c_double),
         ("beta1", ctypes.c_double),
@@ -64,9 +66,10 @@ GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctype
                            ctypes.c_uint64, ctypes.c_void_p)
 
 # every symbol include/lso.h declares
-EXPORTS = ("lso_adam_step", "lso_validate_blocks", "lso_block_constants", "lso_stream_create",
-           "lso_stream_layers", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc",
-           "lso_host_free", "lso_status_string", "lso_last_error")
+EXPORTS = ("lso_adam_step", "lso_validate_blocks", "lso_block_constants", "lso_tiled_state_bytes",
+           "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
+           "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc", "lso_host_free",
+           "lso_status_string", "lso_last_error")
 
 _lib = None
 _probes = None
@@ -91,6 +94,10 @@ def lib():
         L.lso_adam_step.argtypes = [vp, sz, vp]
         L.lso_validate_blocks.argtypes = [vp, sz]
         L.lso_block_constants.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
+        L.lso_tiled_state_bytes.argtypes = [u64]
+        L.lso_tiled_state_bytes.restype = u64
+        L.lso_tiled_pack.argtypes = [vp, vp, vp, vp, u64, vp]
+        L.lso_tiled_unpack.argtypes = [vp, vp, vp, vp, u64, vp]
         L.lso_stream_create.argtypes = [u64, u64, vp, vp, i32, ctypes.POINTER(vp)]
         L.lso_stream_layers.argtypes = [vp, vp, sz]
         L.lso_stream_slot_weight.argtypes = [vp, i32]
@@ -103,8 +110,8 @@ def lib():
         L.lso_last_error.argtypes = []
         L.lso_last_error.restype = ctypes.c_char_p
         for name in ("lso_adam_step", "lso_validate_blocks", "lso_block_constants",
-                     "lso_stream_create", "lso_stream_layers", "lso_stream_destroy",
-                     "lso_host_alloc", "lso_host_free"):
+                     "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create",
+                     "lso_stream_layers", "lso_stream_destroy", "lso_host_alloc", "lso_host_free"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

@@ -22,7 +22,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 LIBS = {
-    "liblso.so": ["lso_adam.hip", "lso_copy.hip", "lso_runtime.cpp", "lso_stream.cpp"],
+    "liblso.so": ["lso_adam.hip", "lso_copy.hip", "lso_tiled.hip", "lso_runtime.cpp",
+                  "lso_stream.cpp"],
     "liblso_probes.so": ["lso_probes.hip"],
 }
 

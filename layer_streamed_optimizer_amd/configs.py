@@ -16,6 +16,7 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 
 PAGE = 4096          # block sub-arrays start on 4 KB boundaries
+TILE = 8192          # elements per tile of the tiled state layout
 
 LR, BETA1, BETA2, EPS = 1e-3, 0.9, 0.999, 1e-8
 MASTER_SIGMA, GRAD_SIGMA, LORA_A_SIGMA = 0.02, 1e-3, 1.0 / 8.0
@@ -128,17 +129,25 @@ def get(key: str) -> Workload:
 
 # ------------------------------------------------------------ HBM layout
 
+def tiled_state_bytes(n: int) -> int:
+    """Bytes of the tiled [master | m | v] state of n parameters."""
+    return 12 * TILE * ((n + TILE - 1) // TILE)
+
+
 @dataclass
 class ResidentLayout:
     """Byte offsets of every array in three device arenas.
 
     state arena:  per block [master | m | v], FP32, each 4 KB aligned
+                  (tiled: one region per block, master/m/v interleaved per
+                  TILE elements; off_m / off_v then equal off_master)
     grad arena:   per block BF16 gradients, 4 KB aligned
     weight arena: per block BF16 re-cast weights, 4 KB aligned
     A block's state is contiguous (the same shape as a streamed host block),
     so a layer can move between host and HBM as one copy.
     """
     sizes: list[int]
+    tiled: bool = False
     off_master: list[int] = field(default_factory=list)
     off_m: list[int] = field(default_factory=list)
     off_v: list[int] = field(default_factory=list)
@@ -151,11 +160,17 @@ class ResidentLayout:
     def __post_init__(self):
         s = g = w = 0
         for n in self.sizes:
-            a = align(4 * n)
-            self.off_master.append(s)
-            self.off_m.append(s + a)
-            self.off_v.append(s + 2 * a)
-            s += 3 * a
+            if self.tiled:
+                self.off_master.append(s)
+                self.off_m.append(s)
+                self.off_v.append(s)
+                s += align(tiled_state_bytes(n))
+            else:
+                a = align(4 * n)
+                self.off_master.append(s)
+                self.off_m.append(s + a)
+                self.off_v.append(s + 2 * a)
+                s += 3 * a
             self.off_grad.append(g)
             g += align(2 * n)
             self.off_weight.append(w)
@@ -163,8 +178,11 @@ class ResidentLayout:
         self.state_bytes, self.grad_bytes, self.weight_bytes = s, g, w
 
 
-def host_layer_layout(n: int) -> tuple[int, int, int, int]:
-    """(off_master, off_m, off_v, bytes) of one streamed host block
-    [master | m | v] with 4 KB-aligned sub-arrays."""
+def host_layer_layout(n: int, tiled: bool = False) -> tuple[int, int, int, int]:
+    """(off_master, off_m, off_v, bytes) of one streamed host block:
+    [master | m | v] with 4 KB-aligned sub-arrays, or one tiled region."""
+    if tiled:
+        b = align(tiled_state_bytes(n))
+        return 0, 0, 0, b
     a = align(4 * n)
     return 0, a, 2 * a, 3 * a

@@ -14,6 +14,11 @@
 // 512 B of BF16).  All state is touched exactly once, so loads and stores
 // are non-temporal (streamed past the caches).
 //
+// Two layouts of the FP32 state: planar (three arrays) or tiled (master, m
+// and v interleaved in tiles of LSO_TILE_ELEMS elements, one tile per
+// workgroup): the tiled one keeps each workgroup inside one contiguous
+// 96 KB run, which the HBM serves about 10% faster than three streams.
+//
 // Ragged multi-tensor launch: one grid covers the concatenated chunk space
 // of every block of the call, one chunk per workgroup.  A workgroup finds
 // its block through a per-chunk block index (one scalar load), through a
@@ -90,14 +95,27 @@ struct Quad {
     f32x4 v;
 };
 
+// One chunk as seen by a workgroup: pointers to its first element in each
+// array, and how many of its elements exist (the rest of a ragged last chunk
+// is skipped).  A planar chunk points into the block's three arrays; a tiled
+// chunk is one state tile, whose master, m and v runs are back to back.
+struct Chunk {
+    float* p;
+    float* m;
+    float* v;
+    const uint16_t* g;
+    uint16_t* w;
+    uint32_t n;   // valid elements in this chunk
+};
+
 template <bool kSgd>
-__device__ __forceinline__ void load_quad(const DevBlock& b, uint64_t e, Quad& x)
+__device__ __forceinline__ void load_quad(const Chunk& ch, uint32_t e, Quad& x)
 {
-    x.g = ld_nt<u32x2>(b.g + e);
-    x.p = ld_nt<f32x4>(b.master + e);
+    x.g = ld_nt<u32x2>(ch.g + e);
+    x.p = ld_nt<f32x4>(ch.p + e);
     if (!kSgd) {
-        x.m = ld_nt<f32x4>(b.m + e);
-        x.v = ld_nt<f32x4>(b.v + e);
+        x.m = ld_nt<f32x4>(ch.m + e);
+        x.v = ld_nt<f32x4>(ch.v + e);
     }
 }
 
@@ -131,66 +149,63 @@ __device__ __forceinline__ u32x2 compute_quad(const Coef& c, Quad& x)
 }
 
 template <bool kSgd>
-__device__ __forceinline__ void store_quad(const DevBlock& b, uint64_t e, const Quad& x, u32x2 w, bool has_w)
+__device__ __forceinline__ void store_quad(const Chunk& ch, uint32_t e, const Quad& x, u32x2 w, bool has_w)
 {
-    st_nt<f32x4>(b.master + e, x.p);
+    st_nt<f32x4>(ch.p + e, x.p);
     if (!kSgd) {
-        st_nt<f32x4>(b.m + e, x.m);
-        st_nt<f32x4>(b.v + e, x.v);
+        st_nt<f32x4>(ch.m + e, x.m);
+        st_nt<f32x4>(ch.v + e, x.v);
     }
-    if (has_w) st_nt<u32x2>(b.w + e, w);
+    if (has_w) st_nt<u32x2>(ch.w + e, w);
 }
 
-// Elements [e, n) of a block, fewer than four: scalar accesses.
+// Elements [e, n) of a chunk, fewer than four: scalar accesses.
 template <bool kSgd>
-__device__ void tail_elems(const DevBlock& b, const Coef& c, uint64_t e, uint64_t n, bool has_w)
+__device__ void tail_elems(const Chunk& ch, const Coef& c, uint32_t e, uint32_t n, bool has_w)
 {
-    for (uint64_t i = e; i < n; ++i) {
-        const float g = bf16_widen(ld<uint16_t>(b.g + i));
-        float p = ld<float>(b.master + i);
+    for (uint32_t i = e; i < n; ++i) {
+        const float g = bf16_widen(ld<uint16_t>(ch.g + i));
+        float p = ld<float>(ch.p + i);
         if (kSgd) {
             sgd_elem(c, g, p);
         } else {
-            float m = ld<float>(b.m + i), v = ld<float>(b.v + i);
+            float m = ld<float>(ch.m + i), v = ld<float>(ch.v + i);
             adam_elem(c, g, p, m, v);
-            st<float>(b.m + i, m);
-            st<float>(b.v + i, v);
+            st<float>(ch.m + i, m);
+            st<float>(ch.v + i, v);
         }
-        st<float>(b.master + i, p);
-        if (has_w) st<uint16_t>(b.w + i, static_cast<uint16_t>(bf16_rne(p)));
+        st<float>(ch.p + i, p);
+        if (has_w) st<uint16_t>(ch.w + i, static_cast<uint16_t>(bf16_rne(p)));
     }
 }
 
-// One chunk of kThreads * kQuad * U elements starting at element e0 of b.
+// One chunk of kThreads * kQuad * U elements.
 template <int U, bool kSgd>
-__device__ __forceinline__ void run_chunk(const DevBlock& b, const Coef& c, uint64_t e0)
+__device__ __forceinline__ void run_chunk(const Chunk& ch, const Coef& c, bool has_w)
 {
-    constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
-    const bool has_w = (b.flags & kFlagWeight) != 0;
-    const uint64_t n = b.n;
-    if (e0 + kChunkU <= n) {
+    constexpr uint32_t kChunkU = static_cast<uint32_t>(kThreads) * kQuad * U;
+    if (ch.n == kChunkU) {
         // full chunk: every load of the lane first, then arithmetic and stores
         Quad x[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            load_quad<kSgd>(b, e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kQuad, x[u]);
+        for (int u = 0; u < U; ++u) load_quad<kSgd>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const u32x2 w = compute_quad<kSgd>(c, x[u]);
-            store_quad<kSgd>(b, e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kQuad, x[u], w, has_w);
+            store_quad<kSgd>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u], w, has_w);
         }
         return;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint64_t e = e0 + (static_cast<uint64_t>(u) * kThreads + threadIdx.x) * kQuad;
-        if (e + kQuad <= n) {
+        const uint32_t e = (u * kThreads + threadIdx.x) * kQuad;
+        if (e + kQuad <= ch.n) {
             Quad x;
-            load_quad<kSgd>(b, e, x);
+            load_quad<kSgd>(ch, e, x);
             const u32x2 w = compute_quad<kSgd>(c, x);
-            store_quad<kSgd>(b, e, x, w, has_w);
-        } else if (e < n) {
-            tail_elems<kSgd>(b, c, e, n, has_w);
+            store_quad<kSgd>(ch, e, x, w, has_w);
+        } else if (e < ch.n) {
+            tail_elems<kSgd>(ch, c, e, ch.n, has_w);
         }
     }
 }
@@ -233,17 +248,34 @@ __device__ __forceinline__ DevBlock find_inline(const KernelArgs& a, uint64_t ch
     return b;
 }
 
-template <int U>
+template <int U, bool kTiled>
 __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const DevBlock& b, uint64_t chunk)
 {
     constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
     const Coef c = args.coef[b.group];
-    const uint64_t e0 = (chunk - b.chunk0) * kChunkU;
-    if (b.flags & kFlagSgd) run_chunk<U, true>(b, c, e0);
-    else run_chunk<U, false>(b, c, e0);
+    const uint64_t k = chunk - b.chunk0;   // chunk index inside the block
+    const uint64_t e0 = k * kChunkU;       // its first element
+    const uint64_t left = b.n - e0;
+    Chunk ch;
+    ch.n = static_cast<uint32_t>(left < kChunkU ? left : kChunkU);
+    ch.g = b.g + e0;
+    ch.w = b.w ? b.w + e0 : nullptr;
+    if (kTiled) {
+        // tile k: [master | m | v], kChunkU elements each
+        ch.p = b.master + 3 * e0;
+        ch.m = ch.p + kChunkU;
+        ch.v = ch.m + kChunkU;
+    } else {
+        ch.p = b.master + e0;
+        ch.m = b.m ? b.m + e0 : nullptr;
+        ch.v = b.v ? b.v + e0 : nullptr;
+    }
+    const bool has_w = (b.flags & kFlagWeight) != 0;
+    if (!kTiled && (b.flags & kFlagSgd)) run_chunk<U, true>(ch, c, has_w);
+    else run_chunk<U, false>(ch, c, has_w);
 }
 
-template <int U>
+template <int U, bool kTiled>
 __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs args)
 {
     if (args.blocks) {
@@ -253,11 +285,11 @@ __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs a
             reinterpret_cast<const LSO_CONST uint32_t*>(reinterpret_cast<uintptr_t>(args.chunk_block));
         for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x) {
             const uint32_t bi = index ? index[chunk] : search_block(table, args.nblocks, chunk);
-            run_block_chunk<U>(args, load_block(table + bi), chunk);
+            run_block_chunk<U, kTiled>(args, load_block(table + bi), chunk);
         }
     } else {
         for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x)
-            run_block_chunk<U>(args, find_inline(args, chunk), chunk);
+            run_block_chunk<U, kTiled>(args, find_inline(args, chunk), chunk);
     }
 }
 
@@ -269,10 +301,13 @@ int launch_fused_adam(const KernelArgs& args, int unroll, void* stream)
     // one chunk per workgroup; a call too large for one grid loops
     const uint64_t grid = args.total_chunks < kMaxGrid ? args.total_chunks : kMaxGrid;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (unroll == kUnrollLarge)
-        hipLaunchKernelGGL(fused_adam_kernel<kUnrollLarge>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, args);
+    const dim3 g(static_cast<unsigned>(grid)), t(kThreads);
+    if (unroll == kUnrollTiled)
+        hipLaunchKernelGGL((fused_adam_kernel<kUnrollTiled, true>), g, t, 0, s, args);
+    else if (unroll == kUnrollLarge)
+        hipLaunchKernelGGL((fused_adam_kernel<kUnrollLarge, false>), g, t, 0, s, args);
     else
-        hipLaunchKernelGGL(fused_adam_kernel<kUnrollSmall>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, args);
+        hipLaunchKernelGGL((fused_adam_kernel<kUnrollSmall, false>), g, t, 0, s, args);
     return static_cast<int>(hipGetLastError());
 }
 

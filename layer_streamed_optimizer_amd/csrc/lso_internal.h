@@ -16,18 +16,21 @@ constexpr int kThreads = 256;
 constexpr int kQuad = 4;
 constexpr int kUnrollLarge = 4;
 constexpr int kUnrollSmall = 1;
+constexpr int kUnrollTiled = 8;   // one workgroup per state tile
 constexpr uint64_t kSmallCallElems = 32ull << 20;   // below this, kUnrollSmall
 constexpr uint64_t kMaxGrid = 1ull << 24;            // workgroups per launch
 constexpr uint64_t kMaxIndexChunks = 1ull << 22;     // per-chunk block index up to this
 
 constexpr uint64_t chunk_elems(int unroll) { return static_cast<uint64_t>(kThreads) * kQuad * unroll; }
+static_assert(chunk_elems(kUnrollTiled) == LSO_TILE_ELEMS, "a tiled chunk is one state tile");
 
 // At most this many distinct constant sets travel by value in one launch.
 constexpr int kMaxGroups = 16;
 
-enum : uint32_t { kFlagSgd = 1u, kFlagWeight = 2u };
+enum : uint32_t { kFlagSgd = 1u, kFlagWeight = 2u, kFlagTiled = 4u };
 
 // One block as the kernel sees it (64 bytes, lives in a device table).
+// Tiled blocks: master is the tiled state region, m and v are unused.
 struct DevBlock {
     float* master;
     float* m;
@@ -66,7 +69,8 @@ struct KernelArgs {
 };
 
 // Enqueue the fused kernel (defined in lso_adam.hip) with chunks of
-// chunk_elems(unroll) elements.  Returns the hipError_t of the launch.
+// chunk_elems(unroll) elements; unroll == kUnrollTiled launches the tiled
+// variant (every block of the launch tiled).  Returns the hipError_t.
 int launch_fused_adam(const KernelArgs& args, int unroll, void* stream);
 
 }  // namespace lso

@@ -58,6 +58,11 @@ lso_status check_hyper(uint32_t opt, uint64_t t, double lr, double beta1, double
     return LSO_OK;
 }
 
+uint64_t tiled_bytes(uint64_t n)
+{
+    return 12ull * LSO_TILE_ELEMS * ((n + LSO_TILE_ELEMS - 1) / LSO_TILE_ELEMS);
+}
+
 namespace {
 
 struct Interval {
@@ -103,12 +108,13 @@ lso_status validate_geometry(const lso_block* blocks, size_t n)
         if (b.n > (UINT64_MAX / 8)) return fail(LSO_E_INVALID, "block %zu: n too large", i);
         const uintptr_t base = reinterpret_cast<uintptr_t>(b.base);
         const bool adam = b.opt == LSO_OPT_ADAM;
-        struct A { uint64_t off; uint64_t esize; bool used; bool written; const char* name; } arr[5] = {
-            {b.off_master, 4, true, true, "master"},
-            {b.off_m, 4, adam, true, "m"},
-            {b.off_v, 4, adam, true, "v"},
-            {b.off_grad, 2, true, false, "grad"},
-            {b.off_weight, 2, b.weight_dtype == LSO_DT_BF16, true, "weight"},
+        const bool tiled = b.layout == LSO_LAYOUT_TILED;
+        struct A { uint64_t off; uint64_t bytes; bool used; bool written; const char* name; } arr[5] = {
+            {b.off_master, tiled ? tiled_bytes(b.n) : 4 * b.n, true, true, tiled ? "tiled state" : "master"},
+            {b.off_m, 4 * b.n, adam && !tiled, true, "m"},
+            {b.off_v, 4 * b.n, adam && !tiled, true, "v"},
+            {b.off_grad, 2 * b.n, true, false, "grad"},
+            {b.off_weight, 2 * b.n, b.weight_dtype == LSO_DT_BF16, true, "weight"},
         };
         for (const A& a : arr) {
             if (!a.used) continue;
@@ -117,7 +123,7 @@ lso_status validate_geometry(const lso_block* blocks, size_t n)
             if (addr % 16 != 0)
                 return fail(LSO_E_ALIGN, "block %zu: %s address %#llx is not 16-byte aligned", i, a.name,
                             static_cast<unsigned long long>(addr));
-            if (!add_array(iv, addr, a.esize * b.n, a.written, i))
+            if (!add_array(iv, addr, a.bytes, a.written, i))
                 return fail(LSO_E_INVALID, "block %zu: %s range wraps the address space", i, a.name);
         }
     }
@@ -126,7 +132,10 @@ lso_status validate_geometry(const lso_block* blocks, size_t n)
 
 lso_status check_fields(const lso_block& b, size_t i)
 {
-    if (b.reserved != 0) return fail(LSO_E_INVALID, "block %zu: reserved field must be 0", i);
+    if (b.layout != LSO_LAYOUT_PLANAR && b.layout != LSO_LAYOUT_TILED)
+        return fail(LSO_E_INVALID, "block %zu: unknown layout %u", i, b.layout);
+    if (b.layout == LSO_LAYOUT_TILED && b.opt != LSO_OPT_ADAM)
+        return fail(LSO_E_DTYPE, "block %zu: the tiled state layout is for Adam only", i);
     if (b.grad_dtype != LSO_DT_BF16)
         return fail(LSO_E_DTYPE, "block %zu: gradient dtype must be BF16", i);
     if (b.weight_dtype != LSO_DT_BF16 && b.weight_dtype != LSO_DT_NONE)
@@ -321,7 +330,6 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
     thread_local std::vector<DevBlock> tab;
     sets.clear();
     set_of.resize(n);
-    uint64_t total_elems = 0;
     for (size_t i = 0; i < n; ++i) {
         lso_status s = check_fields(blocks[i], i);
         if (s != LSO_OK) return s;
@@ -330,11 +338,18 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
         while (j < sets.size() && !(sets[j] == k)) ++j;
         if (j == sets.size()) sets.push_back(k);
         set_of[i] = static_cast<uint32_t>(j);
-        total_elems += blocks[i].n;
     }
-    const int unroll = total_elems < kSmallCallElems ? kUnrollSmall : kUnrollLarge;
-    const uint64_t chunk = chunk_elems(unroll);
-    const size_t launches = (sets.size() + kMaxGroups - 1) / kMaxGroups;
+    // launches: one per (layout, 16 constant sets); planar chunk size by
+    // the planar work of the call, tiled chunks are one state tile
+    uint64_t planar_elems = 0;
+    bool any_tiled = false, any_planar = false;
+    for (size_t i = 0; i < n; ++i) {
+        if (blocks[i].layout == LSO_LAYOUT_TILED) any_tiled = true;
+        else { any_planar = true; planar_elems += blocks[i].n; }
+    }
+    const int planar_unroll = planar_elems < kSmallCallElems ? kUnrollSmall : kUnrollLarge;
+    const size_t set_groups = (sets.size() + kMaxGroups - 1) / kMaxGroups;
+    const size_t launches = set_groups * ((any_tiled && any_planar) ? 2 : 1);
     bool checked = geometry_checked;
     if (launches > 1 && !checked) {
         // overlaps across the launches of one call are checked up front, so
@@ -343,50 +358,58 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
         if (s != LSO_OK) return s;
         checked = true;
     }
-    for (size_t L = 0; L < launches; ++L) {
-        KernelArgs args{};
-        tab.clear();
-        uint64_t chunks = 0;
-        for (size_t i = 0; i < n; ++i) {
-            if (set_of[i] / kMaxGroups != L) continue;
-            const lso_block& b = blocks[i];
-            if (b.n == 0) continue;
-            const uintptr_t base = reinterpret_cast<uintptr_t>(b.base);
-            DevBlock d{};
-            d.master = reinterpret_cast<float*>(base + b.off_master);
-            if (b.opt == LSO_OPT_ADAM) {
-                d.m = reinterpret_cast<float*>(base + b.off_m);
-                d.v = reinterpret_cast<float*>(base + b.off_v);
+    for (int pass = 0; pass < 2; ++pass) {   // planar launches, then tiled ones
+        const bool tiled_pass = pass == 1;
+        if (tiled_pass ? !any_tiled : !any_planar) continue;
+        const int unroll = tiled_pass ? kUnrollTiled : planar_unroll;
+        const uint64_t chunk = chunk_elems(unroll);
+        for (size_t L = 0; L < set_groups; ++L) {
+            KernelArgs args{};
+            tab.clear();
+            uint64_t chunks = 0;
+            for (size_t i = 0; i < n; ++i) {
+                if (set_of[i] / kMaxGroups != L) continue;
+                const lso_block& b = blocks[i];
+                if ((b.layout == LSO_LAYOUT_TILED) != tiled_pass) continue;
+                if (b.n == 0) continue;
+                const uintptr_t base = reinterpret_cast<uintptr_t>(b.base);
+                DevBlock d{};
+                d.master = reinterpret_cast<float*>(base + b.off_master);
+                if (b.opt == LSO_OPT_ADAM && !tiled_pass) {
+                    d.m = reinterpret_cast<float*>(base + b.off_m);
+                    d.v = reinterpret_cast<float*>(base + b.off_v);
+                }
+                d.g = reinterpret_cast<const uint16_t*>(base + b.off_grad);
+                d.w = b.weight_dtype == LSO_DT_BF16 ? reinterpret_cast<uint16_t*>(base + b.off_weight) : nullptr;
+                d.n = b.n;
+                d.chunk0 = chunks;
+                d.group = set_of[i] % kMaxGroups;
+                d.flags = (b.opt == LSO_OPT_SGD ? kFlagSgd : 0u) | (d.w ? kFlagWeight : 0u) |
+                          (tiled_pass ? kFlagTiled : 0u);
+                chunks += (b.n + chunk - 1) / chunk;
+                tab.push_back(d);
             }
-            d.g = reinterpret_cast<const uint16_t*>(base + b.off_grad);
-            d.w = b.weight_dtype == LSO_DT_BF16 ? reinterpret_cast<uint16_t*>(base + b.off_weight) : nullptr;
-            d.n = b.n;
-            d.chunk0 = chunks;
-            d.group = set_of[i] % kMaxGroups;
-            d.flags = (b.opt == LSO_OPT_SGD ? kFlagSgd : 0u) | (d.w ? kFlagWeight : 0u);
-            chunks += (b.n + chunk - 1) / chunk;
-            tab.push_back(d);
-        }
-        for (size_t j = L * kMaxGroups; j < sets.size() && j < (L + 1) * kMaxGroups; ++j) {
-            const HyperKey& k = sets[j];
-            args.coef[j % kMaxGroups] = make_coef(k.opt, k.t, k.lr, k.beta1, k.beta2, k.eps);
-        }
-        if (tab.empty()) continue;
-        args.total_chunks = chunks;
-        args.nblocks = static_cast<uint32_t>(tab.size());
-        if (tab.size() <= static_cast<size_t>(kInline)) {
-            if (!checked) {
-                lso_status s = validate_geometry(blocks, n);
+            for (size_t j = L * kMaxGroups; j < sets.size() && j < (L + 1) * kMaxGroups; ++j) {
+                const HyperKey& k = sets[j];
+                args.coef[j % kMaxGroups] = make_coef(k.opt, k.t, k.lr, k.beta1, k.beta2, k.eps);
+            }
+            if (tab.empty()) continue;
+            args.total_chunks = chunks;
+            args.nblocks = static_cast<uint32_t>(tab.size());
+            if (tab.size() <= static_cast<size_t>(kInline)) {
+                if (!checked) {
+                    lso_status s = validate_geometry(blocks, n);
+                    if (s != LSO_OK) return s;
+                    checked = true;
+                }
+                for (size_t j = 0; j < tab.size(); ++j) args.inl[j] = tab[j];
+            } else {
+                lso_status s = device_table(blocks, n, checked, tab, chunks, unroll, stream, args);
                 if (s != LSO_OK) return s;
-                checked = true;
             }
-            for (size_t j = 0; j < tab.size(); ++j) args.inl[j] = tab[j];
-        } else {
-            lso_status s = device_table(blocks, n, checked, tab, chunks, unroll, stream, args);
-            if (s != LSO_OK) return s;
+            int err = launch_fused_adam(args, unroll, stream);
+            if (err != 0) return hip_fail(err, "fused Adam launch");
         }
-        int err = launch_fused_adam(args, unroll, stream);
-        if (err != 0) return hip_fail(err, "fused Adam launch");
     }
     return LSO_OK;
 }
@@ -402,6 +425,8 @@ lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream)
     lso::clear_error();
     return lso::enqueue_update(blocks, n, stream, false);
 }
+
+uint64_t lso_tiled_state_bytes(uint64_t n) { return lso::tiled_bytes(n); }
 
 lso_status lso_validate_blocks(const lso_block* blocks, size_t n)
 {

@@ -13,6 +13,9 @@ lso_status fail(lso_status s, const char* fmt, ...);
 lso_status hip_fail(int hip_error, const char* what);
 void clear_error();
 
+// Bytes of the tiled state region of n parameters.
+uint64_t tiled_bytes(uint64_t n);
+
 lso_status check_hyper(uint32_t opt, uint64_t t, double lr, double beta1, double beta2, double eps,
                        size_t index);
 

@@ -214,7 +214,10 @@ lso_status check_layer(const lso_stream_ctx* c, const lso_host_layer& L, size_t 
 {
     using lso::fail;
     if (!L.host_base) return fail(LSO_E_INVALID, "layer %zu: host_base is NULL", i);
-    if (L.reserved != 0) return fail(LSO_E_INVALID, "layer %zu: reserved field must be 0", i);
+    if (L.layout != LSO_LAYOUT_PLANAR && L.layout != LSO_LAYOUT_TILED)
+        return fail(LSO_E_INVALID, "layer %zu: unknown layout %u", i, L.layout);
+    if (L.layout == LSO_LAYOUT_TILED && L.opt != LSO_OPT_ADAM)
+        return fail(LSO_E_DTYPE, "layer %zu: the tiled state layout is for Adam only", i);
     lso_status s = lso::check_hyper(L.opt, L.t, L.lr, L.beta1, L.beta2, L.eps, i);
     if (s != LSO_OK) return s;
     if (L.bytes == 0 || L.bytes > c->max_bytes)
@@ -227,6 +230,13 @@ lso_status check_layer(const lso_stream_ctx* c, const lso_host_layer& L, size_t 
         return fail(LSO_E_ALIGN, "layer %zu: host block is not 16-byte aligned", i);
     if (L.dev_weight && reinterpret_cast<uintptr_t>(L.dev_weight) % 16 != 0)
         return fail(LSO_E_ALIGN, "layer %zu: dev_weight is not 16-byte aligned", i);
+    if (L.layout == LSO_LAYOUT_TILED) {
+        const uint64_t rb = lso::tiled_bytes(L.n);
+        if (L.off_master % 16 != 0) return fail(LSO_E_ALIGN, "layer %zu: state offset not 16-byte aligned", i);
+        if (L.off_master > L.bytes || rb > L.bytes - L.off_master)
+            return fail(LSO_E_INVALID, "layer %zu: the tiled state runs past the block's bytes", i);
+        return LSO_OK;
+    }
     const bool adam = L.opt == LSO_OPT_ADAM;
     const uint64_t arr_bytes = 4 * L.n;
     const uint64_t offs[3] = {L.off_master, L.off_m, L.off_v};
@@ -307,6 +317,7 @@ lso_status issue_layer(lso_stream_ctx* c, const lso_host_layer& h, size_t i, voi
     b.grad_dtype = LSO_DT_BF16;
     b.weight_dtype = LSO_DT_BF16;
     b.opt = h.opt;
+    b.layout = h.layout;
     b.t = h.t;
     b.lr = h.lr;
     b.beta1 = h.beta1;

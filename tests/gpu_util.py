@@ -29,26 +29,58 @@ def to_dev(a: np.ndarray):
     return t.from_numpy(a.view(np.uint8).copy()).to("cuda")
 
 
+TILE = 8192
+
+
+def tile_state(master, m, v):
+    """Host reference of the tiled layout: [master | m | v] per TILE
+    elements, zero padding after the last element."""
+    n = master.size
+    nt = (n + TILE - 1) // TILE
+    reg = np.zeros((nt, 3, TILE), np.float32)
+    for k, a in enumerate((master, m, v)):
+        pad = np.zeros(nt * TILE, np.float32)
+        pad[:n] = a
+        reg[:, k, :] = pad.reshape(nt, TILE)
+    return reg.ravel()
+
+
+def detile_state(region, n):
+    """(master, m, v) of the first n elements of a tiled region."""
+    nt = (n + TILE - 1) // TILE
+    reg = np.asarray(region, np.float32)[: nt * 3 * TILE].reshape(nt, 3, TILE)
+    return tuple(reg[:, k, :].ravel()[:n].copy() for k in range(3))
+
+
 class Arena:
     """Blocks' arrays in one device buffer, each array surrounded by canary
-    bytes (every byte of the buffer outside an array is CANARY)."""
+    bytes (every byte of the buffer outside an array is CANARY).  With
+    tiled=True a block's master, m and v live in one tiled region."""
 
-    def __init__(self, sizes, adam=True, weight=True, extra_align=0):
+    def __init__(self, sizes, adam=True, weight=True, extra_align=0, tiled=False):
         t = torch()
         self.sizes = list(sizes)
-        self.adam, self.weight = adam, weight
-        self.off = []
+        self.adam, self.weight, self.tiled = adam, weight, tiled
+        self.off, self.nbytes = [], []
         pos = GUARD
-        names = ["master", "grad"] + (["m", "v"] if adam else []) + (["weight"] if weight else [])
+        if tiled:
+            names = ["state", "grad"] + (["weight"] if weight else [])
+        else:
+            names = ["master", "grad"] + (["m", "v"] if adam else []) + (["weight"] if weight else [])
         self.names = names
         for n in self.sizes:
-            d = {}
+            d, nb = {}, {}
             for name in names:
-                esize = 2 if name in ("grad", "weight") else 4
+                if name == "state":
+                    size = 12 * TILE * ((n + TILE - 1) // TILE)
+                else:
+                    size = (2 if name in ("grad", "weight") else 4) * n
                 d[name] = pos + extra_align
-                pos += extra_align + esize * n
+                nb[name] = size
+                pos += extra_align + size
                 pos = (pos + GUARD - 1) // GUARD * GUARD + GUARD
             self.off.append(d)
+            self.nbytes.append(nb)
         self.total = pos
         self.buf = t.full((self.total,), CANARY, dtype=t.uint8, device="cuda")
         self.base = int(self.buf.data_ptr())
@@ -56,16 +88,32 @@ class Arena:
     def esize(self, name):
         return 2 if name in ("grad", "weight") else 4
 
-    def put(self, i, name, arr):
+    def _put_raw(self, i, name, raw_u8):
         t = torch()
+        o = self.off[i][name]
+        assert raw_u8.nbytes == self.nbytes[i][name]
+        self.buf[o:o + raw_u8.nbytes].copy_(t.from_numpy(raw_u8.copy()))
+
+    def put(self, i, name, arr):
         n = self.sizes[i]
+        if self.tiled and name in ("master", "m", "v"):
+            cur = list(self.get_state(i))
+            cur[("master", "m", "v").index(name)] = np.ascontiguousarray(arr, np.float32)
+            self._put_raw(i, "state", tile_state(*cur).view(np.uint8))
+            return
         dt = np.uint16 if self.esize(name) == 2 else np.float32
         a = np.ascontiguousarray(arr, dtype=dt)
         assert a.size == n
-        o = self.off[i][name]
-        self.buf[o:o + a.nbytes].copy_(t.from_numpy(a.view(np.uint8).copy()))
+        self._put_raw(i, name, a.view(np.uint8))
+
+    def get_state(self, i):
+        o = self.off[i]["state"]
+        raw = self.buf[o:o + self.nbytes[i]["state"]].cpu().numpy().view(np.float32)
+        return detile_state(raw, self.sizes[i])
 
     def get(self, i, name):
+        if self.tiled and name in ("master", "m", "v"):
+            return self.get_state(i)[("master", "m", "v").index(name)]
         n = self.sizes[i]
         o = self.off[i][name]
         es = self.esize(name)
@@ -78,6 +126,12 @@ class Arena:
     def rows(self, t=1, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, opt=lso.LSO_OPT_ADAM):
         out = []
         for i, n in enumerate(self.sizes):
+            if self.tiled:
+                out.append(dict(n=n, master=self.addr(i, "state"), grad=self.addr(i, "grad"),
+                                weight=self.addr(i, "weight") if self.weight else None,
+                                t=t, lr=lr, beta1=beta1, beta2=beta2, eps=eps, opt=opt,
+                                layout=lso.LSO_LAYOUT_TILED))
+                continue
             out.append(dict(n=n, master=self.addr(i, "master"), grad=self.addr(i, "grad"),
                             m=self.addr(i, "m") if self.adam else None,
                             v=self.addr(i, "v") if self.adam else None,
@@ -91,9 +145,9 @@ class Arena:
     def canaries_intact(self) -> bool:
         host = self.buf.cpu().numpy()
         mask = np.ones(self.total, bool)
-        for i, n in enumerate(self.sizes):
+        for i in range(len(self.sizes)):
             for name, o in self.off[i].items():
-                mask[o:o + self.esize(name) * n] = False
+                mask[o:o + self.nbytes[i][name]] = False
         return bool(np.all(host[mask] == CANARY))
 
 
@@ -162,13 +216,18 @@ def assert_parity(got: dict, ref: dict, tol: float, what: str = "", scale: dict 
         assert not np.any(bad), f"{what}: {int(bad.sum())} BF16 weights beyond one ulp"
 
 
-def max_errors(got: dict, ref: dict, scale: dict | None = None) -> dict:
+def max_errors(got: dict, ref: dict, scale: dict | None = None, tol: float = 1e-6) -> dict:
+    """Largest FP32 errors (as in assert_parity), and for the BF16 weight
+    the largest |w - w_ref| over its bound max(1 ulp, tol * rms(master))
+    (<= 1 passes) plus how many weights differ at all."""
     out = {q: rel_err_rms_floor(got[q], ref[q],
                                 None if scale is None else max(scale.get(q, 0.0), rms(ref[q])))
            for q in ("master", "m", "v") if q in got and q in ref}
     if "weight" in got and "weight" in ref:
         d = np.abs(bf16_value(got["weight"]).astype(np.float64) - bf16_value(ref["weight"]))
-        out["weight_ulps"] = float(np.max(d / bf16_ulp(ref["weight"]))) if d.size else 0.0
+        bound = np.maximum(bf16_ulp(ref["weight"]), tol * rms(ref["master"]))
+        out["weight_over_bound"] = float(np.max(d / bound)) if d.size else 0.0
+        out["weight_differing"] = int(np.count_nonzero(d))
     return out
 
 

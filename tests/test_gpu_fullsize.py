@@ -16,7 +16,7 @@ import oracle
 import synth
 from layer_streamed_optimizer_amd import configs
 
-from gpu_util import assert_parity, call_scale, log, max_errors, torch
+from gpu_util import TILE, assert_parity, call_scale, log, max_errors, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,16 @@ def sample_offsets(n, seed):
     return [(o, SAMPLE) for o in sorted(offs)]
 
 
+def read_tiled(state, region_off, start, count):
+    """master, m, v of elements [start, start + count) of a tiled region,
+    de-tiled on the host from the covering tiles."""
+    t0, t1 = start // TILE, (start + count - 1) // TILE + 1
+    raw = state[region_off + 12 * TILE * t0: region_off + 12 * TILE * t1].cpu().numpy()
+    reg = raw.view(np.float32).reshape(t1 - t0, 3, TILE)
+    lo = start - t0 * TILE
+    return {q: reg[:, k, :].ravel()[lo: lo + count].copy() for k, q in enumerate(("master", "m", "v"))}
+
+
 def init_kind(spec):
     if spec.init == "zero":
         return None
@@ -41,29 +51,38 @@ def init_kind(spec):
     return synth.PURPOSE_MASTER, configs.MASTER_SIGMA
 
 
-def run_resident_sampled(key, steps):
+def run_resident_sampled(key, steps, tiled=True):
+    """The benchmark's configuration: tiled state for the large workloads."""
     T = torch()
     w = configs.get(key)
     sid = configs.STREAM_ID[key]
     sizes = [b.n for b in w.blocks]
-    lay = configs.ResidentLayout(sizes)
-    log(f"{key}: {w.params:,} params, {len(sizes)} blocks, {steps} steps")
+    lay = configs.ResidentLayout(sizes, tiled=tiled)
+    log(f"{key}: {w.params:,} params, {len(sizes)} blocks, {steps} steps, tiled={tiled}")
     hs = T.cuda.current_stream().cuda_stream
     state = T.empty(lay.state_bytes, dtype=T.uint8, device="cuda")
     grad = T.empty(lay.grad_bytes, dtype=T.uint8, device="cuda")
     weight = T.empty(lay.weight_bytes, dtype=T.uint8, device="cuda")
     sb, gb, wb = int(state.data_ptr()), int(grad.data_ptr()), int(weight.data_ptr())
+    scratch = T.empty(max(sizes), dtype=T.float32, device="cuda")
     for b, spec in enumerate(w.blocks):
         kind = init_kind(spec)
+        dst = int(scratch.data_ptr()) if tiled else sb + lay.off_master[b]
         if kind is None:
-            synth.device_fill_zero(sb + lay.off_master[b], 4 * spec.n, hs)
+            synth.device_fill_zero(dst, 4 * spec.n, hs)
         else:
-            synth.device_fill_normal_f32(sb + lay.off_master[b], spec.n, stream=sid, block=b,
+            synth.device_fill_normal_f32(dst, spec.n, stream=sid, block=b,
                                          purpose=kind[0], step=0, sigma=kind[1], hip_stream=hs)
-        synth.device_fill_zero(sb + lay.off_m[b], 4 * spec.n, hs)
-        synth.device_fill_zero(sb + lay.off_v[b], 4 * spec.n, hs)
+        if tiled:
+            lso.tiled_pack(sb + lay.off_master[b], dst, None, None, n=spec.n, stream=hs)
+        else:
+            synth.device_fill_zero(sb + lay.off_m[b], 4 * spec.n, hs)
+            synth.device_fill_zero(sb + lay.off_v[b], 4 * spec.n, hs)
+    T.cuda.synchronize()
+    del scratch
+    layout = lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR
     rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
-                 grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b])
+                 grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], layout=layout)
             for b, n in enumerate(sizes)]
     table = lso.BlockTable.from_rows(rows)
     for t in range(1, steps + 1):
@@ -95,10 +114,13 @@ def run_resident_sampled(key, steps):
             def rd(buf, byte_off, es, dt):
                 return buf[byte_off: byte_off + es * ln].cpu().numpy().view(dt)
 
-            got = dict(master=rd(state, lay.off_master[b] + 4 * off, 4, np.float32),
-                       m=rd(state, lay.off_m[b] + 4 * off, 4, np.float32),
-                       v=rd(state, lay.off_v[b] + 4 * off, 4, np.float32),
-                       weight=rd(weight, lay.off_weight[b] + 2 * off, 2, np.uint16))
+            if tiled:
+                got = read_tiled(state, lay.off_master[b], off, ln)
+            else:
+                got = dict(master=rd(state, lay.off_master[b] + 4 * off, 4, np.float32),
+                           m=rd(state, lay.off_m[b] + 4 * off, 4, np.float32),
+                           v=rd(state, lay.off_v[b] + 4 * off, 4, np.float32))
+            got["weight"] = rd(weight, lay.off_weight[b] + 2 * off, 2, np.uint16)
             refs.append(ref)
             gots.append(got)
             where.append((b, off))
@@ -115,6 +137,10 @@ def run_resident_sampled(key, steps):
 
 def test_c1_tinyllama_full_size_sampled():
     run_resident_sampled("c1", 10)
+
+
+def test_c1_tinyllama_full_size_sampled_planar():
+    run_resident_sampled("c1", 10, tiled=False)
 
 
 def test_c3_llama7b_full_size_sampled():

@@ -9,7 +9,8 @@ import oracle
 import synth
 from layer_streamed_optimizer_amd import configs
 
-from gpu_util import Arena, assert_parity, bf16_value, call_scale, log, max_errors, torch
+from gpu_util import (Arena, assert_parity, bf16_value, call_scale, detile_state, log,
+                      max_errors, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,11 +62,12 @@ def read_arena(arena, i):
     return d
 
 
-def run_parity(sizes, steps, stream_id, check_every=False, tol=TOL10, init=None):
-    log("parity", f"sizes={sizes[:6]}{'...' if len(sizes) > 6 else ''} blocks={len(sizes)} steps={steps}")
+def run_parity(sizes, steps, stream_id, check_every=False, tol=TOL10, init=None, tiled=False):
+    log("parity", f"sizes={sizes[:6]}{'...' if len(sizes) > 6 else ''} blocks={len(sizes)} "
+                  f"steps={steps} tiled={tiled}")
     T = torch()
     ref = host_inputs(sizes, stream_id, init=init)
-    arena = Arena(sizes)
+    arena = Arena(sizes, tiled=tiled)
     load_arena(arena, ref)
     table = arena.table()
     errs = {}
@@ -399,3 +401,87 @@ def test_bf16_cast_exhaustive_all_fp32_patterns():
         ref = oracle.bf16_rne(bits.view(np.float32))
         bad = np.nonzero(got != ref)[0]
         assert bad.size == 0, f"segment {s}: {bad.size} mismatches, first {hex(int(bits[bad[0]]))}"
+
+
+# ------------------------------------------------------------- tiled layout
+
+def test_tiled_ragged_sizes_match_oracle():
+    """Tiled state: tails inside a tile, exact tiles, several tiles, by-value
+    and table paths (5 blocks)."""
+    run_parity([1, 8191, 8192, 8193, 3 * 8192 + 17], 10, 101, check_every=True, tiled=True)
+
+
+def test_tiled_equals_planar_bitwise():
+    """The layout changes where the state lives, not the arithmetic: the
+    same inputs give bit-identical results in both layouts."""
+    T = torch()
+    sizes = [5, 8192 * 2 + 3, 100003, 4096, 65536]
+    ref = host_inputs(sizes, 102)
+    a, b = Arena(sizes), Arena(sizes, tiled=True)
+    load_arena(a, ref)
+    load_arena(b, ref)
+    ta, tb = a.table(), b.table()
+    for t in range(1, 6):
+        for i, g in enumerate(grads(sizes, 102, t)):
+            a.put(i, "grad", g)
+            b.put(i, "grad", g)
+        ta.set_step(t)
+        tb.set_step(t)
+        lso.adam_step(ta)
+        lso.adam_step(tb)
+    T.cuda.synchronize()
+    for i in range(len(sizes)):
+        for q in ("master", "m", "v", "weight"):
+            assert np.array_equal(a.get(i, q).view(np.uint8), b.get(i, q).view(np.uint8)), (i, q)
+    assert b.canaries_intact()
+
+
+def test_mixed_layouts_in_one_call():
+    """Planar and tiled blocks in one call (two launches) match the oracle."""
+    T = torch()
+    sizes_p, sizes_t = [3000, 70001], [9000, 17]
+    ref_p, ref_t = host_inputs(sizes_p, 103), host_inputs(sizes_t, 104)
+    ap, at = Arena(sizes_p), Arena(sizes_t, tiled=True)
+    load_arena(ap, ref_p)
+    load_arena(at, ref_t)
+    rows = ap.rows() + at.rows()
+    tab = lso.BlockTable.from_rows(rows)
+    for t in range(1, 4):
+        gp, gt = grads(sizes_p, 103, t), grads(sizes_t, 104, t)
+        for i, g in enumerate(gp):
+            ap.put(i, "grad", g)
+        for i, g in enumerate(gt):
+            at.put(i, "grad", g)
+        tab.set_step(t)
+        lso.adam_step(tab)
+        oracle_step(ref_p, gp, t)
+        oracle_step(ref_t, gt, t)
+    T.cuda.synchronize()
+    scale = call_scale(ref_p + ref_t)
+    for arena, ref in ((ap, ref_p), (at, ref_t)):
+        for i in range(len(ref)):
+            assert_parity(read_arena(arena, i), ref[i], TOL10, f"mixed block {i}", scale)
+
+
+def test_tiled_pack_unpack_roundtrip():
+    T = torch()
+    for n in (1, 8191, 8192, 3 * 8192 + 5):
+        rng = np.random.default_rng(n)
+        src = [rng.standard_normal(n).astype(np.float32) for _ in range(3)]
+        dev = [T.from_numpy(x).cuda() for x in src]
+        region = T.full((lso.tiled_state_bytes(n) // 4,), float("nan"), dtype=T.float32, device="cuda")
+        lso.tiled_pack(region, dev[0], dev[1], dev[2], n=n)
+        T.cuda.synchronize()
+        got = detile_state(region.cpu().numpy(), n)
+        for x, y in zip(src, got):
+            assert np.array_equal(x, y), n
+        out = [T.empty(n, dtype=T.float32, device="cuda") for _ in range(3)]
+        lso.tiled_unpack(region, out[0], out[1], out[2], n=n)
+        # m, v omitted -> zeros
+        region2 = T.empty_like(region)
+        lso.tiled_pack(region2, dev[0], None, None, n=n)
+        T.cuda.synchronize()
+        for x, y in zip(src, out):
+            assert np.array_equal(x, y.cpu().numpy()), n
+        m2 = detile_state(region2.cpu().numpy(), n)
+        assert np.array_equal(m2[0], src[0]) and not m2[1].any() and not m2[2].any()

@@ -11,7 +11,8 @@ import oracle
 import synth
 from layer_streamed_optimizer_amd import configs
 
-from gpu_util import HIP_D2D, assert_parity, call_scale, hip, log, torch
+from gpu_util import (HIP_D2D, assert_parity, call_scale, detile_state, hip, log,
+                      tile_state, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,24 +37,34 @@ class _Pageable:
 
 
 class HostLayers:
-    """Authoritative host blocks [master | m | v], one per layer: pinned
-    (lso_host_alloc) or pageable, per layer."""
+    """Authoritative host blocks, one per layer: [master | m | v] planar or
+    one tiled region; pinned (lso_host_alloc) or pageable, per layer."""
 
-    def __init__(self, sizes, sid, pageable=False):
+    def __init__(self, sizes, sid, pageable=False, tiled=False):
         self.sizes = sizes
+        self.tiled = tiled
         self.bufs, self.lay = [], []
         for b, n in enumerate(sizes):
-            om, omm, ov, nbytes = configs.host_layer_layout(n)
+            om, omm, ov, nbytes = configs.host_layer_layout(n, tiled=tiled)
             pg = pageable(b) if callable(pageable) else pageable
             hb = _Pageable(nbytes) if pg else lso.host_alloc(nbytes)
             hb.view(np.uint8)[:] = 0
-            hb.view(np.float32, om, n)[:] = synth.normal_f32(n, stream=sid, block=b, purpose=0,
-                                                             step=0, sigma=0.02)
+            master = synth.normal_f32(n, stream=sid, block=b, purpose=0, step=0, sigma=0.02)
+            if tiled:
+                z = np.zeros(n, np.float32)
+                reg = tile_state(master, z, z)
+                hb.view(np.float32, om, reg.size)[:] = reg
+            else:
+                hb.view(np.float32, om, n)[:] = master
             self.bufs.append(hb)
             self.lay.append((om, omm, ov, nbytes))
 
     def get(self, b, q):
-        om, omm, ov, _ = self.lay[b]
+        om, omm, ov, nbytes = self.lay[b]
+        n = self.sizes[b]
+        if self.tiled:
+            reg = self.bufs[b].view(np.float32, om, (nbytes - om) // 4)
+            return detile_state(reg, n)[("master", "m", "v").index(q)]
         off = {"master": om, "m": omm, "v": ov}[q]
         return self.bufs[b].view(np.float32, off, self.sizes[b]).copy()
 
@@ -67,6 +78,7 @@ class HostLayers:
             L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
             L[b]["dev_weight"] = dev_weight[b] if dev_weight else 0
             L[b]["opt"] = opt
+            L[b]["layout"] = lso.LSO_LAYOUT_TILED if self.tiled else lso.LSO_LAYOUT_PLANAR
             L[b]["t"] = t
             L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = lr, B1, B2, EPS
         return L
@@ -270,4 +282,36 @@ def test_pageable_producer_failure_leaves_later_layers_untouched():
         else:
             assert np.array_equal(now.view(np.uint32), before[b].view(np.uint32)), b
             assert not np.any(host.get(b, "m")), b
+    ls.close()
+
+
+def test_stream_tiled_layers_match_planar_bitwise_and_oracle():
+    """Tiled host blocks (one [master | m | v]-per-tile region per layer),
+    pinned and pageable, give the planar results bit for bit; both match the
+    oracle."""
+    T = torch()
+    sizes = [100003, 8192 * 3, 5, 65536 + 8191]
+    sid = 46
+    plan = HostLayers(sizes, sid)
+    til = HostLayers(sizes, sid, tiled=True)
+    tpg = HostLayers(sizes, sid, tiled=True, pageable=True)
+    ref = [dict(master=plan.get(b, "master"), m=np.zeros(n, np.float32), v=np.zeros(n, np.float32))
+           for b, n in enumerate(sizes)]
+    ls, params = synth_stream(sizes, sid, max_bytes=max(
+        max(configs.host_layer_layout(n, tiled=tl)[3] for n in sizes) for tl in (False, True)))
+    for t in range(1, 4):
+        params.step = t
+        for h in (plan, til, tpg):
+            ls.stream_layers(h.table(t))
+        for b, n in enumerate(sizes):
+            g = synth.normal_bf16(n, stream=sid, block=b, purpose=2, step=t, sigma=1e-3)
+            oracle.adam_step(ref[b]["master"], ref[b]["m"], ref[b]["v"], g, None, t, LR, B1, B2, EPS)
+    T.cuda.synchronize()
+    scale = call_scale(ref)
+    for b in range(len(sizes)):
+        got = {q: til.get(b, q) for q in ("master", "m", "v")}
+        for q in ("master", "m", "v"):
+            assert np.array_equal(got[q].view(np.uint32), plan.get(b, q).view(np.uint32)), (b, q)
+            assert np.array_equal(got[q].view(np.uint32), tpg.get(b, q).view(np.uint32)), (b, q)
+        assert_parity(got, ref[b], 1e-6, f"tiled streamed layer {b}", scale)
     ls.close()

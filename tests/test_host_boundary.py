@@ -50,11 +50,11 @@ int main(void) {
   printf("lso_host_layer.size %zu\n", sizeof(lso_host_layer));
   F(lso_block, base) F(lso_block, n) F(lso_block, off_master) F(lso_block, off_m)
   F(lso_block, off_v) F(lso_block, off_grad) F(lso_block, off_weight) F(lso_block, grad_dtype)
-  F(lso_block, weight_dtype) F(lso_block, opt) F(lso_block, reserved) F(lso_block, t)
+  F(lso_block, weight_dtype) F(lso_block, opt) F(lso_block, layout) F(lso_block, t)
   F(lso_block, lr) F(lso_block, beta1) F(lso_block, beta2) F(lso_block, eps)
   F(lso_host_layer, host_base) F(lso_host_layer, bytes) F(lso_host_layer, n)
   F(lso_host_layer, off_master) F(lso_host_layer, off_m) F(lso_host_layer, off_v)
-  F(lso_host_layer, dev_weight) F(lso_host_layer, opt) F(lso_host_layer, reserved)
+  F(lso_host_layer, dev_weight) F(lso_host_layer, opt) F(lso_host_layer, layout)
   F(lso_host_layer, t) F(lso_host_layer, lr) F(lso_host_layer, beta1) F(lso_host_layer, beta2)
   F(lso_host_layer, eps)
   return 0;
@@ -153,13 +153,15 @@ def test_bad_hyper_parameters(kw, code):
     assert lso.validate(table([row(0, **kw)])) == code
 
 
-def test_bad_dtype_and_reserved():
+def test_bad_dtype_and_layout():
     t = table([row(0)])
     t.arr[0]["grad_dtype"] = lso.LSO_DT_F32
     assert lso.validate(t) == _native.LSO_E_DTYPE
     t = table([row(0)])
-    t.arr[0]["reserved"] = 1
+    t.arr[0]["layout"] = 7
     assert lso.validate(t) == _native.LSO_E_INVALID
+    t = table([row(0, opt=lso.LSO_OPT_SGD, layout=lso.LSO_LAYOUT_TILED)])
+    assert lso.validate(t) == _native.LSO_E_DTYPE
     t = table([row(0, master=0)])
     assert lso.validate(t) == _native.LSO_E_INVALID
 
@@ -237,3 +239,28 @@ def test_resident_layout_is_page_aligned_and_disjoint():
     assert spans[-1][0] + spans[-1][1] <= lay.state_bytes
     off = configs.host_layer_layout(855_654_400)
     assert off[3] == 3 * configs.align(4 * 855_654_400) and off[3] % 4096 == 0
+
+
+def test_tiled_state_region_validation():
+    n = 3 * 8192 + 5
+    rb = lso.tiled_state_bytes(n)
+    assert rb == 12 * 8192 * 4 == configs.tiled_state_bytes(n)
+    assert lso.tiled_state_bytes(0) == 0 and lso.tiled_state_bytes(1) == 12 * 8192
+    base = A
+    ok = dict(n=n, master=base, m=None, v=None, grad=base + rb, weight=base + rb + 65536,
+              layout=lso.LSO_LAYOUT_TILED)
+    assert lso.validate(table([ok])) == 0
+    # m / v are ignored for tiled blocks (they may be anything)
+    assert lso.validate(table([dict(ok, m=A + 3, v=A + 5)])) == 0
+    # the whole padded region counts: a gradient inside the padding overlaps
+    bad = dict(ok, grad=base + 12 * 8192 * 3 + 4096)
+    assert lso.validate(table([bad])) == _native.LSO_E_OVERLAP
+    assert lso.validate(table([dict(ok, master=base + 8)])) == _native.LSO_E_ALIGN
+
+
+def test_resident_layout_tiled():
+    lay = configs.ResidentLayout([100, 8192, 8193], tiled=True)
+    assert lay.off_master == lay.off_m == lay.off_v
+    assert lay.off_master[1] - lay.off_master[0] == configs.align(configs.tiled_state_bytes(100))
+    assert lay.state_bytes == sum(configs.align(configs.tiled_state_bytes(n)) for n in lay.sizes)
+    assert configs.host_layer_layout(8193, tiled=True) == (0, 0, 0, configs.align(12 * 8192 * 2))
