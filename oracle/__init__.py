@@ -53,8 +53,12 @@ def _load():
         lib.lso_oracle_adam.argtypes = [u64, f32p, f32p, f32p, u16p, u16p, u64,
                                         dbl, dbl, dbl, dbl, i32]
         lib.lso_oracle_adam.restype = i32
+        lib.lso_oracle_adam_g32.argtypes = lib.lso_oracle_adam.argtypes
+        lib.lso_oracle_adam_g32.restype = i32
         lib.lso_oracle_sgd.argtypes = [u64, f32p, u16p, u16p, dbl, i32]
         lib.lso_oracle_sgd.restype = i32
+        lib.lso_oracle_sgd_g32.argtypes = lib.lso_oracle_sgd.argtypes
+        lib.lso_oracle_sgd_g32.restype = i32
         lib.lso_oracle_accumulate_f32.argtypes = [u64, f32p, f32p]
         lib.lso_oracle_accumulate_f32.restype = i32
         lib.lso_oracle_bf16_rne.argtypes = [ctypes.c_float]
@@ -80,19 +84,22 @@ def adam_step(master: np.ndarray, m: np.ndarray, v: np.ndarray, g_bits: np.ndarr
     """One Adam step in place (frozen-incremental page, section "The Math").
 
     master, m, v: float32 state, updated in place.  g_bits: uint16 BF16
-    gradient patterns.  w_bits: uint16 output for the BF16 re-cast of the
-    new master, or None.  Returns the number of host threads used.
+    gradient patterns, or float32 gradients (the LoRA article's FP32 adapter
+    gradients).  w_bits: uint16 output for the BF16 re-cast of the new
+    master, or None.  Returns the number of host threads used.
     """
     n = master.size
     _check(master, np.float32, n, "master")
     _check(m, np.float32, n, "m")
     _check(v, np.float32, n, "v")
-    _check(g_bits, np.uint16, n, "g")
+    g32 = g_bits.dtype == np.float32
+    _check(g_bits, np.float32 if g32 else np.uint16, n, "g")
     if w_bits is not None:
         _check(w_bits, np.uint16, n, "w")
-    rc = _load().lso_oracle_adam(n, _ptr(master), _ptr(m), _ptr(v), _ptr(g_bits), _ptr(w_bits),
-                                 int(t), float(lr), float(beta1), float(beta2), float(eps),
-                                 int(threads))
+    lib = _load()
+    fn = lib.lso_oracle_adam_g32 if g32 else lib.lso_oracle_adam
+    rc = fn(n, _ptr(master), _ptr(m), _ptr(v), _ptr(g_bits), _ptr(w_bits),
+            int(t), float(lr), float(beta1), float(beta2), float(eps), int(threads))
     if rc < 0:
         raise ValueError("oracle rejected the arguments (t must be >= 1)")
     return rc
@@ -102,14 +109,16 @@ def sgd_step(master: np.ndarray, g_bits: np.ndarray, w_bits: np.ndarray | None, 
              subtractive: bool = False) -> None:
     """One plain gradient-descent step in FP32, additive (default) or
     subtractive spelling (frozen-incremental page, "The Assumption Everyone
-    Makes")."""
+    Makes").  g_bits: uint16 BF16 patterns or float32 gradients."""
     n = master.size
     _check(master, np.float32, n, "master")
-    _check(g_bits, np.uint16, n, "g")
+    g32 = g_bits.dtype == np.float32
+    _check(g_bits, np.float32 if g32 else np.uint16, n, "g")
     if w_bits is not None:
         _check(w_bits, np.uint16, n, "w")
-    _load().lso_oracle_sgd(n, _ptr(master), _ptr(g_bits), _ptr(w_bits), float(lr),
-                           1 if subtractive else 0)
+    lib = _load()
+    fn = lib.lso_oracle_sgd_g32 if g32 else lib.lso_oracle_sgd
+    fn(n, _ptr(master), _ptr(g_bits), _ptr(w_bits), float(lr), 1 if subtractive else 0)
 
 
 def accumulate_f32(w: np.ndarray, delta: np.ndarray) -> None:

@@ -27,6 +27,10 @@
  *  - The MegaTrain summary (blog.hotdry.top), section on the memory
  *    bottleneck of the traditional paradigm: BF16 weights and gradients,
  *    FP32 moments.
+ *  - The LoRA memory accounting on the Cloudera community article, its
+ *    "everything else" part: adapter gradients are FP32 (4 bytes each).
+ *    The _g32 entry points take FP32 gradients and are otherwise the same
+ *    step.
  *
  * Readings where the pages leave a step open:
  *  - Arithmetic is FP64 evaluated from the stored FP32/BF16 values; every
@@ -80,7 +84,10 @@ void lso_oracle_bf16_rne_array(const float* x, uint16_t* out, uint64_t n)
 
 typedef struct {
     uint64_t lo, hi;
-    float* master; float* m; float* v; const uint16_t* g; uint16_t* w;
+    float* master; float* m; float* v;
+    const uint16_t* g;      /* BF16 gradients, or NULL when g32 is given */
+    const float* g32;       /* FP32 gradients */
+    uint16_t* w;
     double lr, beta1, beta2, eps, bc1, bc2;
 } adam_job;
 
@@ -89,7 +96,7 @@ static void adam_range(const adam_job* j)
     const double b1 = j->beta1, b2 = j->beta2;
     const double one_minus_b1 = 1.0 - b1, one_minus_b2 = 1.0 - b2;
     for (uint64_t i = j->lo; i < j->hi; ++i) {
-        double g = bf16_widen(j->g[i]);
+        double g = j->g32 ? (double)j->g32[i] : bf16_widen(j->g[i]);
         /* moments: exponential averages of g and g^2 */
         double m = b1 * (double)j->m[i] + one_minus_b1 * g;
         double v = b2 * (double)j->v[i] + one_minus_b2 * (g * g);
@@ -126,12 +133,11 @@ static int pick_threads(int nthreads, uint64_t n)
  * place.  g: BF16 gradient bits.  w: BF16 weight bits written from the new
  * master, or NULL to skip.  t >= 1.  nthreads <= 0 uses every online core.
  * Returns the number of threads used, or -1 on invalid arguments. */
-int lso_oracle_adam(uint64_t n, float* master, float* m, float* v,
-                    const uint16_t* g, uint16_t* w, uint64_t t,
-                    double lr, double beta1, double beta2, double eps,
-                    int nthreads)
+static int adam_any(uint64_t n, float* master, float* m, float* v,
+                    const uint16_t* g, const float* g32, uint16_t* w, uint64_t t,
+                    double lr, double beta1, double beta2, double eps, int nthreads)
 {
-    if (t < 1 || !master || !m || !v || !g) return -1;
+    if (t < 1 || !master || !m || !v || (!g && !g32)) return -1;
     double bc1 = 1.0 - pow(beta1, (double)t);
     double bc2 = 1.0 - pow(beta2, (double)t);
     int nt = pick_threads(nthreads, n);
@@ -140,7 +146,7 @@ int lso_oracle_adam(uint64_t n, float* master, float* m, float* v,
     uint64_t per = n / (uint64_t)nt, rem = n % (uint64_t)nt, lo = 0;
     for (int k = 0; k < nt; ++k) {
         uint64_t len = per + ((uint64_t)k < rem ? 1u : 0u);
-        adam_job j = { lo, lo + len, master, m, v, g, w, lr, beta1, beta2, eps, bc1, bc2 };
+        adam_job j = { lo, lo + len, master, m, v, g, g32, w, lr, beta1, beta2, eps, bc1, bc2 };
         jobs[k] = j;
         lo += len;
     }
@@ -155,19 +161,38 @@ int lso_oracle_adam(uint64_t n, float* master, float* m, float* v,
     return nt;
 }
 
+int lso_oracle_adam(uint64_t n, float* master, float* m, float* v,
+                    const uint16_t* g, uint16_t* w, uint64_t t,
+                    double lr, double beta1, double beta2, double eps,
+                    int nthreads)
+{
+    if (!g) return -1;
+    return adam_any(n, master, m, v, g, NULL, w, t, lr, beta1, beta2, eps, nthreads);
+}
+
+/* The same step with FP32 gradients g (LoRA adapters keep FP32 grads). */
+int lso_oracle_adam_g32(uint64_t n, float* master, float* m, float* v,
+                        const float* g, uint16_t* w, uint64_t t,
+                        double lr, double beta1, double beta2, double eps,
+                        int nthreads)
+{
+    if (!g) return -1;
+    return adam_any(n, master, m, v, NULL, g, w, t, lr, beta1, beta2, eps, nthreads);
+}
+
 /* ---- one plain SGD step (FP32, two roundings) -------------------------- */
 
 /* master <- fl32(master + fl32(-(fl32(lr) * g))), the additive rewrite of
  * W - lr*g.  sub selects the subtractive spelling fl32(master - fl32(lr*g))
  * instead, so the two spellings can be compared bit for bit.  Built with
  * contraction off, so each operator below is one IEEE FP32 rounding. */
-int lso_oracle_sgd(uint64_t n, float* master, const uint16_t* g, uint16_t* w,
-                   double lr, int sub)
+static int sgd_any(uint64_t n, float* master, const uint16_t* g, const float* g32,
+                   uint16_t* w, double lr, int sub)
 {
-    if (!master || !g) return -1;
+    if (!master || (!g && !g32)) return -1;
     const float lr32 = (float)lr;
     for (uint64_t i = 0; i < n; ++i) {
-        float gi = f32_from_bits((uint32_t)g[i] << 16);
+        float gi = g32 ? g32[i] : f32_from_bits((uint32_t)g[i] << 16);
         float prod = lr32 * gi;
         if (sub) {
             master[i] = master[i] - prod;
@@ -178,6 +203,21 @@ int lso_oracle_sgd(uint64_t n, float* master, const uint16_t* g, uint16_t* w,
         if (w) w[i] = lso_oracle_bf16_rne(master[i]);
     }
     return 1;
+}
+
+int lso_oracle_sgd(uint64_t n, float* master, const uint16_t* g, uint16_t* w,
+                   double lr, int sub)
+{
+    if (!g) return -1;
+    return sgd_any(n, master, g, NULL, w, lr, sub);
+}
+
+/* The same step with FP32 gradients. */
+int lso_oracle_sgd_g32(uint64_t n, float* master, const float* g, uint16_t* w,
+                       double lr, int sub)
+{
+    if (!g) return -1;
+    return sgd_any(n, master, NULL, g, w, lr, sub);
 }
 
 /* ---- the bare additive write-back -------------------------------------- */

@@ -26,6 +26,12 @@ MUTANTS = {
                           "double w = (double)j->master[i] + delta;\n        j->m[i] = (float)m;\n        j->v[i] = (float)v;\n        if (j->w) j->w[i] = lso_oracle_bf16_rne(j->master[i]);\n        j->master[i] = (float)w;"),
     "sgd_sign": ("float delta = -prod;", "float delta = prod;"),
     "accumulate_drops": ("w[i] = w[i] + delta[i];", "w[i] = delta[i];"),
+    "g32_read_as_bf16": ("double g = j->g32 ? (double)j->g32[i] : bf16_widen(j->g[i]);",
+                         "double g = j->g32 ? bf16_widen((uint16_t)(bits_from_f32(j->g32[i]) >> 16))"
+                         " : bf16_widen(j->g[i]);"),
+    "sgd_g32_read_as_bf16": ("float gi = g32 ? g32[i] : f32_from_bits((uint32_t)g[i] << 16);",
+                             "float gi = g32 ? f32_from_bits(bits_from_f32(g32[i]) & 0xFFFF0000u)"
+                             " : f32_from_bits((uint32_t)g[i] << 16);"),
 }
 
 

@@ -330,6 +330,102 @@ def test_brute_force_50_digit_t2_t3():
                 assert abs(float(got) - exf) <= f32_ulp(exf) * 1.0 + 1e-45, (t, i, float(got), exf)
 
 
+# ------------------------------------------------------- FP32 gradients
+# LoRA article, "everything else": adapter gradients are FP32.  The step is
+# the same; only the gradient's storage changes.
+
+def random_f32_not_bf16(n, sigma, seed):
+    rng = np.random.default_rng(seed)
+    f = (rng.standard_normal(n) * sigma).astype(np.float32)
+    f.view(np.uint32)[:] |= 0x1  # at least one bit below the BF16 significand
+    return f
+
+
+def test_fp32_gradient_brute_force_t1():
+    rng = np.random.default_rng(31)
+    n = 64
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = random_f32_not_bf16(n, 1e-3, seed=32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    w = np.zeros(n, np.uint16)
+    om = master.copy()
+    oracle.adam_step(om, m, v, g, w, 1, LR, B1, B2, EPS)
+    for i, (w_ex, m_ex, v_ex) in enumerate(exact_step_t1(master, g, LR, B1, B2, EPS)):
+        assert abs(float(om[i]) - float(w_ex)) <= f32_ulp(w_ex), i
+        assert abs(float(m[i]) - float(m_ex)) <= f32_ulp(m_ex), i
+        assert abs(float(v[i]) - float(v_ex)) <= f32_ulp(v_ex), i
+    assert np.array_equal(w, oracle.bf16_rne(om))
+
+
+def test_fp32_gradient_low_bits_reach_the_moments():
+    """g = 1 + 2^-10 is not a BF16 number.  With beta1 = 1/2, beta2 = 3/4
+    and t = 1 the moments are g/2 and g^2/4 (both exact in FP32 here), the
+    bias-corrected ones g and g^2, and the step -lr g / (|g| + eps)."""
+    g = np.array([1 + 2.0 ** -10, -(1 + 2.0 ** -9)], np.float32)
+    master = np.zeros(2, np.float32)
+    m = np.zeros(2, np.float32)
+    v = np.zeros(2, np.float32)
+    oracle.adam_step(master, m, v, g, None, 1, 1.0, 0.5, 0.75, 1.0)
+    for i in range(2):
+        gi = Fraction(float(g[i]))
+        assert Fraction(float(m[i])) == gi / 2
+        assert frac_to_f32(gi * gi / 4) == v[i]
+        assert frac_to_f32(-gi / (abs(gi) + 1)) == master[i]
+
+
+def test_fp32_gradient_50_digit_t2_t3():
+    getcontext().prec = 50
+    D = Decimal
+    rng = np.random.default_rng(33)
+    n = 32
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    lr, b1, b2, eps = (D(Fraction(x).numerator) / D(Fraction(x).denominator) for x in (LR, B1, B2, EPS))
+    for t in (1, 2, 3):
+        g = random_f32_not_bf16(n, 1e-3, seed=40 + t)
+        pm, pmm, pv = master.copy(), m.copy(), v.copy()
+        oracle.adam_step(master, m, v, g, None, t, LR, B1, B2, EPS)
+        if t == 1:
+            continue
+        for i in range(n):
+            gi = D(float(g[i]))
+            mm = b1 * D(float(pmm[i])) + (1 - b1) * gi
+            vv = b2 * D(float(pv[i])) + (1 - b2) * gi * gi
+            delta = -lr * (mm / (1 - b1 ** t)) / ((vv / (1 - b2 ** t)).sqrt() + eps)
+            ww = D(float(pm[i])) + delta
+            for got, ex in ((master[i], ww), (m[i], mm), (v[i], vv)):
+                exf = float(ex)
+                assert abs(float(got) - exf) <= f32_ulp(exf) + 1e-45, (t, i)
+
+
+def test_fp32_gradients_holding_bf16_numbers_match_the_bf16_step_bitwise():
+    n = 5000
+    rng = np.random.default_rng(34)
+    gb = random_bf16(n, 1e-3, seed=35)
+    gf = bf16_value(gb).copy()
+    a = [(rng.standard_normal(n) * 0.02).astype(np.float32), np.zeros(n, np.float32),
+         np.zeros(n, np.float32), np.zeros(n, np.uint16)]
+    b = [x.copy() for x in a]
+    for t in (1, 2):
+        oracle.adam_step(*a[:3], gb, a[3], t, LR, B1, B2, EPS)
+        oracle.adam_step(*b[:3], gf, b[3], t, LR, B1, B2, EPS)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_fp32_gradient_sgd_exact():
+    """lr = 1/2: the product is exact, so the step is the FP32 rounding of
+    the exact difference master - g/2."""
+    master = (np.random.default_rng(36).standard_normal(256) * 0.02).astype(np.float32)
+    g = random_f32_not_bf16(256, 1e-2, seed=37)
+    out = master.copy()
+    oracle.sgd_step(out, g, None, 0.5)
+    for i in range(256):
+        assert out[i] == frac_to_f32(Fraction(float(master[i])) - Fraction(float(g[i])) / 2), i
+
+
 # ---------------------------------------------------------------- BF16 cast
 
 def _torch_bf16_bits(x):
