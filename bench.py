@@ -4,7 +4,8 @@
 
 A step is one pass of the whole update over every block of the workload
 (host constants, one ragged multi-tensor launch, the fused kernel) with
-that step's BF16 gradients already resident in HBM.  W untimed steps, then
+that step's gradients (BF16; FP32 with --grad-dtype f32) already resident
+in HBM.  W untimed steps, then
 K timed steps between two device synchronisations; one JSON line on stdout.
 
 Workloads (shapes from the pages, values synthetic, see
@@ -17,7 +18,8 @@ layer_streamed_optimizer_amd/configs.py):
       ~164 GB of pinned host memory                          (streamed)
 
 Roofline: the fused kernel moves 28 algorithmic bytes per parameter (reads
-2 g + 4 master + 4 m + 4 v, writes 4 + 4 + 4 + 2 w); its average launch
+2 g + 4 master + 4 m + 4 v, writes 4 + 4 + 4 + 2 w; 30 with FP32
+gradients); its average launch
 duration is measured with HIP events on the launch stream.  The CPU
 baseline is the oracle (plain scalar FP64 C, all host cores) timed on a
 bounded sample of the same workload.
@@ -37,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gparams/s Adam step; % HBM peak (resident) / % host-link peak (streamed)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-BYTES_PER_PARAM = 28            # algorithmic, resident kernel
+BYTES_PER_PARAM = {"bf16": 28, "f32": 30}   # algorithmic, resident kernel, by gradient dtype
 LINK_BYTES_PER_PARAM = 12       # streamed: [master | m | v] each way
 
 
@@ -50,10 +52,11 @@ def kernel_hash() -> str:
     return kh()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, grad_dtype: str = "bf16"):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fused_adam_{workload}_pmc.md")
+    tag = workload if grad_dtype == "bf16" else f"{workload}_g32"
+    path = os.path.join(ROOT, "profiles", f"fused_adam_{tag}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -78,14 +81,17 @@ def resident(args, w):
     sid = configs.STREAM_ID[w.key]
     sizes = [b.n for b in w.blocks]
     tiled = args.layout == "tiled"
-    lay = configs.ResidentLayout(sizes, tiled=tiled)
+    g32 = args.grad_dtype == "f32"
+    bpp = BYTES_PER_PARAM[args.grad_dtype]
+    lay = configs.ResidentLayout(sizes, tiled=tiled, grad_f32=g32)
     params = w.params
     total_steps = args.warmup + args.steps
     free, _total = torch.cuda.mem_get_info()
     budget = free - lay.state_bytes - lay.weight_bytes - (8 << 30)
     n_sets = max(1, min(total_steps, budget // max(lay.grad_bytes, 1)))
     progress(f"{w.key}: {len(sizes)} blocks, {params:,} params, {args.layout} state "
-             f"{lay.state_bytes / 1e9:.1f} GB, {n_sets} gradient sets of {lay.grad_bytes / 1e9:.2f} GB")
+             f"{lay.state_bytes / 1e9:.1f} GB, {n_sets} {args.grad_dtype} gradient sets of "
+             f"{lay.grad_bytes / 1e9:.2f} GB")
     stream = torch.cuda.current_stream()
     hs = int(stream.cuda_stream)
     state = torch.empty(lay.state_bytes, dtype=torch.uint8, device=dev)
@@ -120,17 +126,18 @@ def resident(args, w):
     init_state()
     for r in range(n_sets):
         gb = int(grads[r].data_ptr())
+        fill = synth.device_fill_normal_f32 if g32 else synth.device_fill_normal_bf16
         for b, n in enumerate(sizes):
-            synth.device_fill_normal_bf16(gb + lay.off_grad[b], n, stream=sid, block=b,
-                                          purpose=synth.PURPOSE_GRAD, step=r + 1,
-                                          sigma=configs.GRAD_SIGMA, hip_stream=hs)
+            fill(gb + lay.off_grad[b], n, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=r + 1,
+                 sigma=configs.GRAD_SIGMA, hip_stream=hs)
     tables = []
     for r in range(n_sets):
         gb = int(grads[r].data_ptr())
         rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
                      grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], t=1,
                      lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2, eps=configs.EPS,
-                     layout=lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR)
+                     layout=lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR,
+                     grad_dtype=lso.LSO_DT_F32 if g32 else lso.LSO_DT_BF16)
                 for b, n in enumerate(sizes)]
         tables.append(lso.BlockTable.from_rows(rows))
     # Upload every table once outside the timed region: an lr = 0 step
@@ -163,11 +170,11 @@ def resident(args, w):
     wall = time.perf_counter() - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(kernel_ms) / len(kernel_ms)
-    achieved = BYTES_PER_PARAM * params / (avg_ms * 1e-3) / 1e9
+    achieved = bpp * params / (avg_ms * 1e-3) / 1e9
     ceiling = copy_ceiling(torch, dev)
     progress(f"steps: wall {wall * 1e3:.3f} ms for {args.steps}; kernel avg {avg_ms * 1e3:.1f} us; "
              f"{achieved:.0f} GB/s; copy ceiling {ceiling:.0f} GB/s")
-    traffic = measured_traffic(w.key)
+    traffic = measured_traffic(w.key, args.grad_dtype)
     result = dict(
         metric=METRIC, value=params * args.steps / wall / 1e9, unit="Gparams/s",
         ms_per_step=wall * 1e3 / args.steps,
@@ -176,7 +183,8 @@ def resident(args, w):
         kernel_avg_us=avg_ms * 1e3, kernel_min_us=min(kernel_ms) * 1e3,
         hbm_copy_ceiling_GBps=ceiling,
         config=dict(workload=f"{w.key}: {w.title}", blocks=len(sizes), params=params,
-                    state_layout=args.layout, bytes_per_param=BYTES_PER_PARAM, gradient_sets=n_sets,
+                    state_layout=args.layout, grad_dtype=args.grad_dtype, bytes_per_param=bpp,
+                    gradient_sets=n_sets,
                     hyper=dict(lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2,
                                eps=configs.EPS)),
     )
@@ -380,6 +388,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="c4: layers to stream (0 = all 16)")
     ap.add_argument("--layout", choices=["tiled", "planar"], default=None,
                     help="FP32 state layout (default: tiled for c1, c3, c4; planar for c0, c2)")
+    ap.add_argument("--grad-dtype", choices=["bf16", "f32"], default="bf16",
+                    help="gradient dtype of the resident workloads (f32: the LoRA article's FP32 "
+                         "adapter gradients)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the update is elementwise and would shard by "
@@ -396,6 +407,9 @@ def main():
     args.steps = dk if args.steps is None else args.steps
     if args.steps < 1:
         sys.exit("--steps must be >= 1")
+    if w.streamed and args.grad_dtype != "bf16":
+        sys.exit("--grad-dtype f32 applies to the resident workloads; the layer stream's "
+                 "gradient producer writes BF16")
     res = streamed(args, w) if w.streamed else resident(args, w)
     out = dict(metric=res.pop("metric"), value=res.pop("value"), unit=res.pop("unit"), n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=res.pop("ms_per_step"),

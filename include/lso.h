@@ -10,7 +10,7 @@
  *
  * The update, per element i of a block (all arithmetic below is what the
  * library computes; the pages define it in exact arithmetic):
- *   g      = BF16 gradient widened to FP32 (exact)
+ *   g      = BF16 gradient widened to FP32 (exact), or an FP32 gradient
  *   m'     = beta1*m + (1-beta1)*g
  *   v'     = beta2*v + (1-beta2)*g^2
  *   delta  = -lr * (m'/(1-beta1^t)) / (sqrt(v'/(1-beta2^t)) + eps)
@@ -27,6 +27,9 @@
  * bottleneck), layer-contiguous 4 KB-aligned host blocks, double buffering
  * and three streams joined by weights-ready / backward-done / buffer-free
  * events (section on streaming execution and the double-buffered pipeline).
+ * FP32 gradients (grad_dtype LSO_DT_F32) follow the LoRA memory accounting
+ * of the Cloudera community article ("everything else": adapter gradients
+ * in FP32, 4 bytes each).
  *
  * Precision: the per-block constants 1-beta, lr/(1-beta1^t),
  * 1/sqrt(1-beta2^t) are computed in FP64 on the host and rounded once to
@@ -94,7 +97,7 @@ typedef enum lso_layout { LSO_LAYOUT_PLANAR = 0, LSO_LAYOUT_TILED = 1 } lso_layo
  * to parameter i.
  *   master  FP32, read and written           (always)
  *   m, v    FP32, read and written           (LSO_OPT_ADAM; ignored for SGD)
- *   grad    BF16, read                       (grad_dtype must be LSO_DT_BF16)
+ *   grad    BF16 or FP32, read               (grad_dtype LSO_DT_BF16 or LSO_DT_F32)
  *   weight  BF16, written                    (weight_dtype BF16; NONE skips it)
  * layout (lso_layout): PLANAR, or TILED with master, m and v interleaved in
  * one region at off_master (off_m and off_v are then ignored).
@@ -129,9 +132,9 @@ typedef struct lso_block {
  * lso_adam_step: one update of n device-resident blocks, enqueued on
  * stream as ONE kernel launch (a ragged multi-tensor launch: hundreds of
  * small tensors cost one launch).  More than 16 distinct
- * (opt, t, lr, beta1, beta2, eps) sets in one call, or planar and tiled
- * blocks mixed in one call, split it into one launch per layout and per 16
- * sets.
+ * (opt, t, lr, beta1, beta2, eps) sets in one call, or blocks of different
+ * layouts or gradient dtypes mixed in one call, split it into one launch
+ * per (layout, gradient dtype) and per 16 sets.
  * blocks: host array, read before return; the caller may reuse it at once.
  * Arrays: device memory owned by the caller; they must stay untouched until
  * stream passes the step.  Asynchronous: returns after enqueueing.

@@ -70,7 +70,8 @@ class BlockTable:
 
     def set_row(self, i: int, *, n: int, master, grad, m=None, v=None, weight=None, t: int = 1,
                 lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
-                opt: int = LSO_OPT_ADAM, base: int = 0, layout: int = LSO_LAYOUT_PLANAR) -> None:
+                opt: int = LSO_OPT_ADAM, base: int = 0, layout: int = LSO_LAYOUT_PLANAR,
+                grad_dtype: int = LSO_DT_BF16) -> None:
         """Arrays are torch tensors (their data_ptr) or integer device
         addresses; with base != 0 the integers are offsets from base.  With
         layout = LSO_LAYOUT_TILED, master is the tiled state region and m, v
@@ -83,7 +84,7 @@ class BlockTable:
         row["off_v"] = _addr(v)
         row["off_grad"] = _addr(grad)
         row["off_weight"] = _addr(weight)
-        row["grad_dtype"] = LSO_DT_BF16
+        row["grad_dtype"] = grad_dtype
         row["weight_dtype"] = LSO_DT_BF16 if weight is not None else LSO_DT_NONE
         row["opt"] = opt
         row["layout"] = layout
@@ -98,10 +99,16 @@ class BlockTable:
         return self._ptr
 
 
+_step_fn = None
+
+
 def adam_step(table: BlockTable, stream=None) -> None:
     """One fused update of every block in the table, enqueued on stream
     (one kernel launch).  Asynchronous."""
-    st = _native.lib().lso_adam_step(table._ptr, len(table.arr), stream_handle(stream))
+    global _step_fn
+    if _step_fn is None:
+        _step_fn = _native.lib().lso_adam_step
+    st = _step_fn(table._ptr, len(table.arr), stream if type(stream) is int else stream_handle(stream))
     if st:
         _native.check(st, "lso_adam_step")
 

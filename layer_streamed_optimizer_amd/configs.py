@@ -141,13 +141,14 @@ class ResidentLayout:
     state arena:  per block [master | m | v], FP32, each 4 KB aligned
                   (tiled: one region per block, master/m/v interleaved per
                   TILE elements; off_m / off_v then equal off_master)
-    grad arena:   per block BF16 gradients, 4 KB aligned
+    grad arena:   per block BF16 gradients (FP32 with grad_f32), 4 KB aligned
     weight arena: per block BF16 re-cast weights, 4 KB aligned
     A block's state is contiguous (the same shape as a streamed host block),
     so a layer can move between host and HBM as one copy.
     """
     sizes: list[int]
     tiled: bool = False
+    grad_f32: bool = False
     off_master: list[int] = field(default_factory=list)
     off_m: list[int] = field(default_factory=list)
     off_v: list[int] = field(default_factory=list)
@@ -172,7 +173,7 @@ class ResidentLayout:
                 self.off_v.append(s + 2 * a)
                 s += 3 * a
             self.off_grad.append(g)
-            g += align(2 * n)
+            g += align((4 if self.grad_f32 else 2) * n)
             self.off_weight.append(w)
             w += align(2 * n)
         self.state_bytes, self.grad_bytes, self.weight_bytes = s, g, w

@@ -5,8 +5,8 @@
 // m and v; update the two moments; form the bias-corrected step with eps
 // outside the root; add it to the master (the additive write-back); store
 // master, m, v and the BF16 round-to-nearest-even re-cast of the new master.
-// 14 bytes read + 14 bytes written per parameter and nothing else: no
-// scratch, no second pass.
+// 14 bytes read + 14 bytes written per parameter (16 + 14 with FP32
+// gradients) and nothing else: no scratch, no second pass.
 //
 // Memory access: a lane owns groups of four consecutive elements, so every
 // FP32 access is one 128-bit load or store and every BF16 access one 64-bit
@@ -73,7 +73,7 @@ __device__ __forceinline__ void st(void* p, T v)
 __device__ __forceinline__ void adam_elem(const Coef& c, float g, float& master, float& m, float& v)
 {
     const float m1 = fmaf(c.b1, m, c.c1 * g);
-    const float v1 = fmaf(c.b2, v, c.c2 * (g * g));   // g*g is exact: g has 8 significant bits
+    const float v1 = fmaf(c.b2, v, c.c2 * (g * g));   // g*g is exact for BF16 g (8 significant bits)
     const float den = fmaf(__fsqrt_rn(v1), c.r, c.e);  // sqrt(v_hat) + eps, v_hat = v1 * r^2
     const float delta = -__fdiv_rn(c.s * m1, den);
     master = master + delta;
@@ -89,7 +89,8 @@ __device__ __forceinline__ void sgd_elem(const Coef& c, float g, float& master)
 
 // Four consecutive elements held by one lane.
 struct Quad {
-    u32x2 g;     // 4 BF16
+    u32x2 g;     // 4 BF16 gradients
+    f32x4 gf;    // or 4 FP32 gradients
     f32x4 p;     // master
     f32x4 m;
     f32x4 v;
@@ -103,15 +104,17 @@ struct Chunk {
     float* p;
     float* m;
     float* v;
-    const uint16_t* g;
+    const uint16_t* g;   // BF16 gradients
+    const float* gf;     // FP32 gradients
     uint16_t* w;
     uint32_t n;   // valid elements in this chunk
 };
 
-template <bool kSgd>
+template <bool kSgd, bool kG32>
 __device__ __forceinline__ void load_quad(const Chunk& ch, uint32_t e, Quad& x)
 {
-    x.g = ld_nt<u32x2>(ch.g + e);
+    if (kG32) x.gf = ld_nt<f32x4>(ch.gf + e);
+    else x.g = ld_nt<u32x2>(ch.g + e);
     x.p = ld_nt<f32x4>(ch.p + e);
     if (!kSgd) {
         x.m = ld_nt<f32x4>(ch.m + e);
@@ -119,14 +122,14 @@ __device__ __forceinline__ void load_quad(const Chunk& ch, uint32_t e, Quad& x)
     }
 }
 
-template <bool kSgd>
+template <bool kSgd, bool kG32>
 __device__ __forceinline__ u32x2 compute_quad(const Coef& c, Quad& x)
 {
     u32x2 w;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const float g0 = bf16_widen(x.g[k] & 0xFFFFu);
-        const float g1 = bf16_widen(x.g[k] >> 16);
+        const float g0 = kG32 ? x.gf[2 * k] : bf16_widen(x.g[k] & 0xFFFFu);
+        const float g1 = kG32 ? x.gf[2 * k + 1] : bf16_widen(x.g[k] >> 16);
         float p0 = x.p[2 * k], p1 = x.p[2 * k + 1];
         if (kSgd) {
             sgd_elem(c, g0, p0);
@@ -160,11 +163,11 @@ __device__ __forceinline__ void store_quad(const Chunk& ch, uint32_t e, const Qu
 }
 
 // Elements [e, n) of a chunk, fewer than four: scalar accesses.
-template <bool kSgd>
+template <bool kSgd, bool kG32>
 __device__ void tail_elems(const Chunk& ch, const Coef& c, uint32_t e, uint32_t n, bool has_w)
 {
     for (uint32_t i = e; i < n; ++i) {
-        const float g = bf16_widen(ld<uint16_t>(ch.g + i));
+        const float g = kG32 ? ld<float>(ch.gf + i) : bf16_widen(ld<uint16_t>(ch.g + i));
         float p = ld<float>(ch.p + i);
         if (kSgd) {
             sgd_elem(c, g, p);
@@ -180,7 +183,7 @@ __device__ void tail_elems(const Chunk& ch, const Coef& c, uint32_t e, uint32_t 
 }
 
 // One chunk of kThreads * kQuad * U elements.
-template <int U, bool kSgd>
+template <int U, bool kSgd, bool kG32>
 __device__ __forceinline__ void run_chunk(const Chunk& ch, const Coef& c, bool has_w)
 {
     constexpr uint32_t kChunkU = static_cast<uint32_t>(kThreads) * kQuad * U;
@@ -188,10 +191,10 @@ __device__ __forceinline__ void run_chunk(const Chunk& ch, const Coef& c, bool h
         // full chunk: every load of the lane first, then arithmetic and stores
         Quad x[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_quad<kSgd>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u]);
+        for (int u = 0; u < U; ++u) load_quad<kSgd, kG32>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const u32x2 w = compute_quad<kSgd>(c, x[u]);
+            const u32x2 w = compute_quad<kSgd, kG32>(c, x[u]);
             store_quad<kSgd>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u], w, has_w);
         }
         return;
@@ -201,11 +204,11 @@ __device__ __forceinline__ void run_chunk(const Chunk& ch, const Coef& c, bool h
         const uint32_t e = (u * kThreads + threadIdx.x) * kQuad;
         if (e + kQuad <= ch.n) {
             Quad x;
-            load_quad<kSgd>(ch, e, x);
-            const u32x2 w = compute_quad<kSgd>(c, x);
+            load_quad<kSgd, kG32>(ch, e, x);
+            const u32x2 w = compute_quad<kSgd, kG32>(c, x);
             store_quad<kSgd>(ch, e, x, w, has_w);
         } else if (e < ch.n) {
-            tail_elems<kSgd>(ch, c, e, ch.n, has_w);
+            tail_elems<kSgd, kG32>(ch, c, e, ch.n, has_w);
         }
     }
 }
@@ -248,7 +251,7 @@ __device__ __forceinline__ DevBlock find_inline(const KernelArgs& a, uint64_t ch
     return b;
 }
 
-template <int U, bool kTiled>
+template <int U, bool kTiled, bool kG32>
 __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const DevBlock& b, uint64_t chunk)
 {
     constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
@@ -259,6 +262,7 @@ __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const De
     Chunk ch;
     ch.n = static_cast<uint32_t>(left < kChunkU ? left : kChunkU);
     ch.g = b.g + e0;
+    ch.gf = reinterpret_cast<const float*>(b.g) + e0;
     ch.w = b.w ? b.w + e0 : nullptr;
     if (kTiled) {
         // tile k: [master | m | v], kChunkU elements each
@@ -271,11 +275,11 @@ __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const De
         ch.v = b.v ? b.v + e0 : nullptr;
     }
     const bool has_w = (b.flags & kFlagWeight) != 0;
-    if (!kTiled && (b.flags & kFlagSgd)) run_chunk<U, true>(ch, c, has_w);
-    else run_chunk<U, false>(ch, c, has_w);
+    if (!kTiled && (b.flags & kFlagSgd)) run_chunk<U, true, kG32>(ch, c, has_w);
+    else run_chunk<U, false, kG32>(ch, c, has_w);
 }
 
-template <int U, bool kTiled>
+template <int U, bool kTiled, bool kG32>
 __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs args)
 {
     if (args.blocks) {
@@ -285,29 +289,38 @@ __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs a
             reinterpret_cast<const LSO_CONST uint32_t*>(reinterpret_cast<uintptr_t>(args.chunk_block));
         for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x) {
             const uint32_t bi = index ? index[chunk] : search_block(table, args.nblocks, chunk);
-            run_block_chunk<U, kTiled>(args, load_block(table + bi), chunk);
+            run_block_chunk<U, kTiled, kG32>(args, load_block(table + bi), chunk);
         }
     } else {
         for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x)
-            run_block_chunk<U, kTiled>(args, find_inline(args, chunk), chunk);
+            run_block_chunk<U, kTiled, kG32>(args, find_inline(args, chunk), chunk);
     }
 }
 
 }  // namespace
 
-int launch_fused_adam(const KernelArgs& args, int unroll, void* stream)
+int launch_fused_adam(const KernelArgs& args, int unroll, bool grad_f32, void* stream)
 {
     if (args.total_chunks == 0) return 0;
     // one chunk per workgroup; a call too large for one grid loops
     const uint64_t grid = args.total_chunks < kMaxGrid ? args.total_chunks : kMaxGrid;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 g(static_cast<unsigned>(grid)), t(kThreads);
-    if (unroll == kUnrollTiled)
-        hipLaunchKernelGGL((fused_adam_kernel<kUnrollTiled, true>), g, t, 0, s, args);
-    else if (unroll == kUnrollLarge)
-        hipLaunchKernelGGL((fused_adam_kernel<kUnrollLarge, false>), g, t, 0, s, args);
-    else
-        hipLaunchKernelGGL((fused_adam_kernel<kUnrollSmall, false>), g, t, 0, s, args);
+    if (grad_f32) {
+        if (unroll == kUnrollTiled)
+            hipLaunchKernelGGL((fused_adam_kernel<kUnrollTiled, true, true>), g, t, 0, s, args);
+        else if (unroll == kUnrollLarge)
+            hipLaunchKernelGGL((fused_adam_kernel<kUnrollLarge, false, true>), g, t, 0, s, args);
+        else
+            hipLaunchKernelGGL((fused_adam_kernel<kUnrollSmall, false, true>), g, t, 0, s, args);
+    } else {
+        if (unroll == kUnrollTiled)
+            hipLaunchKernelGGL((fused_adam_kernel<kUnrollTiled, true, false>), g, t, 0, s, args);
+        else if (unroll == kUnrollLarge)
+            hipLaunchKernelGGL((fused_adam_kernel<kUnrollLarge, false, false>), g, t, 0, s, args);
+        else
+            hipLaunchKernelGGL((fused_adam_kernel<kUnrollSmall, false, false>), g, t, 0, s, args);
+    }
     return static_cast<int>(hipGetLastError());
 }
 

@@ -27,7 +27,7 @@ static_assert(chunk_elems(kUnrollTiled) == LSO_TILE_ELEMS, "a tiled chunk is one
 // At most this many distinct constant sets travel by value in one launch.
 constexpr int kMaxGroups = 16;
 
-enum : uint32_t { kFlagSgd = 1u, kFlagWeight = 2u, kFlagTiled = 4u };
+enum : uint32_t { kFlagSgd = 1u, kFlagWeight = 2u, kFlagTiled = 4u, kFlagGradF32 = 8u };
 
 // One block as the kernel sees it (64 bytes, lives in a device table).
 // Tiled blocks: master is the tiled state region, m and v are unused.
@@ -35,7 +35,7 @@ struct DevBlock {
     float* master;
     float* m;
     float* v;
-    const uint16_t* g;
+    const uint16_t* g;   // BF16 gradients (FP32 ones when kFlagGradF32)
     uint16_t* w;
     uint64_t n;
     uint64_t chunk0;     // first global chunk index of this block
@@ -70,7 +70,8 @@ struct KernelArgs {
 
 // Enqueue the fused kernel (defined in lso_adam.hip) with chunks of
 // chunk_elems(unroll) elements; unroll == kUnrollTiled launches the tiled
-// variant (every block of the launch tiled).  Returns the hipError_t.
-int launch_fused_adam(const KernelArgs& args, int unroll, void* stream);
+// variant (every block of the launch tiled); grad_f32 the FP32-gradient
+// variant (every block of the launch).  Returns the hipError_t.
+int launch_fused_adam(const KernelArgs& args, int unroll, bool grad_f32, void* stream);
 
 }  // namespace lso

@@ -113,7 +113,7 @@ lso_status validate_geometry(const lso_block* blocks, size_t n)
             {b.off_master, tiled ? tiled_bytes(b.n) : 4 * b.n, true, true, tiled ? "tiled state" : "master"},
             {b.off_m, 4 * b.n, adam && !tiled, true, "m"},
             {b.off_v, 4 * b.n, adam && !tiled, true, "v"},
-            {b.off_grad, 2 * b.n, true, false, "grad"},
+            {b.off_grad, (b.grad_dtype == LSO_DT_F32 ? 4 : 2) * b.n, true, false, "grad"},
             {b.off_weight, 2 * b.n, b.weight_dtype == LSO_DT_BF16, true, "weight"},
         };
         for (const A& a : arr) {
@@ -136,8 +136,8 @@ lso_status check_fields(const lso_block& b, size_t i)
         return fail(LSO_E_INVALID, "block %zu: unknown layout %u", i, b.layout);
     if (b.layout == LSO_LAYOUT_TILED && b.opt != LSO_OPT_ADAM)
         return fail(LSO_E_DTYPE, "block %zu: the tiled state layout is for Adam only", i);
-    if (b.grad_dtype != LSO_DT_BF16)
-        return fail(LSO_E_DTYPE, "block %zu: gradient dtype must be BF16", i);
+    if (b.grad_dtype != LSO_DT_BF16 && b.grad_dtype != LSO_DT_F32)
+        return fail(LSO_E_DTYPE, "block %zu: gradient dtype must be BF16 or F32", i);
     if (b.weight_dtype != LSO_DT_BF16 && b.weight_dtype != LSO_DT_NONE)
         return fail(LSO_E_DTYPE, "block %zu: weight dtype must be BF16 or NONE", i);
     return check_hyper(b.opt, b.t, b.lr, b.beta1, b.beta2, b.eps, i);
@@ -341,15 +341,20 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
     }
     // launches: one per (layout, 16 constant sets); planar chunk size by
     // the planar work of the call, tiled chunks are one state tile
+    // launch kinds: (tiled or planar) x (BF16 or FP32 gradients)
     uint64_t planar_elems = 0;
-    bool any_tiled = false, any_planar = false;
+    bool present[4] = {false, false, false, false};
+    auto kind_of = [](const lso_block& b) {
+        return (b.layout == LSO_LAYOUT_TILED ? 1 : 0) + (b.grad_dtype == LSO_DT_F32 ? 2 : 0);
+    };
     for (size_t i = 0; i < n; ++i) {
-        if (blocks[i].layout == LSO_LAYOUT_TILED) any_tiled = true;
-        else { any_planar = true; planar_elems += blocks[i].n; }
+        present[kind_of(blocks[i])] = true;
+        if (blocks[i].layout != LSO_LAYOUT_TILED) planar_elems += blocks[i].n;
     }
+    const int kinds = present[0] + present[1] + present[2] + present[3];
     const int planar_unroll = planar_elems < kSmallCallElems ? kUnrollSmall : kUnrollLarge;
     const size_t set_groups = (sets.size() + kMaxGroups - 1) / kMaxGroups;
-    const size_t launches = set_groups * ((any_tiled && any_planar) ? 2 : 1);
+    const size_t launches = set_groups * static_cast<size_t>(kinds);
     bool checked = geometry_checked;
     if (launches > 1 && !checked) {
         // overlaps across the launches of one call are checked up front, so
@@ -358,9 +363,10 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
         if (s != LSO_OK) return s;
         checked = true;
     }
-    for (int pass = 0; pass < 2; ++pass) {   // planar launches, then tiled ones
-        const bool tiled_pass = pass == 1;
-        if (tiled_pass ? !any_tiled : !any_planar) continue;
+    for (int kind = 0; kind < 4; ++kind) {   // one pass per launch kind present
+        if (!present[kind]) continue;
+        const bool tiled_pass = (kind & 1) != 0;
+        const bool g32_pass = (kind & 2) != 0;
         const int unroll = tiled_pass ? kUnrollTiled : planar_unroll;
         const uint64_t chunk = chunk_elems(unroll);
         for (size_t L = 0; L < set_groups; ++L) {
@@ -370,7 +376,7 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
             for (size_t i = 0; i < n; ++i) {
                 if (set_of[i] / kMaxGroups != L) continue;
                 const lso_block& b = blocks[i];
-                if ((b.layout == LSO_LAYOUT_TILED) != tiled_pass) continue;
+                if (kind_of(b) != kind) continue;
                 if (b.n == 0) continue;
                 const uintptr_t base = reinterpret_cast<uintptr_t>(b.base);
                 DevBlock d{};
@@ -385,7 +391,7 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
                 d.chunk0 = chunks;
                 d.group = set_of[i] % kMaxGroups;
                 d.flags = (b.opt == LSO_OPT_SGD ? kFlagSgd : 0u) | (d.w ? kFlagWeight : 0u) |
-                          (tiled_pass ? kFlagTiled : 0u);
+                          (tiled_pass ? kFlagTiled : 0u) | (g32_pass ? kFlagGradF32 : 0u);
                 chunks += (b.n + chunk - 1) / chunk;
                 tab.push_back(d);
             }
@@ -397,17 +403,28 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
             args.total_chunks = chunks;
             args.nblocks = static_cast<uint32_t>(tab.size());
             if (tab.size() <= static_cast<size_t>(kInline)) {
-                if (!checked) {
+                // The address checks of a by-value table are remembered per
+                // thread: a loop passing the same few blocks every step skips
+                // them (the table holds every address and size they look at).
+                thread_local DevBlock last_ok[kInline];
+                thread_local size_t last_ok_n = 0;
+                const bool same = last_ok_n == tab.size() &&
+                                  std::memcmp(last_ok, tab.data(), tab.size() * sizeof(DevBlock)) == 0;
+                if (!checked && !same) {
                     lso_status s = validate_geometry(blocks, n);
                     if (s != LSO_OK) return s;
                     checked = true;
+                }
+                if (launches == 1) {
+                    std::memcpy(last_ok, tab.data(), tab.size() * sizeof(DevBlock));
+                    last_ok_n = tab.size();
                 }
                 for (size_t j = 0; j < tab.size(); ++j) args.inl[j] = tab[j];
             } else {
                 lso_status s = device_table(blocks, n, checked, tab, chunks, unroll, stream, args);
                 if (s != LSO_OK) return s;
             }
-            int err = launch_fused_adam(args, unroll, stream);
+            int err = launch_fused_adam(args, unroll, g32_pass, stream);
             if (err != 0) return hip_fail(err, "fused Adam launch");
         }
     }

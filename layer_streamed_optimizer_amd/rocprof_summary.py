@@ -75,7 +75,7 @@ def pmc(args) -> str:
     sf, sw = copy_kib / f_copy, copy_kib / w_copy
     read_b = f_adam * sf * 1024.0
     write_b = w_adam * sw * 1024.0
-    algo_r, algo_w = 14.0 * args.params, 14.0 * args.params
+    algo_r, algo_w = float(args.read_bytes) * args.params, 14.0 * args.params
     out = [f"# rocprofv3 HBM counters: {args.title}", "",
            f"FETCH_SIZE command: `{args.command_fetch}`", "",
            f"WRITE_SIZE command: `{args.command_write}`", "",
@@ -90,7 +90,7 @@ def pmc(args) -> str:
            "| Per launch | Read (B) | Write (B) | Total (B) |",
            "|---|---|---|---|",
            f"| Measured (scaled) | {read_b:,.0f} | {write_b:,.0f} | {read_b + write_b:,.0f} |",
-           f"| Algorithmic (14 + 14 B x {args.params:,}) | {algo_r:,.0f} | {algo_w:,.0f} | "
+           f"| Algorithmic ({args.read_bytes} + 14 B x {args.params:,}) | {algo_r:,.0f} | {algo_w:,.0f} | "
            f"{algo_r + algo_w:,.0f} |",
            f"| Measured / algorithmic | {read_b / algo_r:.4f} | {write_b / algo_w:.4f} | "
            f"{(read_b + write_b) / (algo_r + algo_w):.4f} |",
@@ -160,6 +160,8 @@ def main(argv=None):
     b.add_argument("--params", type=int, required=True)
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--kernel", default="fused_adam")
+    b.add_argument("--read-bytes", type=int, default=14,
+                   help="algorithmic bytes read per parameter (16 with FP32 gradients)")
     b.add_argument("--command-fetch", required=True)
     b.add_argument("--command-write", required=True)
     b.add_argument("--title", default="")

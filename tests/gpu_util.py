@@ -55,12 +55,13 @@ def detile_state(region, n):
 class Arena:
     """Blocks' arrays in one device buffer, each array surrounded by canary
     bytes (every byte of the buffer outside an array is CANARY).  With
-    tiled=True a block's master, m and v live in one tiled region."""
+    tiled=True a block's master, m and v live in one tiled region; with
+    grad_f32=True the gradients are FP32 instead of BF16."""
 
-    def __init__(self, sizes, adam=True, weight=True, extra_align=0, tiled=False):
+    def __init__(self, sizes, adam=True, weight=True, extra_align=0, tiled=False, grad_f32=False):
         t = torch()
         self.sizes = list(sizes)
-        self.adam, self.weight, self.tiled = adam, weight, tiled
+        self.adam, self.weight, self.tiled, self.grad_f32 = adam, weight, tiled, grad_f32
         self.off, self.nbytes = [], []
         pos = GUARD
         if tiled:
@@ -74,7 +75,7 @@ class Arena:
                 if name == "state":
                     size = 12 * TILE * ((n + TILE - 1) // TILE)
                 else:
-                    size = (2 if name in ("grad", "weight") else 4) * n
+                    size = self.esize(name) * n
                 d[name] = pos + extra_align
                 nb[name] = size
                 pos += extra_align + size
@@ -86,7 +87,9 @@ class Arena:
         self.base = int(self.buf.data_ptr())
 
     def esize(self, name):
-        return 2 if name in ("grad", "weight") else 4
+        if name == "grad":
+            return 4 if self.grad_f32 else 2
+        return 2 if name == "weight" else 4
 
     def _put_raw(self, i, name, raw_u8):
         t = torch()
@@ -125,18 +128,19 @@ class Arena:
 
     def rows(self, t=1, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, opt=lso.LSO_OPT_ADAM):
         out = []
+        gd = lso.LSO_DT_F32 if self.grad_f32 else lso.LSO_DT_BF16
         for i, n in enumerate(self.sizes):
             if self.tiled:
                 out.append(dict(n=n, master=self.addr(i, "state"), grad=self.addr(i, "grad"),
                                 weight=self.addr(i, "weight") if self.weight else None,
                                 t=t, lr=lr, beta1=beta1, beta2=beta2, eps=eps, opt=opt,
-                                layout=lso.LSO_LAYOUT_TILED))
+                                layout=lso.LSO_LAYOUT_TILED, grad_dtype=gd))
                 continue
             out.append(dict(n=n, master=self.addr(i, "master"), grad=self.addr(i, "grad"),
                             m=self.addr(i, "m") if self.adam else None,
                             v=self.addr(i, "v") if self.adam else None,
                             weight=self.addr(i, "weight") if self.weight else None,
-                            t=t, lr=lr, beta1=beta1, beta2=beta2, eps=eps, opt=opt))
+                            t=t, lr=lr, beta1=beta1, beta2=beta2, eps=eps, opt=opt, grad_dtype=gd))
         return out
 
     def table(self, **kw):

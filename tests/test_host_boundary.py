@@ -155,7 +155,10 @@ def test_bad_hyper_parameters(kw, code):
 
 def test_bad_dtype_and_layout():
     t = table([row(0)])
-    t.arr[0]["grad_dtype"] = lso.LSO_DT_F32
+    t.arr[0]["grad_dtype"] = lso.LSO_DT_NONE
+    assert lso.validate(t) == _native.LSO_E_DTYPE
+    t = table([row(0)])
+    t.arr[0]["weight_dtype"] = lso.LSO_DT_F32
     assert lso.validate(t) == _native.LSO_E_DTYPE
     t = table([row(0)])
     t.arr[0]["layout"] = 7
@@ -164,6 +167,25 @@ def test_bad_dtype_and_layout():
     assert lso.validate(t) == _native.LSO_E_DTYPE
     t = table([row(0, master=0)])
     assert lso.validate(t) == _native.LSO_E_INVALID
+
+
+def test_fp32_gradients_span_four_bytes_per_element():
+    """An FP32 gradient array covers 4n bytes: the same placement that is
+    fine for BF16 gradients overlaps the next array with FP32 ones."""
+    n = 1024
+    r = dict(n=n, master=A, m=A + 4 * n, v=A + 8 * n, grad=A + 12 * n, weight=A + 14 * n)
+    assert lso.validate(table([r])) == 0
+    assert lso.validate(table([dict(r, grad_dtype=lso.LSO_DT_F32)])) == _native.LSO_E_OVERLAP
+    r["weight"] = A + 16 * n
+    assert lso.validate(table([dict(r, grad_dtype=lso.LSO_DT_F32)])) == 0
+    tiled = lso.tiled_state_bytes(n)
+    t = dict(n=n, master=A, grad=A + tiled, weight=A + tiled + 4 * n, layout=lso.LSO_LAYOUT_TILED)
+    assert lso.validate(table([dict(t, grad_dtype=lso.LSO_DT_F32)])) == 0
+    assert lso.validate(table([dict(t, grad_dtype=lso.LSO_DT_F32, weight=A + tiled + 2 * n)])) \
+        == _native.LSO_E_OVERLAP
+    assert lso.validate(table([dict(r, grad_dtype=lso.LSO_DT_F32, opt=lso.LSO_OPT_SGD)])) == 0
+    # BF16 and FP32 gradient blocks in one call
+    assert lso.validate(table([row(0, grad_dtype=lso.LSO_DT_F32), row(1)])) == 0
 
 
 def test_adam_step_rejects_before_touching_the_device():
