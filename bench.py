@@ -15,7 +15,9 @@ layer_streamed_optimizer_amd/configs.py):
   c2  LoRA r=8 on TinyLlama, 308 ragged tensors, 6,307,840  (resident)
   c3  LLaMA-7B shape, 35 blocks, 6,738,415,616 params       (resident, ~108 GB)
   c4  70B-shaped slice, 16 layers of 855,654,400 params, streamed from
-      ~164 GB of pinned host memory                          (streamed)
+      ~164 GB of host memory                                 (streamed)
+      --host-memory pageable (default) | pinned | file (the disk tier:
+      one O_DIRECT file per layer, 6 layers by default)
 
 Roofline: the fused kernel moves 28 algorithmic bytes per parameter (reads
 2 g + 4 master + 4 m + 4 v, writes 4 + 4 + 4 + 2 w; 30 with FP32
@@ -29,6 +31,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
+import mmap
 import os
 import re
 import sys
@@ -332,6 +335,120 @@ def streamed(args, w):
     return result
 
 
+def storage_peak(directory: str, nbytes: int = 4 << 30, threads: int = 8) -> dict:
+    """Sequential O_DIRECT pread / pwrite rates of the file system that holds
+    the layer files, alone and both at once (lso_probe_file)."""
+    import layer_streamed_optimizer_amd as lso
+
+    path = os.path.join(directory, "storage_probe.bin")
+    fd = os.open(path, os.O_RDWR | os.O_CREAT | os.O_DIRECT, 0o644)
+    try:
+        os.posix_fallocate(fd, 0, 2 * nbytes)
+        out = (ctypes.c_double * 4)()
+        rc = lso._native.probes().lso_probe_file(fd, 0, nbytes, nbytes, threads, out)
+        if rc != 0:
+            raise RuntimeError(f"lso_probe_file failed: {os.strerror(rc)}")
+    finally:
+        os.close(fd)
+        os.remove(path)
+    r = dict(read=out[0], write=out[1], duplex_read=out[2], duplex_write=out[3])
+    r["duplex_per_direction"] = min(out[2], out[3])
+    return r
+
+
+def streamed_files(args, w):
+    """c4's layers with their authoritative blocks in files (the disk tier):
+    one preallocated file per layer, opened O_DIRECT."""
+    import shutil
+    import tempfile
+
+    import torch
+
+    import layer_streamed_optimizer_amd as lso
+    import synth
+    from layer_streamed_optimizer_amd import configs
+    from layer_streamed_optimizer_amd.disk import LayerFiles
+
+    torch.cuda.set_device(0)
+    sid = configs.STREAM_ID[w.key]
+    n = w.blocks[0].n
+    tiled = args.layout == "tiled"
+    om, _omm, _ov, nbytes = configs.host_layer_layout(n, tiled=tiled)
+    base = args.file_dir or os.environ.get("LSO_FILE_DIR", "/var/tmp")
+    free = shutil.disk_usage(base).free
+    n_layers = args.layers or 6
+    if n_layers * nbytes + (10 << 30) > free:
+        sys.exit(f"{base} has {free / 1e9:.0f} GB free; {n_layers} layers need "
+                 f"{n_layers * nbytes / 1e9:.0f} GB plus 10 GB of headroom (use --layers)")
+    d = tempfile.mkdtemp(prefix="lso_disk_", dir=base)
+    try:
+        peak = storage_peak(d)
+        progress(f"storage: {peak}")
+        files = LayerFiles.create(d, [n] * n_layers, tiled=tiled, direct=True)
+        hs = torch.cuda.current_stream().cuda_stream
+        stage = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        scratch = torch.empty(n, dtype=torch.float32, device="cuda") if tiled else None
+        # page-aligned ordinary memory: O_DIRECT cannot transfer from
+        # HIP-allocated pinned memory
+        host = mmap.mmap(-1, nbytes)
+        host_ptr = ctypes.addressof(ctypes.c_char.from_buffer(host))
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        view = memoryview(host)
+        for b in range(n_layers):
+            # initial state made on the device, written to the file (untimed)
+            synth.device_fill_zero(int(stage.data_ptr()), nbytes, hs)
+            dst = int(scratch.data_ptr()) if tiled else int(stage.data_ptr()) + om
+            synth.device_fill_normal_f32(dst, n, stream=sid, block=b, purpose=synth.PURPOSE_MASTER,
+                                         step=0, sigma=configs.MASTER_SIGMA, hip_stream=hs)
+            if tiled:
+                lso.tiled_pack(int(stage.data_ptr()) + om, dst, None, None, n=n, stream=hs)
+            torch.cuda.synchronize()
+            assert hip.hipMemcpy(host_ptr, int(stage.data_ptr()), nbytes, 2) == 0
+            done = 0
+            while done < nbytes:
+                done += os.pwritev(files.fds[b], [view[done:]], done)
+            progress(f"layer {b} written")
+        del view
+        del stage, scratch
+        fn, Params = synth.grad_callback()
+        prm = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
+                     scale=synth.scale_for(configs.GRAD_SIGMA), block_base=0)
+        ls = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
+        step_s = []
+        for j in range(1, args.warmup + args.steps + 1):
+            prm.step = j
+            L = files.table(j, configs.LR, configs.BETA1, configs.BETA2, configs.EPS)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ls.stream_files(L)
+            dt = time.perf_counter() - t0
+            files.commit(j)
+            progress(f"step {j}: {dt:.3f} s")
+            if j > args.warmup:
+                step_s.append(dt)
+        ls.close()
+        files.close()
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    wall = sum(step_s)
+    params = n * n_layers
+    per_dir = LINK_BYTES_PER_PARAM * params / (wall / len(step_s)) / 1e9
+    top = peak["duplex_per_direction"]
+    return dict(
+        metric=METRIC, value=params * len(step_s) / wall / 1e9, unit="Gparams/s",
+        ms_per_step=wall * 1e3 / len(step_s),
+        roofline=dict(bound="storage", achieved=per_dir, peak=top, unit="GB/s per direction",
+                      frac=per_dir / top, traffic=None),
+        storage_peak_GBps=peak,
+        config=dict(workload=f"{w.key}: 70B-shaped slice, layer-streamed from files (disk tier)",
+                    layers=n_layers, layers_in_config=len(w.blocks), params=params,
+                    host_memory="file (O_DIRECT, one preallocated file per layer)",
+                    state_layout=args.layout, file_bytes=nbytes * n_layers,
+                    storage_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
+    )
+
+
 # -------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, budget_s=12.0):
@@ -381,11 +498,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--host-memory", choices=["pageable", "pinned"], default="pageable",
-                    help="c4: authoritative host blocks in pageable memory (staged through two "
-                         "pinned buffers) or page-locked (direct DMA; limited by the host's "
-                         "page-locked budget)")
-    ap.add_argument("--layers", type=int, default=0, help="c4: layers to stream (0 = all 16)")
+    ap.add_argument("--host-memory", choices=["pageable", "pinned", "file"], default="pageable",
+                    help="c4: authoritative blocks in pageable memory (staged through pinned "
+                         "buffers), page-locked (direct; limited by the host's page-locked "
+                         "budget), or files (the disk tier, O_DIRECT)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="c4: layers to stream (0 = all 16; 6 for --host-memory file)")
+    ap.add_argument("--file-dir", default=None,
+                    help="c4 with --host-memory file: where the layer files go "
+                         "(default $LSO_FILE_DIR or /var/tmp)")
     ap.add_argument("--layout", choices=["tiled", "planar"], default=None,
                     help="FP32 state layout (default: tiled for c1, c3, c4; planar for c0, c2)")
     ap.add_argument("--grad-dtype", choices=["bf16", "f32"], default="bf16",
@@ -410,7 +531,10 @@ def main():
     if w.streamed and args.grad_dtype != "bf16":
         sys.exit("--grad-dtype f32 applies to the resident workloads; the layer stream's "
                  "gradient producer writes BF16")
-    res = streamed(args, w) if w.streamed else resident(args, w)
+    if w.streamed:
+        res = streamed_files(args, w) if args.host_memory == "file" else streamed(args, w)
+    else:
+        res = resident(args, w)
     out = dict(metric=res.pop("metric"), value=res.pop("value"), unit=res.pop("unit"), n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=res.pop("ms_per_step"),
                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",

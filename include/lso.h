@@ -66,7 +66,8 @@ typedef enum lso_status {
     LSO_E_OVERLAP = 4,   /* a written array overlaps another array of the call */
     LSO_E_NOMEM = 5,     /* device or pinned host allocation failed */
     LSO_E_HIP = 6,       /* a HIP runtime call failed */
-    LSO_E_CALLBACK = 7   /* the gradient producer of lso_stream_layers failed */
+    LSO_E_CALLBACK = 7,  /* the gradient producer of the layer stream failed */
+    LSO_E_IO = 8         /* reading or writing a layer's file failed */
 } lso_status;
 
 typedef enum lso_dtype { LSO_DT_NONE = 0, LSO_DT_F32 = 1, LSO_DT_BF16 = 2 } lso_dtype;
@@ -181,11 +182,13 @@ lso_status lso_tiled_unpack(const void* state, float* master, float* m, float* v
  * and update, records step-done[slot]; D2H waits step-done, copies back,
  * records buffer-free[slot].
  * Host blocks may be pinned (lso_host_alloc, or any page-locked HIP host
- * allocation): the DMA engines then read and write them directly and the
- * host thread never waits inside the layer loop.  Or they may be ordinary
- * pageable memory (for state larger than the page-locked budget): each then
- * passes through one of two pinned CPU-side staging buffers of the context,
- * copied in by worker threads before its H2D and out after its D2H.
+ * allocation): the copies then read and write them directly.  Or they may
+ * be ordinary pageable memory (for state larger than the page-locked
+ * budget): each then passes through one of the context's nslots + 1 pinned
+ * staging buffers, copied in by worker threads before its H2D and out after
+ * its D2H.  lso_stream_files does the same with blocks held in files (the
+ * disk tier).  Stage-ins and write-outs run on two worker pools, so reading
+ * layer i + 1, updating layer i and writing layer i - 1 overlap.
  * ------------------------------------------------------------------- */
 
 typedef struct lso_host_layer {
@@ -216,10 +219,11 @@ typedef int (*lso_grad_fn)(void* user, size_t layer, void* dev_grad_bf16, uint64
 typedef struct lso_stream_ctx lso_stream_ctx;
 
 /* Create a streaming context on `device`: three streams, two device slots
- * of max_layer_bytes of state plus max_layer_params BF16 gradients and
- * BF16 weights each, and the events (the two pinned staging buffers of
- * max_layer_bytes are added on the first pageable layer).  fn/user: the
- * gradient producer.  Errors: INVALID, NOMEM, HIP.  *out is NULL on error. */
+ * of max_layer_bytes (rounded up to 4 KB) of state plus max_layer_params
+ * BF16 gradients and BF16 weights each, and the events (the three pinned
+ * staging buffers of that size and the worker threads are added on the
+ * first staged layer).  fn/user: the gradient producer.  Errors: INVALID,
+ * NOMEM, HIP.  *out is NULL on error. */
 lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params,
                              lso_grad_fn fn, void* user, int device, lso_stream_ctx** out);
 
@@ -227,10 +231,51 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
  * respect to host memory: on LSO_OK every host block holds its updated
  * state.  On LSO_E_CALLBACK at layer k, layers < k are fully written back
  * and layers >= k are untouched on the host.  Validation (bytes, alignment,
- * hyper-parameters) covers all layers before anything is enqueued.  Calls
- * on one context must not overlap (one caller thread at a time). */
+ * hyper-parameters, blocks of different layers not overlapping) covers all
+ * layers before anything is enqueued.  Calls on one context must not
+ * overlap (one caller thread at a time). */
 lso_status lso_stream_layers(lso_stream_ctx* ctx, const lso_host_layer* host_blocks,
                              size_t n_layers);
+
+/* The disk tier.  The frozen-incremental page ("Training 70B Models on
+ * Consumer Hardware", sections "Storage" and "Training Loop") keeps each
+ * layer's W, M, V in files on an SSD and loads, updates and flushes one
+ * layer at a time; its "Limitations" section asks for files preallocated
+ * contiguously; the MegaTrain summary names NVMe tiering as the next step.
+ * Here a layer's block (the same [master | m | v] or tiled bytes as a host
+ * block) is a region of a file: read with pread into a pinned staging
+ * buffer, streamed through the device like a pageable host block, and
+ * written back over the same region with pwrite. */
+#define LSO_FILE_SYNC 1u   /* fdatasync the file after the layer's write-back */
+
+typedef struct lso_file_layer {
+    int      fd;             /* open O_RDWR (O_DIRECT allowed); the caller owns it */
+    uint32_t flags;          /* 0 or LSO_FILE_SYNC */
+    uint64_t file_offset;    /* start of the block in the file, 4096-byte multiple */
+    uint64_t bytes;          /* block size, 4096-byte multiple; the file must hold it */
+    uint64_t n;              /* the rest as in lso_host_layer, offsets inside the block */
+    uint64_t off_master;
+    uint64_t off_m;
+    uint64_t off_v;
+    void*    dev_weight;
+    uint32_t opt;
+    uint32_t layout;
+    uint64_t t;
+    double   lr, beta1, beta2, eps;
+} lso_file_layer;
+
+/* Stream n_layers file blocks through the pipeline, in order.  On LSO_OK
+ * every region holds its updated state (and is on stable storage if
+ * LSO_FILE_SYNC was set).  Errors before anything runs: INVALID (bad fd,
+ * not O_RDWR, file shorter than offset + bytes, flags), ALIGN, OVERLAP
+ * (two regions of one call share bytes of the same file), DTYPE, NOMEM.
+ * During the run: on LSO_E_CALLBACK or a failed read (LSO_E_IO) at layer
+ * k, regions of layers < k hold their new state and regions of layers >= k
+ * are untouched; on a failed write (LSO_E_IO) of layer k, regions < k are
+ * new, region k may be partly written, regions > k are untouched.  The
+ * step t is the caller's to persist beside the files (the page keeps the
+ * global step with the model state so a resumed run continues from it). */
+lso_status lso_stream_files(lso_stream_ctx* ctx, const lso_file_layer* layers, size_t n_layers);
 
 /* Device address of slot s's BF16 weight buffer (s = layer index % 2 of
  * the most recent lso_stream_layers call), or NULL. */

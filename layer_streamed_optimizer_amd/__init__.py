@@ -20,16 +20,18 @@ from typing import Iterable
 import numpy as np
 
 from . import _native
-from ._native import (LSO_DT_BF16, LSO_DT_F32, LSO_DT_NONE, LSO_LAYOUT_PLANAR, LSO_LAYOUT_TILED,
-                      LSO_OPT_ADAM, LSO_OPT_SGD, LSO_TILE_ELEMS, LsoBlock, LsoError, LsoHostLayer)
+from ._native import (LSO_DT_BF16, LSO_DT_F32, LSO_DT_NONE, LSO_FILE_SYNC, LSO_LAYOUT_PLANAR,
+                      LSO_LAYOUT_TILED, LSO_OPT_ADAM, LSO_OPT_SGD, LSO_TILE_ELEMS, LsoBlock, LsoError,
+                      LsoFileLayer, LsoHostLayer)
 
 BLOCK_DTYPE = np.dtype(LsoBlock)
 HOST_LAYER_DTYPE = np.dtype(LsoHostLayer)
+FILE_LAYER_DTYPE = np.dtype(LsoFileLayer)
 
 __all__ = ["BlockTable", "adam_step", "validate", "block_constants", "LayerStream", "HostBuffer",
            "host_alloc", "LsoError", "LSO_OPT_ADAM", "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE",
            "LSO_DT_F32", "LSO_LAYOUT_PLANAR", "LSO_LAYOUT_TILED", "LSO_TILE_ELEMS", "BLOCK_DTYPE",
-           "HOST_LAYER_DTYPE", "stream_handle", "tiled_state_bytes", "tiled_pack", "tiled_unpack"]
+           "HOST_LAYER_DTYPE", "FILE_LAYER_DTYPE", "LSO_FILE_SYNC", "stream_handle", "tiled_state_bytes", "tiled_pack", "tiled_unpack"]
 
 
 def stream_handle(stream=None) -> int:
@@ -223,6 +225,20 @@ class LayerStream:
 
     def stream_layers_status(self, host_layers: np.ndarray) -> int:
         return _native.lib().lso_stream_layers(self.ctx, host_layers.ctypes.data, len(host_layers))
+
+    @staticmethod
+    def file_layers(n: int) -> np.ndarray:
+        return np.zeros(n, FILE_LAYER_DTYPE)
+
+    def stream_files(self, file_layers: np.ndarray) -> None:
+        """lso_stream_files: the disk tier (blocks held in file regions)."""
+        st = self.stream_files_status(file_layers)
+        _native.check(st, "lso_stream_files")
+
+    def stream_files_status(self, file_layers: np.ndarray) -> int:
+        if file_layers.dtype != FILE_LAYER_DTYPE or not file_layers.flags.c_contiguous:
+            raise TypeError("file_layers must be a contiguous FILE_LAYER_DTYPE array")
+        return _native.lib().lso_stream_files(self.ctx, file_layers.ctypes.data, len(file_layers))
 
     def slot_weight(self, slot: int) -> int:
         return int(_native.lib().lso_stream_slot_weight(self.ctx, slot) or 0)

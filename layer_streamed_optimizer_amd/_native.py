@@ -12,14 +12,16 @@ import os
 from . import build as _build
 
 LSO_OK, LSO_E_INVALID, LSO_E_ALIGN, LSO_E_DTYPE, LSO_E_OVERLAP = 0, 1, 2, 3, 4
-LSO_E_NOMEM, LSO_E_HIP, LSO_E_CALLBACK = 5, 6, 7
+LSO_E_NOMEM, LSO_E_HIP, LSO_E_CALLBACK, LSO_E_IO = 5, 6, 7, 8
 LSO_DT_NONE, LSO_DT_F32, LSO_DT_BF16 = 0, 1, 2
 LSO_OPT_ADAM, LSO_OPT_SGD = 0, 1
 LSO_LAYOUT_PLANAR, LSO_LAYOUT_TILED = 0, 1
 LSO_TILE_ELEMS = 8192
+LSO_FILE_SYNC = 1
 
 STATUS_NAMES = {0: "LSO_OK", 1: "LSO_E_INVALID", 2: "LSO_E_ALIGN", 3: "LSO_E_DTYPE",
-                4: "LSO_E_OVERLAP", 5: "LSO_E_NOMEM", 6: "LSO_E_HIP", 7: "LSO_E_CALLBACK"}
+                4: "LSO_E_OVERLAP", 5: "LSO_E_NOMEM", 6: "LSO_E_HIP", 7: "LSO_E_CALLBACK",
+                8: "LSO_E_IO"}
 
 
 class LsoBlock(ctypes.Structure):
@@ -62,13 +64,34 @@ class LsoHostLayer(ctypes.Structure):
     ]
 
 
+class LsoFileLayer(ctypes.Structure):
+    _fields_ = [
+        ("fd", ctypes.c_int),
+        ("flags", ctypes.c_uint32),
+        ("file_offset", ctypes.c_uint64),
+        ("bytes", ctypes.c_uint64),
+        ("n", ctypes.c_uint64),
+        ("off_master", ctypes.c_uint64),
+        ("off_m", ctypes.c_uint64),
+        ("off_v", ctypes.c_uint64),
+        ("dev_weight", ctypes.c_void_p),
+        ("opt", ctypes.c_uint32),
+        ("layout", ctypes.c_uint32),
+        ("t", ctypes.c_uint64),
+        ("lr", ctypes.c_double),
+        ("beta1", ctypes.c_double),
+        ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double),
+    ]
+
+
 GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                            ctypes.c_uint64, ctypes.c_void_p)
 
 # every symbol include/lso.h declares
 EXPORTS = ("lso_adam_step", "lso_validate_blocks", "lso_block_constants", "lso_tiled_state_bytes",
            "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
-           "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc", "lso_host_free",
+           "lso_stream_files", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc", "lso_host_free",
            "lso_status_string", "lso_last_error")
 
 _lib = None
@@ -100,6 +123,7 @@ def lib():
         L.lso_tiled_unpack.argtypes = [vp, vp, vp, vp, u64, vp]
         L.lso_stream_create.argtypes = [u64, u64, vp, vp, i32, ctypes.POINTER(vp)]
         L.lso_stream_layers.argtypes = [vp, vp, sz]
+        L.lso_stream_files.argtypes = [vp, vp, sz]
         L.lso_stream_slot_weight.argtypes = [vp, i32]
         L.lso_stream_slot_weight.restype = vp
         L.lso_stream_destroy.argtypes = [vp]
@@ -111,7 +135,7 @@ def lib():
         L.lso_last_error.restype = ctypes.c_char_p
         for name in ("lso_adam_step", "lso_validate_blocks", "lso_block_constants",
                      "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create",
-                     "lso_stream_layers", "lso_stream_destroy", "lso_host_alloc", "lso_host_free"):
+                     "lso_stream_layers", "lso_stream_files", "lso_stream_destroy", "lso_host_alloc", "lso_host_free"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -134,6 +158,9 @@ def probes():
         P.lso_probe_link_mode.argtypes = [u64, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
                                           ctypes.POINTER(ctypes.c_double)]
         P.lso_probe_link_mode.restype = ctypes.c_int
+        P.lso_probe_file.argtypes = [ctypes.c_int, u64, u64, u64, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_double)]
+        P.lso_probe_file.restype = ctypes.c_int
         _probes = P
     return _probes
 

@@ -498,6 +498,7 @@ const char* lso_status_string(lso_status s)
     case LSO_E_NOMEM: return "out of memory";
     case LSO_E_HIP: return "HIP runtime error";
     case LSO_E_CALLBACK: return "gradient producer failed";
+    case LSO_E_IO: return "file read or write failed";
     }
     return "unknown status";
 }

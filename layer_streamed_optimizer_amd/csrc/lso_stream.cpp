@@ -1,42 +1,69 @@
-// Layer streaming: CPU-authoritative state, GPU as a transient update engine.
+// Layer streaming: authoritative state off the GPU (host memory or files),
+// the GPU as a transient update engine.
 //
 // MegaTrain summary (blog.hotdry.top), section on streaming execution and
 // the double-buffered pipeline: each layer's state is one contiguous,
-// page-aligned host block moved by one burst DMA; two sets of staging
-// buffers (CPU side and GPU side) alternate so the next layer loads while
-// the current one computes; three streams (weight transfer H2D, compute,
-// transfer back D2H) are tied only by events -- weights-ready, backward-done
-// (here: step-done) and buffer-free -- with no host barrier in the GPU
-// pipeline; the slot size is the largest layer (section on key engineering
-// parameters).  The write-back of each layer is the frozen-incremental
-// page's "stored W += delta": the device computes master + delta and the
-// updated block overwrites the authoritative host copy.
+// page-aligned block moved by one burst; staging buffers on the CPU side
+// and slots on the GPU side alternate so the next layer loads while the
+// current one computes; three streams (weight transfer H2D, compute,
+// transfer back D2H) are tied only by events -- weights-ready,
+// backward-done (here: step-done) and buffer-free -- with no host barrier
+// in the GPU pipeline; the slot size is the largest layer (section on key
+// engineering parameters).  The write-back of each layer is the
+// frozen-incremental page's "stored W += delta" (section "The Math"): the
+// device computes master + delta and the updated block overwrites the
+// authoritative copy.  The same page's storage design (sections "Storage"
+// and "Training Loop": per-layer W, M, V files on an SSD, loaded, updated
+// and flushed one layer at a time) and its advice to preallocate the files
+// (section "Limitations") give the file tier; the MegaTrain summary names
+// NVMe tiering as the next step (section on limits and directions).
 //
-// Per layer i, slot s = i % 2:
+// Per layer i, device slot s = i % nslots:
 //   H2D:     wait buffer-free[s]; copy src[i] -> slot[s]; record weights-ready[s]
 //   compute: wait weights-ready[s]; gradient producer; fused update;
 //            record step-done[s]
 //   D2H:     wait step-done[s]; copy slot[s] -> dst[i]; record buffer-free[s]
-// Every wait refers to an event recorded earlier in host order.
-//
-// Each copy is one burst over the whole block, issued by a copy kernel on
-// the transfer stream (lso_copy.hip says why not the DMA engines; set
+// Every wait refers to an event recorded earlier in host order.  Each copy
+// is one burst over the whole block, issued by a copy kernel on the
+// transfer stream (lso_copy.hip says why not the DMA engines; set
 // LSO_STREAM_COPY=dma to use them).
 //
-// Two kinds of host block:
-//  - pinned (page-locked, e.g. lso_host_alloc): src = dst = the block itself,
-//    one copy each way, and the host thread never waits inside the loop;
-//  - pageable: the DMA engines cannot reach it, so the block goes through
-//    the context's two pinned CPU-side staging buffers; worker threads copy
-//    it in before its H2D and back out after its D2H (the host waits for
-//    that D2H only, two layers behind the one it is issuing).
+// Three kinds of authoritative block:
+//  - pinned host memory (page-locked, e.g. lso_host_alloc): src = dst = the
+//    block itself; nothing for the host to do but issue;
+//  - pageable host memory: the copy engines cannot reach it, so the block
+//    passes through one of the context's pinned staging buffers (nslots + 1
+//    unless LSO_STREAM_STAGING asks for more),
+//    copied in and out by worker threads;
+//  - a region of a file: read into a staging buffer with pread and written
+//    back with pwrite, optionally followed by fdatasync.  O_DIRECT
+//    descriptors work (offsets and sizes are 4 KB multiples), but the
+//    kernel cannot pin the HIP-allocated staging memory for a direct
+//    transfer (EFAULT), so their parts go through a small page-aligned
+//    buffer per worker thread.
+// The host thread runs an event loop over the layers: it starts the
+// stage-in of a layer as soon as a staging buffer is free, issues the
+// layer's GPU work as soon as its stage-in is complete, starts the
+// write-out as soon as its D2H is complete, and frees the buffer when the
+// write-out is complete.  Stage-ins and write-outs run on two separate
+// worker pools, so reading layer i + 1, updating layer i and writing layer
+// i - 1 overlap.
+#include <fcntl.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cerrno>
+#include <chrono>
 #include <condition_variable>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <functional>
+#include <deque>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <thread>
@@ -47,14 +74,41 @@
 
 namespace {
 
-// A fixed pool that splits one memcpy over all its threads.
-class CopyPool {
-public:
-    explicit CopyPool(unsigned n) : n_(n ? n : 1)
+// ------------------------------------------------------------ worker pools
+
+enum IoOp { kIoCopy = 0, kIoRead = 1, kIoWrite = 2 };
+
+// One transfer between a staging buffer and the authoritative copy, split
+// into parts that the pool's threads take in order.
+struct IoRequest {
+    IoOp op = kIoCopy;
+    char* dst = nullptr;         // copy destination, or the pread buffer
+    const char* src = nullptr;   // copy source, or the pwrite buffer
+    int fd = -1;
+    uint64_t foff = 0;           // file offset of byte 0
+    uint64_t bytes = 0;
+    bool sync = false;           // fdatasync(fd) after the last part
+    bool direct = false;         // fd is O_DIRECT: transfer through a bounce buffer
+    std::atomic<uint32_t> parts_left{0};
+    std::atomic<int> err{0};     // first errno seen; EIO for end of file
+    std::atomic<bool> done{false};
+
+    void reset()
     {
-        for (unsigned k = 1; k < n_; ++k) workers_.emplace_back([this, k] { run(k); });
+        parts_left.store(0);
+        err.store(0);
+        done.store(false);
     }
-    ~CopyPool()
+};
+
+class IoPool {
+public:
+    IoPool(unsigned threads, std::mutex* note_mu, std::condition_variable* note_cv)
+        : n_(threads ? threads : 1), note_mu_(note_mu), note_cv_(note_cv)
+    {
+        for (unsigned k = 0; k < n_; ++k) workers_.emplace_back([this] { run(); });
+    }
+    ~IoPool()
     {
         {
             std::lock_guard<std::mutex> l(mu_);
@@ -63,63 +117,143 @@ public:
         cv_.notify_all();
         for (auto& t : workers_) t.join();
     }
-    // dst[0..bytes) = src[0..bytes), split in n contiguous parts.
-    void copy(void* dst, const void* src, uint64_t bytes)
+
+    // r must stay alive (and untouched) until r->done.
+    void submit(IoRequest* r)
     {
+        // parts of 4 KB multiples, about 4 per thread, 4-256 MB each
+        uint64_t part = (r->bytes / (4ull * n_) + 4095) & ~uint64_t(4095);
+        part = std::min<uint64_t>(std::max<uint64_t>(part, 4ull << 20), 256ull << 20);
+        const uint64_t parts = r->bytes == 0 ? 1 : (r->bytes + part - 1) / part;
+        r->parts_left.store(static_cast<uint32_t>(parts));
         {
             std::lock_guard<std::mutex> l(mu_);
-            dst_ = static_cast<char*>(dst);
-            src_ = static_cast<const char*>(src);
-            bytes_ = bytes;
-            pending_ = n_ - 1;
-            ++gen_;
+            for (uint64_t k = 0; k < parts; ++k)
+                q_.push_back({r, k * part, std::min(r->bytes, (k + 1) * part)});
         }
         cv_.notify_all();
-        part(0);
-        std::unique_lock<std::mutex> l(mu_);
-        done_cv_.wait(l, [this] { return pending_ == 0; });
     }
 
 private:
-    void part(unsigned k)
+    struct Part {
+        IoRequest* r;
+        uint64_t lo, hi;
+    };
+
+    static void note_error(IoRequest* r, int e)
     {
-        const uint64_t per = (bytes_ / n_ + 4095) & ~uint64_t(4095);
-        const uint64_t lo = std::min<uint64_t>(bytes_, per * k);
-        const uint64_t hi = std::min<uint64_t>(bytes_, lo + per);
-        if (hi > lo) std::memcpy(dst_ + lo, src_ + lo, hi - lo);
+        int expected = 0;
+        r->err.compare_exchange_strong(expected, e ? e : EIO);
     }
-    void run(unsigned k)
+
+    // pread / pwrite of [off, off + len) of the file to / from buf, whole.
+    static bool file_io(IoRequest* r, char* buf, uint64_t off, uint64_t len, bool read)
     {
-        uint64_t seen = 0;
+        uint64_t done = 0;
+        while (done < len) {
+            const size_t step = static_cast<size_t>(std::min<uint64_t>(len - done, 1ull << 30));
+            const off_t fo = static_cast<off_t>(r->foff + off + done);
+            const ssize_t k = read ? ::pread(r->fd, buf + done, step, fo)
+                                   : ::pwrite(r->fd, buf + done, step, fo);
+            if (k < 0) {
+                if (errno == EINTR) continue;
+                note_error(r, errno);
+                return false;
+            }
+            if (k == 0) {   // end of file on a read, or a device that takes nothing
+                note_error(r, EIO);
+                return false;
+            }
+            done += static_cast<uint64_t>(k);
+        }
+        return true;
+    }
+
+    static uint64_t bounce_bytes()
+    {
+        static const uint64_t b = [] {
+            const char* e = std::getenv("LSO_IO_BOUNCE_MB");
+            const int mb = e ? std::atoi(e) : 0;
+            return static_cast<uint64_t>(mb >= 1 && mb <= 256 ? mb : 64) << 20;
+        }();
+        return b;
+    }
+
+    static void do_part(const Part& p)
+    {
+        IoRequest* r = p.r;
+        if (r->op == kIoCopy) {
+            if (p.hi > p.lo) std::memcpy(r->dst + p.lo, r->src + p.lo, p.hi - p.lo);
+            return;
+        }
+        const bool read = r->op == kIoRead;
+        if (!r->direct) {
+            if (read) file_io(r, r->dst + p.lo, p.lo, p.hi - p.lo, true);
+            else file_io(r, const_cast<char*>(r->src) + p.lo, p.lo, p.hi - p.lo, false);
+            return;
+        }
+        // O_DIRECT: through this thread's page-aligned bounce buffer
+        thread_local std::unique_ptr<char, decltype(&std::free)> bounce(nullptr, &std::free);
+        if (!bounce) {
+            void* q = nullptr;
+            if (posix_memalign(&q, 4096, bounce_bytes()) != 0) {
+                note_error(r, ENOMEM);
+                return;
+            }
+            bounce.reset(static_cast<char*>(q));
+        }
+        for (uint64_t off = p.lo; off < p.hi && r->err.load(std::memory_order_relaxed) == 0;) {
+            const uint64_t len = std::min(bounce_bytes(), p.hi - off);
+            if (read) {
+                if (!file_io(r, bounce.get(), off, len, true)) return;
+                std::memcpy(r->dst + off, bounce.get(), len);
+            } else {
+                std::memcpy(bounce.get(), r->src + off, len);
+                if (!file_io(r, bounce.get(), off, len, false)) return;
+            }
+            off += len;
+        }
+    }
+
+    void run()
+    {
         for (;;) {
+            Part p{};
             {
                 std::unique_lock<std::mutex> l(mu_);
-                cv_.wait(l, [&] { return stop_ || gen_ != seen; });
-                if (stop_) return;
-                seen = gen_;
+                cv_.wait(l, [&] { return stop_ || !q_.empty(); });
+                if (q_.empty()) return;   // stop_ with nothing left
+                p = q_.front();
+                q_.pop_front();
             }
-            part(k);
-            {
-                std::lock_guard<std::mutex> l(mu_);
-                if (--pending_ == 0) done_cv_.notify_one();
+            do_part(p);
+            IoRequest* r = p.r;
+            if (r->parts_left.fetch_sub(1) == 1) {
+                if (r->sync && r->op == kIoWrite && r->err.load() == 0 && ::fdatasync(r->fd) != 0)
+                    note_error(r, errno);
+                {
+                    std::lock_guard<std::mutex> l(*note_mu_);
+                    r->done.store(true);
+                }
+                note_cv_->notify_all();
             }
         }
     }
+
     unsigned n_;
+    std::mutex* note_mu_;
+    std::condition_variable* note_cv_;
     std::vector<std::thread> workers_;
     std::mutex mu_;
-    std::condition_variable cv_, done_cv_;
+    std::condition_variable cv_;
+    std::deque<Part> q_;
     bool stop_ = false;
-    uint64_t gen_ = 0;
-    unsigned pending_ = 0;
-    char* dst_ = nullptr;
-    const char* src_ = nullptr;
-    uint64_t bytes_ = 0;
 };
 
 }  // namespace
 
 constexpr int kMaxSlots = 4;
+constexpr int kMaxStaging = 8;
 
 // Which engine moves each direction of a layer block.
 enum CopyMode { kCopyKernels = 0, kCopyDma = 1, kCopyDmaIn = 2 };
@@ -131,16 +265,20 @@ struct lso_stream_ctx {
     lso_grad_fn fn = nullptr;
     void* user = nullptr;
     int nslots = 2;
+    int nstaging = 3;   // CPU-side staging buffers, >= nslots + 1
     hipStream_t h2d = nullptr, compute = nullptr, d2h = nullptr;
     void* slot_state[kMaxSlots] = {};
     void* slot_grad[kMaxSlots] = {};
     void* slot_weight[kMaxSlots] = {};
-    void* staging[kMaxSlots + 1] = {};   // pinned, allocated on first pageable layer
+    void* staging[kMaxStaging] = {};   // pinned, allocated on the first staged layer
     hipEvent_t weights_ready[kMaxSlots] = {};
     hipEvent_t step_done[kMaxSlots] = {};
     hipEvent_t buffer_free[kMaxSlots] = {};
-    hipEvent_t d2h_done[kMaxSlots + 1] = {};   // per staging buffer: its layer's D2H ended
-    CopyPool* pool = nullptr;
+    hipEvent_t d2h_done[kMaxStaging] = {};   // per staging buffer: its layer's D2H ended
+    IoPool* reader = nullptr;   // stage-ins
+    IoPool* writer = nullptr;   // write-outs
+    std::mutex note_mu;          // signalled when a request completes
+    std::condition_variable note_cv;
     int copy_mode = kCopyKernels;
     unsigned copy_grid = lso::kCopyGrid;
 };
@@ -157,7 +295,9 @@ void release(lso_stream_ctx* c)
     (void)hipSetDevice(c->device);
     for (hipStream_t s : {c->h2d, c->compute, c->d2h})
         if (s) (void)hipStreamSynchronize(s);
-    for (int s = 0; s <= kMaxSlots; ++s) {
+    delete c->reader;   // joins its threads; no request is in flight between calls
+    delete c->writer;
+    for (int s = 0; s < kMaxStaging; ++s) {
         if (c->staging[s]) (void)hipHostFree(c->staging[s]);
         if (c->d2h_done[s]) (void)hipEventDestroy(c->d2h_done[s]);
     }
@@ -171,7 +311,6 @@ void release(lso_stream_ctx* c)
     }
     for (hipStream_t s : {c->h2d, c->compute, c->d2h})
         if (s) (void)hipStreamDestroy(s);
-    delete c->pool;
     (void)hipSetDevice(prev);
     delete c;
 }
@@ -190,8 +329,8 @@ struct DeviceGuard {
     }
 };
 
-// True if the DMA engines can reach the whole block (page-locked host
-// memory registered with HIP); false for ordinary pageable memory.
+// True if the copy engines can reach the whole block (page-locked host
+// memory known to HIP); false for ordinary pageable memory.
 bool is_pinned(const void* p, uint64_t bytes)
 {
     hipPointerAttribute_t a{};
@@ -210,10 +349,28 @@ bool is_pinned(const void* p, uint64_t bytes)
     return b.type == hipMemoryTypeHost;
 }
 
-lso_status check_layer(const lso_stream_ctx* c, const lso_host_layer& L, size_t i)
+// One layer as the pipeline sees it, whatever holds its authoritative copy.
+enum Kind { kPinned = 0, kPageable = 1, kFile = 2 };
+
+struct Job {
+    int kind = kPinned;
+    char* host = nullptr;     // pinned or pageable block
+    int fd = -1;              // file block
+    uint64_t foff = 0;
+    bool sync = false;
+    bool direct = false;      // fd opened O_DIRECT
+    uint64_t bytes = 0, n = 0, off_master = 0, off_m = 0, off_v = 0;
+    void* dev_weight = nullptr;
+    uint32_t opt = 0, layout = 0;
+    uint64_t t = 0;
+    double lr = 0, beta1 = 0, beta2 = 0, eps = 0;
+};
+
+// Checks shared by host and file layers: layout, optimizer, hyper-
+// parameters, sizes and the state's place inside the block.
+lso_status check_state(const lso_stream_ctx* c, const Job& L, size_t i)
 {
     using lso::fail;
-    if (!L.host_base) return fail(LSO_E_INVALID, "layer %zu: host_base is NULL", i);
     if (L.layout != LSO_LAYOUT_PLANAR && L.layout != LSO_LAYOUT_TILED)
         return fail(LSO_E_INVALID, "layer %zu: unknown layout %u", i, L.layout);
     if (L.layout == LSO_LAYOUT_TILED && L.opt != LSO_OPT_ADAM)
@@ -226,8 +383,6 @@ lso_status check_layer(const lso_stream_ctx* c, const lso_host_layer& L, size_t 
     if (L.n > c->max_params)
         return fail(LSO_E_INVALID, "layer %zu: %llu params exceed the context's %llu", i,
                     static_cast<unsigned long long>(L.n), static_cast<unsigned long long>(c->max_params));
-    if (reinterpret_cast<uintptr_t>(L.host_base) % 16 != 0)
-        return fail(LSO_E_ALIGN, "layer %zu: host block is not 16-byte aligned", i);
     if (L.dev_weight && reinterpret_cast<uintptr_t>(L.dev_weight) % 16 != 0)
         return fail(LSO_E_ALIGN, "layer %zu: dev_weight is not 16-byte aligned", i);
     if (L.layout == LSO_LAYOUT_TILED) {
@@ -253,13 +408,49 @@ lso_status check_layer(const lso_stream_ctx* c, const lso_host_layer& L, size_t 
     return LSO_OK;
 }
 
-// Staging buffers: one more than device slots, so a layer can be copied in
-// while the layer two slots back is still on its way out.
-int staging_count(const lso_stream_ctx* c) { return c->nslots + 1; }
+// Blocks of one call must not overlap: their stage-ins and write-outs run
+// concurrently.  An extent is [lo, hi) in a space: (0, 0) for host memory,
+// (device + 1, inode) of the file otherwise.
+struct Extent {
+    uint64_t dev, ino, lo, hi;
+    size_t layer;
+};
+
+lso_status check_disjoint(std::vector<Extent>& ex)
+{
+    std::sort(ex.begin(), ex.end(), [](const Extent& a, const Extent& b) {
+        if (a.dev != b.dev) return a.dev < b.dev;
+        if (a.ino != b.ino) return a.ino < b.ino;
+        return a.lo < b.lo;
+    });
+    for (size_t k = 1; k < ex.size(); ++k) {
+        const Extent& a = ex[k - 1];
+        const Extent& b = ex[k];
+        if (a.dev == b.dev && a.ino == b.ino && b.lo < a.hi)
+            return lso::fail(LSO_E_OVERLAP, "layers %zu and %zu share bytes of their blocks",
+                             std::min(a.layer, b.layer), std::max(a.layer, b.layer));
+    }
+    return LSO_OK;
+}
+
+// Staging buffers: at least one more than device slots, so a layer can be
+// read in while the layer before it is still being written out; more let
+// stage-ins run further ahead of slow write-outs.
+size_t staging_count(const lso_stream_ctx* c) { return static_cast<size_t>(c->nstaging); }
+
+unsigned io_threads()
+{
+    if (const char* e = std::getenv("LSO_IO_THREADS")) {
+        const int k = std::atoi(e);
+        if (k >= 1 && k <= 64) return static_cast<unsigned>(k);
+    }
+    const unsigned hw = std::thread::hardware_concurrency();
+    return std::max(2u, std::min(8u, (hw ? hw : 2u) / 2));
+}
 
 lso_status ensure_staging(lso_stream_ctx* c)
 {
-    for (int s = 0; s < staging_count(c); ++s) {
+    for (size_t s = 0; s < staging_count(c); ++s) {
         if (c->staging[s]) continue;
         if (hipHostMalloc(&c->staging[s], c->max_bytes, hipHostMallocDefault) != hipSuccess) {
             (void)hipGetLastError();
@@ -268,11 +459,9 @@ lso_status ensure_staging(lso_stream_ctx* c)
                              static_cast<unsigned long long>(c->max_bytes));
         }
     }
-    if (!c->pool) {
-        unsigned n = std::thread::hardware_concurrency();
-        c->pool = new (std::nothrow) CopyPool(std::min(n ? n : 1u, 16u));
-        if (!c->pool) return lso::fail(LSO_E_NOMEM, "copy pool");
-    }
+    if (!c->reader) c->reader = new (std::nothrow) IoPool(io_threads(), &c->note_mu, &c->note_cv);
+    if (!c->writer) c->writer = new (std::nothrow) IoPool(io_threads(), &c->note_mu, &c->note_cv);
+    if (!c->reader || !c->writer) return lso::fail(LSO_E_NOMEM, "worker pools");
     return LSO_OK;
 }
 
@@ -287,17 +476,18 @@ hipError_t copy_block(const lso_stream_ctx* c, void* dst, const void* src, uint6
     return static_cast<hipError_t>(lso::launch_block_copy(dst, src, bytes, c->copy_grid, st));
 }
 
-// Enqueue H2D, gradient producer, update and D2H of layer i (slot i % nslots).
-// src/dst: where the H2D reads and the D2H writes (the block itself when
-// pinned, the slot's staging buffer otherwise).
-lso_status issue_layer(lso_stream_ctx* c, const lso_host_layer& h, size_t i, void* src, void* dst)
+// Enqueue H2D, gradient producer, update and D2H of layer i (slot i % nslots),
+// and record d2h_done[i % nstaging] after its D2H.  buf: where the H2D
+// reads and the D2H writes (the block itself when pinned, a staging buffer
+// otherwise).
+lso_status issue_layer(lso_stream_ctx* c, const Job& h, size_t i, void* buf)
 {
     const int s = static_cast<int>(i % c->nslots);
     hipError_t err;
     // StreamIn: the device slot is free once the layer that used it last
     // (nslots layers ago) has been copied back.
     if ((err = hipStreamWaitEvent(c->h2d, c->buffer_free[s], 0)) != hipSuccess ||
-        (err = copy_block(c, c->slot_state[s], src, h.bytes, hipMemcpyHostToDevice, c->h2d)) != hipSuccess ||
+        (err = copy_block(c, c->slot_state[s], buf, h.bytes, hipMemcpyHostToDevice, c->h2d)) != hipSuccess ||
         (err = hipEventRecord(c->weights_ready[s], c->h2d)) != hipSuccess)
         return lso::hip_fail(err, "H2D stage");
     // Compute: gradients of this layer, then the fused update on the slot.
@@ -329,11 +519,219 @@ lso_status issue_layer(lso_stream_ctx* c, const lso_host_layer& h, size_t i, voi
         return lso::hip_fail(err, "hipEventRecord(step-done)");
     // Offload: the updated block goes back over the authoritative copy.
     if ((err = hipStreamWaitEvent(c->d2h, c->step_done[s], 0)) != hipSuccess ||
-        (err = copy_block(c, dst, c->slot_state[s], h.bytes, hipMemcpyDeviceToHost, c->d2h)) != hipSuccess ||
+        (err = copy_block(c, buf, c->slot_state[s], h.bytes, hipMemcpyDeviceToHost, c->d2h)) != hipSuccess ||
         (err = hipEventRecord(c->buffer_free[s], c->d2h)) != hipSuccess ||
-        (err = hipEventRecord(c->d2h_done[i % (c->nslots + 1)], c->d2h)) != hipSuccess)
+        (err = hipEventRecord(c->d2h_done[i % staging_count(c)], c->d2h)) != hipSuccess)
         return lso::hip_fail(err, "D2H stage");
     return LSO_OK;
+}
+
+const char* io_what(const Job& j) { return j.kind == kFile ? "file" : "host block"; }
+
+// With LSO_STREAM_TRACE set, each call prints one line per layer to stderr:
+// when its stage-in started, when the loop saw it complete and issued the
+// layer, when it saw the D2H complete (write-out start) and when it saw the
+// write-out complete, in ms from the start of the call.
+struct Trace {
+    bool on = false;
+    std::chrono::steady_clock::time_point t0;
+    std::vector<double> read, issue, retire, done;
+
+    explicit Trace(size_t n)
+    {
+        const char* e = std::getenv("LSO_STREAM_TRACE");
+        on = e && *e && std::strcmp(e, "0") != 0;
+        if (!on) return;
+        t0 = std::chrono::steady_clock::now();
+        read.assign(n, -1);
+        issue.assign(n, -1);
+        retire.assign(n, -1);
+        done.assign(n, -1);
+    }
+    void mark(std::vector<double>& v, size_t i)
+    {
+        if (on) v[i] = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    }
+    void print() const
+    {
+        if (!on) return;
+        std::fprintf(stderr, "[lso trace] layer  read_start  issued  d2h_done  written   (ms)\n");
+        for (size_t i = 0; i < read.size(); ++i)
+            std::fprintf(stderr, "[lso trace] %5zu  %10.1f  %6.1f  %8.1f  %7.1f\n", i, read[i], issue[i],
+                         retire[i], done[i]);
+    }
+};
+
+// The event loop over all layers of one call (see the top of this file).
+// Layer i owns staging buffer i % K (K = nstaging) from the start of its
+// stage-in until its write-out is complete.
+lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
+{
+    bool any_staged = false;
+    for (size_t i = 0; i < n; ++i) any_staged |= J[i].kind != kPinned;
+    if (any_staged) {
+        lso_status s = ensure_staging(c);
+        if (s != LSO_OK) return s;
+    }
+    const size_t K = staging_count(c);
+    std::unique_ptr<IoRequest[]> rd(new IoRequest[K]), wr(new IoRequest[K]);
+    std::vector<char> wr_live(K, 0);   // a write-out was submitted for the buffer
+    lso_status result = LSO_OK;
+    auto record = [&](lso_status s) {
+        if (result == LSO_OK) result = s;
+    };
+    size_t next_read = 0;     // next layer to stage in
+    size_t next_issue = 0;    // next layer to enqueue on the GPU
+    size_t next_retire = 0;   // next layer whose D2H completion is awaited
+    size_t next_done = 0;     // next layer whose write-out completion is awaited
+    size_t stop_at = n;       // after an error no layer >= stop_at is read or issued
+    bool gpu_ok = true;       // after a failed GPU stage no staged data is written out
+    Trace trace(n);
+
+    auto read_complete = [&](size_t i) {
+        return J[i].kind == kPinned || rd[i % K].done.load();
+    };
+    auto reads_in_flight = [&] {
+        for (size_t i = next_issue; i < next_read; ++i)
+            if (!read_complete(i)) return true;
+        return false;
+    };
+    for (;;) {
+        bool progress = false;
+        // 1. stage in while a buffer is free
+        while (next_read < stop_at && next_read < next_done + K) {
+            const Job& j = J[next_read];
+            if (j.kind != kPinned) {
+                IoRequest& r = rd[next_read % K];
+                r.reset();
+                r.direct = false;
+                r.bytes = j.bytes;
+                r.dst = static_cast<char*>(c->staging[next_read % K]);
+                if (j.kind == kFile) {
+                    r.op = kIoRead;
+                    r.fd = j.fd;
+                    r.foff = j.foff;
+                    r.direct = j.direct;
+                } else {
+                    r.op = kIoCopy;
+                    r.src = j.host;
+                }
+                c->reader->submit(&r);
+            }
+            trace.mark(trace.read, next_read);
+            ++next_read;
+            progress = true;
+        }
+        // 2. issue staged layers in order
+        while (next_issue < next_read && next_issue < stop_at && read_complete(next_issue)) {
+            const Job& j = J[next_issue];
+            if (j.kind != kPinned) {
+                if (const int e = rd[next_issue % K].err.load()) {
+                    record(lso::fail(LSO_E_IO, "layer %zu: reading its %s failed: %s", next_issue,
+                                     io_what(j), std::strerror(e)));
+                    stop_at = next_issue;
+                    break;
+                }
+            }
+            void* buf = j.kind == kPinned ? static_cast<void*>(j.host) : c->staging[next_issue % K];
+            trace.mark(trace.issue, next_issue);
+            const lso_status s = issue_layer(c, j, next_issue, buf);
+            if (s != LSO_OK) {
+                record(s);
+                stop_at = next_issue;
+                if (s == LSO_E_HIP) gpu_ok = false;
+                break;
+            }
+            ++next_issue;
+            progress = true;
+        }
+        // 3. start the write-out of layers whose D2H is complete, one at a
+        //    time in layer order (so a failed write leaves every later
+        //    layer untouched)
+        while (next_retire < next_issue && next_done == next_retire) {
+            const hipError_t q = gpu_ok ? hipEventQuery(c->d2h_done[next_retire % K]) : hipSuccess;
+            if (q == hipErrorNotReady) break;
+            if (q != hipSuccess) {
+                record(lso::hip_fail(q, "D2H completion"));
+                gpu_ok = false;
+                stop_at = std::min(stop_at, next_issue);
+            }
+            const Job& j = J[next_retire];
+            if (j.kind != kPinned && gpu_ok && next_retire < stop_at) {
+                IoRequest& w = wr[next_retire % K];
+                w.reset();
+                w.direct = j.direct;
+                w.sync = false;
+                w.bytes = j.bytes;
+                w.src = static_cast<const char*>(c->staging[next_retire % K]);
+                if (j.kind == kFile) {
+                    w.op = kIoWrite;
+                    w.fd = j.fd;
+                    w.foff = j.foff;
+                    w.sync = j.sync;
+                } else {
+                    w.op = kIoCopy;
+                    w.dst = j.host;
+                }
+                wr_live[next_retire % K] = 1;
+                c->writer->submit(&w);
+            }
+            trace.mark(trace.retire, next_retire);
+            ++next_retire;
+            progress = true;
+        }
+        // 4. free the buffers of layers whose write-out is complete
+        while (next_done < next_retire) {
+            const size_t b = next_done % K;
+            if (wr_live[b]) {
+                if (!wr[b].done.load()) break;
+                wr_live[b] = 0;
+                if (const int e = wr[b].err.load()) {
+                    // this region may be partly written; no later layer is
+                    // written back
+                    record(lso::fail(LSO_E_IO, "layer %zu: writing its %s back failed: %s", next_done,
+                                     io_what(J[next_done]), std::strerror(e)));
+                    stop_at = std::min(stop_at, next_done + 1);
+                }
+            }
+            trace.mark(trace.done, next_done);
+            ++next_done;
+            progress = true;
+        }
+        const size_t last = std::min(stop_at, n);
+        if (next_done == next_issue && next_issue >= last && !reads_in_flight()) break;
+        if (!progress) {
+            std::unique_lock<std::mutex> l(c->note_mu);
+            c->note_cv.wait_for(l, std::chrono::microseconds(200));
+        }
+    }
+    // Every enqueued stage finishes before return (on error too, so no copy
+    // into a block is still running when the caller looks at it).
+    for (hipStream_t st : {c->h2d, c->compute, c->d2h}) {
+        const hipError_t err = hipStreamSynchronize(st);
+        if (err != hipSuccess) record(lso::hip_fail(err, "hipStreamSynchronize"));
+    }
+    trace.print();
+    return result;
+}
+
+// Fields shared by lso_host_layer and lso_file_layer.
+template <class T>
+void copy_state_fields(Job& j, const T& L)
+{
+    j.bytes = L.bytes;
+    j.n = L.n;
+    j.off_master = L.off_master;
+    j.off_m = L.off_m;
+    j.off_v = L.off_v;
+    j.dev_weight = L.dev_weight;
+    j.opt = L.opt;
+    j.layout = L.layout;
+    j.t = L.t;
+    j.lr = L.lr;
+    j.beta1 = L.beta1;
+    j.beta2 = L.beta2;
+    j.eps = L.eps;
 }
 
 }  // namespace
@@ -356,7 +754,8 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     auto* c = new (std::nothrow) lso_stream_ctx;
     if (!c) return lso::fail(LSO_E_NOMEM, "context allocation failed");
     c->device = device;
-    c->max_bytes = max_layer_bytes;
+    // staging buffers serve file blocks too, whose sizes are 4 KB multiples
+    c->max_bytes = (max_layer_bytes + 4095) & ~uint64_t(4095);
     c->max_params = max_layer_params;
     c->fn = fn;
     c->user = user;
@@ -367,6 +766,11 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     if (const char* e = std::getenv("LSO_STREAM_SLOTS")) {
         const int k = std::atoi(e);
         if (k >= 2 && k <= kMaxSlots) c->nslots = k;
+    }
+    c->nstaging = c->nslots + 1;
+    if (const char* e = std::getenv("LSO_STREAM_STAGING")) {
+        const int k = std::atoi(e);
+        if (k >= c->nslots + 1 && k <= kMaxStaging) c->nstaging = k;
     }
     if (const char* e = std::getenv("LSO_STREAM_COPY_GRID")) {
         const int k = std::atoi(e);
@@ -379,12 +783,12 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     }
     const uint64_t pbytes = round16(2 * (max_layer_params ? max_layer_params : 1));
     for (int s = 0; s < c->nslots; ++s) {
-        if (hipMalloc(&c->slot_state[s], max_layer_bytes) != hipSuccess ||
+        if (hipMalloc(&c->slot_state[s], c->max_bytes) != hipSuccess ||
             hipMalloc(&c->slot_grad[s], pbytes) != hipSuccess ||
             hipMalloc(&c->slot_weight[s], pbytes) != hipSuccess) {
             release(c);
             return lso::fail(LSO_E_NOMEM, "slot allocation (%llu + 2 x %llu bytes) failed",
-                             static_cast<unsigned long long>(max_layer_bytes),
+                             static_cast<unsigned long long>(c->max_bytes),
                              static_cast<unsigned long long>(pbytes));
         }
         for (hipEvent_t* e : {&c->weights_ready[s], &c->step_done[s], &c->buffer_free[s]}) {
@@ -392,7 +796,7 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
             if (err != hipSuccess) { release(c); return lso::hip_fail(err, "hipEventCreateWithFlags"); }
         }
     }
-    for (int s = 0; s <= c->nslots; ++s) {
+    for (size_t s = 0; s < staging_count(c); ++s) {
         err = hipEventCreateWithFlags(&c->d2h_done[s], hipEventDisableTiming);
         if (err != hipSuccess) { release(c); return lso::hip_fail(err, "hipEventCreateWithFlags"); }
     }
@@ -406,75 +810,66 @@ lso_status lso_stream_layers(lso_stream_ctx* c, const lso_host_layer* L, size_t 
     if (!c) return lso::fail(LSO_E_INVALID, "ctx is NULL");
     if (n_layers == 0) return LSO_OK;
     if (!L) return lso::fail(LSO_E_INVALID, "host_blocks is NULL");
+    std::vector<Job> jobs(n_layers);
+    std::vector<Extent> ex;
+    ex.reserve(n_layers);
     for (size_t i = 0; i < n_layers; ++i) {
-        lso_status s = check_layer(c, L[i], i);
+        Job& j = jobs[i];
+        copy_state_fields(j, L[i]);
+        j.host = static_cast<char*>(L[i].host_base);
+        if (!j.host) return lso::fail(LSO_E_INVALID, "layer %zu: host_base is NULL", i);
+        if (reinterpret_cast<uintptr_t>(j.host) % 16 != 0)
+            return lso::fail(LSO_E_ALIGN, "layer %zu: host block is not 16-byte aligned", i);
+        lso_status s = check_state(c, j, i);
         if (s != LSO_OK) return s;
+        const uint64_t lo = reinterpret_cast<uintptr_t>(j.host);
+        ex.push_back({0, 0, lo, lo + j.bytes, i});
     }
+    lso_status s = check_disjoint(ex);
+    if (s != LSO_OK) return s;
     DeviceGuard guard(c->device);
-    std::vector<char> pinned(n_layers);
-    bool any_pageable = false;
+    for (Job& j : jobs) j.kind = is_pinned(j.host, j.bytes) ? kPinned : kPageable;
+    return run_pipeline(c, jobs.data(), n_layers);
+}
+
+lso_status lso_stream_files(lso_stream_ctx* c, const lso_file_layer* L, size_t n_layers)
+{
+    lso::clear_error();
+    if (!c) return lso::fail(LSO_E_INVALID, "ctx is NULL");
+    if (n_layers == 0) return LSO_OK;
+    if (!L) return lso::fail(LSO_E_INVALID, "layers is NULL");
+    std::vector<Job> jobs(n_layers);
+    std::vector<Extent> ex;
+    ex.reserve(n_layers);
     for (size_t i = 0; i < n_layers; ++i) {
-        pinned[i] = is_pinned(L[i].host_base, L[i].bytes);
-        any_pageable |= !pinned[i];
-    }
-    if (any_pageable) {
-        lso_status s = ensure_staging(c);
+        Job& j = jobs[i];
+        copy_state_fields(j, L[i]);
+        j.kind = kFile;
+        j.fd = L[i].fd;
+        j.foff = L[i].file_offset;
+        if (L[i].flags & ~static_cast<uint32_t>(LSO_FILE_SYNC))
+            return lso::fail(LSO_E_INVALID, "layer %zu: unknown flags %#x", i, L[i].flags);
+        j.sync = (L[i].flags & LSO_FILE_SYNC) != 0;
+        if (j.foff % 4096 != 0 || j.bytes % 4096 != 0)
+            return lso::fail(LSO_E_ALIGN, "layer %zu: file offset and bytes must be 4096-byte multiples", i);
+        struct stat st {};
+        if (j.fd < 0 || ::fstat(j.fd, &st) != 0)
+            return lso::fail(LSO_E_INVALID, "layer %zu: fd %d is not an open file", i, j.fd);
+        const int acc = ::fcntl(j.fd, F_GETFL);
+        if (acc < 0 || (acc & O_ACCMODE) != O_RDWR)
+            return lso::fail(LSO_E_INVALID, "layer %zu: fd %d is not open for reading and writing", i, j.fd);
+        j.direct = (acc & O_DIRECT) != 0;
+        if (S_ISREG(st.st_mode) && static_cast<uint64_t>(st.st_size) < j.foff + j.bytes)
+            return lso::fail(LSO_E_INVALID, "layer %zu: the file ends before its block does", i);
+        lso_status s = check_state(c, j, i);
         if (s != LSO_OK) return s;
+        ex.push_back({static_cast<uint64_t>(st.st_dev) + 1, static_cast<uint64_t>(st.st_ino), j.foff,
+                      j.foff + j.bytes, i});
     }
-    lso_status result = LSO_OK;
-    hipError_t err = hipSuccess;
-    // Host order: issue layers ahead while a staging buffer is free, else
-    // retire the oldest layer.  retire(i) waits for layer i's D2H and copies
-    // a staged layer back out of its staging buffer, which frees that buffer
-    // for layer i + nstage; with one more staging buffer than device slots
-    // the copy-in of a layer overlaps the D2H of the layer before it.  A
-    // pinned layer needs no staging and its retire does not wait.
-    const size_t nst = static_cast<size_t>(staging_count(c));
-    size_t issued = 0, retired = 0;
-    auto issue = [&](size_t i) -> lso_status {
-        void* blk = L[i].host_base;
-        if (!pinned[i]) {
-            void* stg = c->staging[i % nst];
-            c->pool->copy(stg, blk, L[i].bytes);   // stage in
-            blk = stg;
-        }
-        return issue_layer(c, L[i], i, blk, blk);
-    };
-    auto retire = [&](size_t i) -> lso_status {
-        if (pinned[i]) return LSO_OK;
-        // d2h_done[i % nst] still refers to layer i: layer i + nst, which
-        // re-records it, is issued only after this retire
-        hipError_t e = hipEventSynchronize(c->d2h_done[i % nst]);
-        if (e != hipSuccess) return lso::hip_fail(e, "hipEventSynchronize(buffer-free)");
-        c->pool->copy(L[i].host_base, c->staging[i % nst], L[i].bytes);   // stage out
-        return LSO_OK;
-    };
-    while (retired < n_layers) {
-        if (issued < n_layers && issued < retired + nst) {
-            result = issue(issued);
-            if (result != LSO_OK) break;
-            ++issued;
-        } else {
-            result = retire(retired);
-            if (result != LSO_OK) break;
-            ++retired;
-        }
-    }
-    // Drain: every enqueued stage finishes (on error too, so no copy into a
-    // host block is still running when the caller looks at it); a staged
-    // layer whose D2H was enqueued is still copied out.
-    for (hipStream_t st : {c->h2d, c->compute, c->d2h}) {
-        err = hipStreamSynchronize(st);
-        if (err != hipSuccess && result == LSO_OK) result = lso::hip_fail(err, "hipStreamSynchronize");
-    }
-    if (result == LSO_E_CALLBACK || result == LSO_E_HIP) {
-        // layers whose D2H completed are whole; copy the staged ones out
-        // (a failed layer never reached its D2H, so it is not among them)
-        const size_t failed = issued;   // the layer that failed was not counted
-        for (size_t i = retired; i < failed; ++i)
-            if (!pinned[i]) c->pool->copy(L[i].host_base, c->staging[i % nst], L[i].bytes);
-    }
-    return result;
+    lso_status s = check_disjoint(ex);
+    if (s != LSO_OK) return s;
+    DeviceGuard guard(c->device);
+    return run_pipeline(c, jobs.data(), n_layers);
 }
 
 void* lso_stream_slot_weight(lso_stream_ctx* c, int slot)

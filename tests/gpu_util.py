@@ -8,6 +8,8 @@ import sys
 import numpy as np
 
 import layer_streamed_optimizer_amd as lso
+import synth
+from layer_streamed_optimizer_amd import configs
 
 CANARY = 0xA5
 GUARD = 256
@@ -251,3 +253,86 @@ def hip():
 
 
 HIP_D2D = 3
+
+
+# ------------------------------------------------------------ layer stream
+
+LR, B1, B2, EPS = configs.LR, configs.BETA1, configs.BETA2, configs.EPS
+
+
+class _Pageable:
+    """Ordinary (pageable) host memory with the HostBuffer interface."""
+
+    def __init__(self, nbytes):
+        self.arr = np.empty(nbytes + 64, np.uint8)
+        shift = (-self.arr.ctypes.data) % 64
+        self.ptr = self.arr.ctypes.data + shift
+        self.nbytes = nbytes
+        self._shift = shift
+
+    def view(self, dtype=np.uint8, offset=0, count=None):
+        dt = np.dtype(dtype)
+        if count is None:
+            count = (self.nbytes - offset) // dt.itemsize
+        return self.arr[self._shift + offset:self._shift + offset + count * dt.itemsize].view(dt)
+
+
+class HostLayers:
+    """Authoritative host blocks, one per layer: [master | m | v] planar or
+    one tiled region; pinned (lso_host_alloc) or pageable, per layer."""
+
+    def __init__(self, sizes, sid, pageable=False, tiled=False):
+        self.sizes = sizes
+        self.tiled = tiled
+        self.bufs, self.lay = [], []
+        for b, n in enumerate(sizes):
+            om, omm, ov, nbytes = configs.host_layer_layout(n, tiled=tiled)
+            pg = pageable(b) if callable(pageable) else pageable
+            hb = _Pageable(nbytes) if pg else lso.host_alloc(nbytes)
+            hb.view(np.uint8)[:] = 0
+            master = synth.normal_f32(n, stream=sid, block=b, purpose=0, step=0, sigma=0.02)
+            if tiled:
+                z = np.zeros(n, np.float32)
+                reg = tile_state(master, z, z)
+                hb.view(np.float32, om, reg.size)[:] = reg
+            else:
+                hb.view(np.float32, om, n)[:] = master
+            self.bufs.append(hb)
+            self.lay.append((om, omm, ov, nbytes))
+
+    def raw(self, b):
+        """The whole block's bytes (a copy)."""
+        return self.bufs[b].view(np.uint8, 0, self.lay[b][3]).copy()
+
+    def get(self, b, q):
+        om, omm, ov, nbytes = self.lay[b]
+        n = self.sizes[b]
+        if self.tiled:
+            reg = self.bufs[b].view(np.float32, om, (nbytes - om) // 4)
+            return detile_state(reg, n)[("master", "m", "v").index(q)]
+        off = {"master": om, "m": omm, "v": ov}[q]
+        return self.bufs[b].view(np.float32, off, self.sizes[b]).copy()
+
+    def table(self, t, opt=lso.LSO_OPT_ADAM, lr=LR, dev_weight=None):
+        L = lso.LayerStream.layers(len(self.sizes))
+        for b, n in enumerate(self.sizes):
+            om, omm, ov, nbytes = self.lay[b]
+            L[b]["host_base"] = self.bufs[b].ptr
+            L[b]["bytes"] = nbytes
+            L[b]["n"] = n
+            L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
+            L[b]["dev_weight"] = dev_weight[b] if dev_weight else 0
+            L[b]["opt"] = opt
+            L[b]["layout"] = lso.LSO_LAYOUT_TILED if self.tiled else lso.LSO_LAYOUT_PLANAR
+            L[b]["t"] = t
+            L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = lr, B1, B2, EPS
+        return L
+
+
+def synth_stream(sizes, sid, max_bytes=None):
+    fn, Params = synth.grad_callback()
+    params = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
+                    scale=synth.scale_for(1e-3), block_base=0)
+    mb = max_bytes or max(configs.host_layer_layout(n)[3] for n in sizes)
+    ls = lso.LayerStream(mb, max(sizes), fn, ctypes.addressof(params))
+    return ls, params

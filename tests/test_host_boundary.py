@@ -57,6 +57,12 @@ int main(void) {
   F(lso_host_layer, dev_weight) F(lso_host_layer, opt) F(lso_host_layer, layout)
   F(lso_host_layer, t) F(lso_host_layer, lr) F(lso_host_layer, beta1) F(lso_host_layer, beta2)
   F(lso_host_layer, eps)
+  printf("lso_file_layer.size %zu\n", sizeof(lso_file_layer));
+  F(lso_file_layer, fd) F(lso_file_layer, flags) F(lso_file_layer, file_offset)
+  F(lso_file_layer, bytes) F(lso_file_layer, n) F(lso_file_layer, off_master)
+  F(lso_file_layer, off_m) F(lso_file_layer, off_v) F(lso_file_layer, dev_weight)
+  F(lso_file_layer, opt) F(lso_file_layer, layout) F(lso_file_layer, t) F(lso_file_layer, lr)
+  F(lso_file_layer, beta1) F(lso_file_layer, beta2) F(lso_file_layer, eps)
   return 0;
 }
 """
@@ -69,7 +75,9 @@ int main(void) {
     got = dict(l.split() for l in lines if l)
     assert int(got["lso_block.size"]) == ctypes.sizeof(_native.LsoBlock) == lso.BLOCK_DTYPE.itemsize
     assert int(got["lso_host_layer.size"]) == ctypes.sizeof(_native.LsoHostLayer)
-    for struct, cls in (("lso_block", _native.LsoBlock), ("lso_host_layer", _native.LsoHostLayer)):
+    assert int(got["lso_file_layer.size"]) == ctypes.sizeof(_native.LsoFileLayer)
+    for struct, cls in (("lso_block", _native.LsoBlock), ("lso_host_layer", _native.LsoHostLayer),
+                        ("lso_file_layer", _native.LsoFileLayer)):
         for fname, _ in cls._fields_:
             assert int(got[f"{struct}.{fname}"]) == getattr(cls, fname).offset, (struct, fname)
 
