@@ -61,6 +61,8 @@ def _load():
         lib.lso_oracle_sgd_g32.restype = i32
         lib.lso_oracle_accumulate_f32.argtypes = [u64, f32p, f32p]
         lib.lso_oracle_accumulate_f32.restype = i32
+        lib.lso_oracle_sq_norm.argtypes = [u64, u16p, f32p]
+        lib.lso_oracle_sq_norm.restype = dbl
         lib.lso_oracle_bf16_rne.argtypes = [ctypes.c_float]
         lib.lso_oracle_bf16_rne.restype = ctypes.c_uint16
         lib.lso_oracle_bf16_rne_array.argtypes = [f32p, u16p, u64]
@@ -127,6 +129,19 @@ def accumulate_f32(w: np.ndarray, delta: np.ndarray) -> None:
     _check(w, np.float32, n, "w")
     _check(delta, np.float32, n, "delta")
     _load().lso_oracle_accumulate_f32(n, _ptr(w), _ptr(delta))
+
+
+def sq_norm(g: np.ndarray) -> float:
+    """Squared L2 norm of a gradient (uint16 BF16 patterns or float32), FP64
+    in index order: the magnitude that progressive layer locking compares
+    with its threshold (frozen-incremental page, "Progressive Layer
+    Locking")."""
+    g = np.ascontiguousarray(g)
+    if g.dtype == np.uint16:
+        return float(_load().lso_oracle_sq_norm(g.size, _ptr(g), None))
+    if g.dtype == np.float32:
+        return float(_load().lso_oracle_sq_norm(g.size, None, _ptr(g)))
+    raise ValueError(f"gradient must be uint16 (BF16) or float32, got {g.dtype}")
 
 
 def bf16_rne(x: np.ndarray) -> np.ndarray:

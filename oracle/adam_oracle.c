@@ -230,3 +230,21 @@ int lso_oracle_accumulate_f32(uint64_t n, float* w, const float* delta)
     for (uint64_t i = 0; i < n; ++i) w[i] = w[i] + delta[i];
     return 1;
 }
+
+/* ---- the squared L2 norm of a gradient --------------------------------- */
+
+/* sum_i g_i^2 in FP64, in index order.  Progressive layer locking on the
+ * frozen-incremental page (section "Progressive Layer Locking") locks a
+ * layer once its gradient magnitude falls below a threshold; the magnitude
+ * is read as the Euclidean norm, whose square this returns.  g: BF16 bit
+ * patterns (g16) or FP32 values (g32); exactly one is non-NULL. */
+double lso_oracle_sq_norm(uint64_t n, const uint16_t* g16, const float* g32)
+{
+    double s = 0.0;
+    for (uint64_t i = 0; i < n; ++i) {
+        double g = g32 ? (double)g32[i] : bf16_widen(g16[i]);
+        s += g * g;
+    }
+    return s;
+}
+

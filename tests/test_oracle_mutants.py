@@ -32,6 +32,11 @@ MUTANTS = {
     "sgd_g32_read_as_bf16": ("float gi = g32 ? g32[i] : f32_from_bits((uint32_t)g[i] << 16);",
                              "float gi = g32 ? f32_from_bits(bits_from_f32(g32[i]) & 0xFFFF0000u)"
                              " : f32_from_bits((uint32_t)g[i] << 16);"),
+    "sq_norm_drops_last": ("for (uint64_t i = 0; i < n; ++i) {\n        double g = g32 ?",
+                           "for (uint64_t i = 0; i + 1 < n; ++i) {\n        double g = g32 ?"),
+    "sq_norm_abs": ("s += g * g;", "s += fabs(g);"),
+    "sq_norm_bf16_path_reads_low_half": ("double g = g32 ? (double)g32[i] : bf16_widen(g16[i]);",
+                                         "double g = g32 ? (double)g32[i] : (double)g16[i];"),
 }
 
 

@@ -426,6 +426,45 @@ def test_fp32_gradient_sgd_exact():
         assert out[i] == frac_to_f32(Fraction(float(master[i])) - Fraction(float(g[i])) / 2), i
 
 
+# ------------------------------------------------- gradient norm (locking)
+# The frozen-incremental page locks a layer once its "gradient magnitude"
+# is below a threshold; read as the Euclidean norm, the oracle returns its
+# square.
+
+def test_sq_norm_closed_forms():
+    assert oracle.sq_norm(bf16_bits([3.0, 4.0])) == 25.0
+    assert oracle.sq_norm(np.array([3.0, -4.0, 12.0], np.float32)) == 169.0
+    n = 12345
+    assert oracle.sq_norm(bf16_bits(np.full(n, -0.5, np.float32))) == n * 0.25
+    assert oracle.sq_norm(np.zeros(0, np.uint16)) == 0.0
+    assert oracle.sq_norm(bf16_bits([0.0, -0.0])) == 0.0
+
+
+def test_sq_norm_matches_exactly_rounded_sum():
+    """math.fsum of the exact squares (each BF16 / FP32 square is exact in
+    FP64) is the correctly rounded sum; the oracle's running FP64 sum is
+    within n * 2^-53 of it."""
+    for seed, n in ((70, 1000), (71, 100003)):
+        g = random_bf16(n, 1e-3, seed)
+        gv = bf16_value(g).astype(np.float64)
+        exact = math.fsum(gv * gv)
+        assert abs(oracle.sq_norm(g) - exact) <= n * 2.0 ** -53 * exact
+        f = random_f32_not_bf16(n, 1e-2, seed)
+        fv = f.astype(np.float64)
+        exact = math.fsum(fv * fv)
+        assert abs(oracle.sq_norm(f) - exact) <= n * 2.0 ** -53 * exact
+
+
+def test_sq_norm_scales_by_powers_of_two_and_counts_every_element():
+    g = random_f32_not_bf16(777, 1e-2, 72)
+    assert oracle.sq_norm(g * np.float32(2.0)) == 4.0 * oracle.sq_norm(g)
+    one_hot = np.zeros(1001, np.float32)
+    for k in (0, 500, 1000):
+        one_hot[:] = 0
+        one_hot[k] = 3.0
+        assert oracle.sq_norm(one_hot) == 9.0, k
+
+
 # ---------------------------------------------------------------- BF16 cast
 
 def _torch_bf16_bits(x):
