@@ -145,6 +145,32 @@ typedef struct lso_block {
 lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream);
 
 /*
+ * Gradient norms for progressive layer locking.  The frozen-incremental
+ * page (section "Progressive Layer Locking") locks a layer once its
+ * gradient magnitude is below a threshold: locked layers get no gradient,
+ * no update and no I/O; its section "The Math" notes that per-layer steps t
+ * keep Adam exact for layers that are locked and later resumed (lso_block
+ * and the layer structs carry their own t).  The magnitude is taken as the
+ * Euclidean norm of the layer's gradient; these calls return its square.
+ *
+ * lso_adam_step_norms: lso_adam_step plus, from the same pass over the
+ * gradients, sq_norms[i] = sum over block i's elements of g^2, in FP64
+ * (per chunk of the kernel a fixed-order sum; chunks added in a fixed
+ * order, so results repeat bit for bit).  sq_norms: device array of n
+ * doubles (entries of blocks with n == 0 are not written).  workspace:
+ * device memory of at least lso_norm_workspace_bytes(blocks, n) bytes,
+ * 8-byte aligned; it holds per-chunk sums while the call runs on stream, so
+ * calls that run at the same time need separate workspaces.  Neither may
+ * overlap the other or any array of the call.  Relative error of each
+ * entry against the exact sum: below 2e-6 (FP32 sums of at most 32 squares
+ * per lane, FP64 above that).  Errors: as lso_adam_step, and INVALID for a
+ * NULL or too small buffer, ALIGN, OVERLAP.
+ */
+uint64_t lso_norm_workspace_bytes(const lso_block* blocks, size_t n);
+lso_status lso_adam_step_norms(const lso_block* blocks, size_t n, double* sq_norms, void* workspace,
+                               uint64_t workspace_bytes, void* stream);
+
+/*
  * Host-only helpers (no device work, callable without a GPU).
  * lso_validate_blocks: the checks lso_adam_step runs, without enqueueing.
  * lso_block_constants: the FP32 constants the kernel uses for one block,
@@ -207,6 +233,9 @@ typedef struct lso_host_layer {
     uint32_t layout;         /* lso_layout of the state inside the block */
     uint64_t t;
     double   lr, beta1, beta2, eps;
+    double*  sq_norm;        /* host address that receives the sum of g^2 of
+                                this layer's gradient (FP64) when the call
+                                returns LSO_OK, or NULL */
 } lso_host_layer;
 
 /* Gradient producer: enqueue (never synchronise) work on compute_stream
@@ -229,7 +258,11 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
 
 /* Stream n_layers layers through the pipeline, in order.  Synchronous with
  * respect to host memory: on LSO_OK every host block holds its updated
- * state.  On LSO_E_CALLBACK at layer k, layers < k are fully written back
+ * state, and each layer's sq_norm (if not NULL) its gradient's sum of g^2
+ * (as lso_adam_step_norms).  A layer with n == 0 is skipped entirely -- no
+ * transfer, no producer call, no update, no write-back, no checks of its
+ * other fields -- which is how a locked layer is passed; the producer is
+ * still called with the layer's position in host_blocks.  On LSO_E_CALLBACK at layer k, layers < k are fully written back
  * and layers >= k are untouched on the host.  Validation (bytes, alignment,
  * hyper-parameters, blocks of different layers not overlapping) covers all
  * layers before anything is enqueued.  Calls on one context must not
@@ -262,6 +295,7 @@ typedef struct lso_file_layer {
     uint32_t layout;
     uint64_t t;
     double   lr, beta1, beta2, eps;
+    double*  sq_norm;
 } lso_file_layer;
 
 /* Stream n_layers file blocks through the pipeline, in order.  On LSO_OK

@@ -1,5 +1,5 @@
 """Per-layer mixed-precision Adam on MI355X (gfx950), HBM-resident or
-layer-streamed from pinned host memory.
+layer-streamed from host memory or files.
 
 A thin binding over liblso.so (include/lso.h): it marshals descriptor tables
 and stream handles; every step of the update runs in the HIP library.
@@ -28,10 +28,11 @@ BLOCK_DTYPE = np.dtype(LsoBlock)
 HOST_LAYER_DTYPE = np.dtype(LsoHostLayer)
 FILE_LAYER_DTYPE = np.dtype(LsoFileLayer)
 
-__all__ = ["BlockTable", "adam_step", "validate", "block_constants", "LayerStream", "HostBuffer",
-           "host_alloc", "LsoError", "LSO_OPT_ADAM", "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE",
-           "LSO_DT_F32", "LSO_LAYOUT_PLANAR", "LSO_LAYOUT_TILED", "LSO_TILE_ELEMS", "BLOCK_DTYPE",
-           "HOST_LAYER_DTYPE", "FILE_LAYER_DTYPE", "LSO_FILE_SYNC", "stream_handle", "tiled_state_bytes", "tiled_pack", "tiled_unpack"]
+__all__ = ["BlockTable", "adam_step", "adam_step_norms", "norm_workspace_bytes", "validate",
+           "block_constants", "LayerStream", "HostBuffer", "host_alloc", "LsoError", "LSO_OPT_ADAM",
+           "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE", "LSO_DT_F32", "LSO_LAYOUT_PLANAR",
+           "LSO_LAYOUT_TILED", "LSO_TILE_ELEMS", "BLOCK_DTYPE", "HOST_LAYER_DTYPE", "FILE_LAYER_DTYPE",
+           "LSO_FILE_SYNC", "stream_handle", "tiled_state_bytes", "tiled_pack", "tiled_unpack"]
 
 
 def stream_handle(stream=None) -> int:
@@ -61,6 +62,15 @@ class BlockTable:
 
     def __len__(self) -> int:
         return len(self.arr)
+
+    @classmethod
+    def from_array(cls, arr: np.ndarray) -> "BlockTable":
+        """A table holding a copy of an lso_block structured array."""
+        if arr.dtype != BLOCK_DTYPE:
+            raise TypeError("need a BLOCK_DTYPE array")
+        tab = cls(len(arr))
+        tab.arr[:] = arr
+        return tab
 
     @classmethod
     def from_rows(cls, rows: Iterable[dict]) -> "BlockTable":
@@ -113,6 +123,20 @@ def adam_step(table: BlockTable, stream=None) -> None:
     st = _step_fn(table._ptr, len(table.arr), stream if type(stream) is int else stream_handle(stream))
     if st:
         _native.check(st, "lso_adam_step")
+
+
+def norm_workspace_bytes(table: BlockTable) -> int:
+    """Device workspace adam_step_norms needs for this table."""
+    return int(_native.lib().lso_norm_workspace_bytes(table.ptr, len(table)))
+
+
+def adam_step_norms(table: BlockTable, sq_norms, workspace, workspace_bytes: int, stream=None) -> None:
+    """adam_step plus sq_norms[i] = sum of g^2 of block i (FP64, device
+    array of len(table) doubles), from the same pass over the gradients.
+    workspace: device memory of at least norm_workspace_bytes(table) bytes."""
+    st = _native.lib().lso_adam_step_norms(table.ptr, len(table), _addr(sq_norms), _addr(workspace),
+                                           int(workspace_bytes), stream_handle(stream))
+    _native.check(st, "lso_adam_step_norms")
 
 
 def validate(table: BlockTable) -> int:

@@ -61,6 +61,7 @@ class LsoHostLayer(ctypes.Structure):
         ("beta1", ctypes.c_double),
         ("beta2", ctypes.c_double),
         ("eps", ctypes.c_double),
+        ("sq_norm", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +83,7 @@ class LsoFileLayer(ctypes.Structure):
         ("beta1", ctypes.c_double),
         ("beta2", ctypes.c_double),
         ("eps", ctypes.c_double),
+        ("sq_norm", ctypes.c_void_p),
     ]
 
 
@@ -89,7 +91,7 @@ GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctype
                            ctypes.c_uint64, ctypes.c_void_p)
 
 # every symbol include/lso.h declares
-EXPORTS = ("lso_adam_step", "lso_validate_blocks", "lso_block_constants", "lso_tiled_state_bytes",
+EXPORTS = ("lso_adam_step", "lso_norm_workspace_bytes", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants", "lso_tiled_state_bytes",
            "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
            "lso_stream_files", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc", "lso_host_free",
            "lso_status_string", "lso_last_error")
@@ -115,6 +117,9 @@ def lib():
         L = ctypes.CDLL(path)
         vp, sz, u64, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint64, ctypes.c_int
         L.lso_adam_step.argtypes = [vp, sz, vp]
+        L.lso_norm_workspace_bytes.argtypes = [vp, sz]
+        L.lso_norm_workspace_bytes.restype = u64
+        L.lso_adam_step_norms.argtypes = [vp, sz, vp, vp, u64, vp]
         L.lso_validate_blocks.argtypes = [vp, sz]
         L.lso_block_constants.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
         L.lso_tiled_state_bytes.argtypes = [u64]
@@ -133,7 +138,7 @@ def lib():
         L.lso_status_string.restype = ctypes.c_char_p
         L.lso_last_error.argtypes = []
         L.lso_last_error.restype = ctypes.c_char_p
-        for name in ("lso_adam_step", "lso_validate_blocks", "lso_block_constants",
+        for name in ("lso_adam_step", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants",
                      "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create",
                      "lso_stream_layers", "lso_stream_files", "lso_stream_destroy", "lso_host_alloc", "lso_host_free"):
             getattr(L, name).restype = i32

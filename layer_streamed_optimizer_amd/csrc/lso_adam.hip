@@ -6,7 +6,11 @@
 // outside the root; add it to the master (the additive write-back); store
 // master, m, v and the BF16 round-to-nearest-even re-cast of the new master.
 // 14 bytes read + 14 bytes written per parameter (16 + 14 with FP32
-// gradients) and nothing else: no scratch, no second pass.
+// gradients) and nothing else: no scratch, no second pass.  The norm
+// variant also sums g^2 over each chunk while the gradient is in registers
+// (one FP64 per chunk, 1/1000 of the traffic) for progressive layer
+// locking; a small second kernel adds each block's chunk sums in a fixed
+// order.
 //
 // Memory access: a lane owns groups of four consecutive elements, so every
 // FP32 access is one 128-bit load or store and every BF16 access one 64-bit
@@ -122,14 +126,18 @@ __device__ __forceinline__ void load_quad(const Chunk& ch, uint32_t e, Quad& x)
     }
 }
 
-template <bool kSgd, bool kG32>
-__device__ __forceinline__ u32x2 compute_quad(const Coef& c, Quad& x)
+template <bool kSgd, bool kG32, bool kNorm>
+__device__ __forceinline__ u32x2 compute_quad(const Coef& c, Quad& x, float& sq)
 {
     u32x2 w;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const float g0 = kG32 ? x.gf[2 * k] : bf16_widen(x.g[k] & 0xFFFFu);
         const float g1 = kG32 ? x.gf[2 * k + 1] : bf16_widen(x.g[k] >> 16);
+        if (kNorm) {
+            sq = fmaf(g0, g0, sq);
+            sq = fmaf(g1, g1, sq);
+        }
         float p0 = x.p[2 * k], p1 = x.p[2 * k + 1];
         if (kSgd) {
             sgd_elem(c, g0, p0);
@@ -163,11 +171,12 @@ __device__ __forceinline__ void store_quad(const Chunk& ch, uint32_t e, const Qu
 }
 
 // Elements [e, n) of a chunk, fewer than four: scalar accesses.
-template <bool kSgd, bool kG32>
-__device__ void tail_elems(const Chunk& ch, const Coef& c, uint32_t e, uint32_t n, bool has_w)
+template <bool kSgd, bool kG32, bool kNorm>
+__device__ void tail_elems(const Chunk& ch, const Coef& c, uint32_t e, uint32_t n, bool has_w, float& sq)
 {
     for (uint32_t i = e; i < n; ++i) {
         const float g = kG32 ? ld<float>(ch.gf + i) : bf16_widen(ld<uint16_t>(ch.g + i));
+        if (kNorm) sq = fmaf(g, g, sq);
         float p = ld<float>(ch.p + i);
         if (kSgd) {
             sgd_elem(c, g, p);
@@ -182,11 +191,13 @@ __device__ void tail_elems(const Chunk& ch, const Coef& c, uint32_t e, uint32_t 
     }
 }
 
-// One chunk of kThreads * kQuad * U elements.
-template <int U, bool kSgd, bool kG32>
-__device__ __forceinline__ void run_chunk(const Chunk& ch, const Coef& c, bool has_w)
+// One chunk of kThreads * kQuad * U elements.  Returns this lane's sum of
+// g^2 (norm variant; 0 otherwise).
+template <int U, bool kSgd, bool kG32, bool kNorm>
+__device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool has_w)
 {
     constexpr uint32_t kChunkU = static_cast<uint32_t>(kThreads) * kQuad * U;
+    float sq = 0.0f;
     if (ch.n == kChunkU) {
         // full chunk: every load of the lane first, then arithmetic and stores
         Quad x[U];
@@ -194,10 +205,10 @@ __device__ __forceinline__ void run_chunk(const Chunk& ch, const Coef& c, bool h
         for (int u = 0; u < U; ++u) load_quad<kSgd, kG32>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const u32x2 w = compute_quad<kSgd, kG32>(c, x[u]);
+            const u32x2 w = compute_quad<kSgd, kG32, kNorm>(c, x[u], sq);
             store_quad<kSgd>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u], w, has_w);
         }
-        return;
+        return sq;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -205,12 +216,32 @@ __device__ __forceinline__ void run_chunk(const Chunk& ch, const Coef& c, bool h
         if (e + kQuad <= ch.n) {
             Quad x;
             load_quad<kSgd, kG32>(ch, e, x);
-            const u32x2 w = compute_quad<kSgd, kG32>(c, x);
+            const u32x2 w = compute_quad<kSgd, kG32, kNorm>(c, x, sq);
             store_quad<kSgd>(ch, e, x, w, has_w);
         } else if (e < ch.n) {
-            tail_elems<kSgd, kG32>(ch, c, e, ch.n, has_w);
+            tail_elems<kSgd, kG32, kNorm>(ch, c, e, ch.n, has_w, sq);
         }
     }
+    return sq;
+}
+
+// Sum of v over the workgroup in a fixed order (lanes by xor butterfly,
+// then the waves in order); the result is valid in thread 0.  Every thread
+// of the workgroup must call it.
+__device__ __forceinline__ double workgroup_sum(double v)
+{
+    __shared__ double wave_sum[kThreads / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((threadIdx.x & 63) == 0) wave_sum[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < kThreads / 64; ++k) s += wave_sum[k];
+    }
+    __syncthreads();   // wave_sum may be rewritten by the next call
+    return s;
 }
 
 __device__ __forceinline__ DevBlock load_block(const LSO_CONST DevBlock* p)
@@ -251,7 +282,7 @@ __device__ __forceinline__ DevBlock find_inline(const KernelArgs& a, uint64_t ch
     return b;
 }
 
-template <int U, bool kTiled, bool kG32>
+template <int U, bool kTiled, bool kG32, bool kNorm>
 __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const DevBlock& b, uint64_t chunk)
 {
     constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
@@ -275,11 +306,15 @@ __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const De
         ch.v = b.v ? b.v + e0 : nullptr;
     }
     const bool has_w = (b.flags & kFlagWeight) != 0;
-    if (!kTiled && (b.flags & kFlagSgd)) run_chunk<U, true, kG32>(ch, c, has_w);
-    else run_chunk<U, false, kG32>(ch, c, has_w);
+    const float sq = (!kTiled && (b.flags & kFlagSgd)) ? run_chunk<U, true, kG32, kNorm>(ch, c, has_w)
+                                                       : run_chunk<U, false, kG32, kNorm>(ch, c, has_w);
+    if (kNorm) {
+        const double s = workgroup_sum(static_cast<double>(sq));
+        if (threadIdx.x == 0) st<double>(args.partials + chunk, s);
+    }
 }
 
-template <int U, bool kTiled, bool kG32>
+template <int U, bool kTiled, bool kG32, bool kNorm>
 __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs args)
 {
     if (args.blocks) {
@@ -289,12 +324,44 @@ __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs a
             reinterpret_cast<const LSO_CONST uint32_t*>(reinterpret_cast<uintptr_t>(args.chunk_block));
         for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x) {
             const uint32_t bi = index ? index[chunk] : search_block(table, args.nblocks, chunk);
-            run_block_chunk<U, kTiled, kG32>(args, load_block(table + bi), chunk);
+            run_block_chunk<U, kTiled, kG32, kNorm>(args, load_block(table + bi), chunk);
         }
     } else {
         for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x)
-            run_block_chunk<U, kTiled, kG32>(args, find_inline(args, chunk), chunk);
+            run_block_chunk<U, kTiled, kG32, kNorm>(args, find_inline(args, chunk), chunk);
     }
+}
+
+// One workgroup per block of the launch: the block's chunk partials summed
+// in a fixed order, written to sq_norms[the block's position in the call].
+template <int U>
+__global__ void __launch_bounds__(kThreads) norm_reduce_kernel(const KernelArgs args, double* sq_norms)
+{
+    constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
+    DevBlock b;
+    if (args.blocks) {
+        const LSO_CONST DevBlock* table =
+            reinterpret_cast<const LSO_CONST DevBlock*>(reinterpret_cast<uintptr_t>(args.blocks));
+        b = load_block(table + blockIdx.x);
+    } else {
+        b = args.inl[0];
+#pragma unroll
+        for (int k = 1; k < kInline; ++k)
+            if (static_cast<uint32_t>(k) == blockIdx.x) b = args.inl[k];
+    }
+    const uint64_t nch = (b.n + kChunkU - 1) / kChunkU;
+    double s = 0.0;
+    for (uint64_t k = threadIdx.x; k < nch; k += kThreads) s += ld<double>(args.partials + b.chunk0 + k);
+    s = workgroup_sum(s);
+    if (threadIdx.x == 0) st<double>(sq_norms + (b.flags >> kIndexShift), s);
+}
+
+template <int U, bool kTiled, bool kG32>
+void launch_variant(const KernelArgs& args, dim3 g, hipStream_t s)
+{
+    const dim3 t(kThreads);
+    if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true>), g, t, 0, s, args);
+    else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false>), g, t, 0, s, args);
 }
 
 }  // namespace
@@ -305,22 +372,27 @@ int launch_fused_adam(const KernelArgs& args, int unroll, bool grad_f32, void* s
     // one chunk per workgroup; a call too large for one grid loops
     const uint64_t grid = args.total_chunks < kMaxGrid ? args.total_chunks : kMaxGrid;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 g(static_cast<unsigned>(grid)), t(kThreads);
+    const dim3 g(static_cast<unsigned>(grid));
     if (grad_f32) {
-        if (unroll == kUnrollTiled)
-            hipLaunchKernelGGL((fused_adam_kernel<kUnrollTiled, true, true>), g, t, 0, s, args);
-        else if (unroll == kUnrollLarge)
-            hipLaunchKernelGGL((fused_adam_kernel<kUnrollLarge, false, true>), g, t, 0, s, args);
-        else
-            hipLaunchKernelGGL((fused_adam_kernel<kUnrollSmall, false, true>), g, t, 0, s, args);
+        if (unroll == kUnrollTiled) launch_variant<kUnrollTiled, true, true>(args, g, s);
+        else if (unroll == kUnrollLarge) launch_variant<kUnrollLarge, false, true>(args, g, s);
+        else launch_variant<kUnrollSmall, false, true>(args, g, s);
     } else {
-        if (unroll == kUnrollTiled)
-            hipLaunchKernelGGL((fused_adam_kernel<kUnrollTiled, true, false>), g, t, 0, s, args);
-        else if (unroll == kUnrollLarge)
-            hipLaunchKernelGGL((fused_adam_kernel<kUnrollLarge, false, false>), g, t, 0, s, args);
-        else
-            hipLaunchKernelGGL((fused_adam_kernel<kUnrollSmall, false, false>), g, t, 0, s, args);
+        if (unroll == kUnrollTiled) launch_variant<kUnrollTiled, true, false>(args, g, s);
+        else if (unroll == kUnrollLarge) launch_variant<kUnrollLarge, false, false>(args, g, s);
+        else launch_variant<kUnrollSmall, false, false>(args, g, s);
     }
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_norm_reduce(const KernelArgs& args, int unroll, double* sq_norms, void* stream)
+{
+    if (args.nblocks == 0 || !args.partials) return 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 g(args.nblocks), t(kThreads);
+    if (unroll == kUnrollTiled) hipLaunchKernelGGL((norm_reduce_kernel<kUnrollTiled>), g, t, 0, s, args, sq_norms);
+    else if (unroll == kUnrollLarge) hipLaunchKernelGGL((norm_reduce_kernel<kUnrollLarge>), g, t, 0, s, args, sq_norms);
+    else hipLaunchKernelGGL((norm_reduce_kernel<kUnrollSmall>), g, t, 0, s, args, sq_norms);
     return static_cast<int>(hipGetLastError());
 }
 

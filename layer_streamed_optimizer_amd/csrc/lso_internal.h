@@ -40,8 +40,11 @@ struct DevBlock {
     uint64_t n;
     uint64_t chunk0;     // first global chunk index of this block
     uint32_t group;      // index into KernelArgs::coef
-    uint32_t flags;      // kFlagSgd | kFlagWeight
+    uint32_t flags;      // kFlag* in bits 0-7; the block's position in the
+                         // caller's array in bits 8-31
 };
+constexpr int kIndexShift = 8;
+constexpr uint64_t kMaxBlocksPerCall = 1ull << 24;
 static_assert(sizeof(DevBlock) == 64, "DevBlock layout");
 
 // FP32 constants of one (opt, t, lr, beta1, beta2, eps) set.
@@ -61,6 +64,7 @@ constexpr int kInline = 4;
 struct KernelArgs {
     const DevBlock* blocks;        // device table, or nullptr: use inl[]
     const uint32_t* chunk_block;   // block index per chunk, or nullptr: search
+    double* partials;              // norm variant: sum of g^2 per chunk of this launch
     uint64_t total_chunks;
     uint32_t nblocks;
     uint32_t pad;
@@ -71,7 +75,14 @@ struct KernelArgs {
 // Enqueue the fused kernel (defined in lso_adam.hip) with chunks of
 // chunk_elems(unroll) elements; unroll == kUnrollTiled launches the tiled
 // variant (every block of the launch tiled); grad_f32 the FP32-gradient
-// variant (every block of the launch).  Returns the hipError_t.
+// variant (every block of the launch).  With args.partials set, the norm
+// variant also writes each chunk's sum of g^2 to args.partials[chunk].
+// Returns the hipError_t.
 int launch_fused_adam(const KernelArgs& args, int unroll, bool grad_f32, void* stream);
+
+// Sum the chunk partials of each block of the launch (one workgroup per
+// block, fixed order) into sq_norms[the block's position in the call].
+// Returns the hipError_t.
+int launch_norm_reduce(const KernelArgs& args, int unroll, double* sq_norms, void* stream);
 
 }  // namespace lso

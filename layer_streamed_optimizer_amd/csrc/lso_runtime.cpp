@@ -98,10 +98,13 @@ bool add_array(std::vector<Interval>& iv, uintptr_t addr, uint64_t bytes, bool w
 
 }  // namespace
 
-lso_status validate_geometry(const lso_block* blocks, size_t n)
+namespace {
+
+// Every used array of the call as an interval (NULL, alignment and wrap
+// checks on the way).
+lso_status collect_geometry(const lso_block* blocks, size_t n, std::vector<Interval>& iv)
 {
-    std::vector<Interval> iv;
-    iv.reserve(n * 5);
+    iv.reserve(iv.size() + n * 5);
     for (size_t i = 0; i < n; ++i) {
         const lso_block& b = blocks[i];
         if (b.n == 0) continue;
@@ -127,7 +130,40 @@ lso_status validate_geometry(const lso_block* blocks, size_t n)
                 return fail(LSO_E_INVALID, "block %zu: %s range wraps the address space", i, a.name);
         }
     }
+    return LSO_OK;
+}
+
+}  // namespace
+
+lso_status validate_geometry(const lso_block* blocks, size_t n)
+{
+    std::vector<Interval> iv;
+    lso_status s = collect_geometry(blocks, n, iv);
+    if (s != LSO_OK) return s;
     return check_overlap(iv);
+}
+
+lso_status validate_norm_buffers(const lso_block* blocks, size_t n, const NormOut& o)
+{
+    if (!o.sq_norms || !o.workspace) return fail(LSO_E_INVALID, "sq_norms and workspace must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(o.sq_norms) % 8 != 0 || reinterpret_cast<uintptr_t>(o.workspace) % 8 != 0)
+        return fail(LSO_E_ALIGN, "sq_norms and workspace must be 8-byte aligned");
+    const uint64_t need = norm_workspace_bytes(blocks, n);
+    if (o.workspace_bytes < need)
+        return fail(LSO_E_INVALID, "workspace of %llu bytes is smaller than the %llu this call needs",
+                    static_cast<unsigned long long>(o.workspace_bytes), static_cast<unsigned long long>(need));
+    lso_status s = validate_geometry(blocks, n);
+    if (s != LSO_OK) return s;
+    std::vector<Interval> iv;
+    s = collect_geometry(blocks, n, iv);
+    if (s != LSO_OK) return s;
+    // both are written
+    if (!add_array(iv, reinterpret_cast<uintptr_t>(o.sq_norms), 8ull * n, true, n) ||
+        (need > 0 && !add_array(iv, reinterpret_cast<uintptr_t>(o.workspace), need, true, n)))
+        return fail(LSO_E_INVALID, "sq_norms or workspace range wraps the address space");
+    s = check_overlap(iv);
+    if (s != LSO_OK) fail(s, "sq_norms or workspace overlaps an array of the call, or each other");
+    return s;
 }
 
 lso_status check_fields(const lso_block& b, size_t i)
@@ -320,10 +356,44 @@ lso_status device_table(const lso_block* blocks, size_t n, bool geometry_checked
 
 }  // namespace
 
-lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked)
+namespace {
+
+int kind_of(const lso_block& b)
+{
+    return (b.layout == LSO_LAYOUT_TILED ? 1 : 0) + (b.grad_dtype == LSO_DT_F32 ? 2 : 0);
+}
+
+// Chunk size of each launch kind of a call: planar chunks by the planar
+// work of the call (small calls take small chunks to fill the chip), tiled
+// chunks are one state tile.
+int planar_unroll_of(const lso_block* blocks, size_t n)
+{
+    uint64_t planar_elems = 0;
+    for (size_t i = 0; i < n; ++i)
+        if (blocks[i].layout != LSO_LAYOUT_TILED) planar_elems += blocks[i].n;
+    return planar_elems < kSmallCallElems ? kUnrollSmall : kUnrollLarge;
+}
+
+}  // namespace
+
+uint64_t norm_workspace_bytes(const lso_block* blocks, size_t n)
+{
+    if (!blocks) return 0;
+    const uint64_t planar_chunk = chunk_elems(planar_unroll_of(blocks, n));
+    uint64_t chunks = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const uint64_t c = blocks[i].layout == LSO_LAYOUT_TILED ? chunk_elems(kUnrollTiled) : planar_chunk;
+        chunks += (blocks[i].n + c - 1) / c;
+    }
+    return chunks * sizeof(double);
+}
+
+lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked,
+                          const NormOut* norms)
 {
     if (n == 0) return LSO_OK;
     if (!blocks) return fail(LSO_E_INVALID, "blocks is NULL");
+    if (n > kMaxBlocksPerCall) return fail(LSO_E_INVALID, "more than 2^24 blocks in one call");
     // per-thread scratch, reused across calls (no allocation in steady state)
     thread_local std::vector<HyperKey> sets;
     thread_local std::vector<uint32_t> set_of;
@@ -339,20 +409,13 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
         if (j == sets.size()) sets.push_back(k);
         set_of[i] = static_cast<uint32_t>(j);
     }
-    // launches: one per (layout, 16 constant sets); planar chunk size by
-    // the planar work of the call, tiled chunks are one state tile
-    // launch kinds: (tiled or planar) x (BF16 or FP32 gradients)
-    uint64_t planar_elems = 0;
+    // launches: one per launch kind ((tiled or planar) x (BF16 or FP32
+    // gradients)) and per 16 constant sets
     bool present[4] = {false, false, false, false};
-    auto kind_of = [](const lso_block& b) {
-        return (b.layout == LSO_LAYOUT_TILED ? 1 : 0) + (b.grad_dtype == LSO_DT_F32 ? 2 : 0);
-    };
-    for (size_t i = 0; i < n; ++i) {
-        present[kind_of(blocks[i])] = true;
-        if (blocks[i].layout != LSO_LAYOUT_TILED) planar_elems += blocks[i].n;
-    }
+    for (size_t i = 0; i < n; ++i) present[kind_of(blocks[i])] = true;
     const int kinds = present[0] + present[1] + present[2] + present[3];
-    const int planar_unroll = planar_elems < kSmallCallElems ? kUnrollSmall : kUnrollLarge;
+    const int planar_unroll = planar_unroll_of(blocks, n);
+    uint64_t part_offset = 0;   // norm variant: this launch's first partial
     const size_t set_groups = (sets.size() + kMaxGroups - 1) / kMaxGroups;
     const size_t launches = set_groups * static_cast<size_t>(kinds);
     bool checked = geometry_checked;
@@ -391,7 +454,8 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
                 d.chunk0 = chunks;
                 d.group = set_of[i] % kMaxGroups;
                 d.flags = (b.opt == LSO_OPT_SGD ? kFlagSgd : 0u) | (d.w ? kFlagWeight : 0u) |
-                          (tiled_pass ? kFlagTiled : 0u) | (g32_pass ? kFlagGradF32 : 0u);
+                          (tiled_pass ? kFlagTiled : 0u) | (g32_pass ? kFlagGradF32 : 0u) |
+                          (static_cast<uint32_t>(i) << kIndexShift);
                 chunks += (b.n + chunk - 1) / chunk;
                 tab.push_back(d);
             }
@@ -424,8 +488,14 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
                 lso_status s = device_table(blocks, n, checked, tab, chunks, unroll, stream, args);
                 if (s != LSO_OK) return s;
             }
+            if (norms) args.partials = norms->workspace + part_offset;
             int err = launch_fused_adam(args, unroll, g32_pass, stream);
             if (err != 0) return hip_fail(err, "fused Adam launch");
+            if (norms) {
+                err = launch_norm_reduce(args, unroll, norms->sq_norms, stream);
+                if (err != 0) return hip_fail(err, "norm reduction launch");
+                part_offset += chunks;
+            }
         }
     }
     return LSO_OK;
@@ -441,6 +511,30 @@ lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream)
 {
     lso::clear_error();
     return lso::enqueue_update(blocks, n, stream, false);
+}
+
+uint64_t lso_norm_workspace_bytes(const lso_block* blocks, size_t n)
+{
+    return lso::norm_workspace_bytes(blocks, n);
+}
+
+lso_status lso_adam_step_norms(const lso_block* blocks, size_t n, double* sq_norms, void* workspace,
+                               uint64_t workspace_bytes, void* stream)
+{
+    lso::clear_error();
+    if (n == 0) return LSO_OK;
+    if (!blocks) return lso::fail(LSO_E_INVALID, "blocks is NULL");
+    lso::NormOut o;
+    o.sq_norms = sq_norms;
+    o.workspace = static_cast<double*>(workspace);
+    o.workspace_bytes = workspace_bytes;
+    for (size_t i = 0; i < n; ++i) {
+        lso_status s = lso::check_fields(blocks[i], i);
+        if (s != LSO_OK) return s;
+    }
+    lso_status s = lso::validate_norm_buffers(blocks, n, o);   // covers the blocks' geometry
+    if (s != LSO_OK) return s;
+    return lso::enqueue_update(blocks, n, stream, true, &o);
 }
 
 uint64_t lso_tiled_state_bytes(uint64_t n) { return lso::tiled_bytes(n); }

@@ -19,8 +19,25 @@ uint64_t tiled_bytes(uint64_t n);
 lso_status check_hyper(uint32_t opt, uint64_t t, double lr, double beta1, double beta2, double eps,
                        size_t index);
 
+// Where the norm variant puts its results: sq_norms[i] = sum of g^2 of
+// block i (device, n doubles); workspace: device, norm_workspace_bytes().
+struct NormOut {
+    double* sq_norms = nullptr;
+    double* workspace = nullptr;
+    uint64_t workspace_bytes = 0;
+};
+
+// Device workspace the norm variant needs for these blocks: one double per
+// chunk of every launch of the call.
+uint64_t norm_workspace_bytes(const lso_block* blocks, size_t n);
+
+// Checks of the norm variant's outputs: non-NULL, aligned, workspace
+// large enough, and neither overlapping the other or any array of the call.
+lso_status validate_norm_buffers(const lso_block* blocks, size_t n, const NormOut& o);
+
 // Validate (unless geometry_checked) and enqueue one update of the blocks
-// on stream.
-lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked);
+// on stream; with norms, also each block's sum of g^2.
+lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked,
+                          const NormOut* norms = nullptr);
 
 }  // namespace lso

@@ -70,6 +70,7 @@
 #include <vector>
 
 #include "lso_copy.h"
+#include "lso_internal.h"
 #include "lso_runtime.h"
 
 namespace {
@@ -277,6 +278,10 @@ struct lso_stream_ctx {
     hipEvent_t d2h_done[kMaxStaging] = {};   // per staging buffer: its layer's D2H ended
     IoPool* reader = nullptr;   // stage-ins
     IoPool* writer = nullptr;   // write-outs
+    double* dev_norms = nullptr;   // per layer of a call: sum of g^2
+    size_t norm_cap = 0;
+    double* norm_ws = nullptr;     // chunk sums of the layer being updated
+    uint64_t norm_ws_bytes = 0;
     std::mutex note_mu;          // signalled when a request completes
     std::condition_variable note_cv;
     int copy_mode = kCopyKernels;
@@ -297,6 +302,8 @@ void release(lso_stream_ctx* c)
         if (s) (void)hipStreamSynchronize(s);
     delete c->reader;   // joins its threads; no request is in flight between calls
     delete c->writer;
+    if (c->dev_norms) (void)hipFree(c->dev_norms);
+    if (c->norm_ws) (void)hipFree(c->norm_ws);
     for (int s = 0; s < kMaxStaging; ++s) {
         if (c->staging[s]) (void)hipHostFree(c->staging[s]);
         if (c->d2h_done[s]) (void)hipEventDestroy(c->d2h_done[s]);
@@ -353,6 +360,8 @@ bool is_pinned(const void* p, uint64_t bytes)
 enum Kind { kPinned = 0, kPageable = 1, kFile = 2 };
 
 struct Job {
+    size_t index = 0;         // position in the caller's array
+    double* sq_norm = nullptr;
     int kind = kPinned;
     char* host = nullptr;     // pinned or pageable block
     int fd = -1;              // file block
@@ -476,10 +485,10 @@ hipError_t copy_block(const lso_stream_ctx* c, void* dst, const void* src, uint6
     return static_cast<hipError_t>(lso::launch_block_copy(dst, src, bytes, c->copy_grid, st));
 }
 
-// Enqueue H2D, gradient producer, update and D2H of layer i (slot i % nslots),
-// and record d2h_done[i % nstaging] after its D2H.  buf: where the H2D
-// reads and the D2H writes (the block itself when pinned, a staging buffer
-// otherwise).
+// Enqueue H2D, gradient producer, update and D2H of the layer at position
+// i of the pipeline (slot i % nslots), and record d2h_done[i % nstaging]
+// after its D2H.  buf: where the H2D reads and the D2H writes (the block
+// itself when pinned, a staging buffer otherwise).
 lso_status issue_layer(lso_stream_ctx* c, const Job& h, size_t i, void* buf)
 {
     const int s = static_cast<int>(i % c->nslots);
@@ -493,8 +502,8 @@ lso_status issue_layer(lso_stream_ctx* c, const Job& h, size_t i, void* buf)
     // Compute: gradients of this layer, then the fused update on the slot.
     if ((err = hipStreamWaitEvent(c->compute, c->weights_ready[s], 0)) != hipSuccess)
         return lso::hip_fail(err, "hipStreamWaitEvent(weights-ready)");
-    const int rc = c->fn(c->user, i, c->slot_grad[s], h.n, c->compute);
-    if (rc != 0) return lso::fail(LSO_E_CALLBACK, "gradient producer returned %d at layer %zu", rc, i);
+    const int rc = c->fn(c->user, h.index, c->slot_grad[s], h.n, c->compute);
+    if (rc != 0) return lso::fail(LSO_E_CALLBACK, "gradient producer returned %d at layer %zu", rc, h.index);
     lso_block b{};
     const uintptr_t base = reinterpret_cast<uintptr_t>(c->slot_state[s]);
     b.base = nullptr;   // absolute addresses below
@@ -513,7 +522,13 @@ lso_status issue_layer(lso_stream_ctx* c, const Job& h, size_t i, void* buf)
     b.beta1 = h.beta1;
     b.beta2 = h.beta2;
     b.eps = h.eps;
-    lso_status st = lso::enqueue_update(&b, 1, c->compute, false);
+    lso::NormOut o;
+    o.sq_norms = c->dev_norms + i;
+    o.workspace = c->norm_ws;
+    o.workspace_bytes = c->norm_ws_bytes;
+    if (h.sq_norm && lso::norm_workspace_bytes(&b, 1) > o.workspace_bytes)
+        return lso::fail(LSO_E_INVALID, "layer %zu: norm workspace too small", h.index);
+    lso_status st = lso::enqueue_update(&b, 1, c->compute, false, h.sq_norm ? &o : nullptr);
     if (st != LSO_OK) return st;
     if ((err = hipEventRecord(c->step_done[s], c->compute)) != hipSuccess)
         return lso::hip_fail(err, "hipEventRecord(step-done)");
@@ -567,11 +582,22 @@ struct Trace {
 // stage-in until its write-out is complete.
 lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
 {
-    bool any_staged = false;
-    for (size_t i = 0; i < n; ++i) any_staged |= J[i].kind != kPinned;
+    bool any_staged = false, any_norm = false;
+    for (size_t i = 0; i < n; ++i) {
+        any_staged |= J[i].kind != kPinned;
+        any_norm |= J[i].sq_norm != nullptr;
+    }
     if (any_staged) {
         lso_status s = ensure_staging(c);
         if (s != LSO_OK) return s;
+    }
+    if (any_norm && c->norm_cap < n) {
+        if (c->dev_norms) (void)hipFree(c->dev_norms);
+        c->dev_norms = nullptr;
+        c->norm_cap = 0;
+        if (hipMalloc(&c->dev_norms, n * sizeof(double)) != hipSuccess)
+            return lso::fail(LSO_E_NOMEM, "device array of %zu layer norms", n);
+        c->norm_cap = n;
     }
     const size_t K = staging_count(c);
     std::unique_ptr<IoRequest[]> rd(new IoRequest[K]), wr(new IoRequest[K]);
@@ -627,7 +653,7 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
             const Job& j = J[next_issue];
             if (j.kind != kPinned) {
                 if (const int e = rd[next_issue % K].err.load()) {
-                    record(lso::fail(LSO_E_IO, "layer %zu: reading its %s failed: %s", next_issue,
+                    record(lso::fail(LSO_E_IO, "layer %zu: reading its %s failed: %s", j.index,
                                      io_what(j), std::strerror(e)));
                     stop_at = next_issue;
                     break;
@@ -689,8 +715,8 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
                 if (const int e = wr[b].err.load()) {
                     // this region may be partly written; no later layer is
                     // written back
-                    record(lso::fail(LSO_E_IO, "layer %zu: writing its %s back failed: %s", next_done,
-                                     io_what(J[next_done]), std::strerror(e)));
+                    record(lso::fail(LSO_E_IO, "layer %zu: writing its %s back failed: %s",
+                                     J[next_done].index, io_what(J[next_done]), std::strerror(e)));
                     stop_at = std::min(stop_at, next_done + 1);
                 }
             }
@@ -712,6 +738,13 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
         if (err != hipSuccess) record(lso::hip_fail(err, "hipStreamSynchronize"));
     }
     trace.print();
+    if (result == LSO_OK && any_norm) {
+        std::vector<double> sq(n);
+        const hipError_t err = hipMemcpy(sq.data(), c->dev_norms, n * sizeof(double), hipMemcpyDeviceToHost);
+        if (err != hipSuccess) return lso::hip_fail(err, "hipMemcpy (layer norms)");
+        for (size_t i = 0; i < n; ++i)
+            if (J[i].sq_norm) *J[i].sq_norm = sq[i];
+    }
     return result;
 }
 
@@ -732,6 +765,7 @@ void copy_state_fields(Job& j, const T& L)
     j.beta1 = L.beta1;
     j.beta2 = L.beta2;
     j.eps = L.eps;
+    j.sq_norm = L.sq_norm;
 }
 
 }  // namespace
@@ -800,6 +834,14 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
         err = hipEventCreateWithFlags(&c->d2h_done[s], hipEventDisableTiming);
         if (err != hipSuccess) { release(c); return lso::hip_fail(err, "hipEventCreateWithFlags"); }
     }
+    // chunk sums of one layer at the smallest chunk size (any layout)
+    const uint64_t min_chunk = lso::chunk_elems(lso::kUnrollSmall);
+    const uint64_t max_chunks = ((max_layer_params ? max_layer_params : 1) + min_chunk - 1) / min_chunk;
+    c->norm_ws_bytes = sizeof(double) * max_chunks;
+    if (hipMalloc(&c->norm_ws, c->norm_ws_bytes) != hipSuccess) {
+        release(c);
+        return lso::fail(LSO_E_NOMEM, "norm workspace of %llu bytes", static_cast<unsigned long long>(c->norm_ws_bytes));
+    }
     *out = c;
     return LSO_OK;
 }
@@ -810,11 +852,15 @@ lso_status lso_stream_layers(lso_stream_ctx* c, const lso_host_layer* L, size_t 
     if (!c) return lso::fail(LSO_E_INVALID, "ctx is NULL");
     if (n_layers == 0) return LSO_OK;
     if (!L) return lso::fail(LSO_E_INVALID, "host_blocks is NULL");
-    std::vector<Job> jobs(n_layers);
+    std::vector<Job> jobs;
+    jobs.reserve(n_layers);
     std::vector<Extent> ex;
     ex.reserve(n_layers);
     for (size_t i = 0; i < n_layers; ++i) {
-        Job& j = jobs[i];
+        if (L[i].n == 0) continue;   // skipped (a locked layer)
+        jobs.emplace_back();
+        Job& j = jobs.back();
+        j.index = i;
         copy_state_fields(j, L[i]);
         j.host = static_cast<char*>(L[i].host_base);
         if (!j.host) return lso::fail(LSO_E_INVALID, "layer %zu: host_base is NULL", i);
@@ -829,7 +875,7 @@ lso_status lso_stream_layers(lso_stream_ctx* c, const lso_host_layer* L, size_t 
     if (s != LSO_OK) return s;
     DeviceGuard guard(c->device);
     for (Job& j : jobs) j.kind = is_pinned(j.host, j.bytes) ? kPinned : kPageable;
-    return run_pipeline(c, jobs.data(), n_layers);
+    return run_pipeline(c, jobs.data(), jobs.size());
 }
 
 lso_status lso_stream_files(lso_stream_ctx* c, const lso_file_layer* L, size_t n_layers)
@@ -838,11 +884,15 @@ lso_status lso_stream_files(lso_stream_ctx* c, const lso_file_layer* L, size_t n
     if (!c) return lso::fail(LSO_E_INVALID, "ctx is NULL");
     if (n_layers == 0) return LSO_OK;
     if (!L) return lso::fail(LSO_E_INVALID, "layers is NULL");
-    std::vector<Job> jobs(n_layers);
+    std::vector<Job> jobs;
+    jobs.reserve(n_layers);
     std::vector<Extent> ex;
     ex.reserve(n_layers);
     for (size_t i = 0; i < n_layers; ++i) {
-        Job& j = jobs[i];
+        if (L[i].n == 0) continue;   // skipped (a locked layer)
+        jobs.emplace_back();
+        Job& j = jobs.back();
+        j.index = i;
         copy_state_fields(j, L[i]);
         j.kind = kFile;
         j.fd = L[i].fd;
@@ -869,7 +919,7 @@ lso_status lso_stream_files(lso_stream_ctx* c, const lso_file_layer* L, size_t n
     lso_status s = check_disjoint(ex);
     if (s != LSO_OK) return s;
     DeviceGuard guard(c->device);
-    return run_pipeline(c, jobs.data(), n_layers);
+    return run_pipeline(c, jobs.data(), jobs.size());
 }
 
 void* lso_stream_slot_weight(lso_stream_ctx* c, int slot)

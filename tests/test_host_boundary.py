@@ -56,13 +56,13 @@ int main(void) {
   F(lso_host_layer, off_master) F(lso_host_layer, off_m) F(lso_host_layer, off_v)
   F(lso_host_layer, dev_weight) F(lso_host_layer, opt) F(lso_host_layer, layout)
   F(lso_host_layer, t) F(lso_host_layer, lr) F(lso_host_layer, beta1) F(lso_host_layer, beta2)
-  F(lso_host_layer, eps)
+  F(lso_host_layer, eps) F(lso_host_layer, sq_norm)
   printf("lso_file_layer.size %zu\n", sizeof(lso_file_layer));
   F(lso_file_layer, fd) F(lso_file_layer, flags) F(lso_file_layer, file_offset)
   F(lso_file_layer, bytes) F(lso_file_layer, n) F(lso_file_layer, off_master)
   F(lso_file_layer, off_m) F(lso_file_layer, off_v) F(lso_file_layer, dev_weight)
   F(lso_file_layer, opt) F(lso_file_layer, layout) F(lso_file_layer, t) F(lso_file_layer, lr)
-  F(lso_file_layer, beta1) F(lso_file_layer, beta2) F(lso_file_layer, eps)
+  F(lso_file_layer, beta1) F(lso_file_layer, beta2) F(lso_file_layer, eps) F(lso_file_layer, sq_norm)
   return 0;
 }
 """
@@ -294,3 +294,36 @@ def test_resident_layout_tiled():
     assert lay.off_master[1] - lay.off_master[0] == configs.align(configs.tiled_state_bytes(100))
     assert lay.state_bytes == sum(configs.align(configs.tiled_state_bytes(n)) for n in lay.sizes)
     assert configs.host_layer_layout(8193, tiled=True) == (0, 0, 0, configs.align(12 * 8192 * 2))
+
+
+def test_norm_workspace_bytes_follow_the_launch_plan():
+    """One FP64 per chunk: planar chunks of 1024 elements in calls under 32M
+    planar elements, 4096 above; tiled chunks are one 8192-element tile."""
+    assert lso.norm_workspace_bytes(table([])) == 0
+    assert lso.norm_workspace_bytes(table([row(0, n=1), row(1, n=1024), row(2, n=1025)])) == 8 * (1 + 1 + 2)
+    big = row(0, n=32 << 20)
+    assert lso.norm_workspace_bytes(table([big])) == 8 * ((32 << 20) // 4096)
+    t = dict(n=8193, master=A, grad=A + (1 << 20), layout=lso.LSO_LAYOUT_TILED)
+    assert lso.norm_workspace_bytes(table([t, row(1, n=5000)])) == 8 * (2 + 5)
+
+
+def _norms_status(tab, sq, ws, ws_bytes):
+    return _native.lib().lso_adam_step_norms(tab.ptr, len(tab), sq, ws, ws_bytes, 0)
+
+
+def test_norm_call_rejects_bad_buffers_before_touching_the_device():
+    """Every case below is invalid, so nothing is enqueued (fake addresses)."""
+    tab = table([row(0), row(1)])
+    need = lso.norm_workspace_bytes(tab)
+    sq, ws = A + (200 << 20), A + (300 << 20)
+    E = _native
+    assert _norms_status(tab, 0, ws, need) == E.LSO_E_INVALID
+    assert _norms_status(tab, sq, 0, need) == E.LSO_E_INVALID
+    assert _norms_status(tab, sq, ws, need - 8) == E.LSO_E_INVALID
+    assert "workspace" in lso.last_error()
+    assert _norms_status(tab, sq + 4, ws, need) == E.LSO_E_ALIGN
+    assert _norms_status(tab, row(0)["master"] + 16, ws, need) == E.LSO_E_OVERLAP
+    assert _norms_status(tab, sq, row(1)["grad"], need) == E.LSO_E_OVERLAP
+    assert _norms_status(tab, sq, sq, need) == E.LSO_E_OVERLAP
+    bad = table([row(0), row(1, beta1=1.5)])
+    assert _norms_status(bad, sq, ws, need) == E.LSO_E_INVALID
