@@ -55,10 +55,10 @@ def kernel_hash() -> str:
     return kh()
 
 
-def measured_traffic(workload: str, grad_dtype: str = "bf16"):
+def measured_traffic(workload: str, grad_dtype: str = "bf16", norms: bool = False):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
-    tag = workload if grad_dtype == "bf16" else f"{workload}_g32"
+    tag = workload + ("" if grad_dtype == "bf16" else "_g32") + ("_norms" if norms else "")
     path = os.path.join(ROOT, "profiles", f"fused_adam_{tag}_pmc.md")
     if not os.path.exists(path):
         return None
@@ -153,10 +153,19 @@ def resident(args, w):
     torch.cuda.synchronize()
     progress("inputs resident; warming up")
 
+    if args.norms:
+        # the norm variant (progressive layer locking): per-block sums of g^2
+        sq = torch.empty(len(sizes), dtype=torch.float64, device=dev)
+        ws_bytes = lso.norm_workspace_bytes(tables[0])
+        ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
+
     def step(j):          # j = 1-based global step; grads of set (j-1) % n_sets
         tab = tables[(j - 1) % n_sets]
         tab.set_step(j)
-        lso.adam_step(tab, hs)
+        if args.norms:
+            lso.adam_step_norms(tab, sq, ws, ws_bytes, hs)
+        else:
+            lso.adam_step(tab, hs)
 
     for j in range(1, args.warmup + 1):
         step(j)
@@ -177,7 +186,7 @@ def resident(args, w):
     ceiling = copy_ceiling(torch, dev)
     progress(f"steps: wall {wall * 1e3:.3f} ms for {args.steps}; kernel avg {avg_ms * 1e3:.1f} us; "
              f"{achieved:.0f} GB/s; copy ceiling {ceiling:.0f} GB/s")
-    traffic = measured_traffic(w.key, args.grad_dtype)
+    traffic = measured_traffic(w.key, args.grad_dtype, args.norms)
     result = dict(
         metric=METRIC, value=params * args.steps / wall / 1e9, unit="Gparams/s",
         ms_per_step=wall * 1e3 / args.steps,
@@ -187,6 +196,7 @@ def resident(args, w):
         hbm_copy_ceiling_GBps=ceiling,
         config=dict(workload=f"{w.key}: {w.title}", blocks=len(sizes), params=params,
                     state_layout=args.layout, grad_dtype=args.grad_dtype, bytes_per_param=bpp,
+                    gradient_norms=bool(args.norms),
                     gradient_sets=n_sets,
                     hyper=dict(lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2,
                                eps=configs.EPS)),
@@ -509,6 +519,9 @@ def main():
                          "(default $LSO_FILE_DIR or /var/tmp)")
     ap.add_argument("--layout", choices=["tiled", "planar"], default=None,
                     help="FP32 state layout (default: tiled for c1, c3, c4; planar for c0, c2)")
+    ap.add_argument("--norms", action="store_true",
+                    help="resident workloads: the update with per-block gradient norms "
+                         "(progressive layer locking)")
     ap.add_argument("--grad-dtype", choices=["bf16", "f32"], default="bf16",
                     help="gradient dtype of the resident workloads (f32: the LoRA article's FP32 "
                          "adapter gradients)")

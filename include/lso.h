@@ -155,8 +155,8 @@ lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream);
  *
  * lso_adam_step_norms: lso_adam_step plus, from the same pass over the
  * gradients, sq_norms[i] = sum over block i's elements of g^2, in FP64
- * (per chunk of the kernel a fixed-order sum; chunks added in a fixed
- * order, so results repeat bit for bit).  sq_norms: device array of n
+ * (a fixed-order sum per wave of the kernel, the waves' sums added in a
+ * fixed order, so results repeat bit for bit).  sq_norms: device array of n
  * doubles (entries of blocks with n == 0 are not written).  workspace:
  * device memory of at least lso_norm_workspace_bytes(blocks, n) bytes,
  * 8-byte aligned; it holds per-chunk sums while the call runs on stream, so

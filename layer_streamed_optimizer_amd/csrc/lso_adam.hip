@@ -7,9 +7,9 @@
 // master, m, v and the BF16 round-to-nearest-even re-cast of the new master.
 // 14 bytes read + 14 bytes written per parameter (16 + 14 with FP32
 // gradients) and nothing else: no scratch, no second pass.  The norm
-// variant also sums g^2 over each chunk while the gradient is in registers
-// (one FP64 per chunk, 1/1000 of the traffic) for progressive layer
-// locking; a small second kernel adds each block's chunk sums in a fixed
+// variant also sums g^2 while the gradient is in registers (one FP64 per
+// wave and chunk, 1/250 of the traffic or less) for progressive layer
+// locking; a small second kernel adds each block's wave sums in a fixed
 // order.
 //
 // Memory access: a lane owns groups of four consecutive elements, so every
@@ -225,6 +225,17 @@ __device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool 
     return sq;
 }
 
+constexpr int kWaves = kThreads / 64;
+
+// Sum of v over the wave by an xor butterfly (fixed order; every lane ends
+// with the same value).
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
 // Sum of v over the workgroup in a fixed order (lanes by xor butterfly,
 // then the waves in order); the result is valid in thread 0.  Every thread
 // of the workgroup must call it.
@@ -309,8 +320,10 @@ __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const De
     const float sq = (!kTiled && (b.flags & kFlagSgd)) ? run_chunk<U, true, kG32, kNorm>(ch, c, has_w)
                                                        : run_chunk<U, false, kG32, kNorm>(ch, c, has_w);
     if (kNorm) {
-        const double s = workgroup_sum(static_cast<double>(sq));
-        if (threadIdx.x == 0) st<double>(args.partials + chunk, s);
+        // one sum per wave (no barrier in the update kernel); the reduce
+        // kernel adds a block's wave sums in order
+        const double s = wave_sum(static_cast<double>(sq));
+        if ((threadIdx.x & 63) == 0) st<double>(args.partials + chunk * kWaves + (threadIdx.x >> 6), s);
     }
 }
 
@@ -349,9 +362,10 @@ __global__ void __launch_bounds__(kThreads) norm_reduce_kernel(const KernelArgs 
         for (int k = 1; k < kInline; ++k)
             if (static_cast<uint32_t>(k) == blockIdx.x) b = args.inl[k];
     }
-    const uint64_t nch = (b.n + kChunkU - 1) / kChunkU;
+    const uint64_t nparts = (b.n + kChunkU - 1) / kChunkU * kWaves;
+    const double* parts = args.partials + b.chunk0 * kWaves;
     double s = 0.0;
-    for (uint64_t k = threadIdx.x; k < nch; k += kThreads) s += ld<double>(args.partials + b.chunk0 + k);
+    for (uint64_t k = threadIdx.x; k < nparts; k += kThreads) s += ld<double>(parts + k);
     s = workgroup_sum(s);
     if (threadIdx.x == 0) st<double>(sq_norms + (b.flags >> kIndexShift), s);
 }

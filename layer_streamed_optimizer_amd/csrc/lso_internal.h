@@ -22,6 +22,7 @@ constexpr uint64_t kMaxGrid = 1ull << 24;            // workgroups per launch
 constexpr uint64_t kMaxIndexChunks = 1ull << 22;     // per-chunk block index up to this
 
 constexpr uint64_t chunk_elems(int unroll) { return static_cast<uint64_t>(kThreads) * kQuad * unroll; }
+constexpr uint64_t kNormPartsPerChunk = kThreads / 64;   // one FP64 per wave
 static_assert(chunk_elems(kUnrollTiled) == LSO_TILE_ELEMS, "a tiled chunk is one state tile");
 
 // At most this many distinct constant sets travel by value in one launch.
@@ -64,7 +65,7 @@ constexpr int kInline = 4;
 struct KernelArgs {
     const DevBlock* blocks;        // device table, or nullptr: use inl[]
     const uint32_t* chunk_block;   // block index per chunk, or nullptr: search
-    double* partials;              // norm variant: sum of g^2 per chunk of this launch
+    double* partials;              // norm variant: sum of g^2 per wave and chunk of this launch
     uint64_t total_chunks;
     uint32_t nblocks;
     uint32_t pad;
@@ -76,7 +77,8 @@ struct KernelArgs {
 // chunk_elems(unroll) elements; unroll == kUnrollTiled launches the tiled
 // variant (every block of the launch tiled); grad_f32 the FP32-gradient
 // variant (every block of the launch).  With args.partials set, the norm
-// variant also writes each chunk's sum of g^2 to args.partials[chunk].
+// variant also writes each wave's sum of g^2 to
+// args.partials[chunk * kNormPartsPerChunk + wave].
 // Returns the hipError_t.
 int launch_fused_adam(const KernelArgs& args, int unroll, bool grad_f32, void* stream);
 

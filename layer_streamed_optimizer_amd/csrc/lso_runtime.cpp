@@ -385,7 +385,7 @@ uint64_t norm_workspace_bytes(const lso_block* blocks, size_t n)
         const uint64_t c = blocks[i].layout == LSO_LAYOUT_TILED ? chunk_elems(kUnrollTiled) : planar_chunk;
         chunks += (blocks[i].n + c - 1) / c;
     }
-    return chunks * sizeof(double);
+    return chunks * kNormPartsPerChunk * sizeof(double);
 }
 
 lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked,
@@ -488,7 +488,7 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
                 lso_status s = device_table(blocks, n, checked, tab, chunks, unroll, stream, args);
                 if (s != LSO_OK) return s;
             }
-            if (norms) args.partials = norms->workspace + part_offset;
+            if (norms) args.partials = norms->workspace + part_offset * kNormPartsPerChunk;
             int err = launch_fused_adam(args, unroll, g32_pass, stream);
             if (err != 0) return hip_fail(err, "fused Adam launch");
             if (norms) {

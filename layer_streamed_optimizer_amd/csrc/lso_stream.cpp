@@ -837,7 +837,7 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     // chunk sums of one layer at the smallest chunk size (any layout)
     const uint64_t min_chunk = lso::chunk_elems(lso::kUnrollSmall);
     const uint64_t max_chunks = ((max_layer_params ? max_layer_params : 1) + min_chunk - 1) / min_chunk;
-    c->norm_ws_bytes = sizeof(double) * max_chunks;
+    c->norm_ws_bytes = sizeof(double) * lso::kNormPartsPerChunk * max_chunks;
     if (hipMalloc(&c->norm_ws, c->norm_ws_bytes) != hipSuccess) {
         release(c);
         return lso::fail(LSO_E_NOMEM, "norm workspace of %llu bytes", static_cast<unsigned long long>(c->norm_ws_bytes));
