@@ -279,7 +279,8 @@ lso_status lso_stream_layers(lso_stream_ctx* ctx, const lso_host_layer* host_blo
  * block) is a region of a file: read with pread into a pinned staging
  * buffer, streamed through the device like a pageable host block, and
  * written back over the same region with pwrite. */
-#define LSO_FILE_SYNC 1u   /* fdatasync the file after the layer's write-back */
+#define LSO_FILE_SYNC 1u     /* fdatasync the file after the layer's write-back */
+#define LSO_FILE_SHADOW 2u   /* crash-consistent shadow region, see below */
 
 typedef struct lso_file_layer {
     int      fd;             /* open O_RDWR (O_DIRECT allowed); the caller owns it */
@@ -306,10 +307,55 @@ typedef struct lso_file_layer {
  * During the run: on LSO_E_CALLBACK or a failed read (LSO_E_IO) at layer
  * k, regions of layers < k hold their new state and regions of layers >= k
  * are untouched; on a failed write (LSO_E_IO) of layer k, regions < k are
- * new, region k may be partly written, regions > k are untouched.  The
+ * new, region k may be partly written (with LSO_FILE_SHADOW: is wholly at
+ * its old epoch), regions > k are untouched.  The
  * step t is the caller's to persist beside the files (the page keeps the
  * global step with the model state so a resumed run continues from it). */
 lso_status lso_stream_files(lso_stream_ctx* ctx, const lso_file_layer* layers, size_t n_layers);
+
+/* ---------------------------------------------------------------------
+ * Crash-consistent write-back (LSO_FILE_SHADOW).  The frozen-incremental
+ * page (section "Verification", its safety note) warns that a crash
+ * between the in-place update and the flush can corrupt the state, and
+ * asks for atomic writes or shadow copies.  A shadow region keeps two
+ * copies of the layer's block and commits each new one with a per-layer
+ * epoch only once it is on stable storage:
+ *
+ *   file_offset + 0                : header copy 0 (4096 bytes)
+ *   file_offset + 4096             : header copy 1
+ *   file_offset + 8192             : data slot 0 (bytes)
+ *   file_offset + 8192 + bytes     : data slot 1 (bytes)
+ *
+ * The committed state is the valid header copy (checksum, magic and bytes
+ * match) with the highest epoch e; its data is slot e % 2 and it records
+ * the step t that produced it.  With LSO_FILE_SHADOW, lso_stream_files
+ * reads the committed slot, writes the updated block to the other slot,
+ * flushes it (fdatasync), then writes header copy (e + 1) % 2 with epoch
+ * e + 1 and the layer's t, and flushes again.  A crash or error at any
+ * point leaves every layer either wholly at its old epoch or wholly at its
+ * new one.  The region needs LSO_SHADOW_HEADER_BYTES + 2 * bytes bytes of
+ * file; the file must have been formatted by lso_shadow_format.
+ * ------------------------------------------------------------------- */
+#define LSO_SHADOW_HEADER_BYTES 8192u
+
+/* Host-only (no device work).  Format a shadow region: epoch 0 in header
+ * copy 0 with step t0, header copy 1 cleared; data slot 0 is the caller's
+ * to fill before the first update.  Flushes the headers.  Errors: INVALID
+ * (bad fd, sizes), ALIGN (offset or bytes not a 4096 multiple), IO. */
+lso_status lso_shadow_format(int fd, uint64_t file_offset, uint64_t bytes, uint64_t t0);
+
+/* Host-only.  The committed state of a shadow region: its epoch, the step
+ * t recorded with it, and the absolute file offset of its data slot.
+ * Errors: INVALID, ALIGN, IO (no valid header: never formatted, or both
+ * copies damaged). */
+lso_status lso_shadow_state(int fd, uint64_t file_offset, uint64_t bytes, uint64_t* epoch,
+                            uint64_t* t, uint64_t* data_offset);
+
+/* Host-only.  Commit epoch `epoch` with step t by writing its header copy
+ * (epoch % 2) and flushing it: the step lso_stream_files takes after the
+ * data slot epoch % 2 is flushed.  For callers that write slots themselves
+ * (initial state, tools).  Errors: INVALID, ALIGN, IO. */
+lso_status lso_shadow_commit(int fd, uint64_t file_offset, uint64_t bytes, uint64_t epoch, uint64_t t);
 
 /* Device address of slot s's BF16 weight buffer (s = layer index % 2 of
  * the most recent lso_stream_layers call), or NULL. */

@@ -20,9 +20,10 @@ from typing import Iterable
 import numpy as np
 
 from . import _native
-from ._native import (LSO_DT_BF16, LSO_DT_F32, LSO_DT_NONE, LSO_FILE_SYNC, LSO_LAYOUT_PLANAR,
-                      LSO_LAYOUT_TILED, LSO_OPT_ADAM, LSO_OPT_SGD, LSO_TILE_ELEMS, LsoBlock, LsoError,
-                      LsoFileLayer, LsoHostLayer)
+from ._native import (LSO_DT_BF16, LSO_DT_F32, LSO_DT_NONE, LSO_FILE_SHADOW, LSO_FILE_SYNC,
+                      LSO_LAYOUT_PLANAR, LSO_LAYOUT_TILED, LSO_OPT_ADAM, LSO_OPT_SGD,
+                      LSO_SHADOW_HEADER_BYTES, LSO_TILE_ELEMS, LsoBlock, LsoError, LsoFileLayer,
+                      LsoHostLayer)
 
 BLOCK_DTYPE = np.dtype(LsoBlock)
 HOST_LAYER_DTYPE = np.dtype(LsoHostLayer)
@@ -32,7 +33,8 @@ __all__ = ["BlockTable", "adam_step", "adam_step_norms", "norm_workspace_bytes",
            "block_constants", "LayerStream", "HostBuffer", "host_alloc", "LsoError", "LSO_OPT_ADAM",
            "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE", "LSO_DT_F32", "LSO_LAYOUT_PLANAR",
            "LSO_LAYOUT_TILED", "LSO_TILE_ELEMS", "BLOCK_DTYPE", "HOST_LAYER_DTYPE", "FILE_LAYER_DTYPE",
-           "LSO_FILE_SYNC", "stream_handle", "tiled_state_bytes", "tiled_pack", "tiled_unpack"]
+           "LSO_FILE_SYNC", "LSO_FILE_SHADOW", "LSO_SHADOW_HEADER_BYTES", "shadow_format",
+           "shadow_state", "shadow_commit", "stream_handle", "tiled_state_bytes", "tiled_pack", "tiled_unpack"]
 
 
 def stream_handle(stream=None) -> int:
@@ -162,6 +164,24 @@ def tiled_unpack(state, master=None, m=None, v=None, *, n: int, stream=None) -> 
     st = _native.lib().lso_tiled_unpack(_addr(state), _addr(master) or None, _addr(m) or None,
                                         _addr(v) or None, n, stream_handle(stream))
     _native.check(st, "lso_tiled_unpack")
+
+
+def shadow_format(fd: int, file_offset: int, nbytes: int, t0: int = 0) -> None:
+    """Format a crash-consistent shadow region (host only)."""
+    _native.check(_native.lib().lso_shadow_format(fd, file_offset, nbytes, t0), "lso_shadow_format")
+
+
+def shadow_state(fd: int, file_offset: int, nbytes: int) -> tuple[int, int, int]:
+    """(epoch, t, data_offset) of a shadow region's committed state (host only)."""
+    e, t, off = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    _native.check(_native.lib().lso_shadow_state(fd, file_offset, nbytes, ctypes.byref(e),
+                                                 ctypes.byref(t), ctypes.byref(off)), "lso_shadow_state")
+    return int(e.value), int(t.value), int(off.value)
+
+
+def shadow_commit(fd: int, file_offset: int, nbytes: int, epoch: int, t: int) -> None:
+    """Write and flush the header copy that commits `epoch` (host only)."""
+    _native.check(_native.lib().lso_shadow_commit(fd, file_offset, nbytes, epoch, t), "lso_shadow_commit")
 
 
 def last_error() -> str:

@@ -18,6 +18,8 @@ LSO_OPT_ADAM, LSO_OPT_SGD = 0, 1
 LSO_LAYOUT_PLANAR, LSO_LAYOUT_TILED = 0, 1
 LSO_TILE_ELEMS = 8192
 LSO_FILE_SYNC = 1
+LSO_FILE_SHADOW = 2
+LSO_SHADOW_HEADER_BYTES = 8192
 
 STATUS_NAMES = {0: "LSO_OK", 1: "LSO_E_INVALID", 2: "LSO_E_ALIGN", 3: "LSO_E_DTYPE",
                 4: "LSO_E_OVERLAP", 5: "LSO_E_NOMEM", 6: "LSO_E_HIP", 7: "LSO_E_CALLBACK",
@@ -93,7 +95,8 @@ GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctype
 # every symbol include/lso.h declares
 EXPORTS = ("lso_adam_step", "lso_norm_workspace_bytes", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants", "lso_tiled_state_bytes",
            "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
-           "lso_stream_files", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc", "lso_host_free",
+           "lso_stream_files", "lso_shadow_format", "lso_shadow_state", "lso_shadow_commit",
+           "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc", "lso_host_free",
            "lso_status_string", "lso_last_error")
 
 _lib = None
@@ -129,6 +132,10 @@ def lib():
         L.lso_stream_create.argtypes = [u64, u64, vp, vp, i32, ctypes.POINTER(vp)]
         L.lso_stream_layers.argtypes = [vp, vp, sz]
         L.lso_stream_files.argtypes = [vp, vp, sz]
+        L.lso_shadow_format.argtypes = [i32, u64, u64, u64]
+        L.lso_shadow_state.argtypes = [i32, u64, u64, ctypes.POINTER(u64), ctypes.POINTER(u64),
+                                       ctypes.POINTER(u64)]
+        L.lso_shadow_commit.argtypes = [i32, u64, u64, u64, u64]
         L.lso_stream_slot_weight.argtypes = [vp, i32]
         L.lso_stream_slot_weight.restype = vp
         L.lso_stream_destroy.argtypes = [vp]
@@ -140,7 +147,8 @@ def lib():
         L.lso_last_error.restype = ctypes.c_char_p
         for name in ("lso_adam_step", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants",
                      "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create",
-                     "lso_stream_layers", "lso_stream_files", "lso_stream_destroy", "lso_host_alloc", "lso_host_free"):
+                     "lso_stream_layers", "lso_stream_files", "lso_shadow_format", "lso_shadow_state",
+                     "lso_shadow_commit", "lso_stream_destroy", "lso_host_alloc", "lso_host_free"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

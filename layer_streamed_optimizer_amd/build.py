@@ -23,7 +23,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 LIBS = {
     "liblso.so": ["lso_adam.hip", "lso_copy.hip", "lso_tiled.hip", "lso_runtime.cpp",
-                  "lso_stream.cpp"],
+                  "lso_stream.cpp", "lso_shadow.cpp"],
     "liblso_probes.so": ["lso_probes.hip", "lso_probe_io.cpp"],
 }
 

@@ -65,6 +65,7 @@
 #include <deque>
 #include <memory>
 #include <mutex>
+#include <string>
 #include <new>
 #include <thread>
 #include <vector>
@@ -72,12 +73,15 @@
 #include "lso_copy.h"
 #include "lso_internal.h"
 #include "lso_runtime.h"
+#include "lso_shadow.h"
 
 namespace {
 
 // ------------------------------------------------------------ worker pools
 
 enum IoOp { kIoCopy = 0, kIoRead = 1, kIoWrite = 2 };
+
+constexpr uint64_t kShadowHeaderCopy = lso::kShadowCopy;
 
 // One transfer between a staging buffer and the authoritative copy, split
 // into parts that the pool's threads take in order.
@@ -90,6 +94,8 @@ struct IoRequest {
     uint64_t bytes = 0;
     bool sync = false;           // fdatasync(fd) after the last part
     bool direct = false;         // fd is O_DIRECT: transfer through a bounce buffer
+    const char* header = nullptr;   // shadow commit: after the data is flushed,
+    uint64_t header_off = 0;        // write this header copy here and flush
     std::atomic<uint32_t> parts_left{0};
     std::atomic<int> err{0};     // first errno seen; EIO for end of file
     std::atomic<bool> done{false};
@@ -230,8 +236,20 @@ private:
             do_part(p);
             IoRequest* r = p.r;
             if (r->parts_left.fetch_sub(1) == 1) {
-                if (r->sync && r->op == kIoWrite && r->err.load() == 0 && ::fdatasync(r->fd) != 0)
-                    note_error(r, errno);
+                if (r->op == kIoWrite && r->err.load() == 0) {
+                    if ((r->sync || r->header) && ::fdatasync(r->fd) != 0) {
+                        note_error(r, errno);
+                    } else if (r->header) {
+                        // the data slot is on stable storage: commit it
+                        IoRequest h;
+                        h.fd = r->fd;
+                        h.foff = r->header_off;
+                        if (!file_io(&h, const_cast<char*>(r->header), 0, kShadowHeaderCopy, false))
+                            note_error(r, h.err.load());
+                        else if (::fdatasync(r->fd) != 0)
+                            note_error(r, errno);
+                    }
+                }
                 {
                     std::lock_guard<std::mutex> l(*note_mu_);
                     r->done.store(true);
@@ -365,9 +383,13 @@ struct Job {
     int kind = kPinned;
     char* host = nullptr;     // pinned or pageable block
     int fd = -1;              // file block
-    uint64_t foff = 0;
+    uint64_t foff = 0;        // where it is read from
+    uint64_t woff = 0;        // where it is written back (another slot if shadow)
     bool sync = false;
     bool direct = false;      // fd opened O_DIRECT
+    bool shadow = false;      // commit header copy for new_epoch after the write
+    uint64_t region = 0;      // start of the shadow region
+    uint64_t new_epoch = 0;
     uint64_t bytes = 0, n = 0, off_master = 0, off_m = 0, off_v = 0;
     void* dev_weight = nullptr;
     uint32_t opt = 0, layout = 0;
@@ -601,6 +623,13 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
     }
     const size_t K = staging_count(c);
     std::unique_ptr<IoRequest[]> rd(new IoRequest[K]), wr(new IoRequest[K]);
+    // shadow commits: one page-aligned header copy per staging buffer
+    std::unique_ptr<char, decltype(&std::free)> headers(nullptr, &std::free);
+    {
+        void* q = nullptr;
+        if (posix_memalign(&q, 4096, K * kShadowHeaderCopy) != 0) return lso::fail(LSO_E_NOMEM, "header buffers");
+        headers.reset(static_cast<char*>(q));
+    }
     std::vector<char> wr_live(K, 0);   // a write-out was submitted for the buffer
     lso_status result = LSO_OK;
     auto record = [&](lso_status s) {
@@ -688,13 +717,20 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
                 w.reset();
                 w.direct = j.direct;
                 w.sync = false;
+                w.header = nullptr;
                 w.bytes = j.bytes;
                 w.src = static_cast<const char*>(c->staging[next_retire % K]);
                 if (j.kind == kFile) {
                     w.op = kIoWrite;
                     w.fd = j.fd;
-                    w.foff = j.foff;
+                    w.foff = j.woff;
                     w.sync = j.sync;
+                    if (j.shadow) {
+                        char* h = headers.get() + (next_retire % K) * kShadowHeaderCopy;
+                        lso::shadow_encode(h, j.new_epoch, j.bytes, j.t);
+                        w.header = h;
+                        w.header_off = lso::shadow_header(j.region, j.new_epoch);
+                    }
                 } else {
                     w.op = kIoCopy;
                     w.dst = j.host;
@@ -897,9 +933,11 @@ lso_status lso_stream_files(lso_stream_ctx* c, const lso_file_layer* L, size_t n
         j.kind = kFile;
         j.fd = L[i].fd;
         j.foff = L[i].file_offset;
-        if (L[i].flags & ~static_cast<uint32_t>(LSO_FILE_SYNC))
+        if (L[i].flags & ~static_cast<uint32_t>(LSO_FILE_SYNC | LSO_FILE_SHADOW))
             return lso::fail(LSO_E_INVALID, "layer %zu: unknown flags %#x", i, L[i].flags);
         j.sync = (L[i].flags & LSO_FILE_SYNC) != 0;
+        j.shadow = (L[i].flags & LSO_FILE_SHADOW) != 0;
+        const uint64_t span = j.shadow ? LSO_SHADOW_HEADER_BYTES + 2 * j.bytes : j.bytes;
         if (j.foff % 4096 != 0 || j.bytes % 4096 != 0)
             return lso::fail(LSO_E_ALIGN, "layer %zu: file offset and bytes must be 4096-byte multiples", i);
         struct stat st {};
@@ -909,12 +947,26 @@ lso_status lso_stream_files(lso_stream_ctx* c, const lso_file_layer* L, size_t n
         if (acc < 0 || (acc & O_ACCMODE) != O_RDWR)
             return lso::fail(LSO_E_INVALID, "layer %zu: fd %d is not open for reading and writing", i, j.fd);
         j.direct = (acc & O_DIRECT) != 0;
-        if (S_ISREG(st.st_mode) && static_cast<uint64_t>(st.st_size) < j.foff + j.bytes)
+        if (S_ISREG(st.st_mode) && static_cast<uint64_t>(st.st_size) < j.foff + span)
             return lso::fail(LSO_E_INVALID, "layer %zu: the file ends before its block does", i);
         lso_status s = check_state(c, j, i);
         if (s != LSO_OK) return s;
         ex.push_back({static_cast<uint64_t>(st.st_dev) + 1, static_cast<uint64_t>(st.st_ino), j.foff,
-                      j.foff + j.bytes, i});
+                      j.foff + span, i});
+        j.woff = j.foff;
+        if (j.shadow) {
+            // read the committed slot, write the other one, then commit it
+            lso::ShadowState cur;
+            s = lso::shadow_read(j.fd, j.foff, j.bytes, &cur);
+            if (s != LSO_OK) {
+                const std::string why = lso_last_error();
+                return lso::fail(s, "layer %zu: %s", i, why.c_str());
+            }
+            j.region = j.foff;
+            j.new_epoch = cur.epoch + 1;
+            j.foff = lso::shadow_slot(j.region, j.bytes, cur.epoch);
+            j.woff = lso::shadow_slot(j.region, j.bytes, j.new_epoch);
+        }
     }
     lso_status s = check_disjoint(ex);
     if (s != LSO_OK) return s;
