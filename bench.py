@@ -386,15 +386,16 @@ def streamed_files(args, w):
     om, _omm, _ov, nbytes = configs.host_layer_layout(n, tiled=tiled)
     base = args.file_dir or os.environ.get("LSO_FILE_DIR", "/var/tmp")
     free = shutil.disk_usage(base).free
-    n_layers = args.layers or 6
-    if n_layers * nbytes + (10 << 30) > free:
+    copies = 2 if args.shadow else 1          # shadow regions hold two data slots
+    n_layers = args.layers or (3 if args.shadow else 6)
+    if copies * n_layers * nbytes + (10 << 30) > free:
         sys.exit(f"{base} has {free / 1e9:.0f} GB free; {n_layers} layers need "
-                 f"{n_layers * nbytes / 1e9:.0f} GB plus 10 GB of headroom (use --layers)")
+                 f"{copies * n_layers * nbytes / 1e9:.0f} GB plus 10 GB of headroom (use --layers)")
     d = tempfile.mkdtemp(prefix="lso_disk_", dir=base)
     try:
         peak = storage_peak(d)
         progress(f"storage: {peak}")
-        files = LayerFiles.create(d, [n] * n_layers, tiled=tiled, direct=True)
+        files = LayerFiles.create(d, [n] * n_layers, tiled=tiled, direct=True, shadow=args.shadow)
         hs = torch.cuda.current_stream().cuda_stream
         stage = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         scratch = torch.empty(n, dtype=torch.float32, device="cuda") if tiled else None
@@ -415,9 +416,9 @@ def streamed_files(args, w):
                 lso.tiled_pack(int(stage.data_ptr()) + om, dst, None, None, n=n, stream=hs)
             torch.cuda.synchronize()
             assert hip.hipMemcpy(host_ptr, int(stage.data_ptr()), nbytes, 2) == 0
-            done = 0
+            done, at = 0, files.state(b)[2]       # shadow files: the committed slot
             while done < nbytes:
-                done += os.pwritev(files.fds[b], [view[done:]], done)
+                done += os.pwritev(files.fds[b], [view[done:]], at + done)
             progress(f"layer {b} written")
         del view
         del stage, scratch
@@ -451,9 +452,11 @@ def streamed_files(args, w):
         roofline=dict(bound="storage", achieved=per_dir, peak=top, unit="GB/s per direction",
                       frac=per_dir / top, traffic=None),
         storage_peak_GBps=peak,
-        config=dict(workload=f"{w.key}: 70B-shaped slice, layer-streamed from files (disk tier)",
+        config=dict(workload=f"{w.key}: 70B-shaped slice, layer-streamed from files (disk tier"
+                             + (", crash-consistent shadow regions)" if args.shadow else ")"),
                     layers=n_layers, layers_in_config=len(w.blocks), params=params,
-                    host_memory="file (O_DIRECT, one preallocated file per layer)",
+                    host_memory="file (O_DIRECT, one preallocated file per layer"
+                                + (", shadow region)" if args.shadow else ")"),
                     state_layout=args.layout, file_bytes=nbytes * n_layers,
                     storage_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
     )
@@ -514,6 +517,9 @@ def main():
                          "budget), or files (the disk tier, O_DIRECT)")
     ap.add_argument("--layers", type=int, default=0,
                     help="c4: layers to stream (0 = all 16; 6 for --host-memory file)")
+    ap.add_argument("--shadow", action="store_true",
+                    help="c4 with --host-memory file: crash-consistent shadow regions "
+                         "(3 layers by default: two data slots per layer)")
     ap.add_argument("--file-dir", default=None,
                     help="c4 with --host-memory file: where the layer files go "
                          "(default $LSO_FILE_DIR or /var/tmp)")
