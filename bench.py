@@ -50,6 +50,34 @@ def progress(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def environment() -> dict:
+    """What the numbers were measured on."""
+    import platform
+
+    import torch
+
+    env = dict(torch=torch.__version__, hip=getattr(torch.version, "hip", None),
+               host_threads=os.cpu_count(), python=platform.python_version())
+    try:
+        p = torch.cuda.get_device_properties(0)
+        env.update(gpu=p.name, gcn_arch=getattr(p, "gcnArchName", None),
+                   gpu_memory_GB=round(p.total_memory / 1e9, 1), compute_units=p.multi_processor_count)
+    except Exception as e:   # the record is informative only
+        env["gpu"] = f"unavailable ({e})"
+    try:
+        with open("/proc/cpuinfo") as f:
+            env["cpu"] = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+        with open("/proc/meminfo") as f:
+            mem = {l.split(":")[0]: l.split(":")[1].strip() for l in f}
+        env["host_memory_total"], env["host_memory_available"] = mem.get("MemTotal"), mem.get("MemAvailable")
+        rocm = "/opt/rocm/.info/version"
+        if os.path.exists(rocm):
+            env["rocm"] = open(rocm).read().strip()
+    except Exception:
+        pass
+    return env
+
+
 def kernel_hash() -> str:
     from layer_streamed_optimizer_amd.rocprof_summary import kernel_hash as kh
     return kh()
@@ -167,8 +195,17 @@ def resident(args, w):
         else:
             lso.adam_step(tab, hs)
 
+    cold = None
     for j in range(1, args.warmup + 1):
-        step(j)
+        if j == 1:   # the first update of the run, timed on its own
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step(j)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold = c0.elapsed_time(c1)
+        else:
+            step(j)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -183,6 +220,23 @@ def resident(args, w):
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(kernel_ms) / len(kernel_ms)
     achieved = bpp * params / (avg_ms * 1e-3) / 1e9
+    flushed = None
+    if w.key in ("c0", "c2"):
+        # these fit the 256 MB last-level cache: time the same steps again
+        # with 512 MB written between them, so no state is cache-resident
+        scratch_mall = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for k in range(args.steps):
+            synth.device_fill_zero(int(scratch_mall.data_ptr()), 512 << 20, hs)
+            starts[k].record(stream)
+            step(args.warmup + args.steps + 1 + k)
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+        fl_ms = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
+        f_avg = sum(fl_ms) / len(fl_ms)
+        flushed = dict(kernel_avg_us=f_avg * 1e3, kernel_median_us=fl_ms[len(fl_ms) // 2] * 1e3,
+                       achieved_GBps=bpp * params / (f_avg * 1e-3) / 1e9,
+                       note="512 MB written between steps; the main figures are cache-resident")
+        del scratch_mall
     ceiling = copy_ceiling(torch, dev)
     progress(f"steps: wall {wall * 1e3:.3f} ms for {args.steps}; kernel avg {avg_ms * 1e3:.1f} us; "
              f"{achieved:.0f} GB/s; copy ceiling {ceiling:.0f} GB/s")
@@ -193,6 +247,8 @@ def resident(args, w):
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBPS, traffic=traffic),
         kernel_avg_us=avg_ms * 1e3, kernel_min_us=min(kernel_ms) * 1e3,
+        kernel_median_us=sorted(kernel_ms)[len(kernel_ms) // 2] * 1e3,
+        kernel_first_step_us=cold * 1e3 if cold is not None else None,
         hbm_copy_ceiling_GBps=ceiling,
         config=dict(workload=f"{w.key}: {w.title}", blocks=len(sizes), params=params,
                     state_layout=args.layout, grad_dtype=args.grad_dtype, bytes_per_param=bpp,
@@ -201,6 +257,8 @@ def resident(args, w):
                     hyper=dict(lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2,
                                eps=configs.EPS)),
     )
+    if flushed:
+        result["cache_flushed"] = flushed
     del state, weight, grads, scratch
     return result
 
@@ -497,9 +555,22 @@ def cpu_baseline(w, budget_s=12.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    # one thread on the first block's first 8M params, for the per-core rate
+    master, m, v, g, wb = arrays[0]
+    k1 = min(master.size, 8 << 20)
+    s1, t1 = 0, time.perf_counter()
+    while True:
+        s1 += 1
+        oracle.adam_step(master[:k1], m[:k1], v[:k1], g[:k1], wb[:k1], steps + s1, 1e-3, 0.9, 0.999,
+                         1e-8, threads=1)
+        if time.perf_counter() - t1 >= budget_s / 4:
+            break
+    d1 = time.perf_counter() - t1
     return dict(value=take * steps / dt / 1e9, unit="Gparams/s", cores=threads, kind="oracle",
                 sample=f"first {take:,} params of {w.key} ({len(blocks)} block(s)), {steps} steps, "
-                       f"{dt:.1f} s, inputs in host RAM")
+                       f"{dt:.1f} s, inputs in host RAM",
+                single_thread=dict(value=k1 * s1 / d1 / 1e9, unit="Gparams/s",
+                                   sample=f"{k1:,} params, {s1} steps, {d1:.1f} s"))
 
 
 # ---------------------------------------------------------------------- main
@@ -539,7 +610,7 @@ def main():
         sys.exit(2)
     from layer_streamed_optimizer_amd import configs
     w = configs.get(args.config)
-    defaults = {"c0": (3, 10), "c1": (2, 10), "c2": (5, 100), "c3": (1, 4), "c4": (1, 2)}
+    defaults = {"c0": (10, 100), "c1": (2, 10), "c2": (5, 100), "c3": (1, 4), "c4": (1, 2)}
     dw, dk = defaults[args.config]
     if args.layout is None:
         args.layout = "planar" if args.config in ("c0", "c2") else "tiled"
@@ -562,6 +633,7 @@ def main():
         progress("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(w)
     out.update(res)
+    out["environment"] = environment()
     print(json.dumps(out), flush=True)
 
 

@@ -115,7 +115,7 @@ def c3_llama7b() -> Workload:
 def c4_streamed70b(layers: int = 16) -> Workload:
     per = layer_params(**LLAMA70B)
     blocks = [BlockSpec(f"layer{i}", per) for i in range(layers)]
-    return Workload("c4", "70B-shaped slice, layer-streamed from pinned host memory", blocks,
+    return Workload("c4", "70B-shaped slice, layer-streamed from host memory", blocks,
                     steps=3, streamed=True, notes={"layer_params": per})
 
 
