@@ -237,6 +237,9 @@ def resident(args, w):
                        achieved_GBps=bpp * params / (f_avg * 1e-3) / 1e9,
                        note="512 MB written between steps; the main figures are cache-resident")
         del scratch_mall
+    # the copy ceiling needs 16 GB: the gradient sets go first
+    grads.clear()
+    torch.cuda.empty_cache()
     ceiling = copy_ceiling(torch, dev)
     progress(f"steps: wall {wall * 1e3:.3f} ms for {args.steps}; kernel avg {avg_ms * 1e3:.1f} us; "
              f"{achieved:.0f} GB/s; copy ceiling {ceiling:.0f} GB/s")

@@ -16,14 +16,14 @@ constexpr int kThreads = 256;
 constexpr int kQuad = 4;
 constexpr int kUnrollLarge = 4;
 constexpr int kUnrollSmall = 1;
-constexpr int kUnrollTiled = 8;   // one workgroup per state tile
+constexpr int kUnrollTiled = 1;   // a tile's 8192 elements over 8 workgroups
 constexpr uint64_t kSmallCallElems = 32ull << 20;   // below this, kUnrollSmall
 constexpr uint64_t kMaxGrid = 1ull << 24;            // workgroups per launch
-constexpr uint64_t kMaxIndexChunks = 1ull << 22;     // per-chunk block index up to this
+constexpr uint64_t kMaxIndexChunks = 1ull << 24;     // per-chunk block index up to this
 
 constexpr uint64_t chunk_elems(int unroll) { return static_cast<uint64_t>(kThreads) * kQuad * unroll; }
 constexpr uint64_t kNormPartsPerChunk = kThreads / 64;   // one FP64 per wave
-static_assert(chunk_elems(kUnrollTiled) == LSO_TILE_ELEMS, "a tiled chunk is one state tile");
+static_assert(LSO_TILE_ELEMS % chunk_elems(kUnrollTiled) == 0, "a tiled chunk lies inside one state tile");
 
 // At most this many distinct constant sets travel by value in one launch.
 constexpr int kMaxGroups = 16;
@@ -74,13 +74,14 @@ struct KernelArgs {
 };
 
 // Enqueue the fused kernel (defined in lso_adam.hip) with chunks of
-// chunk_elems(unroll) elements; unroll == kUnrollTiled launches the tiled
-// variant (every block of the launch tiled); grad_f32 the FP32-gradient
-// variant (every block of the launch).  With args.partials set, the norm
+// chunk_elems(unroll) elements (unroll: kUnrollSmall or kUnrollLarge
+// planar, kUnrollTiled tiled); tiled launches the tiled variant (every
+// block of the launch tiled); grad_f32 the FP32-gradient variant (every
+// block of the launch).  With args.partials set, the norm
 // variant also writes each wave's sum of g^2 to
 // args.partials[chunk * kNormPartsPerChunk + wave].
 // Returns the hipError_t.
-int launch_fused_adam(const KernelArgs& args, int unroll, bool grad_f32, void* stream);
+int launch_fused_adam(const KernelArgs& args, int unroll, bool tiled, bool grad_f32, void* stream);
 
 // Sum the chunk partials of each block of the launch (one workgroup per
 // block, fixed order) into sq_norms[the block's position in the call].

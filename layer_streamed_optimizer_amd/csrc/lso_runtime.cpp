@@ -489,7 +489,7 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
                 if (s != LSO_OK) return s;
             }
             if (norms) args.partials = norms->workspace + part_offset * kNormPartsPerChunk;
-            int err = launch_fused_adam(args, unroll, g32_pass, stream);
+            int err = launch_fused_adam(args, unroll, tiled_pass, g32_pass, stream);
             if (err != 0) return hip_fail(err, "fused Adam launch");
             if (norms) {
                 err = launch_norm_reduce(args, unroll, norms->sq_norms, stream);

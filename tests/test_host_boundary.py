@@ -298,15 +298,15 @@ def test_resident_layout_tiled():
 
 def test_norm_workspace_bytes_follow_the_launch_plan():
     """One FP64 per wave (4 per chunk): planar chunks of 1024 elements in
-    calls under 32M planar elements, 4096 above; tiled chunks are one
-    8192-element tile."""
+    calls under 32M planar elements, 4096 above; tiled chunks are an eighth
+    of a state tile (1024 elements)."""
     per = 4 * 8
     assert lso.norm_workspace_bytes(table([])) == 0
     assert lso.norm_workspace_bytes(table([row(0, n=1), row(1, n=1024), row(2, n=1025)])) == per * (1 + 1 + 2)
     big = row(0, n=32 << 20)
     assert lso.norm_workspace_bytes(table([big])) == per * ((32 << 20) // 4096)
     t = dict(n=8193, master=A, grad=A + (1 << 20), layout=lso.LSO_LAYOUT_TILED)
-    assert lso.norm_workspace_bytes(table([t, row(1, n=5000)])) == per * (2 + 5)
+    assert lso.norm_workspace_bytes(table([t, row(1, n=5000)])) == per * (9 + 5)
 
 
 def _norms_status(tab, sq, ws, ws_bytes):
