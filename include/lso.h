@@ -162,8 +162,9 @@ lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream);
  * 8-byte aligned; it holds per-chunk sums while the call runs on stream, so
  * calls that run at the same time need separate workspaces.  Neither may
  * overlap the other or any array of the call.  Relative error of each
- * entry against the exact sum: below 2e-6 (FP32 sums of at most 32 squares
- * per lane, FP64 above that).  Errors: as lso_adam_step, and INVALID for a
+ * entry against the exact sum: below 2e-6 (FP32 sums of at most 1024
+ * squares per wave: at most 16 per lane in sequence, then a 64-lane tree;
+ * FP64 above that).  Errors: as lso_adam_step, and INVALID for a
  * NULL or too small buffer, ALIGN, OVERLAP.
  */
 uint64_t lso_norm_workspace_bytes(const lso_block* blocks, size_t n);
