@@ -215,7 +215,11 @@ lso_status lso_tiled_unpack(const void* state, float* master, float* m, float* v
  * staging buffers, copied in by worker threads before its H2D and out after
  * its D2H.  lso_stream_files does the same with blocks held in files (the
  * disk tier).  Stage-ins and write-outs run on two worker pools, so reading
- * layer i + 1, updating layer i and writing layer i - 1 overlap.
+ * layer i + 1, updating layer i and writing layer i - 1 overlap.  A tiled
+ * layer whose state starts its block moves in pieces of whole tiles (about
+ * 1 GiB; LSO_STREAM_PIECE_BYTES at context creation sets another size),
+ * so the pipeline fills and drains in one piece rather than one layer; its
+ * gradient producer still runs once, before the first piece's update.
  * ------------------------------------------------------------------- */
 
 typedef struct lso_host_layer {
@@ -305,11 +309,12 @@ typedef struct lso_file_layer {
  * LSO_FILE_SYNC was set).  Errors before anything runs: INVALID (bad fd,
  * not O_RDWR, file shorter than offset + bytes, flags), ALIGN, OVERLAP
  * (two regions of one call share bytes of the same file), DTYPE, NOMEM.
- * During the run: on LSO_E_CALLBACK or a failed read (LSO_E_IO) at layer
- * k, regions of layers < k hold their new state and regions of layers >= k
- * are untouched; on a failed write (LSO_E_IO) of layer k, regions < k are
- * new, region k may be partly written (with LSO_FILE_SHADOW: is wholly at
- * its old epoch), regions > k are untouched.  The
+ * During the run: on LSO_E_CALLBACK at layer k, regions of layers < k
+ * hold their new state and regions of layers >= k are untouched; on a
+ * failed read or write (LSO_E_IO) at layer k, regions < k are new, region
+ * k may be partly written (a failed write, or a failed read of a layer that
+ * moves in several pieces; with LSO_FILE_SHADOW it is wholly at its old
+ * epoch), regions > k are untouched.  The
  * step t is the caller's to persist beside the files (the page keeps the
  * global step with the model state so a resumed run continues from it). */
 lso_status lso_stream_files(lso_stream_ctx* ctx, const lso_file_layer* layers, size_t n_layers);

@@ -290,6 +290,7 @@ struct lso_stream_ctx {
     void* slot_grad[kMaxSlots] = {};
     void* slot_weight[kMaxSlots] = {};
     void* staging[kMaxStaging] = {};   // pinned, allocated on the first staged layer
+    uint64_t staging_bytes = 0;         // size of each staging buffer
     hipEvent_t weights_ready[kMaxSlots] = {};
     hipEvent_t step_done[kMaxSlots] = {};
     hipEvent_t buffer_free[kMaxSlots] = {};
@@ -304,6 +305,7 @@ struct lso_stream_ctx {
     std::condition_variable note_cv;
     int copy_mode = kCopyKernels;
     unsigned copy_grid = lso::kCopyGrid;
+    uint64_t piece_bytes = 1ull << 30;   // target size of a tiled layer's pieces
 };
 
 namespace {
@@ -479,15 +481,26 @@ unsigned io_threads()
     return std::max(2u, std::min(8u, (hw ? hw : 2u) / 2));
 }
 
-lso_status ensure_staging(lso_stream_ctx* c)
+// Staging buffers hold one piece each: they are sized for the largest
+// piece of the call (a whole layer unless it moves in pieces) and grown
+// when a later call needs more.
+lso_status ensure_staging(lso_stream_ctx* c, uint64_t need)
 {
+    need = (need + 4095) & ~uint64_t(4095);
+    if (c->staging_bytes < need) {
+        for (int s = 0; s < kMaxStaging; ++s) {
+            if (c->staging[s]) (void)hipHostFree(c->staging[s]);
+            c->staging[s] = nullptr;
+        }
+        c->staging_bytes = need;
+    }
     for (size_t s = 0; s < staging_count(c); ++s) {
         if (c->staging[s]) continue;
-        if (hipHostMalloc(&c->staging[s], c->max_bytes, hipHostMallocDefault) != hipSuccess) {
+        if (hipHostMalloc(&c->staging[s], c->staging_bytes, hipHostMallocDefault) != hipSuccess) {
             (void)hipGetLastError();
             c->staging[s] = nullptr;
             return lso::fail(LSO_E_NOMEM, "pinned staging buffer of %llu bytes",
-                             static_cast<unsigned long long>(c->max_bytes));
+                             static_cast<unsigned long long>(c->staging_bytes));
         }
     }
     if (!c->reader) c->reader = new (std::nothrow) IoPool(io_threads(), &c->note_mu, &c->note_cv);
@@ -507,34 +520,85 @@ hipError_t copy_block(const lso_stream_ctx* c, void* dst, const void* src, uint6
     return static_cast<hipError_t>(lso::launch_block_copy(dst, src, bytes, c->copy_grid, st));
 }
 
-// Enqueue H2D, gradient producer, update and D2H of the layer at position
-// i of the pipeline (slot i % nslots), and record d2h_done[i % nstaging]
-// after its D2H.  buf: where the H2D reads and the D2H writes (the block
-// itself when pinned, a staging buffer otherwise).
-lso_status issue_layer(lso_stream_ctx* c, const Job& h, size_t i, void* buf)
+// One piece of a layer as it moves through the pipeline.  A tiled layer
+// whose state starts the block is cut into pieces of whole tiles (about
+// piece_bytes each), so a piece's state is a tiled region of its own; any
+// other layer is one piece.  Moving pieces rather than whole layers keeps
+// the pipeline's fill and drain (the first stage-in and H2D, the last D2H
+// and write-out, which run with nothing beside them) to one piece.
+struct Unit {
+    const Job* job;
+    size_t layer;        // position of the layer among the call's jobs
+    uint64_t off;        // byte offset of the piece inside the block
+    uint64_t bytes;      // bytes of the piece
+    uint64_t e0, e1;     // the piece's elements of the layer
+    bool first, last;    // first / last piece of its layer
+};
+
+std::vector<Unit> make_units(const lso_stream_ctx* c, const Job* J, size_t n)
 {
+    std::vector<Unit> u;
+    constexpr uint64_t T = LSO_TILE_ELEMS;
+    constexpr uint64_t tile_bytes = 12 * T;
+    for (size_t L = 0; L < n; ++L) {
+        const Job& j = J[L];
+        const uint64_t per = std::max<uint64_t>(1, c->piece_bytes / tile_bytes);   // tiles per piece
+        const uint64_t tiles = (j.n + T - 1) / T;
+        if (j.layout != LSO_LAYOUT_TILED || j.off_master != 0 || tiles <= per) {
+            u.push_back({&j, L, 0, j.bytes, 0, j.n, true, true});
+            continue;
+        }
+        for (uint64_t k = 0; k * per < tiles; ++k) {
+            const uint64_t t0 = k * per, t1 = std::min(tiles, t0 + per);
+            const bool last = t1 == tiles;
+            const uint64_t off = t0 * tile_bytes;
+            u.push_back({&j, L, off, last ? j.bytes - off : (t1 - t0) * tile_bytes, t0 * T,
+                         std::min(j.n, t1 * T), k == 0, last});
+        }
+    }
+    return u;
+}
+
+// Enqueue H2D, (on a layer's first piece) the gradient producer, the update
+// and D2H of the piece at position i of the pipeline (slot i % nslots), and
+// record d2h_done[i % nstaging] after its D2H.  buf: where the H2D reads and
+// the D2H writes (inside the block itself when pinned, a staging buffer
+// otherwise).  A layer's gradients and BF16 weights live in the buffers of
+// its own parity (layer % nslots) for all its pieces.
+lso_status issue_unit(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
+{
+    const Job& h = *U.job;
     const int s = static_cast<int>(i % c->nslots);
+    const int ls = static_cast<int>(U.layer % c->nslots);
     hipError_t err;
-    // StreamIn: the device slot is free once the layer that used it last
-    // (nslots layers ago) has been copied back.
+    // StreamIn: the device slot is free once the piece that used it last
+    // (nslots pieces ago) has been copied back.
     if ((err = hipStreamWaitEvent(c->h2d, c->buffer_free[s], 0)) != hipSuccess ||
-        (err = copy_block(c, c->slot_state[s], buf, h.bytes, hipMemcpyHostToDevice, c->h2d)) != hipSuccess ||
+        (err = copy_block(c, c->slot_state[s], buf, U.bytes, hipMemcpyHostToDevice, c->h2d)) != hipSuccess ||
         (err = hipEventRecord(c->weights_ready[s], c->h2d)) != hipSuccess)
         return lso::hip_fail(err, "H2D stage");
-    // Compute: gradients of this layer, then the fused update on the slot.
+    // Compute: the layer's gradients (once), then the fused update on the slot.
     if ((err = hipStreamWaitEvent(c->compute, c->weights_ready[s], 0)) != hipSuccess)
         return lso::hip_fail(err, "hipStreamWaitEvent(weights-ready)");
-    const int rc = c->fn(c->user, h.index, c->slot_grad[s], h.n, c->compute);
-    if (rc != 0) return lso::fail(LSO_E_CALLBACK, "gradient producer returned %d at layer %zu", rc, h.index);
+    if (U.first) {
+        const int rc = c->fn(c->user, h.index, c->slot_grad[ls], h.n, c->compute);
+        if (rc != 0) return lso::fail(LSO_E_CALLBACK, "gradient producer returned %d at layer %zu", rc, h.index);
+    }
     lso_block b{};
-    const uintptr_t base = reinterpret_cast<uintptr_t>(c->slot_state[s]);
+    // the piece's bytes [off, off + bytes) of the block sit at the slot's start
+    const uintptr_t base = reinterpret_cast<uintptr_t>(c->slot_state[s]) - U.off;
     b.base = nullptr;   // absolute addresses below
-    b.n = h.n;
-    b.off_master = base + h.off_master;
-    b.off_m = base + h.off_m;
-    b.off_v = base + h.off_v;
-    b.off_grad = reinterpret_cast<uintptr_t>(c->slot_grad[s]);
-    b.off_weight = reinterpret_cast<uintptr_t>(h.dev_weight ? h.dev_weight : c->slot_weight[s]);
+    b.n = U.e1 - U.e0;
+    if (h.layout == LSO_LAYOUT_TILED) {
+        b.off_master = base + h.off_master + 12 * U.e0;   // e0 is a tile boundary
+        b.off_m = b.off_v = b.off_master;
+    } else {
+        b.off_master = base + h.off_master;
+        b.off_m = base + h.off_m;
+        b.off_v = base + h.off_v;
+    }
+    b.off_grad = reinterpret_cast<uintptr_t>(c->slot_grad[ls]) + 2 * U.e0;
+    b.off_weight = reinterpret_cast<uintptr_t>(h.dev_weight ? h.dev_weight : c->slot_weight[ls]) + 2 * U.e0;
     b.grad_dtype = LSO_DT_BF16;
     b.weight_dtype = LSO_DT_BF16;
     b.opt = h.opt;
@@ -554,9 +618,9 @@ lso_status issue_layer(lso_stream_ctx* c, const Job& h, size_t i, void* buf)
     if (st != LSO_OK) return st;
     if ((err = hipEventRecord(c->step_done[s], c->compute)) != hipSuccess)
         return lso::hip_fail(err, "hipEventRecord(step-done)");
-    // Offload: the updated block goes back over the authoritative copy.
+    // Offload: the updated piece goes back over the authoritative copy.
     if ((err = hipStreamWaitEvent(c->d2h, c->step_done[s], 0)) != hipSuccess ||
-        (err = copy_block(c, buf, c->slot_state[s], h.bytes, hipMemcpyDeviceToHost, c->d2h)) != hipSuccess ||
+        (err = copy_block(c, buf, c->slot_state[s], U.bytes, hipMemcpyDeviceToHost, c->d2h)) != hipSuccess ||
         (err = hipEventRecord(c->buffer_free[s], c->d2h)) != hipSuccess ||
         (err = hipEventRecord(c->d2h_done[i % staging_count(c)], c->d2h)) != hipSuccess)
         return lso::hip_fail(err, "D2H stage");
@@ -565,10 +629,11 @@ lso_status issue_layer(lso_stream_ctx* c, const Job& h, size_t i, void* buf)
 
 const char* io_what(const Job& j) { return j.kind == kFile ? "file" : "host block"; }
 
-// With LSO_STREAM_TRACE set, each call prints one line per layer to stderr:
-// when its stage-in started, when the loop saw it complete and issued the
-// layer, when it saw the D2H complete (write-out start) and when it saw the
-// write-out complete, in ms from the start of the call.
+// With LSO_STREAM_TRACE set, each call prints one line per piece to stderr:
+// its layer and piece, when its stage-in started, when the loop saw it
+// complete and issued the piece, when it saw the D2H complete (write-out
+// start) and when it saw the write-out complete, in ms from the start of
+// the call.
 struct Trace {
     bool on = false;
     std::chrono::steady_clock::time_point t0;
@@ -589,28 +654,36 @@ struct Trace {
     {
         if (on) v[i] = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     }
-    void print() const
+    void print(const std::vector<Unit>& units) const
     {
         if (!on) return;
-        std::fprintf(stderr, "[lso trace] layer  read_start  issued  d2h_done  written   (ms)\n");
-        for (size_t i = 0; i < read.size(); ++i)
-            std::fprintf(stderr, "[lso trace] %5zu  %10.1f  %6.1f  %8.1f  %7.1f\n", i, read[i], issue[i],
-                         retire[i], done[i]);
+        std::fprintf(stderr, "[lso trace] layer.piece  read_start  issued  d2h_done  written   (ms)\n");
+        size_t piece = 0;
+        for (size_t i = 0; i < read.size(); ++i) {
+            piece = units[i].first ? 0 : piece + 1;
+            std::fprintf(stderr, "[lso trace] %5zu.%-5zu  %10.1f  %6.1f  %8.1f  %7.1f\n", units[i].job->index,
+                         piece, read[i], issue[i], retire[i], done[i]);
+        }
     }
 };
 
-// The event loop over all layers of one call (see the top of this file).
-// Layer i owns staging buffer i % K (K = nstaging) from the start of its
+// The event loop over all pieces of one call (see the top of this file).
+// Piece i owns staging buffer i % K (K = nstaging) from the start of its
 // stage-in until its write-out is complete.
-lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
+lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
 {
+    const std::vector<Unit> units = make_units(c, J, nj);
+    const size_t n = units.size();
     bool any_staged = false, any_norm = false;
-    for (size_t i = 0; i < n; ++i) {
+    uint64_t max_piece = 0;
+    for (size_t i = 0; i < nj; ++i) {
         any_staged |= J[i].kind != kPinned;
         any_norm |= J[i].sq_norm != nullptr;
     }
+    for (const Unit& u : units)
+        if (u.job->kind != kPinned) max_piece = std::max(max_piece, u.bytes);
     if (any_staged) {
-        lso_status s = ensure_staging(c);
+        lso_status s = ensure_staging(c, max_piece);
         if (s != LSO_OK) return s;
     }
     if (any_norm && c->norm_cap < n) {
@@ -618,7 +691,7 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
         c->dev_norms = nullptr;
         c->norm_cap = 0;
         if (hipMalloc(&c->dev_norms, n * sizeof(double)) != hipSuccess)
-            return lso::fail(LSO_E_NOMEM, "device array of %zu layer norms", n);
+            return lso::fail(LSO_E_NOMEM, "device array of %zu piece norms", n);
         c->norm_cap = n;
     }
     const size_t K = staging_count(c);
@@ -635,16 +708,16 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
     auto record = [&](lso_status s) {
         if (result == LSO_OK) result = s;
     };
-    size_t next_read = 0;     // next layer to stage in
-    size_t next_issue = 0;    // next layer to enqueue on the GPU
-    size_t next_retire = 0;   // next layer whose D2H completion is awaited
-    size_t next_done = 0;     // next layer whose write-out completion is awaited
-    size_t stop_at = n;       // after an error no layer >= stop_at is read or issued
+    size_t next_read = 0;     // next piece to stage in
+    size_t next_issue = 0;    // next piece to enqueue on the GPU
+    size_t next_retire = 0;   // next piece whose D2H completion is awaited
+    size_t next_done = 0;     // next piece whose write-out completion is awaited
+    size_t stop_at = n;       // after an error no piece >= stop_at is read or issued
     bool gpu_ok = true;       // after a failed GPU stage no staged data is written out
     Trace trace(n);
 
     auto read_complete = [&](size_t i) {
-        return J[i].kind == kPinned || rd[i % K].done.load();
+        return units[i].job->kind == kPinned || rd[i % K].done.load();
     };
     auto reads_in_flight = [&] {
         for (size_t i = next_issue; i < next_read; ++i)
@@ -655,21 +728,22 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
         bool progress = false;
         // 1. stage in while a buffer is free
         while (next_read < stop_at && next_read < next_done + K) {
-            const Job& j = J[next_read];
+            const Unit& U = units[next_read];
+            const Job& j = *U.job;
             if (j.kind != kPinned) {
                 IoRequest& r = rd[next_read % K];
                 r.reset();
                 r.direct = false;
-                r.bytes = j.bytes;
+                r.bytes = U.bytes;
                 r.dst = static_cast<char*>(c->staging[next_read % K]);
                 if (j.kind == kFile) {
                     r.op = kIoRead;
                     r.fd = j.fd;
-                    r.foff = j.foff;
+                    r.foff = j.foff + U.off;
                     r.direct = j.direct;
                 } else {
                     r.op = kIoCopy;
-                    r.src = j.host;
+                    r.src = j.host + U.off;
                 }
                 c->reader->submit(&r);
             }
@@ -677,9 +751,10 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
             ++next_read;
             progress = true;
         }
-        // 2. issue staged layers in order
+        // 2. issue staged pieces in order
         while (next_issue < next_read && next_issue < stop_at && read_complete(next_issue)) {
-            const Job& j = J[next_issue];
+            const Unit& U = units[next_issue];
+            const Job& j = *U.job;
             if (j.kind != kPinned) {
                 if (const int e = rd[next_issue % K].err.load()) {
                     record(lso::fail(LSO_E_IO, "layer %zu: reading its %s failed: %s", j.index,
@@ -688,9 +763,9 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
                     break;
                 }
             }
-            void* buf = j.kind == kPinned ? static_cast<void*>(j.host) : c->staging[next_issue % K];
+            void* buf = j.kind == kPinned ? static_cast<void*>(j.host + U.off) : c->staging[next_issue % K];
             trace.mark(trace.issue, next_issue);
-            const lso_status s = issue_layer(c, j, next_issue, buf);
+            const lso_status s = issue_unit(c, U, next_issue, buf);
             if (s != LSO_OK) {
                 record(s);
                 stop_at = next_issue;
@@ -700,9 +775,9 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
             ++next_issue;
             progress = true;
         }
-        // 3. start the write-out of layers whose D2H is complete, one at a
-        //    time in layer order (so a failed write leaves every later
-        //    layer untouched)
+        // 3. start the write-out of pieces whose D2H is complete, one at a
+        //    time in order (so a failed write leaves every later piece
+        //    untouched)
         while (next_retire < next_issue && next_done == next_retire) {
             const hipError_t q = gpu_ok ? hipEventQuery(c->d2h_done[next_retire % K]) : hipSuccess;
             if (q == hipErrorNotReady) break;
@@ -711,21 +786,24 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
                 gpu_ok = false;
                 stop_at = std::min(stop_at, next_issue);
             }
-            const Job& j = J[next_retire];
+            const Unit& U = units[next_retire];
+            const Job& j = *U.job;
             if (j.kind != kPinned && gpu_ok && next_retire < stop_at) {
                 IoRequest& w = wr[next_retire % K];
                 w.reset();
                 w.direct = j.direct;
                 w.sync = false;
                 w.header = nullptr;
-                w.bytes = j.bytes;
+                w.bytes = U.bytes;
                 w.src = static_cast<const char*>(c->staging[next_retire % K]);
                 if (j.kind == kFile) {
                     w.op = kIoWrite;
                     w.fd = j.fd;
-                    w.foff = j.woff;
-                    w.sync = j.sync;
-                    if (j.shadow) {
+                    w.foff = j.woff + U.off;
+                    w.sync = j.sync && U.last;
+                    if (j.shadow && U.last) {
+                        // every earlier piece of the layer is written (write-outs
+                        // run one at a time): flush, then commit the new epoch
                         char* h = headers.get() + (next_retire % K) * kShadowHeaderCopy;
                         lso::shadow_encode(h, j.new_epoch, j.bytes, j.t);
                         w.header = h;
@@ -733,7 +811,7 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
                     }
                 } else {
                     w.op = kIoCopy;
-                    w.dst = j.host;
+                    w.dst = j.host + U.off;
                 }
                 wr_live[next_retire % K] = 1;
                 c->writer->submit(&w);
@@ -742,17 +820,18 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
             ++next_retire;
             progress = true;
         }
-        // 4. free the buffers of layers whose write-out is complete
+        // 4. free the buffers of pieces whose write-out is complete
         while (next_done < next_retire) {
             const size_t b = next_done % K;
             if (wr_live[b]) {
                 if (!wr[b].done.load()) break;
                 wr_live[b] = 0;
                 if (const int e = wr[b].err.load()) {
-                    // this region may be partly written; no later layer is
+                    // this region may be partly written; no later piece is
                     // written back
-                    record(lso::fail(LSO_E_IO, "layer %zu: writing its %s back failed: %s",
-                                     J[next_done].index, io_what(J[next_done]), std::strerror(e)));
+                    const Job& j = *units[next_done].job;
+                    record(lso::fail(LSO_E_IO, "layer %zu: writing its %s back failed: %s", j.index,
+                                     io_what(j), std::strerror(e)));
                     stop_at = std::min(stop_at, next_done + 1);
                 }
             }
@@ -773,13 +852,17 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t n)
         const hipError_t err = hipStreamSynchronize(st);
         if (err != hipSuccess) record(lso::hip_fail(err, "hipStreamSynchronize"));
     }
-    trace.print();
+    trace.print(units);
     if (result == LSO_OK && any_norm) {
         std::vector<double> sq(n);
         const hipError_t err = hipMemcpy(sq.data(), c->dev_norms, n * sizeof(double), hipMemcpyDeviceToHost);
-        if (err != hipSuccess) return lso::hip_fail(err, "hipMemcpy (layer norms)");
-        for (size_t i = 0; i < n; ++i)
-            if (J[i].sq_norm) *J[i].sq_norm = sq[i];
+        if (err != hipSuccess) return lso::hip_fail(err, "hipMemcpy (piece norms)");
+        // a layer's norm: its pieces' sums added in piece order
+        double acc = 0.0;
+        for (size_t i = 0; i < n; ++i) {
+            acc = units[i].first ? sq[i] : acc + sq[i];
+            if (units[i].last && units[i].job->sq_norm) *units[i].job->sq_norm = acc;
+        }
     }
     return result;
 }
@@ -836,6 +919,10 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     if (const char* e = std::getenv("LSO_STREAM_SLOTS")) {
         const int k = std::atoi(e);
         if (k >= 2 && k <= kMaxSlots) c->nslots = k;
+    }
+    if (const char* e = std::getenv("LSO_STREAM_PIECE_BYTES")) {
+        const long long k = std::atoll(e);
+        if (k >= 12ll * LSO_TILE_ELEMS) c->piece_bytes = static_cast<uint64_t>(k);
     }
     c->nstaging = c->nslots + 1;
     if (const char* e = std::getenv("LSO_STREAM_STAGING")) {

@@ -2,7 +2,9 @@
 and the parity measures.  Test infrastructure only."""
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import os
 import sys
 
 import numpy as np
@@ -336,3 +338,18 @@ def synth_stream(sizes, sid, max_bytes=None):
     mb = max_bytes or max(configs.host_layer_layout(n)[3] for n in sizes)
     ls = lso.LayerStream(mb, max(sizes), fn, ctypes.addressof(params))
     return ls, params
+
+
+@contextlib.contextmanager
+def stream_pieces(tiles: int):
+    """Layer streams created inside move tiled layers in pieces of `tiles`
+    state tiles (LSO_STREAM_PIECE_BYTES, read at context creation)."""
+    old = os.environ.get("LSO_STREAM_PIECE_BYTES")
+    os.environ["LSO_STREAM_PIECE_BYTES"] = str(tiles * 12 * TILE)
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["LSO_STREAM_PIECE_BYTES"]
+        else:
+            os.environ["LSO_STREAM_PIECE_BYTES"] = old

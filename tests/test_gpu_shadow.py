@@ -16,7 +16,7 @@ import layer_streamed_optimizer_amd as lso
 from layer_streamed_optimizer_amd import configs
 from layer_streamed_optimizer_amd.disk import LayerFiles
 
-from gpu_util import B1, B2, EPS, LR, HostLayers, log, synth_stream, torch
+from gpu_util import B1, B2, EPS, LR, HostLayers, log, stream_pieces, synth_stream, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +30,9 @@ def shadow_like(host, directory, direct=False):
     return f
 
 
-@pytest.mark.parametrize("tiled", [False, True], ids=["planar", "tiled"])
-def test_shadow_files_equal_plain_files_bitwise(tiled):
+@pytest.mark.parametrize("tiled,pieces", [(False, 0), (True, 0), (True, 3)],
+                         ids=["planar", "tiled", "tiled_in_pieces"])
+def test_shadow_files_equal_plain_files_bitwise(tiled, pieces):
     T = torch()
     sizes = [100003, 4096 * 3 + 7, 65536, 1]
     sid = 90
@@ -42,7 +43,11 @@ def test_shadow_files_equal_plain_files_bitwise(tiled):
         for b in range(len(sizes)):
             plain.write_block(b, host.raw(b))
         shadow = shadow_like(host, os.path.join(d, "s"), direct=True)
-        ls, params = synth_stream(sizes, sid, max_bytes=mb)
+        if pieces:
+            with stream_pieces(pieces):
+                ls, params = synth_stream(sizes, sid, max_bytes=mb)
+        else:
+            ls, params = synth_stream(sizes, sid, max_bytes=mb)
         for t in (1, 2, 3):
             params.step = t
             ls.stream_files(plain.table(t, LR, B1, B2, EPS))

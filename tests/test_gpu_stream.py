@@ -11,8 +11,8 @@ import oracle
 import synth
 from layer_streamed_optimizer_amd import configs
 
-from gpu_util import (HIP_D2D, HostLayers, assert_parity, call_scale, hip, log, synth_stream,
-                      torch)
+from gpu_util import (HIP_D2D, HostLayers, assert_parity, call_scale, hip, log, stream_pieces,
+                      synth_stream, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -241,3 +241,38 @@ def test_stream_tiled_layers_match_planar_bitwise_and_oracle():
             assert np.array_equal(got[q].view(np.uint32), tpg.get(b, q).view(np.uint32)), (b, q)
         assert_parity(got, ref[b], 1e-6, f"tiled streamed layer {b}", scale)
     ls.close()
+
+
+@pytest.mark.parametrize("pageable", [False, True], ids=["pinned", "pageable"])
+def test_layers_moved_in_pieces_equal_whole_layers_bitwise(pageable):
+    """Tiled layers cut into pieces of two tiles (ragged last pieces, a layer
+    smaller than a piece) give the bits of whole-layer moves: state, BF16
+    weights, and gradient norms within 1e-12."""
+    T = torch()
+    sizes = [100003, 8192 * 7 + 1, 5, 65536 + 8191]
+    sid = 47
+    whole = HostLayers(sizes, sid, tiled=True)
+    piece = HostLayers(sizes, sid, tiled=True, pageable=pageable)
+    mb = max(configs.host_layer_layout(n, tiled=True)[3] for n in sizes)
+    ls_a, pa = synth_stream(sizes, sid, max_bytes=mb)
+    with stream_pieces(2):
+        ls_b, pb = synth_stream(sizes, sid, max_bytes=mb)
+    wa = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
+    wb = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
+    na, nb = np.zeros(len(sizes)), np.zeros(len(sizes))
+    for t in range(1, 4):
+        pa.step = pb.step = t
+        log("pieces step", t)
+        La = whole.table(t, dev_weight=[int(w.data_ptr()) for w in wa])
+        Lb = piece.table(t, dev_weight=[int(w.data_ptr()) for w in wb])
+        La["sq_norm"] = [na.ctypes.data + 8 * i for i in range(len(sizes))]
+        Lb["sq_norm"] = [nb.ctypes.data + 8 * i for i in range(len(sizes))]
+        ls_a.stream_layers(La)
+        ls_b.stream_layers(Lb)
+        np.testing.assert_allclose(nb, na, rtol=1e-12)
+    T.cuda.synchronize()
+    for b in range(len(sizes)):
+        assert np.array_equal(whole.raw(b), piece.raw(b)), b
+        assert np.array_equal(wa[b].cpu().numpy(), wb[b].cpu().numpy()), b
+    ls_a.close()
+    ls_b.close()
