@@ -4,7 +4,7 @@
     python -m layer_streamed_optimizer_amd.rocprof_summary pmc    --fetch F.csv --write W.csv --params N \
             --copy-bytes B --command-fetch "..." --command-write "..."
     python -m layer_streamed_optimizer_amd.rocprof_summary stream --trace X_kernel_trace.csv --layers L \
-            --layer-bytes B --command "..."
+            --copies C --step-bytes B --command "..."
 
 pmc: FETCH_SIZE and WRITE_SIZE are KiB per dispatch.  Each is scaled by
 what the same counter reads for the plain copy kernel of known size (it
@@ -110,28 +110,30 @@ def stream(args) -> str:
     for r in copies:
         by_q.setdefault(r["Queue_Id"], []).append(r)
     out = [f"# rocprofv3 trace of the layer stream: {args.title}", "", f"Command: `{args.command}`", ""]
-    # the last step: the last `layers` copies of each direction
+    # the last step: the last `copies` copies of each direction (one per
+    # piece; a layer that does not move in pieces is one piece)
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
     out += ["| Stage | Queue | Count (last step) | Mean (ms) | Min (ms) | Max (ms) | GB/s at mean |",
             "|---|---|---|---|---|---|---|"]
+    per_copy = args.step_bytes / args.copies
     for q, rs in sorted(by_q.items()):
-        last = rs[-args.layers:]
+        last = rs[-args.copies:]
         d = [dur(r) for r in last]
-        out.append(f"| layer copy | {q} | {len(last)} | {statistics.mean(d):.1f} | {min(d):.1f} | "
-                   f"{max(d):.1f} | {args.layer_bytes / (statistics.mean(d) * 1e-3) / 1e9:.1f} |")
-    for name, rs in (("gradient producer", grads), ("fused update", upd)):
-        last = rs[-args.layers:]
+        out.append(f"| piece copy | {q} | {len(last)} | {statistics.mean(d):.1f} | {min(d):.1f} | "
+                   f"{max(d):.1f} | {per_copy / (statistics.mean(d) * 1e-3) / 1e9:.1f} |")
+    for name, rs, cnt in (("gradient producer", grads, args.layers), ("fused update", upd, args.copies)):
+        last = rs[-cnt:]
         if last:
             d = [dur(r) for r in last]
             out.append(f"| {name} | {last[0]['Queue_Id']} | {len(last)} | {statistics.mean(d):.1f} | "
                        f"{min(d):.1f} | {max(d):.1f} | - |")
     # hidden compute: time the update/producer run with no copy in flight
-    last_copies = [r for rs in by_q.values() for r in rs[-args.layers:]]
+    last_copies = [r for rs in by_q.values() for r in rs[-args.copies:]]
     t_lo = min(int(r["Start_Timestamp"]) for r in last_copies)
     t_hi = max(int(r["End_Timestamp"]) for r in last_copies)
     busy = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in last_copies)
     exposed = 0
-    for r in upd[-args.layers:] + grads[-args.layers:]:
+    for r in upd[-args.copies:] + grads[-args.layers:]:
         s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
         # length of [s, e) covered by the union of the copy intervals
         covered, cur = 0, s
@@ -168,7 +170,8 @@ def main(argv=None):
     c = sub.add_parser("stream")
     c.add_argument("--trace", required=True)
     c.add_argument("--layers", type=int, required=True)
-    c.add_argument("--layer-bytes", type=int, required=True)
+    c.add_argument("--copies", type=int, required=True, help="copies per direction per step")
+    c.add_argument("--step-bytes", type=int, required=True, help="bytes per direction per step")
     c.add_argument("--command", required=True)
     c.add_argument("--title", default="")
     args = ap.parse_args(argv)
