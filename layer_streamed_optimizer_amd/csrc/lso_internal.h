@@ -19,7 +19,7 @@ constexpr int kUnrollSmall = 1;
 constexpr int kUnrollTiled = 1;   // a tile's 8192 elements over 8 workgroups
 constexpr uint64_t kSmallCallElems = 32ull << 20;   // below this, kUnrollSmall
 constexpr uint64_t kMaxGrid = 1ull << 24;            // workgroups per launch
-constexpr uint64_t kMaxIndexChunks = 1ull << 24;     // per-chunk block index up to this
+constexpr uint64_t kMaxIndexChunks = 1ull << 22;     // per-chunk block index up to this
 
 constexpr uint64_t chunk_elems(int unroll) { return static_cast<uint64_t>(kThreads) * kQuad * unroll; }
 constexpr uint64_t kNormPartsPerChunk = kThreads / 64;   // one FP64 per wave
