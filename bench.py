@@ -328,7 +328,7 @@ def streamed(args, w):
     progress(f"link: {peak}")
     pinned = args.host_memory == "pinned"
     progress(f"{w.key}: {n_layers} x {nbytes / 1e9:.2f} GB host blocks, "
-             f"{'pinned' if pinned else 'pageable (staged through two pinned buffers)'}")
+             f"{'pinned' if pinned else 'pageable (staged through pinned buffers)'}")
     hosts, ptrs = [], []
     hs = torch.cuda.current_stream().cuda_stream
     stage = torch.empty(nbytes, dtype=torch.uint8, device="cuda")

@@ -1,12 +1,15 @@
 /*
  * lso.h -- C ABI of the layer-streamed mixed-precision Adam library (gfx950).
  *
- * One operation, two ways of feeding it:
+ * One operation, three ways of feeding it:
  *   lso_adam_step      updates blocks that already live in device memory
- *                      (HBM-resident state), one kernel launch per call;
+ *                      (HBM-resident state), one kernel launch per call
+ *                      (lso_adam_step_norms: plus per-block gradient norms);
  *   lso_stream_layers  updates layers whose authoritative state lives in
  *                      host memory, streaming each layer in, updating it on
- *                      the GPU and writing it back, double-buffered.
+ *                      the GPU and writing it back, double-buffered;
+ *   lso_stream_files   the same for layers held in files (the disk tier),
+ *                      optionally crash-consistent (LSO_FILE_SHADOW).
  *
  * The update, per element i of a block (all arithmetic below is what the
  * library computes; the pages define it in exact arithmetic):

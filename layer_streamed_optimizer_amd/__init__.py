@@ -5,12 +5,13 @@ A thin binding over liblso.so (include/lso.h): it marshals descriptor tables
 and stream handles; every step of the update runs in the HIP library.
 PyTorch, where used, only provides device memory and streams.
 
-    table = BlockTable.from_arrays([...])     # one row per block
+    table = BlockTable.from_rows([...])       # one dict per block
     table.set_step(t)                         # the caller owns t
     adam_step(table, stream)                  # one kernel launch
 
     ls = LayerStream(max_layer_bytes, max_layer_params, grad_fn, user)
     ls.stream_layers(host_layers)             # H2D / update / D2H, double-buffered
+    ls.stream_files(file_layers)              # the disk tier (see disk.LayerFiles)
 """
 from __future__ import annotations
 
