@@ -6,9 +6,11 @@
 // has queued; the DMA engines reach the same rate in one direction but, in
 // a process with several other streams, the host-to-device and
 // device-to-host copies end up sharing an engine and the second direction
-// drops to about half.  One 16-byte vector per lane and iteration; 128
-// workgroups keep the link busy -- more keep so many long-latency host
-// reads queued that the update kernel running beside them slows down.
+// drops to about half.  The stream therefore runs its D2H copies here and
+// leaves the H2D direction to a DMA engine (or runs both here on request).
+// One 16-byte vector per lane and iteration; 128 workgroups keep the link
+// busy -- more keep so many long-latency host reads queued that the update
+// kernel running beside them slows down.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
