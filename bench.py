@@ -338,19 +338,22 @@ def link_peak(nbytes=4 << 30):
     """Host-link GB/s with page-locked buffers, measured by the probe
     library on its own two streams: each direction alone, and each direction
     while both run at once -- with the DMA engines and with copy kernels
-    (the engine the layer stream uses).  The streamed roofline takes the
-    best concurrent figure, per direction."""
+    (the engine the layer stream uses) -- with the DMA engines, with copy
+    kernels, and with a DMA engine for H2D beside a copy kernel for D2H (the
+    layer stream's default).  The streamed roofline takes the best
+    concurrent figure of the slower direction over the three."""
     from layer_streamed_optimizer_amd import _native
     P = _native.probes()
     res = {}
-    for name, mode in (("dma", 0), ("kernel", 3)):
+    # mode bit 0: H2D by a copy kernel; bit 1: D2H by a copy kernel
+    for name, mode in (("dma", 0), ("kernel", 3), ("dma_h2d_kernel_d2h", 2)):
         out = (ctypes.c_double * 4)()
         rc = P.lso_probe_link_mode(nbytes, 3, mode, 128, out)
         if rc != 0:
             raise RuntimeError(f"lso_probe_link_mode failed ({rc})")
         res[name] = dict(h2d=out[0], d2h=out[1], bidir_h2d=out[2], bidir_d2h=out[3])
     res["bidir_per_direction"] = max(min(r["bidir_h2d"], r["bidir_d2h"])
-                                     for r in (res["dma"], res["kernel"]))
+                                     for r in (res["dma"], res["kernel"], res["dma_h2d_kernel_d2h"]))
     return res
 
 

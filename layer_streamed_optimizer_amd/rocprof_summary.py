@@ -108,12 +108,20 @@ def stream(args) -> str:
     grads = [r for r in rows if "fill_normal_bf16" in r["Kernel_Name"]]
     by_q = {}
     for r in copies:
-        by_q.setdefault(r["Queue_Id"], []).append(r)
+        by_q.setdefault(f"copy kernel, queue {r['Queue_Id']}", []).append(r)
+    if args.memcpy:
+        # DMA-engine copies of at least a piece (the bench's set-up copies are
+        # chunked by the runtime into much smaller ones)
+        for r in csv.DictReader(open(args.memcpy)):
+            if (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) > 1_000_000:
+                by_q.setdefault(f"DMA {r['Direction'].replace('MEMORY_COPY_', '').lower()}", []).append(r)
+        for v in by_q.values():
+            v.sort(key=lambda r: int(r["Start_Timestamp"]))
     out = [f"# rocprofv3 trace of the layer stream: {args.title}", "", f"Command: `{args.command}`", ""]
     # the last step: the last `copies` copies of each direction (one per
     # piece; a layer that does not move in pieces is one piece)
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
-    out += ["| Stage | Queue | Count (last step) | Mean (ms) | Min (ms) | Max (ms) | GB/s at mean |",
+    out += ["| Stage | Engine | Count (last step) | Mean (ms) | Min (ms) | Max (ms) | GB/s at mean |",
             "|---|---|---|---|---|---|---|"]
     per_copy = args.step_bytes / args.copies
     for q, rs in sorted(by_q.items()):
@@ -171,6 +179,7 @@ def main(argv=None):
     c.add_argument("--trace", required=True)
     c.add_argument("--layers", type=int, required=True)
     c.add_argument("--copies", type=int, required=True, help="copies per direction per step")
+    c.add_argument("--memcpy", default=None, help="X_memory_copy_trace.csv (DMA-engine copies)")
     c.add_argument("--step-bytes", type=int, required=True, help="bytes per direction per step")
     c.add_argument("--command", required=True)
     c.add_argument("--title", default="")
