@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Gparams/s Adam step; % HBM peak (resident) / % host-link peak (streamed)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BYTES_PER_PARAM = {"bf16": 28, "f32": 30}   # algorithmic, resident kernel, by gradient dtype
+REPEATS = 20                    # timed-region repeats for the launch-bound workloads
 LINK_BYTES_PER_PARAM = 12       # streamed: [master | m | v] each way
 
 
@@ -228,7 +229,7 @@ def resident(args, w):
             lso.adam_step(tab, hs)
 
     K = args.steps
-    ev = HipEvents(2 * K)            # start of step k: 2k, end: 2k + 1
+    ev = HipEvents(max(2 * K, 2 * REPEATS))   # start of step k: 2k, end: 2k + 1
     rec = ev.record
     cold = None
     for j in range(1, args.warmup + 1):
@@ -262,6 +263,21 @@ def resident(args, w):
         rec(ev.ev[2 * k + 1], hs)
     torch.cuda.synchronize()
     kernel_ms = [ev.ms(2 * k, 2 * k + 1) for k in range(K)]
+    j_next = args.warmup + 2 * K + 1
+    repeats = None
+    if w.key in ("c0", "c2"):
+        # launch-latency-bound steps: the timed region again, REPEATS times,
+        # and the median of its per-step time
+        for r in range(REPEATS):
+            rec(ev.ev[2 * r], hs)
+            for k in range(K):
+                step(j_next)
+                j_next += 1
+            rec(ev.ev[2 * r + 1], hs)
+        torch.cuda.synchronize()
+        per = sorted(ev.ms(2 * r, 2 * r + 1) / K for r in range(REPEATS))
+        repeats = dict(regions=REPEATS, steps_each=K, median_us_per_step=per[REPEATS // 2] * 1e3,
+                       min_us_per_step=per[0] * 1e3, max_us_per_step=per[-1] * 1e3)
     flushed = None
     if w.key in ("c0", "c2"):
         # these fit the 256 MB last-level cache: time the same steps again
@@ -270,7 +286,8 @@ def resident(args, w):
         for k in range(K):
             synth.device_fill_zero(int(scratch_mall.data_ptr()), 512 << 20, hs)
             rec(ev.ev[2 * k], hs)
-            step(args.warmup + 2 * K + 1 + k)
+            step(j_next)
+            j_next += 1
             rec(ev.ev[2 * k + 1], hs)
         torch.cuda.synchronize()
         fl_ms = sorted(ev.ms(2 * k, 2 * k + 1) for k in range(K))
@@ -284,8 +301,9 @@ def resident(args, w):
     grads.clear()
     torch.cuda.empty_cache()
     ceiling = copy_ceiling(torch, dev)
+    shaped = shaped_ceiling(torch, dev, tiled)
     progress(f"steps: wall {wall * 1e3:.3f} ms for {args.steps}; kernel avg {avg_ms * 1e3:.1f} us; "
-             f"{achieved:.0f} GB/s; copy ceiling {ceiling:.0f} GB/s")
+             f"{achieved:.0f} GB/s; copy ceiling {ceiling:.0f} GB/s; update-shaped copy {shaped:.0f} GB/s")
     traffic = measured_traffic(w.key, args.grad_dtype, args.norms)
     result = dict(
         metric=METRIC, value=params * args.steps / wall / 1e9, unit="Gparams/s",
@@ -297,6 +315,7 @@ def resident(args, w):
         kernel_median_us=sorted(kernel_ms)[len(kernel_ms) // 2] * 1e3,
         kernel_first_step_us=cold * 1e3 if cold is not None else None,
         hbm_copy_ceiling_GBps=ceiling,
+        hbm_update_shaped_copy_GBps=shaped,
         config=dict(workload=f"{w.key}: {w.title}", blocks=len(sizes), params=params,
                     state_layout=args.layout, grad_dtype=args.grad_dtype, bytes_per_param=bpp,
                     gradient_norms=bool(args.norms),
@@ -304,6 +323,8 @@ def resident(args, w):
                     hyper=dict(lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2,
                                eps=configs.EPS)),
     )
+    if repeats:
+        result["region_repeats"] = repeats
     if flushed:
         result["cache_flushed"] = flushed
     del state, weight, grads, scratch
@@ -332,16 +353,41 @@ def copy_ceiling(torch, dev, nbytes=8 << 30) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def shaped_ceiling(torch, dev, tiled: bool, n: int = 134_283 * 8192) -> float:
+    """GB/s of the update's own traffic shape with no arithmetic: 14 bytes
+    read and 14 written per element, in the same state layout and one
+    1,024-element chunk per workgroup.  1.1 G elements (31 GB a pass), not a
+    power of two, so the planar arrays do not sit a power of two apart."""
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    state = torch.zeros(12 * n, dtype=torch.uint8, device=dev)
+    grad = torch.zeros(2 * n, dtype=torch.uint8, device=dev)
+    weight = torch.empty(2 * n, dtype=torch.uint8, device=dev)
+    hs = torch.cuda.current_stream().cuda_stream
+    args = (state.data_ptr(), grad.data_ptr(), weight.data_ptr(), n, int(tiled), hs)
+    for _ in range(2):
+        assert P.lso_probe_copy_shaped(*args) == 0
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    reps = 5
+    for _ in range(reps):
+        assert P.lso_probe_copy_shaped(*args) == 0
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del state, grad, weight
+    return 28 * n / (ms * 1e-3) / 1e9
+
+
 # ------------------------------------------------------------ streamed path
 
 def link_peak(nbytes=4 << 30):
     """Host-link GB/s with page-locked buffers, measured by the probe
     library on its own two streams: each direction alone, and each direction
-    while both run at once -- with the DMA engines and with copy kernels
-    (the engine the layer stream uses) -- with the DMA engines, with copy
-    kernels, and with a DMA engine for H2D beside a copy kernel for D2H (the
-    layer stream's default).  The streamed roofline takes the best
-    concurrent figure of the slower direction over the three."""
+    while both run at once -- with the DMA engines, with copy kernels, and
+    with a DMA engine for H2D beside a copy kernel for D2H (the layer
+    stream's default).  The streamed roofline takes the best concurrent
+    figure of the slower direction over the three."""
     from layer_streamed_optimizer_amd import _native
     P = _native.probes()
     res = {}

@@ -164,6 +164,8 @@ def probes():
         vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
         P.lso_probe_copy.argtypes = [vp, vp, u64, ctypes.c_uint, vp]
         P.lso_probe_copy.restype = ctypes.c_int
+        P.lso_probe_copy_shaped.argtypes = [vp, vp, vp, u64, ctypes.c_int, vp]
+        P.lso_probe_copy_shaped.restype = ctypes.c_int
         P.lso_probe_bf16_rne.argtypes = [u32, u64, vp, vp]
         P.lso_probe_bf16_rne.restype = ctypes.c_int
         P.lso_probe_link.argtypes = [u64, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]

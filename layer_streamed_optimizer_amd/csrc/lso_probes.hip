@@ -3,6 +3,11 @@
 //  lso_probe_copy      plain 16-byte-vector device copy: the HBM ceiling a
 //                      read+write stream reaches, and the reference for
 //                      scaling the FETCH_SIZE / WRITE_SIZE counters.
+//  lso_probe_copy_shaped  the update's memory access pattern with no
+//                      arithmetic: per element 2 + 12 bytes read, 12 + 2
+//                      written, in the planar or tiled state layout, one
+//                      1,024-element chunk per workgroup -- the ceiling of
+//                      the update's own traffic shape.
 //  lso_probe_bf16_rne  the fused kernel's BF16 rounding applied to a range
 //                      of FP32 bit patterns, so a test can compare it with
 //                      the host definition over all 2^32 patterns.
@@ -42,6 +47,56 @@ link_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_
         dst[i] = src[i];
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const LSO_GLOBAL T*>(reinterpret_cast<uintptr_t>(p)));
+}
+
+template <typename T>
+__device__ __forceinline__ void st_nt(void* p, T v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<LSO_GLOBAL T*>(reinterpret_cast<uintptr_t>(p)));
+}
+
+constexpr uint32_t kShapedChunk = 1024;   // elements per workgroup: 256 lanes x 4
+constexpr uint32_t kShapedTile = 8192;    // elements per state tile
+
+// Each lane reads four BF16 "gradients" and four FP32 each of master, m and
+// v, and writes the three FP32 quads back in place (bits mixed so nothing
+// is a no-op) and four BF16 "weights".
+template <bool kTiled>
+__global__ void __launch_bounds__(256)
+shaped_copy_kernel(float* __restrict__ state, const uint16_t* __restrict__ grad,
+                   uint16_t* __restrict__ weight, uint64_t n)
+{
+    const uint64_t e0 = static_cast<uint64_t>(blockIdx.x) * kShapedChunk;
+    float *p, *m, *v;
+    if (kTiled) {
+        p = state + 3 * (e0 / kShapedTile) * kShapedTile + e0 % kShapedTile;
+        m = p + kShapedTile;
+        v = m + kShapedTile;
+    } else {
+        p = state + e0;
+        m = state + n + e0;
+        v = state + 2 * n + e0;
+    }
+    const uint32_t i = threadIdx.x * 4;
+    const u32x2 g = ld_nt<u32x2>(grad + e0 + i);
+    f32x4 a = ld_nt<f32x4>(p + i), b = ld_nt<f32x4>(m + i), c = ld_nt<f32x4>(v + i);
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    u32x4v ai = __builtin_bit_cast(u32x4v, a) ^ g.x, bi = __builtin_bit_cast(u32x4v, b) ^ g.y;
+    u32x4v ci = __builtin_bit_cast(u32x4v, c) ^ (g.x + g.y);
+    st_nt<f32x4>(p + i, __builtin_bit_cast(f32x4, ai));
+    st_nt<f32x4>(m + i, __builtin_bit_cast(f32x4, bi));
+    st_nt<f32x4>(v + i, __builtin_bit_cast(f32x4, ci));
+    const u32x2 w = {(ai.x >> 16) | (ai.y & 0xFFFF0000u), (ai.z >> 16) | (ai.w & 0xFFFF0000u)};
+    st_nt<u32x2>(weight + e0 + i, w);
+}
+
 __global__ void __launch_bounds__(256)
 bf16_probe_kernel(uint32_t first, uint64_t count, uint16_t* __restrict__ out)
 {
@@ -71,6 +126,31 @@ int lso_probe_copy(const void* src, void* dst, uint64_t bytes, unsigned grid, vo
     }
     hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+    return static_cast<int>(hipGetLastError());
+}
+
+// The update's traffic shape with no arithmetic, over n elements (a
+// multiple of 8192, at most 2^34): state is 12n bytes (planar: master, m,
+// v arrays of n FP32 back to back; tiled: 8192-element [master|m|v] tiles),
+// grad and weight n BF16 each; all 16-byte aligned.  State and weight are
+// overwritten with mixed bits.  Returns a hipError_t.
+int lso_probe_copy_shaped(void* state, const void* grad, void* weight, uint64_t n, int tiled, void* stream)
+{
+    if (n % kShapedTile != 0 || n > (uint64_t(1) << 34) || !state || !grad || !weight ||
+        reinterpret_cast<uintptr_t>(state) % 16 != 0 || reinterpret_cast<uintptr_t>(grad) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(weight) % 16 != 0)
+        return static_cast<int>(hipErrorInvalidValue);
+    if (n == 0) return 0;
+    const dim3 grid(static_cast<unsigned>(n / kShapedChunk));
+    auto* st = static_cast<float*>(state);
+    auto* g = static_cast<const uint16_t*>(grad);
+    auto* w = static_cast<uint16_t*>(weight);
+    if (tiled)
+        hipLaunchKernelGGL(shaped_copy_kernel<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           st, g, w, n);
+    else
+        hipLaunchKernelGGL(shaped_copy_kernel<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           st, g, w, n);
     return static_cast<int>(hipGetLastError());
 }
 
