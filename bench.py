@@ -383,14 +383,20 @@ def shaped_ceiling(torch, dev, tiled: bool, n: int = 134_283 * 8192) -> float:
 
 def link_peak(nbytes=4 << 30):
     """Host-link GB/s with page-locked buffers, measured by the probe
-    library on its own two streams: each direction alone, and each direction
-    while both run at once -- with the DMA engines, with copy kernels, and
-    with a DMA engine for H2D beside a copy kernel for D2H (the layer
-    stream's default).  The streamed roofline takes the best concurrent
-    figure of the slower direction over the three."""
+    library: each direction alone, and each direction while both run at
+    once -- on the two SDMA engines the layer stream names (its default),
+    with runtime-chosen DMA engines, with copy kernels, and with a DMA engine
+    for H2D beside a copy kernel for D2H.  The streamed roofline takes the
+    best concurrent figure of the slower direction over them."""
     from layer_streamed_optimizer_amd import _native
     P = _native.probes()
     res = {}
+    eng = (ctypes.c_uint32 * 2)()
+    out = (ctypes.c_double * 4)()
+    rc = P.lso_probe_link_sdma(nbytes, 3, eng, out)
+    if rc == 0:
+        res["sdma_pair"] = dict(h2d=out[0], d2h=out[1], bidir_h2d=out[2], bidir_d2h=out[3],
+                                engines=[int(eng[0]), int(eng[1])])
     # mode bit 0: H2D by a copy kernel; bit 1: D2H by a copy kernel
     for name, mode in (("dma", 0), ("kernel", 3), ("dma_h2d_kernel_d2h", 2)):
         out = (ctypes.c_double * 4)()
@@ -398,8 +404,7 @@ def link_peak(nbytes=4 << 30):
         if rc != 0:
             raise RuntimeError(f"lso_probe_link_mode failed ({rc})")
         res[name] = dict(h2d=out[0], d2h=out[1], bidir_h2d=out[2], bidir_d2h=out[3])
-    res["bidir_per_direction"] = max(min(r["bidir_h2d"], r["bidir_d2h"])
-                                     for r in (res["dma"], res["kernel"], res["dma_h2d_kernel_d2h"]))
+    res["bidir_per_direction"] = max(min(r["bidir_h2d"], r["bidir_d2h"]) for r in res.values())
     return res
 
 
@@ -476,6 +481,7 @@ def streamed(args, w):
         progress(f"step {j}: {dt:.3f} s")
         if j > args.warmup:
             step_s.append(dt)
+    copy_mode = ls.copy_mode()
     ls.close()
     wall = sum(step_s)
     params = n * n_layers
@@ -491,7 +497,7 @@ def streamed(args, w):
                     params=params, host_memory="pinned" if pinned else "pageable+staged",
                     state_layout=args.layout,
                     host_bytes=nbytes * n_layers,
-                    link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
+                    link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode),
     )
     for hb in hosts:
         if pinned:
@@ -592,6 +598,7 @@ def streamed_files(args, w):
             progress(f"step {j}: {dt:.3f} s")
             if j > args.warmup:
                 step_s.append(dt)
+        copy_mode = ls.copy_mode()
         ls.close()
         files.close()
     finally:
@@ -612,7 +619,7 @@ def streamed_files(args, w):
                     host_memory="file (O_DIRECT, one preallocated file per layer"
                                 + (", shadow region)" if args.shadow else ")"),
                     state_layout=args.layout, file_bytes=nbytes * n_layers,
-                    storage_bytes_per_param_each_way=LINK_BYTES_PER_PARAM),
+                    storage_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode),
     )
 
 

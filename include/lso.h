@@ -257,10 +257,11 @@ typedef struct lso_stream_ctx lso_stream_ctx;
 
 /* Create a streaming context on `device`: three streams, two device slots
  * of max_layer_bytes (rounded up to 4 KB) of state plus max_layer_params
- * BF16 gradients and BF16 weights each, and the events (the three pinned
- * staging buffers of that size and the worker threads are added on the
- * first staged layer).  fn/user: the gradient producer.  Errors: INVALID,
- * NOMEM, HIP.  *out is NULL on error. */
+ * BF16 gradients and BF16 weights each, the events, and the copy mode (see
+ * lso_stream_copy_mode; the three pinned staging buffers of that size and
+ * the worker threads are added on the first staged layer).  fn/user: the
+ * gradient producer.  Errors: INVALID, NOMEM, HIP.  *out is NULL on
+ * error. */
 lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params,
                              lso_grad_fn fn, void* user, int device, lso_stream_ctx** out);
 
@@ -270,8 +271,9 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
  * (as lso_adam_step_norms).  A layer with n == 0 is skipped entirely -- no
  * transfer, no producer call, no update, no write-back, no checks of its
  * other fields -- which is how a locked layer is passed; the producer is
- * still called with the layer's position in host_blocks.  On LSO_E_CALLBACK at layer k, layers < k are fully written back
- * and layers >= k are untouched on the host.  Validation (bytes, alignment,
+ * still called with the layer's position in host_blocks.  On
+ * LSO_E_CALLBACK at layer k, layers < k are fully written back and layers
+ * >= k are untouched on the host.  Validation (bytes, alignment,
  * hyper-parameters, blocks of different layers not overlapping) covers all
  * layers before anything is enqueued.  Calls on one context must not
  * overlap (one caller thread at a time). */
@@ -369,6 +371,24 @@ lso_status lso_shadow_commit(int fd, uint64_t file_offset, uint64_t bytes, uint6
 /* Device address of slot s's BF16 weight buffer (s = layer index % 2 of
  * the most recent lso_stream_layers call), or NULL. */
 void* lso_stream_slot_weight(lso_stream_ctx* ctx, int slot);
+
+/* How a context moves blocks over the host link (each piece is one burst,
+ * as the MegaTrain summary's section on streaming execution describes).
+ * SDMA engines come in pairs sharing a path to the link: with both
+ * directions busy, H2D on one engine of a pair and D2H on its partner is
+ * the fastest split measured; two directions on one engine take turns. */
+#define LSO_COPY_SDMA_PAIR 0   /* both directions on DMA engines the library names (default) */
+#define LSO_COPY_DMA_IN    1   /* H2D on a DMA engine the runtime picks, D2H by a copy kernel
+                                  (default when the engines cannot be named) */
+#define LSO_COPY_KERNELS   2   /* copy kernels both ways */
+#define LSO_COPY_DMA       3   /* DMA engines the runtime picks, both ways */
+
+/* The context's copy mode, an LSO_COPY_* code (LSO_STREAM_COPY=sdma-pair,
+ * dma-in, kernel or dma at lso_stream_create asks for one; LSO_STREAM_SDMA
+ * = "h,d" names the two engines by number), and with LSO_COPY_SDMA_PAIR
+ * the engine of each direction as a one-bit mask (engine k = bit k), else
+ * 0.  Either pointer may be NULL.  Returns -1 if ctx is NULL. */
+int lso_stream_copy_mode(const lso_stream_ctx* ctx, uint32_t* h2d_engine, uint32_t* d2h_engine);
 
 /* Waits for outstanding work, frees slots, events and streams. */
 lso_status lso_stream_destroy(lso_stream_ctx* ctx);

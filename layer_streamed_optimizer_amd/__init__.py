@@ -288,6 +288,14 @@ class LayerStream:
     def slot_weight(self, slot: int) -> int:
         return int(_native.lib().lso_stream_slot_weight(self.ctx, slot) or 0)
 
+    def copy_mode(self) -> dict:
+        """lso_stream_copy_mode: how the context moves blocks over the link
+        (name and code), and the SDMA engine masks in the sdma-pair mode."""
+        h, d = ctypes.c_uint32(), ctypes.c_uint32()
+        code = _native.lib().lso_stream_copy_mode(self.ctx, ctypes.byref(h), ctypes.byref(d))
+        return dict(mode=_native.COPY_MODE_NAMES.get(code, code), code=code, h2d_engine=h.value,
+                    d2h_engine=d.value)
+
     def close(self) -> None:
         if self.ctx:
             _native.lib().lso_stream_destroy(self.ctx)

@@ -20,6 +20,9 @@ LSO_TILE_ELEMS = 8192
 LSO_FILE_SYNC = 1
 LSO_FILE_SHADOW = 2
 LSO_SHADOW_HEADER_BYTES = 8192
+LSO_COPY_SDMA_PAIR, LSO_COPY_DMA_IN, LSO_COPY_KERNELS, LSO_COPY_DMA = 0, 1, 2, 3
+COPY_MODE_NAMES = {LSO_COPY_SDMA_PAIR: "sdma-pair", LSO_COPY_DMA_IN: "dma-in", LSO_COPY_KERNELS: "kernel",
+                   LSO_COPY_DMA: "dma"}
 
 STATUS_NAMES = {0: "LSO_OK", 1: "LSO_E_INVALID", 2: "LSO_E_ALIGN", 3: "LSO_E_DTYPE",
                 4: "LSO_E_OVERLAP", 5: "LSO_E_NOMEM", 6: "LSO_E_HIP", 7: "LSO_E_CALLBACK",
@@ -96,8 +99,8 @@ GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctype
 EXPORTS = ("lso_adam_step", "lso_norm_workspace_bytes", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants", "lso_tiled_state_bytes",
            "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
            "lso_stream_files", "lso_shadow_format", "lso_shadow_state", "lso_shadow_commit",
-           "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc", "lso_host_free",
-           "lso_status_string", "lso_last_error")
+           "lso_stream_copy_mode", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc",
+           "lso_host_free", "lso_status_string", "lso_last_error")
 
 _lib = None
 _probes = None
@@ -136,6 +139,8 @@ def lib():
         L.lso_shadow_state.argtypes = [i32, u64, u64, ctypes.POINTER(u64), ctypes.POINTER(u64),
                                        ctypes.POINTER(u64)]
         L.lso_shadow_commit.argtypes = [i32, u64, u64, u64, u64]
+        L.lso_stream_copy_mode.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
+        L.lso_stream_copy_mode.restype = i32
         L.lso_stream_slot_weight.argtypes = [vp, i32]
         L.lso_stream_slot_weight.restype = vp
         L.lso_stream_destroy.argtypes = [vp]
@@ -166,6 +171,9 @@ def probes():
         P.lso_probe_copy.restype = ctypes.c_int
         P.lso_probe_copy_shaped.argtypes = [vp, vp, vp, u64, ctypes.c_int, vp]
         P.lso_probe_copy_shaped.restype = ctypes.c_int
+        P.lso_probe_link_sdma.argtypes = [u64, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32),
+                                          ctypes.POINTER(ctypes.c_double)]
+        P.lso_probe_link_sdma.restype = ctypes.c_int
         P.lso_probe_bf16_rne.argtypes = [u32, u64, vp, vp]
         P.lso_probe_bf16_rne.restype = ctypes.c_int
         P.lso_probe_link.argtypes = [u64, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]

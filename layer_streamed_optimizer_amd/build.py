@@ -21,10 +21,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 
+# ROCr, for copies on named SDMA engines (lso_sdma.cpp)
+LINK = ["-lhsa-runtime64"]
+
 LIBS = {
     "liblso.so": ["lso_adam.hip", "lso_copy.hip", "lso_tiled.hip", "lso_runtime.cpp",
-                  "lso_stream.cpp", "lso_shadow.cpp"],
-    "liblso_probes.so": ["lso_probes.hip", "lso_probe_io.cpp"],
+                  "lso_stream.cpp", "lso_shadow.cpp", "lso_sdma.cpp"],
+    "liblso_probes.so": ["lso_probes.hip", "lso_probe_io.cpp", "lso_sdma.cpp"],
 }
 
 
@@ -37,7 +40,7 @@ def build(verbose: bool = False) -> list[str]:
     for name, srcs in LIBS.items():
         target = lib_path(name)
         tmp = target + ".tmp"
-        cmd = [HIPCC, *FLAGS, *[os.path.join(CSRC, s) for s in srcs], "-o", tmp]
+        cmd = [HIPCC, *FLAGS, *[os.path.join(CSRC, s) for s in srcs], "-o", tmp, *LINK]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -8,6 +8,8 @@
 //                      written, in the planar or tiled state layout, one
 //                      1,024-element chunk per workgroup -- the ceiling of
 //                      the update's own traffic shape.
+//  lso_probe_link_mode / lso_probe_link_sdma  host-link rates, each
+//                      direction alone and both at once, per copy engine
 //  lso_probe_bf16_rne  the fused kernel's BF16 rounding applied to a range
 //                      of FP32 bit patterns, so a test can compare it with
 //                      the host definition over all 2^32 patterns.
@@ -17,6 +19,7 @@
 #include <cstdint>
 
 #include "lso_bf16.h"
+#include "lso_sdma.h"
 
 namespace {
 
@@ -174,6 +177,12 @@ int lso_probe_bf16_rne(uint32_t first, uint64_t count, uint16_t* out, void* stre
 // Returns a hipError_t.
 int lso_probe_link_mode(uint64_t bytes, int reps, int mode, unsigned grid, double out[4]);
 
+// The same four rates with the layer stream's default engines: H2D and
+// D2H on the two SDMA engines lso::sdma_open names (engines[0], engines[1]
+// get their masks).  Returns a hipError_t, or -1 if the engines cannot be
+// named, -2 if a copy fails.
+int lso_probe_link_sdma(uint64_t bytes, int reps, uint32_t engines[2], double out[4]);
+
 int lso_probe_link(uint64_t bytes, int reps, double out[4])
 {
     return lso_probe_link_mode(bytes, reps, 0, 0, out);
@@ -259,6 +268,79 @@ done:
     if (h1) (void)hipHostFree(h1);
     if (h2) (void)hipHostFree(h2);
     return static_cast<int>(err);
+}
+
+int lso_probe_link_sdma(uint64_t bytes, int reps, uint32_t engines[2], double out[4])
+{
+    if (bytes % 16 != 0 || bytes == 0) return static_cast<int>(hipErrorInvalidValue);
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return static_cast<int>(err);
+    lso::SdmaLink link;
+    if (!lso::sdma_open(dev, &link)) return -1;
+    engines[0] = link.h2d_engine;
+    engines[1] = link.d2h_engine;
+    void *h1 = nullptr, *h2 = nullptr, *d1 = nullptr, *d2 = nullptr;
+    hsa_signal_t sh{}, sd{};
+    int rc = 0;
+    auto now = [] { return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count(); };
+    // the copies' completion times, from t0; false if a copy failed
+    auto run = [&](bool in, bool outw, double t0, double& th, double& td) {
+        if (in && lso::sdma_copy(link, d1, h1, bytes, true, nullptr, sh) != HSA_STATUS_SUCCESS) return false;
+        if (outw && lso::sdma_copy(link, h2, d2, bytes, false, nullptr, sd) != HSA_STATUS_SUCCESS) {
+            while (in && lso::sdma_state(sh) > 0) {}
+            return false;
+        }
+        bool fh = !in, fd = !outw, ok = true;
+        while (!(fh && fd)) {
+            if (!fh) {
+                const int64_t v = lso::sdma_state(sh);
+                if (v <= 0) { fh = true; th = now() - t0; ok &= v == 0; }
+            }
+            if (!fd) {
+                const int64_t v = lso::sdma_state(sd);
+                if (v <= 0) { fd = true; td = now() - t0; ok &= v == 0; }
+            }
+        }
+        return ok;
+    };
+    double bh1 = 1e30, bd1 = 1e30, bh = 1e30, bd = 1e30;
+    if ((err = hipHostMalloc(&h1, bytes, hipHostMallocDefault)) != hipSuccess ||
+        (err = hipHostMalloc(&h2, bytes, hipHostMallocDefault)) != hipSuccess ||
+        (err = hipMalloc(&d1, bytes)) != hipSuccess || (err = hipMalloc(&d2, bytes)) != hipSuccess) {
+        rc = static_cast<int>(err);
+        goto done;
+    }
+    if (hsa_signal_create(0, 0, nullptr, &sh) != HSA_STATUS_SUCCESS ||
+        hsa_signal_create(0, 0, nullptr, &sd) != HSA_STATUS_SUCCESS) {
+        rc = -1;
+        goto done;
+    }
+    for (int r = 0; r < reps && rc == 0; ++r) {
+        double th = 0, td = 0;
+        if (!run(true, false, now(), th, td)) { rc = -2; break; }
+        bh1 = th < bh1 ? th : bh1;
+        if (!run(false, true, now(), th, td)) { rc = -2; break; }
+        bd1 = td < bd1 ? td : bd1;
+        if (!run(true, true, now(), th, td)) { rc = -2; break; }
+        bh = th < bh ? th : bh;
+        bd = td < bd ? td : bd;
+    }
+    if (rc == 0) {
+        out[0] = bytes / bh1 / 1e9;
+        out[1] = bytes / bd1 / 1e9;
+        out[2] = bytes / bh / 1e9;
+        out[3] = bytes / bd / 1e9;
+    }
+done:
+    if (sh.handle) (void)hsa_signal_destroy(sh);
+    if (sd.handle) (void)hsa_signal_destroy(sd);
+    if (d1) (void)hipFree(d1);
+    if (d2) (void)hipFree(d2);
+    if (h1) (void)hipHostFree(h1);
+    if (h2) (void)hipHostFree(h2);
+    lso::sdma_close(&link);
+    return rc;
 }
 
 }  // extern "C"

@@ -24,10 +24,17 @@
 //            record step-done[s]
 //   D2H:     wait step-done[s]; copy slot[s] -> dst[i]; record buffer-free[s]
 // Every wait refers to an event recorded earlier in host order.  Each copy
-// is one burst over a piece: H2D on a DMA engine, D2H by a copy kernel on
-// the transfer stream (lso_copy.hip says why the two directions cannot both
-// use the DMA engines).  LSO_STREAM_COPY=kernel uses copy kernels both ways,
-// LSO_STREAM_COPY=dma the DMA engines both ways.
+// is one burst over a piece.  By default both directions run on two SDMA
+// engines the library names (lso_sdma.h: H2D on one engine of a pair, D2H
+// on its partner), and the host loop carries the dependencies itself: it
+// issues a piece's H2D once the slot's previous piece has been copied back,
+// enqueues its update once the H2D has ended (the layer's gradient
+// producer is queued ahead, at the H2D), and issues the D2H once the update
+// has ended; no shader core moves a byte over the link.  Where the engines
+// cannot be named, H2D runs on a runtime-chosen DMA engine and D2H by a copy
+// kernel, tied by the events above.  LSO_STREAM_COPY=kernel uses copy
+// kernels both ways, LSO_STREAM_COPY=dma runtime-chosen DMA engines both
+// ways, LSO_STREAM_COPY=dma-in the fallback.
 //
 // Three kinds of authoritative block:
 //  - pinned host memory (page-locked, e.g. lso_host_alloc): src = dst = the
@@ -74,6 +81,7 @@
 #include "lso_copy.h"
 #include "lso_internal.h"
 #include "lso_runtime.h"
+#include "lso_sdma.h"
 #include "lso_shadow.h"
 
 namespace {
@@ -276,7 +284,9 @@ constexpr int kMaxSlots = 4;
 constexpr int kMaxStaging = 8;
 
 // Which engine moves each direction of a layer block.
-enum CopyMode { kCopyKernels = 0, kCopyDma = 1, kCopyDmaIn = 2 };
+// the LSO_COPY_* codes of lso.h
+enum CopyMode { kCopyEngines = LSO_COPY_SDMA_PAIR, kCopyDmaIn = LSO_COPY_DMA_IN, kCopyKernels = LSO_COPY_KERNELS,
+                kCopyDma = LSO_COPY_DMA };
 
 struct lso_stream_ctx {
     int device = 0;
@@ -304,7 +314,10 @@ struct lso_stream_ctx {
     uint64_t norm_ws_bytes = 0;
     std::mutex note_mu;          // signalled when a request completes
     std::condition_variable note_cv;
-    int copy_mode = kCopyDmaIn;   // measured 0.5-2% ahead of kernels both ways
+    int copy_mode = kCopyDmaIn;
+    lso::SdmaLink sdma;                       // kCopyEngines: the two engines
+    hsa_signal_t h2d_sig[kMaxSlots] = {};     // kCopyEngines: per slot, its H2D ended
+    hsa_signal_t d2h_sig[kMaxSlots] = {};     // kCopyEngines: per slot, its D2H ended
     unsigned copy_grid = lso::kCopyGrid;
     uint64_t piece_bytes = 1ull << 30;   // target size of a tiled layer's pieces
 };
@@ -339,6 +352,10 @@ void release(lso_stream_ctx* c)
     }
     for (hipStream_t s : {c->h2d, c->compute, c->d2h})
         if (s) (void)hipStreamDestroy(s);
+    for (int s = 0; s < kMaxSlots; ++s)
+        for (hsa_signal_t sig : {c->h2d_sig[s], c->d2h_sig[s]})
+            if (sig.handle) (void)hsa_signal_destroy(sig);
+    lso::sdma_close(&c->sdma);
     (void)hipSetDevice(prev);
     delete c;
 }
@@ -560,31 +577,24 @@ std::vector<Unit> make_units(const lso_stream_ctx* c, const Job* J, size_t n)
     return u;
 }
 
-// Enqueue H2D, (on a layer's first piece) the gradient producer, the update
-// and D2H of the piece at position i of the pipeline (slot i % nslots), and
-// record d2h_done[i % nstaging] after its D2H.  buf: where the H2D reads and
-// the D2H writes (inside the block itself when pinned, a staging buffer
-// otherwise).  A layer's gradients and BF16 weights live in the buffers of
-// its own parity (layer % nslots) for all its pieces.
-lso_status issue_unit(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
+// (On a layer's first piece) the layer's gradients, into the buffer of its
+// parity: the producer writes them on the compute stream.
+lso_status enqueue_producer(lso_stream_ctx* c, const Unit& U)
+{
+    if (!U.first) return LSO_OK;
+    const Job& h = *U.job;
+    const int rc = c->fn(c->user, h.index, c->slot_grad[U.layer % c->nslots], h.n, c->compute);
+    if (rc != 0) return lso::fail(LSO_E_CALLBACK, "gradient producer returned %d at layer %zu", rc, h.index);
+    return LSO_OK;
+}
+
+// The fused update of the piece at position i, resident in slot i % nslots,
+// on the compute stream; records step_done for the slot.
+lso_status enqueue_piece_update(lso_stream_ctx* c, const Unit& U, size_t i)
 {
     const Job& h = *U.job;
     const int s = static_cast<int>(i % c->nslots);
     const int ls = static_cast<int>(U.layer % c->nslots);
-    hipError_t err;
-    // StreamIn: the device slot is free once the piece that used it last
-    // (nslots pieces ago) has been copied back.
-    if ((err = hipStreamWaitEvent(c->h2d, c->buffer_free[s], 0)) != hipSuccess ||
-        (err = copy_block(c, c->slot_state[s], buf, U.bytes, hipMemcpyHostToDevice, c->h2d)) != hipSuccess ||
-        (err = hipEventRecord(c->weights_ready[s], c->h2d)) != hipSuccess)
-        return lso::hip_fail(err, "H2D stage");
-    // Compute: the layer's gradients (once), then the fused update on the slot.
-    if ((err = hipStreamWaitEvent(c->compute, c->weights_ready[s], 0)) != hipSuccess)
-        return lso::hip_fail(err, "hipStreamWaitEvent(weights-ready)");
-    if (U.first) {
-        const int rc = c->fn(c->user, h.index, c->slot_grad[ls], h.n, c->compute);
-        if (rc != 0) return lso::fail(LSO_E_CALLBACK, "gradient producer returned %d at layer %zu", rc, h.index);
-    }
     lso_block b{};
     // the piece's bytes [off, off + bytes) of the block sit at the slot's start
     const uintptr_t base = reinterpret_cast<uintptr_t>(c->slot_state[s]) - U.off;
@@ -617,14 +627,75 @@ lso_status issue_unit(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
         return lso::fail(LSO_E_INVALID, "layer %zu: norm workspace too small", h.index);
     lso_status st = lso::enqueue_update(&b, 1, c->compute, false, h.sq_norm ? &o : nullptr);
     if (st != LSO_OK) return st;
-    if ((err = hipEventRecord(c->step_done[s], c->compute)) != hipSuccess)
-        return lso::hip_fail(err, "hipEventRecord(step-done)");
+    const hipError_t err = hipEventRecord(c->step_done[s], c->compute);
+    if (err != hipSuccess) return lso::hip_fail(err, "hipEventRecord(step-done)");
+    return LSO_OK;
+}
+
+// HIP-stream modes: enqueue H2D, (on a layer's first piece) the gradient
+// producer, the update and D2H of the piece at position i of the pipeline
+// (slot i % nslots), tied by events, and record d2h_done[i % nstaging]
+// after its D2H.  buf: where the H2D reads and the D2H writes (inside the
+// block itself when pinned, a staging buffer otherwise).  A layer's
+// gradients and BF16 weights live in the buffers of its own parity
+// (layer % nslots) for all its pieces.
+lso_status issue_unit(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
+{
+    const int s = static_cast<int>(i % c->nslots);
+    hipError_t err;
+    // StreamIn: the device slot is free once the piece that used it last
+    // (nslots pieces ago) has been copied back.
+    if ((err = hipStreamWaitEvent(c->h2d, c->buffer_free[s], 0)) != hipSuccess ||
+        (err = copy_block(c, c->slot_state[s], buf, U.bytes, hipMemcpyHostToDevice, c->h2d)) != hipSuccess ||
+        (err = hipEventRecord(c->weights_ready[s], c->h2d)) != hipSuccess)
+        return lso::hip_fail(err, "H2D stage");
+    // Compute: the layer's gradients (once), then the fused update on the slot.
+    if ((err = hipStreamWaitEvent(c->compute, c->weights_ready[s], 0)) != hipSuccess)
+        return lso::hip_fail(err, "hipStreamWaitEvent(weights-ready)");
+    lso_status st = enqueue_producer(c, U);
+    if (st != LSO_OK) return st;
+    st = enqueue_piece_update(c, U, i);
+    if (st != LSO_OK) return st;
     // Offload: the updated piece goes back over the authoritative copy.
     if ((err = hipStreamWaitEvent(c->d2h, c->step_done[s], 0)) != hipSuccess ||
         (err = copy_block(c, buf, c->slot_state[s], U.bytes, hipMemcpyDeviceToHost, c->d2h)) != hipSuccess ||
         (err = hipEventRecord(c->buffer_free[s], c->d2h)) != hipSuccess ||
         (err = hipEventRecord(c->d2h_done[i % staging_count(c)], c->d2h)) != hipSuccess)
         return lso::hip_fail(err, "D2H stage");
+    return LSO_OK;
+}
+
+// SDMA-pair mode, first stage of the piece at position i: (on a layer's
+// first piece) the gradient producer, queued ahead on the compute stream,
+// then the H2D on the link's H2D engine.  The loop calls it only once the
+// piece that used the slot before (nslots pieces ago) has been copied back,
+// so the slot, the piece's completion signals and the gradient buffer of
+// its parity are free.
+lso_status issue_h2d_engine(lso_stream_ctx* c, const Unit& U, size_t i, const void* buf)
+{
+    const int s = static_cast<int>(i % c->nslots);
+    lso_status st = enqueue_producer(c, U);
+    if (st != LSO_OK) return st;
+    const hsa_status_t hs = lso::sdma_copy(c->sdma, c->slot_state[s], buf, U.bytes, true, nullptr, c->h2d_sig[s]);
+    if (hs != HSA_STATUS_SUCCESS) {
+        hsa_signal_store_screlease(c->h2d_sig[s], 0);
+        return lso::fail(LSO_E_HIP, "SDMA H2D copy of %llu bytes not accepted (status %d)",
+                         static_cast<unsigned long long>(U.bytes), static_cast<int>(hs));
+    }
+    return LSO_OK;
+}
+
+// SDMA-pair mode, last stage: the piece's D2H on the link's D2H engine,
+// once its update has completed.
+lso_status issue_d2h_engine(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
+{
+    const int s = static_cast<int>(i % c->nslots);
+    const hsa_status_t hs = lso::sdma_copy(c->sdma, buf, c->slot_state[s], U.bytes, false, nullptr, c->d2h_sig[s]);
+    if (hs != HSA_STATUS_SUCCESS) {
+        hsa_signal_store_screlease(c->d2h_sig[s], 0);
+        return lso::fail(LSO_E_HIP, "SDMA D2H copy of %llu bytes not accepted (status %d)",
+                         static_cast<unsigned long long>(U.bytes), static_cast<int>(hs));
+    }
     return LSO_OK;
 }
 
@@ -709,8 +780,12 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
     auto record = [&](lso_status s) {
         if (result == LSO_OK) result = s;
     };
+    const bool engines = c->copy_mode == kCopyEngines;
+    const size_t S = static_cast<size_t>(c->nslots);
     size_t next_read = 0;     // next piece to stage in
-    size_t next_issue = 0;    // next piece to enqueue on the GPU
+    size_t next_issue = 0;    // next piece to enqueue on the GPU (SDMA-pair mode: its H2D)
+    size_t next_update = 0;   // SDMA-pair mode: next piece whose H2D completion is awaited
+    size_t next_offload = 0;  // SDMA-pair mode: next piece whose update completion is awaited
     size_t next_retire = 0;   // next piece whose D2H completion is awaited
     size_t next_done = 0;     // next piece whose write-out completion is awaited
     size_t stop_at = n;       // after an error no piece >= stop_at is read or issued
@@ -719,6 +794,10 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
 
     auto read_complete = [&](size_t i) {
         return units[i].job->kind == kPinned || rd[i % K].done.load();
+    };
+    auto buf_of = [&](size_t i) -> char* {
+        const Unit& U = units[i];
+        return U.job->kind == kPinned ? U.job->host + U.off : static_cast<char*>(c->staging[i % K]);
     };
     auto reads_in_flight = [&] {
         for (size_t i = next_issue; i < next_read; ++i)
@@ -752,8 +831,10 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
             ++next_read;
             progress = true;
         }
-        // 2. issue staged pieces in order
-        while (next_issue < next_read && next_issue < stop_at && read_complete(next_issue)) {
+        // 2. issue staged pieces in order (SDMA-pair mode: once the piece
+        //    that used the slot before has been copied back)
+        while (next_issue < next_read && next_issue < stop_at && read_complete(next_issue) &&
+               (!engines || next_issue < next_retire + S)) {
             const Unit& U = units[next_issue];
             const Job& j = *U.job;
             if (j.kind != kPinned) {
@@ -764,9 +845,9 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
                     break;
                 }
             }
-            void* buf = j.kind == kPinned ? static_cast<void*>(j.host + U.off) : c->staging[next_issue % K];
             trace.mark(trace.issue, next_issue);
-            const lso_status s = issue_unit(c, U, next_issue, buf);
+            const lso_status s = engines ? issue_h2d_engine(c, U, next_issue, buf_of(next_issue))
+                                         : issue_unit(c, U, next_issue, buf_of(next_issue));
             if (s != LSO_OK) {
                 record(s);
                 stop_at = next_issue;
@@ -776,16 +857,63 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
             ++next_issue;
             progress = true;
         }
+        // 2b. SDMA-pair mode: the update of each piece whose H2D is complete
+        while (engines && next_update < next_issue) {
+            const int64_t st = lso::sdma_state(c->h2d_sig[next_update % S]);
+            if (st > 0) break;
+            if (st < 0 && gpu_ok) {
+                record(lso::fail(LSO_E_HIP, "SDMA H2D copy of layer %zu failed", units[next_update].job->index));
+                gpu_ok = false;
+                stop_at = std::min(stop_at, next_issue);
+            }
+            if (gpu_ok) {
+                const lso_status s = enqueue_piece_update(c, units[next_update], next_update);
+                if (s != LSO_OK) {
+                    record(s);
+                    gpu_ok = false;
+                    stop_at = std::min(stop_at, next_issue);
+                }
+            }
+            ++next_update;
+            progress = true;
+        }
+        // 2c. SDMA-pair mode: the D2H of each piece whose update is complete
+        while (engines && next_offload < next_update) {
+            const size_t i = next_offload;
+            if (gpu_ok) {
+                const hipError_t q = hipEventQuery(c->step_done[i % S]);
+                if (q == hipErrorNotReady) break;
+                const lso_status s = q != hipSuccess ? lso::hip_fail(q, "update completion")
+                                                     : issue_d2h_engine(c, units[i], i, buf_of(i));
+                if (s != LSO_OK) {
+                    record(s);
+                    gpu_ok = false;
+                    stop_at = std::min(stop_at, next_issue);
+                }
+            }
+            ++next_offload;
+            progress = true;
+        }
         // 3. start the write-out of pieces whose D2H is complete, one at a
         //    time in order (so a failed write leaves every later piece
         //    untouched)
-        while (next_retire < next_issue && next_done == next_retire) {
-            const hipError_t q = gpu_ok ? hipEventQuery(c->d2h_done[next_retire % K]) : hipSuccess;
-            if (q == hipErrorNotReady) break;
-            if (q != hipSuccess) {
-                record(lso::hip_fail(q, "D2H completion"));
-                gpu_ok = false;
-                stop_at = std::min(stop_at, next_issue);
+        while (next_retire < (engines ? next_offload : next_issue) && next_done == next_retire) {
+            if (engines) {
+                const int64_t st = gpu_ok ? lso::sdma_state(c->d2h_sig[next_retire % S]) : 0;
+                if (st > 0) break;
+                if (st < 0) {
+                    record(lso::fail(LSO_E_HIP, "SDMA D2H copy of layer %zu failed", units[next_retire].job->index));
+                    gpu_ok = false;
+                    stop_at = std::min(stop_at, next_issue);
+                }
+            } else {
+                const hipError_t q = gpu_ok ? hipEventQuery(c->d2h_done[next_retire % K]) : hipSuccess;
+                if (q == hipErrorNotReady) break;
+                if (q != hipSuccess) {
+                    record(lso::hip_fail(q, "D2H completion"));
+                    gpu_ok = false;
+                    stop_at = std::min(stop_at, next_issue);
+                }
             }
             const Unit& U = units[next_retire];
             const Job& j = *U.job;
@@ -843,12 +971,19 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
         const size_t last = std::min(stop_at, n);
         if (next_done == next_issue && next_issue >= last && !reads_in_flight()) break;
         if (!progress) {
+            // SDMA-pair mode: the loop itself moves each piece from copy to
+            // update to copy, so it looks more often
             std::unique_lock<std::mutex> l(c->note_mu);
-            c->note_cv.wait_for(l, std::chrono::microseconds(200));
+            c->note_cv.wait_for(l, std::chrono::microseconds(engines ? 50 : 200));
         }
     }
     // Every enqueued stage finishes before return (on error too, so no copy
     // into a block is still running when the caller looks at it).
+    if (engines) {
+        for (size_t s = 0; s < S; ++s)
+            while (lso::sdma_state(c->h2d_sig[s]) > 0 || lso::sdma_state(c->d2h_sig[s]) > 0)
+                std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
     for (hipStream_t st : {c->h2d, c->compute, c->d2h}) {
         const hipError_t err = hipStreamSynchronize(st);
         if (err != hipSuccess) record(lso::hip_fail(err, "hipStreamSynchronize"));
@@ -913,10 +1048,11 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     c->max_params = max_layer_params;
     c->fn = fn;
     c->user = user;
+    int want = kCopyEngines;
     if (const char* e = std::getenv("LSO_STREAM_COPY")) {
-        if (!std::strcmp(e, "dma")) c->copy_mode = kCopyDma;
-        else if (!std::strcmp(e, "dma-in")) c->copy_mode = kCopyDmaIn;
-        else if (!std::strcmp(e, "kernel")) c->copy_mode = kCopyKernels;
+        if (!std::strcmp(e, "dma")) want = kCopyDma;
+        else if (!std::strcmp(e, "dma-in")) want = kCopyDmaIn;
+        else if (!std::strcmp(e, "kernel")) want = kCopyKernels;
     }
     if (const char* e = std::getenv("LSO_STREAM_SLOTS")) {
         const int k = std::atoi(e);
@@ -958,6 +1094,20 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     for (size_t s = 0; s < staging_count(c); ++s) {
         err = hipEventCreateWithFlags(&c->d2h_done[s], hipEventDisableTiming);
         if (err != hipSuccess) { release(c); return lso::hip_fail(err, "hipEventCreateWithFlags"); }
+    }
+    // Named SDMA engines need ROCr's agents, engine masks and a completion
+    // signal per slot and direction; without them the context copies H2D on
+    // a runtime-chosen engine and D2H by kernel.
+    c->copy_mode = want == kCopyEngines ? kCopyDmaIn : want;
+    if (want == kCopyEngines && lso::sdma_open(device, &c->sdma)) {
+        bool ok = true;
+        for (int s = 0; s < c->nslots && ok; ++s)
+            for (hsa_signal_t* sig : {&c->h2d_sig[s], &c->d2h_sig[s]})
+                if (ok && hsa_signal_create(0, 0, nullptr, sig) != HSA_STATUS_SUCCESS) {
+                    sig->handle = 0;
+                    ok = false;
+                }
+        if (ok) c->copy_mode = kCopyEngines;
     }
     // chunk sums of one layer at the smallest chunk size (any layout)
     const uint64_t min_chunk = lso::chunk_elems(lso::kUnrollSmall);
@@ -1061,6 +1211,15 @@ lso_status lso_stream_files(lso_stream_ctx* c, const lso_file_layer* L, size_t n
     if (s != LSO_OK) return s;
     DeviceGuard guard(c->device);
     return run_pipeline(c, jobs.data(), jobs.size());
+}
+
+int lso_stream_copy_mode(const lso_stream_ctx* c, uint32_t* h2d_engine, uint32_t* d2h_engine)
+{
+    if (!c) return -1;
+    const bool eng = c->copy_mode == kCopyEngines;
+    if (h2d_engine) *h2d_engine = eng ? c->sdma.h2d_engine : 0;
+    if (d2h_engine) *d2h_engine = eng ? c->sdma.d2h_engine : 0;
+    return c->copy_mode;
 }
 
 void* lso_stream_slot_weight(lso_stream_ctx* c, int slot)

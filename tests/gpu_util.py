@@ -353,3 +353,20 @@ def stream_pieces(tiles: int):
             del os.environ["LSO_STREAM_PIECE_BYTES"]
         else:
             os.environ["LSO_STREAM_PIECE_BYTES"] = old
+
+
+@contextlib.contextmanager
+def stream_env(**env):
+    """Layer streams created inside see these LSO_STREAM_* variables (read at
+    context creation), e.g. stream_env(COPY="kernel")."""
+    old = {k: os.environ.get("LSO_STREAM_" + k) for k in env}
+    for k, v in env.items():
+        os.environ["LSO_STREAM_" + k] = str(v)
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                del os.environ["LSO_STREAM_" + k]
+            else:
+                os.environ["LSO_STREAM_" + k] = v

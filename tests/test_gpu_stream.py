@@ -11,8 +11,8 @@ import oracle
 import synth
 from layer_streamed_optimizer_amd import configs
 
-from gpu_util import (HIP_D2D, HostLayers, assert_parity, call_scale, hip, log, stream_pieces,
-                      synth_stream, torch)
+from gpu_util import (HIP_D2D, HostLayers, assert_parity, call_scale, hip, log, stream_env,
+                      stream_pieces, synth_stream, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -276,3 +276,48 @@ def test_layers_moved_in_pieces_equal_whole_layers_bitwise(pageable):
         assert np.array_equal(wa[b].cpu().numpy(), wb[b].cpu().numpy()), b
     ls_a.close()
     ls_b.close()
+
+
+@pytest.mark.parametrize("pageable", [False, True], ids=["pinned", "pageable"])
+def test_every_copy_mode_gives_the_same_bits(pageable):
+    """The four ways of moving blocks over the link (named SDMA engines, the
+    default; runtime-chosen DMA engine for H2D with a D2H copy kernel; copy
+    kernels; runtime-chosen DMA engines) give the same state, weights and
+    norms bit for bit, on tiled layers in pieces and planar layers in one
+    call, and each context reports the mode it was asked for."""
+    T = torch()
+    sizes_t = [100003, 8192 * 5 + 1]
+    sizes_p = [7, 65536 + 8191]
+    sizes = sizes_t + sizes_p
+    sid = 48
+    mb = max([configs.host_layer_layout(n, tiled=True)[3] for n in sizes_t] +
+             [configs.host_layer_layout(n)[3] for n in sizes_p])
+    runs = {}
+    for mode in ("sdma-pair", "dma-in", "kernel", "dma"):
+        log("copy mode", mode, "pageable" if pageable else "pinned")
+        ht = HostLayers(sizes_t, sid, tiled=True, pageable=pageable)
+        hp = HostLayers(sizes_p, sid + 1, pageable=pageable)
+        with stream_pieces(2), stream_env(COPY=mode):
+            ls, prm = synth_stream(sizes, sid, max_bytes=mb)
+        cm = ls.copy_mode()
+        assert cm["mode"] == mode, cm
+        if mode == "sdma-pair":
+            assert cm["h2d_engine"] and cm["d2h_engine"] and cm["h2d_engine"] != cm["d2h_engine"], cm
+        w = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
+        norms = np.zeros(len(sizes))
+        for t in range(1, 4):
+            prm.step = t
+            L = np.concatenate([ht.table(t), hp.table(t)])
+            L["dev_weight"] = [int(x.data_ptr()) for x in w]
+            L["sq_norm"] = [norms.ctypes.data + 8 * i for i in range(len(sizes))]
+            ls.stream_layers(L)
+        T.cuda.synchronize()
+        raw = [ht.raw(b) for b in range(len(sizes_t))] + [hp.raw(b) for b in range(len(sizes_p))]
+        runs[mode] = (raw, [x.cpu().numpy() for x in w], norms.copy())
+        ls.close()
+    ref = runs["sdma-pair"]
+    for mode, (raw, w, norms) in runs.items():
+        for b in range(len(sizes)):
+            assert np.array_equal(raw[b], ref[0][b]), (mode, b)
+            assert np.array_equal(w[b], ref[1][b]), (mode, b)
+        assert np.array_equal(norms, ref[2]), mode

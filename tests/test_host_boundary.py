@@ -82,6 +82,21 @@ int main(void) {
             assert int(got[f"{struct}.{fname}"]) == getattr(cls, fname).offset, (struct, fname)
 
 
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(LSO_[A-Z0-9_]+)\s+(\d+)u?\b", text))
+    for name in ("LSO_COPY_SDMA_PAIR", "LSO_COPY_DMA_IN", "LSO_COPY_KERNELS", "LSO_COPY_DMA",
+                 "LSO_FILE_SYNC", "LSO_FILE_SHADOW", "LSO_SHADOW_HEADER_BYTES", "LSO_TILE_ELEMS"):
+        assert int(defs[name]) == getattr(_native, name), name
+    codes = [getattr(_native, n) for n in ("LSO_COPY_SDMA_PAIR", "LSO_COPY_DMA_IN", "LSO_COPY_KERNELS",
+                                           "LSO_COPY_DMA")]
+    assert sorted(codes) == sorted(_native.COPY_MODE_NAMES)
+
+
+def test_copy_mode_of_no_context():
+    assert _native.lib().lso_stream_copy_mode(None, None, None) == -1
+
+
 def test_status_strings():
     lib = _native.lib()
     for s in range(8):
