@@ -1,13 +1,12 @@
 // Host <-> device block copies issued by the shader cores.
 //
-// The layer stream moves each layer's block with one copy per direction.
-// Done by a kernel, the two directions run at full duplex (about 47 GB/s
-// each way on this part's PCIe Gen5 x16 link) whatever else the process
-// has queued; the DMA engines reach the same rate in one direction but, in
-// a process with several other streams, the host-to-device and
-// device-to-host copies end up sharing an engine and the second direction
-// drops to about half.  The stream therefore runs its D2H copies here and
-// leaves the H2D direction to a DMA engine (or runs both here on request).
+// The layer stream moves each piece with one copy per direction.  By
+// default both run on two SDMA engines it names (lso_sdma.h); this kernel
+// serves the other modes: D2H when the engines cannot be named (H2D then
+// goes to a runtime-chosen DMA engine, which on its own would often share
+// one engine with the D2H and halve it), or both directions on request.
+// Done by a kernel, the two directions run at about 46-47 GB/s each way on
+// this part's PCIe Gen5 x16 link whatever else the process has queued.
 // One 16-byte vector per lane and iteration; 128 workgroups keep the link
 // busy -- more keep so many long-latency host reads queued that the update
 // kernel running beside them slows down.
