@@ -408,6 +408,22 @@ def link_peak(nbytes=4 << 30):
     return res
 
 
+def best_link_peak(a: dict, b: dict) -> dict:
+    """Per engine choice, the better of two link_peak measurements (by the
+    slower direction while both run), and the streamed roofline peak over
+    them: one probe can catch the link while the machine is still busy
+    with something else (a previous process's pinned memory going away)."""
+    worst = lambda r: min(r["bidir_h2d"], r["bidir_d2h"])
+    res = {}
+    for k in a:
+        if k == "bidir_per_direction":
+            continue
+        res[k] = a[k] if k not in b or worst(a[k]) >= worst(b[k]) else b[k]
+    res["bidir_per_direction"] = max(worst(r) for r in res.values())
+    res["measured"] = "before and after the timed steps; the better of the two per engine choice"
+    return res
+
+
 def streamed(args, w):
     import numpy as np
     import torch
@@ -483,6 +499,12 @@ def streamed(args, w):
             step_s.append(dt)
     copy_mode = ls.copy_mode()
     ls.close()
+    for hb in hosts:
+        if pinned:
+            hb.close()
+    hosts.clear()
+    peak = best_link_peak(peak, link_peak())
+    progress(f"link after the steps, best of both: {peak['bidir_per_direction']:.1f} GB/s per direction")
     wall = sum(step_s)
     params = n * n_layers
     per_dir = LINK_BYTES_PER_PARAM * params / (wall / len(step_s)) / 1e9
@@ -499,9 +521,6 @@ def streamed(args, w):
                     host_bytes=nbytes * n_layers,
                     link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode),
     )
-    for hb in hosts:
-        if pinned:
-            hb.close()
     return result
 
 

@@ -566,9 +566,14 @@ std::vector<Unit> make_units(const lso_stream_ctx* c, const Job* J, size_t n)
             u.push_back({&j, L, 0, j.bytes, 0, j.n, true, true});
             continue;
         }
-        for (uint64_t k = 0; k * per < tiles; ++k) {
-            const uint64_t t0 = k * per, t1 = std::min(tiles, t0 + per);
-            const bool last = t1 == tiles;
+        // as many pieces as pieces of at most `per` tiles take, with the
+        // tiles spread evenly over them: a short last piece would leave the
+        // D2H engine idle while the next layer's first piece comes in
+        const uint64_t k_n = (tiles + per - 1) / per;
+        const uint64_t q = tiles / k_n, r = tiles % k_n;   // the first r pieces take q + 1 <= per
+        for (uint64_t k = 0; k < k_n; ++k) {
+            const uint64_t t0 = k * q + std::min(k, r), t1 = t0 + q + (k < r ? 1 : 0);
+            const bool last = k + 1 == k_n;
             const uint64_t off = t0 * tile_bytes;
             u.push_back({&j, L, off, last ? j.bytes - off : (t1 - t0) * tile_bytes, t0 * T,
                          std::min(j.n, t1 * T), k == 0, last});
