@@ -111,8 +111,14 @@ def stream(args) -> str:
         by_q.setdefault(f"copy kernel, queue {r['Queue_Id']}", []).append(r)
     if args.memcpy:
         # DMA-engine copies of at least a piece (the bench's set-up copies are
-        # chunked by the runtime into much smaller ones)
+        # chunked by the runtime into much smaller ones) that start at most
+        # 10 ms after the last update has ended: the step's last D2H starts
+        # right then, and the link probe the bench runs after the steps can
+        # only start once that D2H (about 20 ms) is over
+        cut = int(upd[-1]["End_Timestamp"]) + 10_000_000 if upd else None
         for r in csv.DictReader(open(args.memcpy)):
+            if cut is not None and int(r["Start_Timestamp"]) > cut:
+                continue
             if (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) > 1_000_000:
                 by_q.setdefault(f"DMA {r['Direction'].replace('MEMORY_COPY_', '').lower()}", []).append(r)
         for v in by_q.values():
