@@ -28,8 +28,9 @@
  * updated and cast back down; the MegaTrain summary on blog.hotdry.top for
  * BF16 weights/gradients with FP32 moments (section on the memory
  * bottleneck), layer-contiguous 4 KB-aligned host blocks, double buffering
- * and three streams joined by weights-ready / backward-done / buffer-free
- * events (section on streaming execution and the double-buffered pipeline).
+ * and a weight-transfer, a compute and a write-back stage joined by
+ * weights-ready / backward-done / buffer-free dependencies (section on
+ * streaming execution and the double-buffered pipeline).
  * FP32 gradients (grad_dtype LSO_DT_F32) follow the LoRA memory accounting
  * of the Cloudera community article ("everything else": adapter gradients
  * in FP32, 4 bytes each).
@@ -207,10 +208,12 @@ lso_status lso_tiled_unpack(const void* state, float* master, float* m, float* v
  * producer write that layer's BF16 gradients into the slot, runs the fused
  * update on the slot, and copies the block back over the host copy -- so
  * the host holds master + delta afterwards.  Two slots alternate (double
- * buffering) on three streams: H2D waits buffer-free[slot], copies,
- * records weights-ready[slot]; compute waits weights-ready, runs producer
- * and update, records step-done[slot]; D2H waits step-done, copies back,
- * records buffer-free[slot].
+ * buffering): a slot's H2D waits until its previous block has been copied
+ * back (buffer-free), the update waits for the H2D (weights-ready), the
+ * D2H waits for the update (step-done).  By default the two copies run on
+ * two SDMA engines the library names and the host loop carries these
+ * dependencies; in the fallback modes (lso_stream_copy_mode) they are
+ * events between three HIP streams.
  * Host blocks may be pinned (lso_host_alloc, or any page-locked HIP host
  * allocation): the copies then read and write them directly.  Or they may
  * be ordinary pageable memory (for state larger than the page-locked
@@ -255,7 +258,7 @@ typedef int (*lso_grad_fn)(void* user, size_t layer, void* dev_grad_bf16, uint64
 
 typedef struct lso_stream_ctx lso_stream_ctx;
 
-/* Create a streaming context on `device`: three streams, two device slots
+/* Create a streaming context on `device`: its streams, two device slots
  * of max_layer_bytes (rounded up to 4 KB) of state plus max_layer_params
  * BF16 gradients and BF16 weights each, the events, and the copy mode (see
  * lso_stream_copy_mode; the three pinned staging buffers of that size and

@@ -527,8 +527,8 @@ lso_status ensure_staging(lso_stream_ctx* c, uint64_t need)
     return LSO_OK;
 }
 
-// One block copy between a page-locked host buffer and a device slot: a
-// copy kernel by default (full duplex), or the DMA engines.
+// The fallback modes' block copy between a page-locked host buffer and a
+// device slot: a copy kernel, or a runtime-chosen DMA engine, by direction.
 hipError_t copy_block(const lso_stream_ctx* c, void* dst, const void* src, uint64_t bytes,
                       hipMemcpyKind kind, hipStream_t st)
 {
