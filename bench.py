@@ -608,7 +608,7 @@ def streamed_files(args, w):
         step_s = []
         for j in range(1, args.warmup + args.steps + 1):
             prm.step = j
-            L = files.table(j, configs.LR, configs.BETA1, configs.BETA2, configs.EPS)
+            L = files.table(j, configs.LR, configs.BETA1, configs.BETA2, configs.EPS, sync=args.sync)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             ls.stream_files(L)
@@ -638,7 +638,8 @@ def streamed_files(args, w):
                     host_memory="file (O_DIRECT, one preallocated file per layer"
                                 + (", shadow region)" if args.shadow else ")"),
                     state_layout=args.layout, file_bytes=nbytes * n_layers,
-                    storage_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode),
+                    storage_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode,
+                    flushed_per_layer=bool(args.sync or args.shadow)),
     )
 
 
@@ -713,6 +714,9 @@ def main():
     ap.add_argument("--shadow", action="store_true",
                     help="c4 with --host-memory file: crash-consistent shadow regions "
                          "(3 layers by default: two data slots per layer)")
+    ap.add_argument("--sync", action="store_true",
+                    help="c4 with --host-memory file: fdatasync each layer's file after its "
+                         "write-back (LSO_FILE_SYNC; shadow regions always flush)")
     ap.add_argument("--file-dir", default=None,
                     help="c4 with --host-memory file: where the layer files go "
                          "(default $LSO_FILE_DIR or /var/tmp)")
