@@ -379,7 +379,10 @@ void* lso_stream_slot_weight(lso_stream_ctx* ctx, int slot);
  * as the MegaTrain summary's section on streaming execution describes).
  * SDMA engines come in pairs sharing a path to the link: with both
  * directions busy, H2D on one engine of a pair and D2H on its partner is
- * the fastest split measured; two directions on one engine take turns. */
+ * the fastest split measured; two directions on one engine take turns.
+ * The named engines are not reserved: other copies the process runs at the
+ * same time (hipMemcpyAsync, another context's stream) may land on them
+ * and share their time. */
 #define LSO_COPY_SDMA_PAIR 0   /* both directions on DMA engines the library names (default) */
 #define LSO_COPY_DMA_IN    1   /* H2D on a DMA engine the runtime picks, D2H by a copy kernel
                                   (default when the engines cannot be named) */

@@ -321,3 +321,45 @@ def test_every_copy_mode_gives_the_same_bits(pageable):
             assert np.array_equal(raw[b], ref[0][b]), (mode, b)
             assert np.array_equal(w[b], ref[1][b]), (mode, b)
         assert np.array_equal(norms, ref[2]), mode
+
+
+@pytest.mark.parametrize("slots", [2, 3, 4])
+def test_named_engines_many_small_pieces_any_slot_count(slots):
+    """Forty layers, tiled ones cut into one-tile pieces and small planar
+    ones, pinned and pageable mixed: the named-engine pipeline, with 2, 3 or
+    4 device slots (the host loop reuses each slot's signals every `slots`
+    pieces, and a layer's producer is queued ahead at its first H2D), gives
+    the bits of copy kernels with two slots -- state, weights and norms."""
+    T = torch()
+    rng = np.random.default_rng(7)
+    sizes_t = [int(x) for x in rng.integers(1, 3 * 8192 + 5, 24)]
+    sizes_p = [int(x) for x in rng.integers(1, 20000, 16)]
+    sizes = sizes_t + sizes_p
+    sid = 49
+    mb = max([configs.host_layer_layout(n, tiled=True)[3] for n in sizes_t] +
+             [configs.host_layer_layout(n)[3] for n in sizes_p])
+    runs = {}
+    for mode, k in (("sdma-pair", slots), ("kernel", 2)):
+        log("many pieces", mode, "slots", k)
+        ht = HostLayers(sizes_t, sid, tiled=True, pageable=lambda b: b % 3 == 1)
+        hp = HostLayers(sizes_p, sid + 1, pageable=lambda b: b % 2 == 0)
+        with stream_pieces(1), stream_env(COPY=mode, SLOTS=k):
+            ls, prm = synth_stream(sizes, sid, max_bytes=mb)
+        assert ls.copy_mode()["mode"] == mode
+        w = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
+        norms = np.zeros(len(sizes))
+        for t in range(1, 3):
+            prm.step = t
+            L = np.concatenate([ht.table(t), hp.table(t)])
+            L["dev_weight"] = [int(x.data_ptr()) for x in w]
+            L["sq_norm"] = [norms.ctypes.data + 8 * i for i in range(len(sizes))]
+            ls.stream_layers(L)
+        T.cuda.synchronize()
+        raw = [ht.raw(b) for b in range(len(sizes_t))] + [hp.raw(b) for b in range(len(sizes_p))]
+        runs[mode] = (raw, [x.cpu().numpy() for x in w], norms.copy())
+        ls.close()
+    a, b = runs["sdma-pair"], runs["kernel"]
+    for i in range(len(sizes)):
+        assert np.array_equal(a[0][i], b[0][i]), i
+        assert np.array_equal(a[1][i], b[1][i]), i
+    assert np.array_equal(a[2], b[2])
