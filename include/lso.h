@@ -393,7 +393,10 @@ void* lso_stream_slot_weight(lso_stream_ctx* ctx, int slot);
  * dma-in, kernel or dma at lso_stream_create asks for one; LSO_STREAM_SDMA
  * = "h,d" names the two engines by number), and with LSO_COPY_SDMA_PAIR
  * the engine of each direction as a one-bit mask (engine k = bit k), else
- * 0.  Either pointer may be NULL.  Returns -1 if ctx is NULL. */
+ * 0.  Either pointer may be NULL.  Returns -1 if ctx is NULL.
+ * Debug: LSO_STREAM_POISON=1 at lso_stream_create makes the context fill
+ * each device slot with NaN once its piece has been copied back, before
+ * the next piece may come in (a slot-reuse race then shows as NaN). */
 int lso_stream_copy_mode(const lso_stream_ctx* ctx, uint32_t* h2d_engine, uint32_t* d2h_engine);
 
 /* Waits for outstanding work, frees slots, events and streams. */

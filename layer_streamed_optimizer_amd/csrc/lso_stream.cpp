@@ -34,7 +34,10 @@
 // cannot be named, H2D runs on a runtime-chosen DMA engine and D2H by a copy
 // kernel, tied by the events above.  LSO_STREAM_COPY=kernel uses copy
 // kernels both ways, LSO_STREAM_COPY=dma runtime-chosen DMA engines both
-// ways, LSO_STREAM_COPY=dma-in the fallback.
+// ways, LSO_STREAM_COPY=dma-in the fallback.  LSO_STREAM_POISON=1 (a debug
+// mode) fills each slot with NaN once its piece has been copied back and
+// before the next piece may come in, so an update that ran ahead of its
+// H2D, or a copy that overtook an update, shows up as NaN in the results.
 //
 // Three kinds of authoritative block:
 //  - pinned host memory (page-locked, e.g. lso_host_alloc): src = dst = the
@@ -318,6 +321,8 @@ struct lso_stream_ctx {
     lso::SdmaLink sdma;                       // kCopyEngines: the two engines
     hsa_signal_t h2d_sig[kMaxSlots] = {};     // kCopyEngines: per slot, its H2D ended
     hsa_signal_t d2h_sig[kMaxSlots] = {};     // kCopyEngines: per slot, its D2H ended
+    bool poison = false;                      // debug: NaN-fill each slot once copied back
+    hipEvent_t poison_done[kMaxSlots] = {};   // kCopyEngines: the slot's fill ended
     unsigned copy_grid = lso::kCopyGrid;
     uint64_t piece_bytes = 1ull << 30;   // target size of a tiled layer's pieces
 };
@@ -349,6 +354,7 @@ void release(lso_stream_ctx* c)
         if (c->weights_ready[s]) (void)hipEventDestroy(c->weights_ready[s]);
         if (c->step_done[s]) (void)hipEventDestroy(c->step_done[s]);
         if (c->buffer_free[s]) (void)hipEventDestroy(c->buffer_free[s]);
+        if (c->poison_done[s]) (void)hipEventDestroy(c->poison_done[s]);
     }
     for (hipStream_t s : {c->h2d, c->compute, c->d2h})
         if (s) (void)hipStreamDestroy(s);
@@ -664,6 +670,7 @@ lso_status issue_unit(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
     // Offload: the updated piece goes back over the authoritative copy.
     if ((err = hipStreamWaitEvent(c->d2h, c->step_done[s], 0)) != hipSuccess ||
         (err = copy_block(c, buf, c->slot_state[s], U.bytes, hipMemcpyDeviceToHost, c->d2h)) != hipSuccess ||
+        (c->poison && (err = hipMemsetAsync(c->slot_state[s], 0xFF, U.bytes, c->d2h)) != hipSuccess) ||
         (err = hipEventRecord(c->buffer_free[s], c->d2h)) != hipSuccess ||
         (err = hipEventRecord(c->d2h_done[i % staging_count(c)], c->d2h)) != hipSuccess)
         return lso::hip_fail(err, "D2H stage");
@@ -842,6 +849,16 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
                (!engines || next_issue < next_retire + S)) {
             const Unit& U = units[next_issue];
             const Job& j = *U.job;
+            if (engines && c->poison && next_issue >= S) {
+                const hipError_t q = hipEventQuery(c->poison_done[next_issue % S]);
+                if (q == hipErrorNotReady) break;
+                if (q != hipSuccess) {
+                    record(lso::hip_fail(q, "slot fill"));
+                    gpu_ok = false;
+                    stop_at = next_issue;
+                    break;
+                }
+            }
             if (j.kind != kPinned) {
                 if (const int e = rd[next_issue % K].err.load()) {
                     record(lso::fail(LSO_E_IO, "layer %zu: reading its %s failed: %s", j.index,
@@ -910,6 +927,16 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
                     record(lso::fail(LSO_E_HIP, "SDMA D2H copy of layer %zu failed", units[next_retire].job->index));
                     gpu_ok = false;
                     stop_at = std::min(stop_at, next_issue);
+                }
+                if (gpu_ok && c->poison) {
+                    const size_t s = next_retire % S;
+                    hipError_t e = hipMemsetAsync(c->slot_state[s], 0xFF, units[next_retire].bytes, c->compute);
+                    if (e == hipSuccess) e = hipEventRecord(c->poison_done[s], c->compute);
+                    if (e != hipSuccess) {
+                        record(lso::hip_fail(e, "slot fill"));
+                        gpu_ok = false;
+                        stop_at = std::min(stop_at, next_issue);
+                    }
                 }
             } else {
                 const hipError_t q = gpu_ok ? hipEventQuery(c->d2h_done[next_retire % K]) : hipSuccess;
@@ -1076,6 +1103,7 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
         const int k = std::atoi(e);
         if (k >= 1 && k <= 4096) c->copy_grid = static_cast<unsigned>(k);
     }
+    if (const char* e = std::getenv("LSO_STREAM_POISON")) c->poison = *e && std::strcmp(e, "0") != 0;
     // default priority on all three (different priorities are not used)
     for (hipStream_t* s : {&c->h2d, &c->compute, &c->d2h}) {
         err = hipStreamCreateWithFlags(s, hipStreamNonBlocking);
@@ -1091,7 +1119,7 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
                              static_cast<unsigned long long>(c->max_bytes),
                              static_cast<unsigned long long>(pbytes));
         }
-        for (hipEvent_t* e : {&c->weights_ready[s], &c->step_done[s], &c->buffer_free[s]}) {
+        for (hipEvent_t* e : {&c->weights_ready[s], &c->step_done[s], &c->buffer_free[s], &c->poison_done[s]}) {
             err = hipEventCreateWithFlags(e, hipEventDisableTiming);
             if (err != hipSuccess) { release(c); return lso::hip_fail(err, "hipEventCreateWithFlags"); }
         }

@@ -329,7 +329,10 @@ def test_named_engines_many_small_pieces_any_slot_count(slots):
     ones, pinned and pageable mixed: the named-engine pipeline, with 2, 3 or
     4 device slots (the host loop reuses each slot's signals every `slots`
     pieces, and a layer's producer is queued ahead at its first H2D), gives
-    the bits of copy kernels with two slots -- state, weights and norms."""
+    the bits of copy kernels with two slots -- state, weights and norms.
+    The named-engine and dma-in runs fill every slot with NaN once its piece
+    is copied back (LSO_STREAM_POISON), so an update that ran before its H2D
+    had landed would leave NaN in the results."""
     T = torch()
     rng = np.random.default_rng(7)
     sizes_t = [int(x) for x in rng.integers(1, 3 * 8192 + 5, 24)]
@@ -339,11 +342,11 @@ def test_named_engines_many_small_pieces_any_slot_count(slots):
     mb = max([configs.host_layer_layout(n, tiled=True)[3] for n in sizes_t] +
              [configs.host_layer_layout(n)[3] for n in sizes_p])
     runs = {}
-    for mode, k in (("sdma-pair", slots), ("kernel", 2)):
-        log("many pieces", mode, "slots", k)
+    for mode, k, poison in (("sdma-pair", slots, 1), ("dma-in", slots, 1), ("kernel", 2, 0)):
+        log("many pieces", mode, "slots", k, "poison", poison)
         ht = HostLayers(sizes_t, sid, tiled=True, pageable=lambda b: b % 3 == 1)
         hp = HostLayers(sizes_p, sid + 1, pageable=lambda b: b % 2 == 0)
-        with stream_pieces(1), stream_env(COPY=mode, SLOTS=k):
+        with stream_pieces(1), stream_env(COPY=mode, SLOTS=k, POISON=poison):
             ls, prm = synth_stream(sizes, sid, max_bytes=mb)
         assert ls.copy_mode()["mode"] == mode
         w = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
@@ -358,8 +361,10 @@ def test_named_engines_many_small_pieces_any_slot_count(slots):
         raw = [ht.raw(b) for b in range(len(sizes_t))] + [hp.raw(b) for b in range(len(sizes_p))]
         runs[mode] = (raw, [x.cpu().numpy() for x in w], norms.copy())
         ls.close()
-    a, b = runs["sdma-pair"], runs["kernel"]
-    for i in range(len(sizes)):
-        assert np.array_equal(a[0][i], b[0][i]), i
-        assert np.array_equal(a[1][i], b[1][i]), i
-    assert np.array_equal(a[2], b[2])
+    b = runs["kernel"]
+    for mode in ("sdma-pair", "dma-in"):
+        a = runs[mode]
+        for i in range(len(sizes)):
+            assert np.array_equal(a[0][i], b[0][i]), (mode, i)
+            assert np.array_equal(a[1][i], b[1][i]), (mode, i)
+        assert np.array_equal(a[2], b[2]), mode
