@@ -583,7 +583,12 @@ lso_status lso_host_free(void* p)
 
 const char* lso_status_string(lso_status s)
 {
-    switch (s) {
+    // a C caller may pass any int; read it as one (a C++ load of an enum
+    // holding a value outside its range is undefined)
+    int code = 0;
+    static_assert(sizeof code == sizeof s, "lso_status is int-sized");
+    std::memcpy(&code, &s, sizeof code);
+    switch (code) {
     case LSO_OK: return "ok";
     case LSO_E_INVALID: return "invalid argument";
     case LSO_E_ALIGN: return "misaligned array";
