@@ -293,16 +293,21 @@ def test_every_copy_mode_gives_the_same_bits(pageable):
     mb = max([configs.host_layer_layout(n, tiled=True)[3] for n in sizes_t] +
              [configs.host_layer_layout(n)[3] for n in sizes_p])
     runs = {}
-    for mode in ("sdma-pair", "dma-in", "kernel", "dma"):
-        log("copy mode", mode, "pageable" if pageable else "pinned")
+    # the last run names the other engine pair itself (LSO_STREAM_SDMA)
+    for name, mode, env in (("sdma-pair", "sdma-pair", {}), ("dma-in", "dma-in", {}),
+                            ("kernel", "kernel", {}), ("dma", "dma", {}),
+                            ("sdma 2,3", "sdma-pair", {"SDMA": "2,3"})):
+        log("copy mode", name, "pageable" if pageable else "pinned")
         ht = HostLayers(sizes_t, sid, tiled=True, pageable=pageable)
         hp = HostLayers(sizes_p, sid + 1, pageable=pageable)
-        with stream_pieces(2), stream_env(COPY=mode):
+        with stream_pieces(2), stream_env(COPY=mode, **env):
             ls, prm = synth_stream(sizes, sid, max_bytes=mb)
         cm = ls.copy_mode()
         assert cm["mode"] == mode, cm
-        if mode == "sdma-pair":
+        if name == "sdma-pair":
             assert cm["h2d_engine"] and cm["d2h_engine"] and cm["h2d_engine"] != cm["d2h_engine"], cm
+        if name == "sdma 2,3":
+            assert (cm["h2d_engine"], cm["d2h_engine"]) == (4, 8), cm
         w = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
         norms = np.zeros(len(sizes))
         for t in range(1, 4):
@@ -313,7 +318,7 @@ def test_every_copy_mode_gives_the_same_bits(pageable):
             ls.stream_layers(L)
         T.cuda.synchronize()
         raw = [ht.raw(b) for b in range(len(sizes_t))] + [hp.raw(b) for b in range(len(sizes_p))]
-        runs[mode] = (raw, [x.cpu().numpy() for x in w], norms.copy())
+        runs[name] = (raw, [x.cpu().numpy() for x in w], norms.copy())
         ls.close()
     ref = runs["sdma-pair"]
     for mode, (raw, w, norms) in runs.items():
