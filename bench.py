@@ -515,6 +515,9 @@ def streamed(args, w):
         roofline=dict(bound="host-link", achieved=per_dir, peak=bidir_peak,
                       unit="GB/s per direction", frac=per_dir / bidir_peak, traffic=None),
         link_peak_GBps=peak,
+        # against a one-way hipMemcpyAsync of page-locked memory (nothing in
+        # the other direction): a looser reference than the duplex peak
+        frac_of_hipmemcpy_one_way=per_dir / min(peak["dma"]["h2d"], peak["dma"]["d2h"]),
         config=dict(workload=f"{w.key}: {w.title}", layers=n_layers, layers_in_config=len(w.blocks),
                     params=params, host_memory="pinned" if pinned else "pageable+staged",
                     state_layout=args.layout,
