@@ -247,13 +247,17 @@ typedef struct lso_host_layer {
     double*  sq_norm;        /* host address that receives the sum of g^2 of
                                 this layer's gradient (FP64) when the call
                                 returns LSO_OK, or NULL */
+    uint32_t grad_dtype;     /* the gradients the producer writes: LSO_DT_BF16
+                                (or 0, the same) or LSO_DT_F32 (4 bytes each,
+                                the FP32-gradient update of lso_adam_step) */
+    uint32_t reserved;       /* must be 0 */
 } lso_host_layer;
 
 /* Gradient producer: enqueue (never synchronise) work on compute_stream
- * that writes n BF16 gradients of layer `layer` into dev_grad_bf16.  A
- * nonzero return stops the stream (lso_stream_layers returns
- * LSO_E_CALLBACK). */
-typedef int (*lso_grad_fn)(void* user, size_t layer, void* dev_grad_bf16, uint64_t n,
+ * that writes the n gradients of layer `layer` into dev_grad, in the
+ * layer's grad_dtype (BF16 unless it asks for LSO_DT_F32).  A nonzero
+ * return stops the stream (lso_stream_layers returns LSO_E_CALLBACK). */
+typedef int (*lso_grad_fn)(void* user, size_t layer, void* dev_grad, uint64_t n,
                            void* compute_stream);
 
 typedef struct lso_stream_ctx lso_stream_ctx;
@@ -262,9 +266,10 @@ typedef struct lso_stream_ctx lso_stream_ctx;
  * of max_layer_bytes (rounded up to 4 KB) of state plus max_layer_params
  * BF16 gradients and BF16 weights each, the events, and the copy mode (see
  * lso_stream_copy_mode; the three pinned staging buffers of that size and
- * the worker threads are added on the first staged layer).  fn/user: the
- * gradient producer.  Errors: INVALID, NOMEM, HIP.  *out is NULL on
- * error. */
+ * the worker threads are added on the first staged layer, and the gradient
+ * buffers grow to FP32 on the first call with an LSO_DT_F32 layer).
+ * fn/user: the gradient producer.  Errors: INVALID, NOMEM, HIP.  *out is
+ * NULL on error. */
 lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params,
                              lso_grad_fn fn, void* user, int device, lso_stream_ctx** out);
 
@@ -310,6 +315,8 @@ typedef struct lso_file_layer {
     uint64_t t;
     double   lr, beta1, beta2, eps;
     double*  sq_norm;
+    uint32_t grad_dtype;
+    uint32_t reserved;
 } lso_file_layer;
 
 /* Stream n_layers file blocks through the pipeline, in order.  On LSO_OK

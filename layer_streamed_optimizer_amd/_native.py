@@ -67,6 +67,8 @@ class LsoHostLayer(ctypes.Structure):
         ("beta2", ctypes.c_double),
         ("eps", ctypes.c_double),
         ("sq_norm", ctypes.c_void_p),
+        ("grad_dtype", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -89,6 +91,8 @@ class LsoFileLayer(ctypes.Structure):
         ("beta2", ctypes.c_double),
         ("eps", ctypes.c_double),
         ("sq_norm", ctypes.c_void_p),
+        ("grad_dtype", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 

@@ -302,6 +302,7 @@ struct lso_stream_ctx {
     hipStream_t h2d = nullptr, compute = nullptr, d2h = nullptr;
     void* slot_state[kMaxSlots] = {};
     void* slot_grad[kMaxSlots] = {};
+    uint64_t grad_elem_bytes = 2;       // slot_grad holds max_params of this size (2 or 4)
     void* slot_weight[kMaxSlots] = {};
     void* staging[kMaxStaging] = {};   // pinned, allocated on the first staged layer
     uint64_t staging_bytes = 0;         // size of each staging buffer
@@ -419,6 +420,8 @@ struct Job {
     uint64_t bytes = 0, n = 0, off_master = 0, off_m = 0, off_v = 0;
     void* dev_weight = nullptr;
     uint32_t opt = 0, layout = 0;
+    uint32_t grad_dtype = 0, reserved = 0;
+    bool grad_f32 = false;    // the producer writes FP32 gradients
     uint64_t t = 0;
     double lr = 0, beta1 = 0, beta2 = 0, eps = 0;
 };
@@ -434,6 +437,9 @@ lso_status check_state(const lso_stream_ctx* c, const Job& L, size_t i)
         return fail(LSO_E_DTYPE, "layer %zu: the tiled state layout is for Adam only", i);
     lso_status s = lso::check_hyper(L.opt, L.t, L.lr, L.beta1, L.beta2, L.eps, i);
     if (s != LSO_OK) return s;
+    if (L.grad_dtype != 0 && L.grad_dtype != LSO_DT_BF16 && L.grad_dtype != LSO_DT_F32)
+        return fail(LSO_E_DTYPE, "layer %zu: gradients must be BF16 or FP32", i);
+    if (L.reserved != 0) return fail(LSO_E_INVALID, "layer %zu: reserved field is not 0", i);
     if (L.bytes == 0 || L.bytes > c->max_bytes)
         return fail(LSO_E_INVALID, "layer %zu: bytes %llu outside (0, %llu]", i,
                     static_cast<unsigned long long>(L.bytes), static_cast<unsigned long long>(c->max_bytes));
@@ -619,9 +625,9 @@ lso_status enqueue_piece_update(lso_stream_ctx* c, const Unit& U, size_t i)
         b.off_m = base + h.off_m;
         b.off_v = base + h.off_v;
     }
-    b.off_grad = reinterpret_cast<uintptr_t>(c->slot_grad[ls]) + 2 * U.e0;
+    b.off_grad = reinterpret_cast<uintptr_t>(c->slot_grad[ls]) + (h.grad_f32 ? 4 : 2) * U.e0;
     b.off_weight = reinterpret_cast<uintptr_t>(h.dev_weight ? h.dev_weight : c->slot_weight[ls]) + 2 * U.e0;
-    b.grad_dtype = LSO_DT_BF16;
+    b.grad_dtype = h.grad_f32 ? LSO_DT_F32 : LSO_DT_BF16;
     b.weight_dtype = LSO_DT_BF16;
     b.opt = h.opt;
     b.layout = h.layout;
@@ -769,6 +775,27 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
     if (any_staged) {
         lso_status s = ensure_staging(c, max_piece);
         if (s != LSO_OK) return s;
+    }
+    if (std::any_of(J, J + nj, [](const Job& j) { return j.grad_f32; }) && c->grad_elem_bytes < 4) {
+        // FP32 gradients: the gradient buffers grow to 4 bytes per parameter,
+        // all or none (no work of an earlier call is pending: every call
+        // ends synchronised)
+        const uint64_t gbytes = round16(4 * (c->max_params ? c->max_params : 1));
+        void* grown[kMaxSlots] = {};
+        for (int s = 0; s < c->nslots; ++s) {
+            if (hipMalloc(&grown[s], gbytes) != hipSuccess) {
+                (void)hipGetLastError();
+                grown[s] = nullptr;
+                for (int k = 0; k < s; ++k) (void)hipFree(grown[k]);
+                return lso::fail(LSO_E_NOMEM, "FP32 gradient buffers of %llu bytes",
+                                 static_cast<unsigned long long>(gbytes));
+            }
+        }
+        for (int s = 0; s < c->nslots; ++s) {
+            if (c->slot_grad[s]) (void)hipFree(c->slot_grad[s]);
+            c->slot_grad[s] = grown[s];
+        }
+        c->grad_elem_bytes = 4;
     }
     if (any_norm && c->norm_cap < n) {
         if (c->dev_norms) (void)hipFree(c->dev_norms);
@@ -1053,6 +1080,9 @@ void copy_state_fields(Job& j, const T& L)
     j.beta2 = L.beta2;
     j.eps = L.eps;
     j.sq_norm = L.sq_norm;
+    j.grad_dtype = L.grad_dtype;
+    j.reserved = L.reserved;
+    j.grad_f32 = L.grad_dtype == LSO_DT_F32;
 }
 
 }  // namespace

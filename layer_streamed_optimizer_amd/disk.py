@@ -137,8 +137,9 @@ class LayerFiles:
         return self.state(i)[2]
 
     def table(self, t: int, lr: float, beta1: float, beta2: float, eps: float,
-              sync: bool = False, opt: int = LSO_OPT_ADAM) -> np.ndarray:
-        """lso_file_layer rows for step t."""
+              sync: bool = False, opt: int = LSO_OPT_ADAM, grad_dtype: int = 0) -> np.ndarray:
+        """lso_file_layer rows for step t (grad_dtype: what the producer
+        writes, LSO_DT_BF16 (0) or LSO_DT_F32)."""
         L = np.zeros(len(self.sizes), FILE_LAYER_DTYPE)
         for i, n in enumerate(self.sizes):
             om, omm, ov, nb = self.geom[i]
@@ -150,6 +151,7 @@ class LayerFiles:
             L[i]["layout"] = LSO_LAYOUT_TILED if self.tiled else LSO_LAYOUT_PLANAR
             L[i]["t"] = t
             L[i]["lr"], L[i]["beta1"], L[i]["beta2"], L[i]["eps"] = lr, beta1, beta2, eps
+            L[i]["grad_dtype"] = grad_dtype
         return L
 
     def write_block(self, i: int, data) -> None:

@@ -196,13 +196,13 @@ def device_fill_zero(ptr: int, nbytes: int, hip_stream: int = 0) -> None:
         raise RuntimeError(f"synth_fill_zero failed ({rc})")
 
 
-def grad_callback():
+def grad_callback(f32: bool = False):
     """(C function pointer, params struct) for the device gradient producer
     that a layer stream calls once per layer: it fills that layer's BF16
-    gradient buffer with purpose-2 deviates for block = block_base + layer.
-    Set ``params.step`` before each streamed step."""
+    gradient buffer (FP32 with ``f32``) with purpose-2 deviates for block =
+    block_base + layer.  Set ``params.step`` before each streamed step."""
     lib = _dev_lib()
-    fn = ctypes.cast(lib.synth_grad_fn, ctypes.c_void_p).value
+    fn = ctypes.cast(lib.synth_grad_fn_f32 if f32 else lib.synth_grad_fn, ctypes.c_void_p).value
     return fn, _FillParams
 
 

@@ -134,4 +134,15 @@ int synth_grad_fn(void* user, size_t layer, void* dev_grad_bf16, uint64_t n, hip
                                   p->scale, s) == 0 ? 0 : 6;
 }
 
+// The same producer for layers whose gradients are FP32: the deviates before
+// their BF16 rounding (synth_fill_normal_f32 with the same counters).
+int synth_grad_fn_f32(void* user, size_t layer, void* dev_grad_f32, uint64_t n, hipStream_t s)
+{
+    const synth_fill_params* p = static_cast<const synth_fill_params*>(user);
+    if (!p || !dev_grad_f32) return 1;
+    return synth_fill_normal_f32(static_cast<float*>(dev_grad_f32), n, 0, p->seed, p->stream,
+                                 p->block_base + static_cast<uint32_t>(layer), p->purpose, p->step,
+                                 p->scale, s) == 0 ? 0 : 6;
+}
+
 }  // extern "C"

@@ -315,7 +315,7 @@ class HostLayers:
         off = {"master": om, "m": omm, "v": ov}[q]
         return self.bufs[b].view(np.float32, off, self.sizes[b]).copy()
 
-    def table(self, t, opt=lso.LSO_OPT_ADAM, lr=LR, dev_weight=None):
+    def table(self, t, opt=lso.LSO_OPT_ADAM, lr=LR, dev_weight=None, grad_dtype=0):
         L = lso.LayerStream.layers(len(self.sizes))
         for b, n in enumerate(self.sizes):
             om, omm, ov, nbytes = self.lay[b]
@@ -328,11 +328,12 @@ class HostLayers:
             L[b]["layout"] = lso.LSO_LAYOUT_TILED if self.tiled else lso.LSO_LAYOUT_PLANAR
             L[b]["t"] = t
             L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = lr, B1, B2, EPS
+            L[b]["grad_dtype"] = grad_dtype
         return L
 
 
-def synth_stream(sizes, sid, max_bytes=None):
-    fn, Params = synth.grad_callback()
+def synth_stream(sizes, sid, max_bytes=None, f32=False):
+    fn, Params = synth.grad_callback(f32)
     params = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
                     scale=synth.scale_for(1e-3), block_base=0)
     mb = max_bytes or max(configs.host_layer_layout(n)[3] for n in sizes)

@@ -9,7 +9,7 @@ import pytest
 import layer_streamed_optimizer_amd as lso
 import oracle
 import synth
-from layer_streamed_optimizer_amd import configs
+from layer_streamed_optimizer_amd import _native, configs
 
 from gpu_util import (HIP_D2D, HostLayers, assert_parity, call_scale, hip, log, stream_env,
                       stream_pieces, synth_stream, torch)
@@ -373,3 +373,136 @@ def test_named_engines_many_small_pieces_any_slot_count(slots):
             assert np.array_equal(a[0][i], b[0][i]), (mode, i)
             assert np.array_equal(a[1][i], b[1][i]), (mode, i)
         assert np.array_equal(a[2], b[2]), mode
+
+
+@pytest.mark.parametrize("pageable", [False, True], ids=["pinned", "pageable"])
+def test_stream_fp32_gradients_match_oracle(pageable):
+    """Layers whose producer writes FP32 gradients (grad_dtype LSO_DT_F32):
+    tiled layers in two-tile pieces and planar layers, three steps, against
+    the oracle's FP32-gradient step (state within 1e-6, weights the RNE of
+    the streamed master) and its sum of g^2 (within 2e-6)."""
+    T = torch()
+    sizes_t = [100003, 8192 * 3 + 1]
+    sizes_p = [7, 50000]
+    sizes = sizes_t + sizes_p
+    sid = 50
+    ht = HostLayers(sizes_t, sid, tiled=True, pageable=pageable)
+    hp = HostLayers(sizes_p, sid + 1, pageable=pageable)
+    ref = [dict(master=ht.get(b, "master"), m=np.zeros(n, np.float32), v=np.zeros(n, np.float32),
+                weight=np.zeros(n, np.uint16)) for b, n in enumerate(sizes_t)]
+    ref += [dict(master=hp.get(b, "master"), m=np.zeros(n, np.float32), v=np.zeros(n, np.float32),
+                 weight=np.zeros(n, np.uint16)) for b, n in enumerate(sizes_p)]
+    mb = max([configs.host_layer_layout(n, tiled=True)[3] for n in sizes_t] +
+             [configs.host_layer_layout(n)[3] for n in sizes_p])
+    with stream_pieces(2):
+        ls, prm = synth_stream(sizes, sid, max_bytes=mb, f32=True)
+    w = [T.zeros(n, dtype=T.int16, device="cuda") for n in sizes]
+    norms = np.zeros(len(sizes))
+    for t in range(1, 4):
+        prm.step = t
+        log("fp32-gradient stream step", t)
+        L = np.concatenate([ht.table(t, grad_dtype=lso.LSO_DT_F32), hp.table(t, grad_dtype=lso.LSO_DT_F32)])
+        L["dev_weight"] = [int(x.data_ptr()) for x in w]
+        L["sq_norm"] = [norms.ctypes.data + 8 * i for i in range(len(sizes))]
+        ls.stream_layers(L)
+        for b, n in enumerate(sizes):
+            g = synth.normal_f32(n, stream=sid, block=b, purpose=2, step=t, sigma=1e-3)
+            oracle.adam_step(ref[b]["master"], ref[b]["m"], ref[b]["v"], g, ref[b]["weight"], t,
+                             LR, B1, B2, EPS)
+            want = oracle.sq_norm(g)
+            assert abs(norms[b] - want) <= 2e-6 * want, (t, b, norms[b], want)
+    T.cuda.synchronize()
+    ls.close()
+    scale = call_scale(ref)
+    for b in range(len(sizes)):
+        h, k = (ht, b) if b < len(sizes_t) else (hp, b - len(sizes_t))
+        got = dict(master=h.get(k, "master"), m=h.get(k, "m"), v=h.get(k, "v"),
+                   weight=w[b].cpu().numpy().view(np.uint16))
+        assert_parity(got, ref[b], 1e-6, f"fp32-gradient streamed layer {b}", scale)
+
+
+def test_stream_gradient_buffers_grow_for_fp32_and_bf16_still_works():
+    """One context: a BF16 call, then an FP32-gradient call (its gradient
+    buffers grow to 4 bytes per parameter), then BF16 again -- the BF16
+    layers match a fresh context's bit for bit and the FP32 layers match
+    the resident FP32-gradient update bit for bit."""
+    T = torch()
+    sizes = [70001, 12345]
+    sid = 51
+    a = HostLayers(sizes, sid)          # BF16 layers, streamed by one context throughout
+    a_ref = HostLayers(sizes, sid)      # the same through a fresh BF16-only context
+    f = HostLayers(sizes, sid + 1)      # FP32-gradient layers
+    fn16, P = synth.grad_callback()
+    fn32, _ = synth.grad_callback(f32=True)
+    mode = {"f32": False}
+    p16 = P(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
+            scale=synth.scale_for(1e-3), block_base=0)
+    p32 = P(seed=synth.SEED, stream=sid + 1, purpose=synth.PURPOSE_GRAD, step=1,
+            scale=synth.scale_for(1e-3), block_base=0)
+    c16 = ctypes.cast(fn16, ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p))
+    c32 = ctypes.cast(fn32, ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p))
+
+    def producer(layer, g, n, s):
+        if mode["f32"]:
+            return c32(ctypes.addressof(p32), layer, g, n, s)
+        return c16(ctypes.addressof(p16), layer, g, n, s)
+
+    mb = max(configs.host_layer_layout(n)[3] for n in sizes)
+    ls = lso.LayerStream(mb, max(sizes), producer)
+    ls_ref, pr = synth_stream(sizes, sid)
+    for t, f32 in ((1, False), (1, True), (2, False), (2, True), (3, False)):
+        log("grow step", t, "f32" if f32 else "bf16")
+        mode["f32"] = f32
+        p16.step = p32.step = pr.step = t
+        if f32:
+            ls.stream_layers(f.table(t, grad_dtype=lso.LSO_DT_F32))
+        else:
+            ls.stream_layers(a.table(t))
+            ls_ref.stream_layers(a_ref.table(t))
+    ls.close()
+    ls_ref.close()
+    for b in range(len(sizes)):
+        assert np.array_equal(a.raw(b), a_ref.raw(b)), b
+    # the FP32-gradient layers against lso_adam_step with FP32 gradients
+    res = []
+    for b, n in enumerate(sizes):
+        res.append(dict(master=T.from_numpy(synth.normal_f32(n, stream=sid + 1, block=b, purpose=0,
+                                                             step=0, sigma=0.02)).cuda(),
+                        m=T.zeros(n, dtype=T.float32, device="cuda"),
+                        v=T.zeros(n, dtype=T.float32, device="cuda"),
+                        g=T.empty(n, dtype=T.float32, device="cuda"),
+                        w=T.empty(n, dtype=T.int16, device="cuda")))
+    for t in (1, 2):
+        rows = []
+        for b, n in enumerate(sizes):
+            synth.device_fill_normal_f32(res[b]["g"].data_ptr(), n, stream=sid + 1, block=b, purpose=2,
+                                         step=t, sigma=1e-3,
+                                         hip_stream=T.cuda.current_stream().cuda_stream)
+            rows.append(dict(n=n, master=res[b]["master"], m=res[b]["m"], v=res[b]["v"],
+                             grad=res[b]["g"], weight=res[b]["w"], t=t, grad_dtype=lso.LSO_DT_F32))
+        lso.adam_step(lso.BlockTable.from_rows(rows))
+    T.cuda.synchronize()
+    for b in range(len(sizes)):
+        for q in ("master", "m", "v"):
+            assert np.array_equal(f.get(b, q).view(np.uint32), res[b][q].cpu().numpy().view(np.uint32)), (b, q)
+
+
+def test_stream_rejects_unknown_gradient_dtype_and_reserved_bits():
+    """grad_dtype outside {0, BF16, FP32} is LSO_E_DTYPE and a nonzero
+    reserved field LSO_E_INVALID, both before anything moves: the host
+    blocks keep their bytes."""
+    sizes = [5000, 300]
+    host = HostLayers(sizes, 52)
+    before = [host.raw(b) for b in range(len(sizes))]
+    ls, prm = synth_stream(sizes, 52)
+    L = host.table(1)
+    L[1]["grad_dtype"] = 7
+    assert ls.stream_layers_status(L) == _native.LSO_E_DTYPE
+    L = host.table(1)
+    L[0]["reserved"] = 1
+    assert ls.stream_layers_status(L) == _native.LSO_E_INVALID
+    ls.close()
+    for b in range(len(sizes)):
+        assert np.array_equal(host.raw(b), before[b]), b

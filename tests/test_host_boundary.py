@@ -56,13 +56,15 @@ int main(void) {
   F(lso_host_layer, off_master) F(lso_host_layer, off_m) F(lso_host_layer, off_v)
   F(lso_host_layer, dev_weight) F(lso_host_layer, opt) F(lso_host_layer, layout)
   F(lso_host_layer, t) F(lso_host_layer, lr) F(lso_host_layer, beta1) F(lso_host_layer, beta2)
-  F(lso_host_layer, eps) F(lso_host_layer, sq_norm)
+  F(lso_host_layer, eps) F(lso_host_layer, sq_norm) F(lso_host_layer, grad_dtype)
+  F(lso_host_layer, reserved)
   printf("lso_file_layer.size %zu\n", sizeof(lso_file_layer));
   F(lso_file_layer, fd) F(lso_file_layer, flags) F(lso_file_layer, file_offset)
   F(lso_file_layer, bytes) F(lso_file_layer, n) F(lso_file_layer, off_master)
   F(lso_file_layer, off_m) F(lso_file_layer, off_v) F(lso_file_layer, dev_weight)
   F(lso_file_layer, opt) F(lso_file_layer, layout) F(lso_file_layer, t) F(lso_file_layer, lr)
   F(lso_file_layer, beta1) F(lso_file_layer, beta2) F(lso_file_layer, eps) F(lso_file_layer, sq_norm)
+  F(lso_file_layer, grad_dtype) F(lso_file_layer, reserved)
   return 0;
 }
 """
