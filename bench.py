@@ -474,11 +474,13 @@ def streamed(args, w):
         ptrs.append(ptr)
         progress(f"layer {b} ready")
     del stage, scratch
-    fn, Params = synth.grad_callback()
+    g32 = args.grad_dtype == "f32"
+    fn, Params = synth.grad_callback(g32)
     prm = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
                  scale=synth.scale_for(configs.GRAD_SIGMA), block_base=0)
     ls = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
     L = lso.LayerStream.layers(n_layers)
+    L["grad_dtype"] = lso.LSO_DT_F32 if g32 else lso.LSO_DT_BF16
     for b in range(n_layers):
         L[b]["host_base"], L[b]["bytes"], L[b]["n"] = ptrs[b], nbytes, n
         L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
@@ -522,7 +524,8 @@ def streamed(args, w):
                     params=params, host_memory="pinned" if pinned else "pageable+staged",
                     state_layout=args.layout,
                     host_bytes=nbytes * n_layers,
-                    link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode),
+                    link_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode,
+                    grad_dtype=args.grad_dtype),
     )
     return result
 
@@ -604,14 +607,16 @@ def streamed_files(args, w):
             progress(f"layer {b} written")
         del view
         del stage, scratch
-        fn, Params = synth.grad_callback()
+        g32 = args.grad_dtype == "f32"
+        fn, Params = synth.grad_callback(g32)
         prm = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
                      scale=synth.scale_for(configs.GRAD_SIGMA), block_base=0)
         ls = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
         step_s = []
         for j in range(1, args.warmup + args.steps + 1):
             prm.step = j
-            L = files.table(j, configs.LR, configs.BETA1, configs.BETA2, configs.EPS, sync=args.sync)
+            L = files.table(j, configs.LR, configs.BETA1, configs.BETA2, configs.EPS, sync=args.sync,
+                            grad_dtype=lso.LSO_DT_F32 if g32 else 0)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             ls.stream_files(L)
@@ -642,6 +647,7 @@ def streamed_files(args, w):
                                 + (", shadow region)" if args.shadow else ")"),
                     state_layout=args.layout, file_bytes=nbytes * n_layers,
                     storage_bytes_per_param_each_way=LINK_BYTES_PER_PARAM, copy_mode=copy_mode,
+                    grad_dtype=args.grad_dtype,
                     flushed_per_layer=bool(args.sync or args.shadow)),
     )
 
@@ -729,8 +735,8 @@ def main():
                     help="resident workloads: the update with per-block gradient norms "
                          "(progressive layer locking)")
     ap.add_argument("--grad-dtype", choices=["bf16", "f32"], default="bf16",
-                    help="gradient dtype of the resident workloads (f32: the LoRA article's FP32 "
-                         "adapter gradients)")
+                    help="gradient dtype (f32: the LoRA article's FP32 adapter gradients; for c4 "
+                         "the device producer writes FP32)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the update is elementwise and would shard by "
@@ -747,9 +753,6 @@ def main():
     args.steps = dk if args.steps is None else args.steps
     if args.steps < 1:
         sys.exit("--steps must be >= 1")
-    if w.streamed and args.grad_dtype != "bf16":
-        sys.exit("--grad-dtype f32 applies to the resident workloads; the layer stream's "
-                 "gradient producer writes BF16")
     if w.streamed:
         res = streamed_files(args, w) if args.host_memory == "file" else streamed(args, w)
     else:
