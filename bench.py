@@ -408,6 +408,36 @@ def link_peak(nbytes=4 << 30):
     return res
 
 
+def link_probe_sweep(sizes=(256 << 20, 1 << 30, 4 << 30, 10 << 30), reps: int = 10) -> list:
+    """The host-link microbenchmark on its own: page-locked buffers of each
+    size, H2D alone, D2H alone and both at once on two streams or engines,
+    best of `reps`, for every engine choice the stream knows: the named SDMA
+    pair, hipMemcpyAsync both ways (the runtime picks the engines), copy
+    kernels both ways (128 workgroups), and hipMemcpyAsync H2D beside a D2H
+    copy kernel."""
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    rows = []
+    for nbytes in sizes:
+        eng = (ctypes.c_uint32 * 2)()
+        out = (ctypes.c_double * 4)()
+        rc = P.lso_probe_link_sdma(nbytes, reps, eng, out)
+        results = {"sdma_pair": (rc, list(out))}
+        for name, mode in (("dma", 0), ("kernel", 3), ("dma_h2d_kernel_d2h", 2)):
+            out = (ctypes.c_double * 4)()
+            rc = P.lso_probe_link_mode(nbytes, reps, mode, 128, out)
+            results[name] = (rc, list(out))
+        for name, (rc, o) in results.items():
+            row = dict(bytes=nbytes, engines=name, status=rc)
+            if rc == 0:
+                row.update(h2d=o[0], d2h=o[1], both_h2d=o[2], both_d2h=o[3])
+            rows.append(row)
+        progress(f"link probe {nbytes >> 20} MiB: " +
+                 ", ".join(f"{r['engines']} {r.get('both_h2d', 0):.1f}/{r.get('both_d2h', 0):.1f}"
+                           for r in rows[-4:]))
+    return rows
+
+
 def best_link_peak(a: dict, b: dict) -> dict:
     """Per engine choice, the better of two link_peak measurements (by the
     slower direction while both run), and the streamed roofline peak over
@@ -714,6 +744,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--link-probe", action="store_true",
+                    help="only the host-link microbenchmark: 256 MiB to 10 GiB page-locked "
+                         "buffers, each direction alone and both at once, best of 10, for every "
+                         "engine choice; one JSON line")
     ap.add_argument("--host-memory", choices=["pageable", "pinned", "file"], default="pageable",
                     help="c4: authoritative blocks in pageable memory (staged through pinned "
                          "buffers), page-locked (direct; limited by the host's page-locked "
@@ -743,6 +777,13 @@ def main():
               "contiguous 1/N ranges with no exchange inside the step; multi-GPU runs are not "
               "part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.link_probe:
+        import torch
+
+        torch.cuda.set_device(0)
+        print(json.dumps(dict(link_probe=link_probe_sweep(), unit="GB/s", best_of=10,
+                              environment=environment())), flush=True)
+        return
     from layer_streamed_optimizer_amd import configs
     w = configs.get(args.config)
     defaults = {"c0": (10, 100), "c1": (2, 10), "c2": (5, 100), "c3": (1, 4), "c4": (1, 2)}
