@@ -391,12 +391,24 @@ def link_peak(nbytes=4 << 30):
     from layer_streamed_optimizer_amd import _native
     P = _native.probes()
     res = {}
-    eng = (ctypes.c_uint32 * 2)()
-    out = (ctypes.c_double * 4)()
-    rc = P.lso_probe_link_sdma(nbytes, 3, eng, out)
-    if rc == 0:
-        res["sdma_pair"] = dict(h2d=out[0], d2h=out[1], bidir_h2d=out[2], bidir_d2h=out[3],
-                                engines=[int(eng[0]), int(eng[1])])
+    # Now and then a D2H copy between one particular device buffer and one
+    # particular page-locked host buffer runs at about half speed (~30 GB/s
+    # even with nothing else running) for as long as both exist, while the
+    # same buffers paired with others are fast: the probe allocates anew and
+    # retries while D2H alone is far below H2D alone.
+    for attempt in range(1, 4):
+        eng = (ctypes.c_uint32 * 2)()
+        out = (ctypes.c_double * 4)()
+        rc = P.lso_probe_link_sdma(nbytes, 3, eng, out)
+        if rc != 0:
+            break
+        r = dict(h2d=out[0], d2h=out[1], bidir_h2d=out[2], bidir_d2h=out[3],
+                 engines=[int(eng[0]), int(eng[1])], attempts=attempt)
+        if "sdma_pair" not in res or min(r["bidir_h2d"], r["bidir_d2h"]) > \
+                min(res["sdma_pair"]["bidir_h2d"], res["sdma_pair"]["bidir_d2h"]):
+            res["sdma_pair"] = r
+        if out[1] >= 0.8 * out[0]:
+            break
     # mode bit 0: H2D by a copy kernel; bit 1: D2H by a copy kernel
     for name, mode in (("dma", 0), ("kernel", 3), ("dma_h2d_kernel_d2h", 2)):
         out = (ctypes.c_double * 4)()
