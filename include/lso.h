@@ -222,8 +222,9 @@ lso_status lso_tiled_unpack(const void* state, float* master, float* m, float* v
  * its D2H.  lso_stream_files does the same with blocks held in files (the
  * disk tier).  Stage-ins and write-outs run on two worker pools, so reading
  * layer i + 1, updating layer i and writing layer i - 1 overlap.  A tiled
- * layer whose state starts its block moves in pieces of whole tiles (about
- * 1 GiB; LSO_STREAM_PIECE_BYTES at context creation sets another size),
+ * layer whose state starts its block moves in equal pieces of whole tiles
+ * (at most 512 MiB; LSO_STREAM_PIECE_BYTES at context creation sets another
+ * size),
  * so the pipeline fills and drains in one piece rather than one layer; its
  * gradient producer still runs once, before the first piece's update.
  * ------------------------------------------------------------------- */
