@@ -399,7 +399,9 @@ def link_peak(nbytes=4 << 30):
     for attempt in range(1, 4):
         eng = (ctypes.c_uint32 * 2)()
         out = (ctypes.c_double * 4)()
-        rc = P.lso_probe_link_sdma(nbytes, 3, eng, out)
+        # a different size each time, so the new buffers do not come back at
+        # the addresses of the ones just freed
+        rc = P.lso_probe_link_sdma(nbytes + (attempt - 1) * (192 << 20), 3, eng, out)
         if rc != 0:
             break
         r = dict(h2d=out[0], d2h=out[1], bidir_h2d=out[2], bidir_d2h=out[3],
