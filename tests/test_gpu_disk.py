@@ -72,6 +72,28 @@ def test_files_equal_host_blocks_bitwise_and_match_oracle(tiled, direct):
         ls.close()
 
 
+def test_files_with_fp32_gradients_equal_host_blocks_bitwise():
+    """FP32-gradient layers (grad_dtype LSO_DT_F32) in O_DIRECT files, tiled:
+    the same bits as the same layers streamed from host blocks, three steps."""
+    T = torch()
+    sid = 66
+    host = HostLayers(SIZES, sid, tiled=True)
+    mb = max(configs.host_layer_layout(n, tiled=True)[3] for n in SIZES)
+    with tempfile.TemporaryDirectory() as d:
+        files = files_like(host, d, direct=True)
+        ls, params = synth_stream(SIZES, sid, max_bytes=mb, f32=True)
+        for t in range(1, 4):
+            params.step = t
+            log("fp32-gradient files step", t)
+            ls.stream_layers(host.table(t, grad_dtype=lso.LSO_DT_F32))
+            ls.stream_files(files.table(t, LR, B1, B2, EPS, grad_dtype=lso.LSO_DT_F32))
+        T.cuda.synchronize()
+        for b in range(len(SIZES)):
+            assert np.array_equal(files.read_block(b), host.raw(b)), b
+        files.close()
+        ls.close()
+
+
 def test_resume_from_manifest_equals_uninterrupted_run():
     """Steps 1-2, close, reopen from the manifest (t comes back as 2), step 3:
     the same bits as three steps in one go.  LSO_FILE_SYNC on."""
