@@ -76,6 +76,19 @@ def environment() -> dict:
             env["rocm"] = open(rocm).read().strip()
     except Exception:
         pass
+    # kernel driver and board, where the system exposes them
+    import glob
+    for key, pattern in (("amdgpu_driver", "/sys/module/amdgpu/version"),
+                         ("gpu_product", "/sys/class/drm/card*/device/product_name"),
+                         ("gpu_vbios", "/sys/class/drm/card*/device/vbios_version")):
+        for path in sorted(glob.glob(pattern)):
+            try:
+                value = open(path).read().strip()
+            except OSError:
+                continue
+            if value:
+                env[key] = value
+                break
     return env
 
 
