@@ -40,7 +40,7 @@ def test_oracle_under_address_and_undefined_sanitizers(tmp_path):
 def test_host_runtime_under_address_and_undefined_sanitizers(tmp_path):
     exe = str(tmp_path / "runtime_driver")
     srcs = [os.path.join(CSRC, f) for f in ("lso_adam.hip", "lso_copy.hip", "lso_tiled.hip", "lso_runtime.cpp",
-                                            "lso_stream.cpp", "lso_shadow.cpp", "lso_sdma.cpp")]
+                                            "lso_stream.cpp", "lso_io.cpp", "lso_shadow.cpp", "lso_sdma.cpp")]
     # each sanitizer flag applies to the host pass only
     host_san = ["-Xarch_host", "-fsanitize=address",
                 "-Xarch_host", "-fsanitize=undefined",
