@@ -1,6 +1,6 @@
 """Benchmark of the per-layer mixed-precision Adam update on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config c1|c0|c2|c3|c4] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config c3|c0|c1|c2|c4] [--gpus 1]
 
 A step is one pass of the whole update over every block of the workload
 (host constants, one ragged multi-tensor launch, the fused kernel) with
@@ -8,12 +8,18 @@ that step's gradients (BF16; FP32 with --grad-dtype f32) already resident
 in HBM.  W untimed steps, then
 K timed steps between two device synchronisations; one JSON line on stdout.
 
+The default run is the LLaMA-7B-shaped resident update (c3, the HBM
+headline), and nested in the same line under "streamed" the 70B-shaped
+slice streamed from host memory (c4, the host-link headline: all 16
+layers in pageable memory, 1 untimed and 3 timed steps of its own;
+--no-streamed leaves it out).
+
 Workloads (shapes from the pages, values synthetic, see
 layer_streamed_optimizer_amd/configs.py):
   c0  one 1024x1024 block                                  (resident)
-  c1  TinyLlama-1.1B shape, 25 blocks, 1,100,048,384 params (resident, default)
+  c1  TinyLlama-1.1B shape, 25 blocks, 1,100,048,384 params (resident)
   c2  LoRA r=8 on TinyLlama, 308 ragged tensors, 6,307,840  (resident)
-  c3  LLaMA-7B shape, 35 blocks, 6,738,415,616 params       (resident, ~108 GB)
+  c3  LLaMA-7B shape, 35 blocks, 6,738,415,616 params       (resident, ~108 GB, default)
   c4  70B-shaped slice, 16 layers of 855,654,400 params, streamed from
       ~164 GB of host memory                                 (streamed)
       --host-memory pageable (default) | pinned | file (the disk tier:
@@ -24,7 +30,8 @@ Roofline: the fused kernel moves 28 algorithmic bytes per parameter (reads
 gradients); its average launch
 duration is measured with HIP events on the launch stream.  The CPU
 baseline is the oracle (plain scalar FP64 C, all host cores) timed on a
-bounded sample of the same workload.
+bounded sample of the same workload: one full decoder-layer block for
+the model-shaped workloads.
 """
 from __future__ import annotations
 
@@ -713,34 +720,57 @@ def streamed_files(args, w):
 
 def cpu_baseline(w, budget_s=12.0):
     """The oracle as it stands, on the host's cores, on a bounded sample:
-    the first blocks of the workload (up to 64M params), repeated steps
-    until budget_s of CPU time has passed."""
+    one full decoder-layer block of a model-shaped workload (its first
+    layer), or the first blocks of the others (up to 64M params), repeated
+    steps until budget_s of CPU time has passed.  Its inputs are drawn on
+    the device and copied down (the device generator equals the host one
+    bit for bit; the oracle's speed does not depend on the values)."""
     import numpy as np
+    import torch
 
     import oracle
     import synth
     from layer_streamed_optimizer_amd import configs
 
     sid = configs.STREAM_ID[w.key]
-    take, blocks = 0, []
-    for b, spec in enumerate(w.blocks):
-        if take >= (64 << 20):
-            break
-        n = min(spec.n, (64 << 20) - take)
-        blocks.append((b, n))
-        take += n
+    layer = next((b for b, spec in enumerate(w.blocks) if spec.name == "layer0"), None)
+    if layer is not None:
+        blocks = [(layer, w.blocks[layer].n)]
+        what = f"one full decoder-layer block of {w.key} (block {layer}, {w.blocks[layer].n:,} params)"
+    else:
+        take, blocks = 0, []
+        for b, spec in enumerate(w.blocks):
+            if take >= (64 << 20):
+                break
+            n = min(spec.n, (64 << 20) - take)
+            blocks.append((b, n))
+            take += n
+        what = f"first {take:,} params of {w.key} ({len(blocks)} block(s))"
+    take = sum(n for _, n in blocks)
+    hs = torch.cuda.current_stream().cuda_stream
+    dev = torch.empty(4 * max(n for _, n in blocks), dtype=torch.uint8, device="cuda")
+
+    def draw(n, b, purpose, step, sigma, bf16):
+        fill = synth.device_fill_normal_bf16 if bf16 else synth.device_fill_normal_f32
+        fill(int(dev.data_ptr()), n, stream=sid, block=b, purpose=purpose, step=step, sigma=sigma,
+             hip_stream=hs)
+        torch.cuda.synchronize()
+        return dev[: (2 if bf16 else 4) * n].cpu().numpy().view(np.uint16 if bf16 else np.float32).copy()
+
     arrays = []
     for b, n in blocks:
-        master = synth.normal_f32(n, stream=sid, block=b, purpose=0, step=0, sigma=0.02)
-        g = synth.normal_bf16(n, stream=sid, block=b, purpose=2, step=1, sigma=1e-3)
+        master = draw(n, b, synth.PURPOSE_MASTER, 0, configs.MASTER_SIGMA, False)
+        g = draw(n, b, synth.PURPOSE_GRAD, 1, configs.GRAD_SIGMA, True)
         arrays.append((master, np.zeros(n, np.float32), np.zeros(n, np.float32), g,
                        np.zeros(n, np.uint16)))
+    del dev
     steps, threads = 0, 0
     t0 = time.perf_counter()
     while True:
         steps += 1
         for master, m, v, g, wb in arrays:
-            threads = oracle.adam_step(master, m, v, g, wb, steps, 1e-3, 0.9, 0.999, 1e-8)
+            threads = oracle.adam_step(master, m, v, g, wb, steps, configs.LR, configs.BETA1, configs.BETA2,
+                                       configs.EPS)
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
@@ -750,14 +780,13 @@ def cpu_baseline(w, budget_s=12.0):
     s1, t1 = 0, time.perf_counter()
     while True:
         s1 += 1
-        oracle.adam_step(master[:k1], m[:k1], v[:k1], g[:k1], wb[:k1], steps + s1, 1e-3, 0.9, 0.999,
-                         1e-8, threads=1)
+        oracle.adam_step(master[:k1], m[:k1], v[:k1], g[:k1], wb[:k1], steps + s1, configs.LR,
+                         configs.BETA1, configs.BETA2, configs.EPS, threads=1)
         if time.perf_counter() - t1 >= budget_s / 4:
             break
     d1 = time.perf_counter() - t1
     return dict(value=take * steps / dt / 1e9, unit="Gparams/s", cores=threads, kind="oracle",
-                sample=f"first {take:,} params of {w.key} ({len(blocks)} block(s)), {steps} steps, "
-                       f"{dt:.1f} s, inputs in host RAM",
+                sample=f"{what}, {steps} steps, {dt:.1f} s, inputs in host RAM",
                 single_thread=dict(value=k1 * s1 / d1 / 1e9, unit="Gparams/s",
                                    sample=f"{k1:,} params, {s1} steps, {d1:.1f} s"))
 
@@ -769,8 +798,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    ap.add_argument("--config", default="c3", choices=["c0", "c1", "c2", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-streamed", action="store_true",
+                    help="c3: leave out the nested streamed record (c4, 16 pageable layers)")
+    ap.add_argument("--streamed-steps", type=int, default=3,
+                    help="timed steps of the nested streamed record (after 1 untimed step)")
     ap.add_argument("--link-probe", action="store_true",
                     help="only the host-link microbenchmark: 256 MiB to 10 GiB page-locked "
                          "buffers, each direction alone and both at once, best of 10, for every "
@@ -813,7 +846,7 @@ def main():
         return
     from layer_streamed_optimizer_amd import configs
     w = configs.get(args.config)
-    defaults = {"c0": (10, 100), "c1": (2, 10), "c2": (5, 100), "c3": (1, 4), "c4": (1, 2)}
+    defaults = {"c0": (10, 100), "c1": (2, 10), "c2": (5, 100), "c3": (2, 10), "c4": (1, 2)}
     dw, dk = defaults[args.config]
     if args.layout is None:
         args.layout = "planar" if args.config in ("c0", "c2") else "tiled"
@@ -833,6 +866,19 @@ def main():
         progress("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(w)
     out.update(res)
+    if w.key == "c3" and not args.no_streamed:
+        # the streamed headline in the same run: c4 as its benchmark
+        # configuration (16 layers, pageable + staged, tiled, 512 MiB pieces)
+        import torch
+        torch.cuda.empty_cache()
+        sa = argparse.Namespace(**vars(args))
+        sa.layers, sa.host_memory, sa.layout, sa.grad_dtype = 0, "pageable", "tiled", "bf16"
+        sa.warmup, sa.steps = 1, max(1, args.streamed_steps)
+        progress(f"streamed record: c4, {sa.warmup} untimed + {sa.steps} timed steps")
+        r = streamed(sa, configs.get("c4"))
+        out["streamed"] = dict(metric=r.pop("metric"), value=r.pop("value"), unit=r.pop("unit"),
+                               steps=sa.steps, warmup=sa.warmup, ms_per_step=r.pop("ms_per_step"),
+                               config=r.pop("config"), roofline=r.pop("roofline"), **r)
     out["environment"] = environment()
     print(json.dumps(out), flush=True)
 

@@ -186,6 +186,12 @@ lso_status lso_adam_step_norms(const lso_block* blocks, size_t n, double* sq_nor
 lso_status lso_validate_blocks(const lso_block* blocks, size_t n);
 lso_status lso_block_constants(const lso_block* block, float out[8]);
 
+/* Fused-update kernel launches this process has enqueued so far (every
+ * entry point, every device).  The update of a call is one launch per
+ * (layout, gradient dtype) and per 16 hyper-parameter sets; this counter is
+ * how a caller checks it.  Host-only, thread-safe. */
+uint64_t lso_kernel_launches(void);
+
 /* Bytes of the tiled state region of n parameters: 12 * T * ceil(n / T),
  * T = LSO_TILE_ELEMS (0 for n == 0). */
 uint64_t lso_tiled_state_bytes(uint64_t n);

@@ -30,7 +30,7 @@ BLOCK_DTYPE = np.dtype(LsoBlock)
 HOST_LAYER_DTYPE = np.dtype(LsoHostLayer)
 FILE_LAYER_DTYPE = np.dtype(LsoFileLayer)
 
-__all__ = ["BlockTable", "adam_step", "adam_step_norms", "norm_workspace_bytes", "validate",
+__all__ = ["BlockTable", "adam_step", "adam_step_norms", "launch_count", "norm_workspace_bytes", "validate",
            "block_constants", "LayerStream", "HostBuffer", "host_alloc", "LsoError", "LSO_OPT_ADAM",
            "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE", "LSO_DT_F32", "LSO_LAYOUT_PLANAR",
            "LSO_LAYOUT_TILED", "LSO_TILE_ELEMS", "BLOCK_DTYPE", "HOST_LAYER_DTYPE", "FILE_LAYER_DTYPE",
@@ -140,6 +140,11 @@ def adam_step_norms(table: BlockTable, sq_norms, workspace, workspace_bytes: int
     st = _native.lib().lso_adam_step_norms(table.ptr, len(table), _addr(sq_norms), _addr(workspace),
                                            int(workspace_bytes), stream_handle(stream))
     _native.check(st, "lso_adam_step_norms")
+
+
+def launch_count() -> int:
+    """Fused-update kernel launches this process has enqueued (host counter)."""
+    return int(_native.lib().lso_kernel_launches())
 
 
 def validate(table: BlockTable) -> int:

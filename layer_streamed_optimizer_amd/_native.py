@@ -100,7 +100,8 @@ GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctype
                            ctypes.c_uint64, ctypes.c_void_p)
 
 # every symbol include/lso.h declares
-EXPORTS = ("lso_adam_step", "lso_norm_workspace_bytes", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants", "lso_tiled_state_bytes",
+EXPORTS = ("lso_adam_step", "lso_norm_workspace_bytes", "lso_adam_step_norms", "lso_validate_blocks",
+           "lso_block_constants", "lso_kernel_launches", "lso_tiled_state_bytes",
            "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
            "lso_stream_files", "lso_shadow_format", "lso_shadow_state", "lso_shadow_commit",
            "lso_stream_copy_mode", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc",
@@ -132,6 +133,8 @@ def lib():
         L.lso_adam_step_norms.argtypes = [vp, sz, vp, vp, u64, vp]
         L.lso_validate_blocks.argtypes = [vp, sz]
         L.lso_block_constants.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
+        L.lso_kernel_launches.argtypes = []
+        L.lso_kernel_launches.restype = u64
         L.lso_tiled_state_bytes.argtypes = [u64]
         L.lso_tiled_state_bytes.restype = u64
         L.lso_tiled_pack.argtypes = [vp, vp, vp, vp, u64, vp]

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -15,6 +16,11 @@
 #include "lso_runtime.h"
 
 namespace lso {
+
+// Fused-update launches enqueued by this process (lso_kernel_launches).
+static std::atomic<uint64_t> g_launches{0};
+
+void count_launch() { g_launches.fetch_add(1, std::memory_order_relaxed); }
 
 // ------------------------------------------------------------------ errors
 
@@ -491,6 +497,7 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
             if (norms) args.partials = norms->workspace + part_offset * kNormPartsPerChunk;
             int err = launch_fused_adam(args, unroll, tiled_pass, g32_pass, stream);
             if (err != 0) return hip_fail(err, "fused Adam launch");
+            count_launch();
             if (norms) {
                 err = launch_norm_reduce(args, unroll, norms->sq_norms, stream);
                 if (err != 0) return hip_fail(err, "norm reduction launch");
@@ -538,6 +545,8 @@ lso_status lso_adam_step_norms(const lso_block* blocks, size_t n, double* sq_nor
 }
 
 uint64_t lso_tiled_state_bytes(uint64_t n) { return lso::tiled_bytes(n); }
+
+uint64_t lso_kernel_launches(void) { return lso::g_launches.load(std::memory_order_relaxed); }
 
 lso_status lso_validate_blocks(const lso_block* blocks, size_t n)
 {

@@ -13,6 +13,9 @@ lso_status fail(lso_status s, const char* fmt, ...);
 lso_status hip_fail(int hip_error, const char* what);
 void clear_error();
 
+// Count one fused-update kernel launch (lso_kernel_launches).
+void count_launch();
+
 // Bytes of the tiled state region of n parameters.
 uint64_t tiled_bytes(uint64_t n);
 

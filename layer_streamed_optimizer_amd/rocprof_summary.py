@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 CSV output as short markdown (for profiles/).
 
-    python -m layer_streamed_optimizer_amd.rocprof_summary stats  --csv X_kernel_stats.csv --command "..."
+    python -m layer_streamed_optimizer_amd.rocprof_summary stats  --csv X_kernel_stats.csv --command "..." \
+            [--trace X_kernel_trace.csv]
     python -m layer_streamed_optimizer_amd.rocprof_summary pmc    --fetch F.csv --write W.csv --params N \
             --copy-bytes B --command-fetch "..." --command-write "..."
     python -m layer_streamed_optimizer_amd.rocprof_summary stream --trace X_kernel_trace.csv --layers L \
@@ -45,6 +46,22 @@ def stats(args) -> str:
         out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                    f"{float(r['Percentage']):.1f}% |")
+    if args.trace:
+        # one kernel can serve several workloads in one run (the resident
+        # update and the streamed pieces): split its dispatches by grid size
+        by = {}
+        for r in csv.DictReader(open(args.trace)):
+            if args.kernel not in r["Kernel_Name"]:
+                continue
+            grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            key = (r["Kernel_Name"], grid)
+            by.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out += ["", f"Dispatches of `{args.kernel}` by grid (workgroups), from the kernel trace:", "",
+                "| Kernel | Workgroups | Calls | Average (us) | Median (us) | Min (us) | Max (us) |",
+                "|---|---|---|---|---|---|---|"]
+        for (name, grid), d in sorted(by.items(), key=lambda kv: -len(kv[1]) * statistics.mean(kv[1])):
+            out.append(f"| `{short(name)}` | {grid:,} | {len(d)} | {statistics.mean(d):.1f} | "
+                       f"{statistics.median(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
     out.append("")
     out.append(f"kernel_source_sha256: {kernel_hash()}")
     return "\n".join(out) + "\n"
@@ -170,6 +187,8 @@ def main(argv=None):
     a.add_argument("--command", required=True)
     a.add_argument("--title", default="")
     a.add_argument("--top", type=int, default=6)
+    a.add_argument("--trace", default=None, help="X_kernel_trace.csv: split --kernel's dispatches by grid")
+    a.add_argument("--kernel", default="fused_adam")
     b = sub.add_parser("pmc")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)

@@ -16,7 +16,7 @@ import oracle
 import synth
 from layer_streamed_optimizer_amd import configs
 
-from gpu_util import TILE, assert_parity, call_scale, log, max_errors, torch
+from gpu_util import TILE, Worst, assert_parity, log, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -124,13 +124,10 @@ def run_resident_sampled(key, steps, tiled=True):
             refs.append(ref)
             gots.append(got)
             where.append((b, off))
-    scale = call_scale(refs)
-    worst = {}
+    worst = Worst()
     for ref, got, (b, off) in zip(refs, gots, where):
-        assert_parity(got, ref, 1e-6, f"{key} block {b} offset {off}", scale)
-        for k, v in max_errors(got, ref, scale).items():
-            worst[k] = max(worst.get(k, 0.0), v)
-    log(f"{key} sampled max errors after {steps} steps", worst)
+        worst.add(f"block {b} offset {off}", assert_parity(got, ref, 1e-6, f"{key} block {b} offset {off}"))
+    log(f"{key} sampled worst errors after {steps} steps: {worst}")
     del state, grad, weight
     T.cuda.empty_cache()
 
@@ -151,27 +148,43 @@ def test_c3_llama7b_full_size_sampled():
     run_resident_sampled("c3", 5)
 
 
-@pytest.mark.parametrize("tiled", [True, False], ids=["tiled_in_pieces", "planar"])
-def test_c4_layer_shape_streamed_sampled(tiled):
-    """Three full 70B-shaped layers (855,654,400 params each, 10.27 GB host
-    blocks) streamed for three steps through the same pipeline the benchmark
-    times (tiled state moves in ~1 GiB pieces); sampled parity of the
-    authoritative host state."""
+PIECE_BYTES = 512 << 20   # the stream's default largest piece of a tiled layer
+
+
+def piece_starts(n, piece_bytes=PIECE_BYTES):
+    """First element of every piece after the first of a tiled layer block:
+    the layer's tiles spread evenly over as many pieces as pieces of at most
+    piece_bytes take, the first (tiles % pieces) of them one tile longer
+    (the rule of the stream's piece plan, restated)."""
+    per = max(1, piece_bytes // (12 * TILE))
+    tiles = (n + TILE - 1) // TILE
+    if tiles <= per:
+        return []
+    k_n = (tiles + per - 1) // per
+    q, r = divmod(tiles, k_n)
+    return [(k * q + min(k, r)) * TILE for k in range(1, k_n)]
+
+
+def make_host_layers(n_layers, n, tiled, pinned, sid):
+    """Authoritative host blocks of n_layers 70B-shaped layers: master drawn
+    on the device (the device generator equals the host one bit for bit),
+    m = v = 0, copied down; page-locked (lso_host_alloc) or pageable."""
     import ctypes
     T = torch()
-    sid = configs.STREAM_ID["c4"]
-    n = configs.layer_params(**configs.LLAMA70B)
     om, omm, ov, nbytes = configs.host_layer_layout(n, tiled=tiled)
-    n_layers, steps = 3, 3
-    log(f"c4 layer shape: {n_layers} x {n:,} params, {nbytes / 1e9:.2f} GB host blocks, tiled={tiled}")
     hs = T.cuda.current_stream().cuda_stream
-    hosts = []
     stage = T.empty(nbytes, dtype=T.uint8, device="cuda")
     scratch = T.empty(n, dtype=T.float32, device="cuda") if tiled else None
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hosts, ptrs = [], []
     for b in range(n_layers):
-        hb = lso.host_alloc(nbytes)
+        if pinned:
+            hb = lso.host_alloc(nbytes)
+            ptr = hb.ptr
+        else:
+            hb = np.empty(nbytes, dtype=np.uint8)
+            ptr = hb.ctypes.data
         synth.device_fill_zero(int(stage.data_ptr()), nbytes, hs)
         dst = int(scratch.data_ptr()) if tiled else int(stage.data_ptr()) + om
         synth.device_fill_normal_f32(dst, n, stream=sid, block=b, purpose=synth.PURPOSE_MASTER, step=0,
@@ -179,16 +192,74 @@ def test_c4_layer_shape_streamed_sampled(tiled):
         if tiled:
             lso.tiled_pack(int(stage.data_ptr()) + om, dst, None, None, n=n, stream=hs)
         T.cuda.synchronize()
-        assert hip.hipMemcpy(hb.ptr, int(stage.data_ptr()), nbytes, 2) == 0
+        assert hip.hipMemcpy(ptr, int(stage.data_ptr()), nbytes, 2) == 0
         hosts.append(hb)
+        ptrs.append(ptr)
+        if b % 4 == 3 or b == n_layers - 1:
+            log(f"host layers ready: {b + 1} of {n_layers}")
     del stage, scratch
+    return hosts, ptrs, (om, omm, ov, nbytes)
+
+
+def host_view(hb, pinned):
+    """(float32 view of a host block, by byte offset and count)."""
+    if pinned:
+        return lambda off, cnt: hb.view(np.float32, off, cnt)
+    return lambda off, cnt: hb[off: off + 4 * cnt].view(np.float32)
+
+
+def oracle_samples(sid, layer, spans, steps, weights=False):
+    """The oracle's state after `steps` steps for each (offset, length)
+    span of a 70B-shaped layer, rebuilt from the host generator."""
+    out = []
+    for off, ln in spans:
+        ref = dict(master=synth.normal_f32(ln, stream=sid, block=layer, purpose=synth.PURPOSE_MASTER,
+                                           step=0, sigma=configs.MASTER_SIGMA, start=off),
+                   m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32))
+        if weights:
+            ref["weight"] = np.zeros(ln, np.uint16)
+        for t in range(1, steps + 1):
+            g = synth.normal_bf16(ln, stream=sid, block=layer, purpose=synth.PURPOSE_GRAD, step=t,
+                                  sigma=configs.GRAD_SIGMA, start=off)
+            oracle.adam_step(ref["master"], ref["m"], ref["v"], g, ref.get("weight"), t, configs.LR,
+                             configs.BETA1, configs.BETA2, configs.EPS)
+        out.append(ref)
+    return out
+
+
+def read_host_sample(view, tiled, lay, off, ln):
+    om, omm, ov, _ = lay
+    if tiled:
+        t0, t1 = off // TILE, (off + ln - 1) // TILE + 1
+        reg = view(om + 12 * TILE * t0, 3 * TILE * (t1 - t0)).reshape(t1 - t0, 3, TILE)
+        lo = off - t0 * TILE
+        return {q: reg[:, k, :].ravel()[lo: lo + ln].copy() for k, q in enumerate(("master", "m", "v"))}
+    return {q: view(o + 4 * off, ln).copy() for q, o in (("master", om), ("m", omm), ("v", ov))}
+
+
+def run_streamed_sampled(n_layers, tiled, pinned, steps=3, check_weights=False):
+    """n_layers full 70B-shaped layers streamed for `steps` steps through
+    the stream's default pipeline; sampled parity of the authoritative host
+    state of every layer (start, ragged end, six seeded offsets, and for a
+    tiled layer the last and first elements around every piece boundary)
+    and, with check_weights, of the BF16 re-cast the last two layers leave
+    in the device slots."""
+    import ctypes
+    T = torch()
+    sid = configs.STREAM_ID["c4"]
+    n = configs.layer_params(**configs.LLAMA70B)
+    log(f"c4 layer shape: {n_layers} x {n:,} params, tiled={tiled}, pinned={pinned}, {steps} steps")
+    hosts, ptrs, lay = make_host_layers(n_layers, n, tiled, pinned, sid)
+    om, omm, ov, nbytes = lay
     fn, Params = synth.grad_callback()
     prm = Params(seed=synth.SEED, stream=sid, purpose=synth.PURPOSE_GRAD, step=1,
                  scale=synth.scale_for(configs.GRAD_SIGMA), block_base=0)
     ls = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
+    mode = ls.copy_mode()
+    log(f"copy mode {mode}")
     L = lso.LayerStream.layers(n_layers)
     for b in range(n_layers):
-        L[b]["host_base"], L[b]["bytes"], L[b]["n"] = hosts[b].ptr, nbytes, n
+        L[b]["host_base"], L[b]["bytes"], L[b]["n"] = ptrs[b], nbytes, n
         L[b]["off_master"], L[b]["off_m"], L[b]["off_v"] = om, omm, ov
         L[b]["layout"] = lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR
         L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = (configs.LR, configs.BETA1,
@@ -198,37 +269,60 @@ def test_c4_layer_shape_streamed_sampled(tiled):
         L["t"] = t
         log(f"c4 streamed step {t}")
         ls.stream_layers(L)
-    ls.close()
-    refs, gots = [], []
+    # the BF16 re-cast of the last two layers, still in the slots (slot = layer % 2)
+    slot_w = {b: ls.slot_weight(b % 2) for b in range(max(0, n_layers - 2), n_layers)} if check_weights else {}
+    worst = Worst()
+    bounds = piece_starts(n) if tiled else []
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    wdev = T.empty(SAMPLE, dtype=T.int16, device="cuda") if slot_w else None
     for b in range(n_layers):
-        # the piece boundaries of a tiled layer fall on multiples of 10,922 tiles
-        extra = [10922 * TILE - SAMPLE // 2] if tiled else []
-        for off, ln in sample_offsets(n, 2000 + b) + [(o, SAMPLE) for o in extra]:
-            ref = dict(master=synth.normal_f32(ln, stream=sid, block=b, purpose=synth.PURPOSE_MASTER,
-                                               step=0, sigma=configs.MASTER_SIGMA, start=off),
-                       m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32))
-            for t in range(1, steps + 1):
-                g = synth.normal_bf16(ln, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=t,
-                                      sigma=configs.GRAD_SIGMA, start=off)
-                oracle.adam_step(ref["master"], ref["m"], ref["v"], g, None, t, configs.LR,
-                                 configs.BETA1, configs.BETA2, configs.EPS)
-            if tiled:
-                t0, t1 = off // TILE, (off + ln - 1) // TILE + 1
-                reg = hosts[b].view(np.float32, om + 12 * TILE * t0, 3 * TILE * (t1 - t0))
-                reg = reg.reshape(t1 - t0, 3, TILE)
-                lo = off - t0 * TILE
-                got = {q: reg[:, k, :].ravel()[lo: lo + ln].copy()
-                       for k, q in enumerate(("master", "m", "v"))}
-            else:
-                got = {q: hosts[b].view(np.float32, o + 4 * off, ln).copy()
-                       for q, o in (("master", om), ("m", omm), ("v", ov))}
-            refs.append(ref)
-            gots.append(got)
-    scale = call_scale(refs)
-    for i, (ref, got) in enumerate(zip(refs, gots)):
-        assert_parity(got, ref, 1e-6, f"c4 sample {i}", scale)
-    for hb in hosts:
-        hb.close()
+        spans = sample_offsets(n, 2000 + b)
+        # just before and just after every piece boundary
+        spans += [(p - SAMPLE // 2, SAMPLE) for p in bounds]
+        refs = oracle_samples(sid, b, spans, steps, weights=b in slot_w)
+        view = host_view(hosts[b], pinned)
+        for (off, ln), ref in zip(spans, refs):
+            got = read_host_sample(view, tiled, lay, off, ln)
+            if b in slot_w:
+                assert hip.hipMemcpy(int(wdev.data_ptr()), slot_w[b] + 2 * off, 2 * ln, 3) == 0
+                got["weight"] = wdev[:ln].cpu().numpy().view(np.uint16).copy()
+            worst.add(f"layer {b} offset {off}",
+                      assert_parity(got, ref, 1e-6, f"c4 layer {b} offset {off} (n={ln})"))
+        log(f"layer {b}: {len(spans)} samples checked")
+    log(f"c4 {n_layers} layers, {steps} steps, worst errors: {worst}")
+    ls.close()
+    if pinned:
+        for hb in hosts:
+            hb.close()
+    hosts.clear()
+
+
+@pytest.mark.parametrize("tiled", [True, False], ids=["tiled_in_pieces", "planar"])
+def test_c4_layer_shape_streamed_sampled(tiled):
+    """Three full 70B-shaped layers (855,654,400 params each, 10.27 GB
+    page-locked host blocks) streamed for three steps; sampled parity of
+    the authoritative host state, the piece boundaries of a tiled layer
+    included."""
+    run_streamed_sampled(3, tiled, pinned=True)
+
+
+def test_c4_benchmark_configuration_16_pageable_layers():
+    """The streamed configuration the benchmark times: all 16 layers of the
+    70B-shaped slice, tiled state in pageable host memory (164 GB) staged
+    through pinned buffers, moved in 512 MiB pieces on the default copy
+    engines, three steps.  Every layer is sampled (its piece boundaries
+    too), and the BF16 weights the last two layers leave in the device slots
+    are checked against the oracle's re-cast."""
+    mem = {}
+    with open("/proc/meminfo") as f:
+        for line in f:
+            k, v = line.split(":", 1)
+            mem[k] = int(v.split()[0]) * 1024
+    need = 16 * configs.host_layer_layout(configs.layer_params(**configs.LLAMA70B), tiled=True)[3]
+    if mem.get("MemAvailable", 0) < need + (24 << 30):
+        pytest.skip(f"needs {need / 1e9:.0f} GB of host memory plus headroom")
+    run_streamed_sampled(16, True, pinned=False, check_weights=True)
 
 
 @pytest.mark.parametrize("tiled", [False, True], ids=["planar", "tiled"])
@@ -290,8 +384,7 @@ def test_block_of_more_than_2_32_elements_sampled(tiled):
         got["weight"] = weight[2 * off: 2 * (off + SAMPLE)].cpu().numpy().view(np.uint16).copy()
         refs.append(ref)
         gots.append(got)
-    scale = call_scale(refs)
     for off, ref, got in zip(offs, refs, gots):
-        assert_parity(got, ref, 1e-6, f"element offset {off}", scale)
+        assert_parity(got, ref, 1e-6, f"element offset {off}")
     del state, grad, weight
     T.cuda.empty_cache()

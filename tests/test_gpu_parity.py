@@ -9,7 +9,7 @@ import oracle
 import synth
 from layer_streamed_optimizer_amd import configs
 
-from gpu_util import (Arena, assert_parity, bf16_value, call_scale, detile_state, log,
+from gpu_util import (Arena, Worst, assert_parity, bf16_value, call_scale, detile_state, log,
                       max_errors, torch)
 
 pytestmark = pytest.mark.gpu
@@ -109,11 +109,13 @@ def test_ragged_sizes_table_path():
     run_parity(sizes, 10, 91)
 
 
-@pytest.mark.parametrize("grad_f32,steps", [(False, 100), (True, 30)], ids=["bf16_grads", "f32_grads"])
+@pytest.mark.parametrize("grad_f32,steps", [(False, 100), (True, 10)], ids=["bf16_grads", "f32_grads"])
 def test_c2_lora_308_tensors_one_launch_per_step(grad_f32, steps):
-    """308 ragged tensors (A ~ N(0, 1/8), B = 0); step 10 at 1e-6; step 100
-    at the stated looser 5e-6 (FP32 rounding accumulates with the steps).
-    The LoRA article keeps adapter gradients in FP32: the f32_grads case."""
+    """308 ragged tensors (A ~ N(0, 1/8), B = 0); every tensor judged at its
+    own RMS: step 10 at 1e-6; step 100 at the stated looser 5e-6 (FP32
+    rounding accumulates with the steps).  The LoRA article keeps adapter
+    gradients in FP32: the f32_grads case, checked at step 10.  Each step is
+    one kernel launch (the library's launch counter)."""
     w = configs.get("c2")
     sizes = [b.n for b in w.blocks]
     init = [b.init for b in w.blocks]
@@ -129,19 +131,21 @@ def test_c2_lora_308_tensors_one_launch_per_step(grad_f32, steps):
         for i, g in enumerate(gs):
             arena.put(i, "grad", g)
         table.set_step(t)
+        before = lso.launch_count()
         lso.adam_step(table, T.cuda.current_stream())
+        assert lso.launch_count() - before == 1, "one kernel launch per step"
         oracle_step(ref, gs, t)
         if t in (10, steps):
             T.cuda.synchronize()
             tol = TOL10 if t <= 10 else 5e-6
-            worst = {}
-            scale = call_scale(ref)
+            worst = {"A": Worst(), "B": Worst()}
             for i in range(len(sizes)):
                 got = read_arena(arena, i)
-                assert_parity(got, ref[i], tol, f"lora tensor {i} step {t}", scale)
-                for k, v in max_errors(got, ref[i], scale).items():
-                    worst[k] = max(worst.get(k, 0.0), v)
-            log(f"c2 step {t} max errors", worst)
+                kind = "A" if init[i] == "lora_a" else "B"
+                worst[kind].add(f"tensor {i} n={sizes[i]}",
+                                assert_parity(got, ref[i], tol, f"lora tensor {i} ({kind}) step {t}"))
+            log(f"c2 step {t} worst per-tensor errors, A tensors: {worst['A']}")
+            log(f"c2 step {t} worst per-tensor errors, B tensors: {worst['B']}")
     assert arena.canaries_intact()
 
 
@@ -348,17 +352,20 @@ def test_gpu_sgd_matches_oracle_bitwise_and_page_test1():
 
 
 def test_gpu_nonfinite_gradients_stay_local():
+    """NaN and +-Inf gradients give the oracle's NaN / Inf at their own
+    elements (the same class and sign per element) and nothing anywhere
+    else: every finite element is judged by assert_parity."""
     T = torch()
-    n = 64
+    n = 4096
     arena = Arena([n])
-    master = np.linspace(-1, 1, n).astype(np.float32)
+    master = synth.normal_f32(n, stream=99, block=0, purpose=0, step=0, sigma=0.02)
     arena.put(0, "master", master)
     arena.put(0, "m", np.zeros(n, np.float32))
     arena.put(0, "v", np.zeros(n, np.float32))
     g = synth.normal_bf16(n, stream=99, block=0, purpose=2, step=1, sigma=1e-3)
-    g[5] = 0x7FC0   # NaN
-    g[9] = 0x7F80   # +Inf
-    g[13] = 0xFF80  # -Inf
+    bad = {5: 0x7FC0, 9: 0x7F80, 13: 0xFF80, 1029: 0xFFC1, 4095: 0x7F80}   # NaN, +Inf, -Inf, NaN, +Inf
+    for i, bits in bad.items():
+        g[i] = bits
     arena.put(0, "grad", g)
     lso.adam_step(arena.table())
     T.cuda.synchronize()
@@ -366,10 +373,15 @@ def test_gpu_nonfinite_gradients_stay_local():
                weight=np.zeros(n, np.uint16))
     oracle.adam_step(ref["master"], ref["m"], ref["v"], g, ref["weight"], 1, LR, B1, B2, EPS)
     got = read_arena(arena, 0)
+    fin = np.ones(n, bool)
     for q in ("master", "m", "v"):
         assert np.array_equal(np.isnan(got[q]), np.isnan(ref[q])), q
-    fin = ~np.isnan(ref["master"])
-    assert np.max(np.abs(got["master"][fin] - ref["master"][fin])) < 1e-6
+        assert np.array_equal(np.isposinf(got[q]), np.isposinf(ref[q])), q
+        assert np.array_equal(np.isneginf(got[q]), np.isneginf(ref[q])), q
+        fin &= np.isfinite(ref[q])
+    assert set(np.flatnonzero(~fin)) == set(bad), "non-finite values spread beyond their elements"
+    assert_parity({k: got[k][fin] for k in ("master", "m", "v", "weight")},
+                  {k: ref[k][fin] for k in ("master", "m", "v", "weight")}, TOL10, "finite elements")
     assert np.array_equal(got["weight"], oracle.bf16_rne(got["master"]))
 
 
