@@ -149,6 +149,29 @@ typedef struct lso_block {
 lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream);
 
 /*
+ * lso_adam_step_noalloc: lso_adam_step for callers that cannot allocate
+ * device memory -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same update, bit for bit, with the
+ * same arguments, validation and launches; it calls no hipMalloc, hipFree
+ * or other allocating routine.  The block table of a launch with more
+ * than 4 blocks goes into a fixed per-device scratch array of
+ * LSO_NOALLOC_MAX_BLOCKS entries (256 KiB, held by each GPU the library
+ * runs on until the process ends), written on `stream` by a small kernel
+ * whose arguments carry it (so nothing is read from host memory after the
+ * call returns); tables of up to 4 blocks travel in the kernel arguments as
+ * with lso_adam_step.  The workgroups of the update then find their blocks
+ * by a binary search over that table.  Limit: the launches of one call
+ * hold at most LSO_NOALLOC_MAX_BLOCKS table entries in all (blocks with
+ * n == 0 and launches of up to 4 blocks take none); a larger call returns
+ * LSO_E_INVALID with nothing enqueued.  Every call on one GPU shares that
+ * GPU's array and leaves its table there: calls that overlap on one GPU
+ * (different streams, or unordered threads) race on it and must not be
+ * issued.  Errors: as lso_adam_step (NOMEM cannot occur).
+ */
+#define LSO_NOALLOC_MAX_BLOCKS 4096u
+lso_status lso_adam_step_noalloc(const lso_block* blocks, size_t n, void* stream);
+
+/*
  * Gradient norms for progressive layer locking.  The frozen-incremental
  * page (section "Progressive Layer Locking") locks a layer once its
  * gradient magnitude is below a threshold: locked layers get no gradient,

@@ -30,7 +30,7 @@ BLOCK_DTYPE = np.dtype(LsoBlock)
 HOST_LAYER_DTYPE = np.dtype(LsoHostLayer)
 FILE_LAYER_DTYPE = np.dtype(LsoFileLayer)
 
-__all__ = ["BlockTable", "adam_step", "adam_step_norms", "launch_count", "norm_workspace_bytes", "validate",
+__all__ = ["BlockTable", "adam_step", "adam_step_noalloc", "adam_step_norms", "launch_count", "norm_workspace_bytes", "validate",
            "block_constants", "LayerStream", "HostBuffer", "host_alloc", "LsoError", "LSO_OPT_ADAM",
            "LSO_OPT_SGD", "LSO_DT_BF16", "LSO_DT_NONE", "LSO_DT_F32", "LSO_LAYOUT_PLANAR",
            "LSO_LAYOUT_TILED", "LSO_TILE_ELEMS", "BLOCK_DTYPE", "HOST_LAYER_DTYPE", "FILE_LAYER_DTYPE",
@@ -126,6 +126,16 @@ def adam_step(table: BlockTable, stream=None) -> None:
     st = _step_fn(table._ptr, len(table.arr), stream if type(stream) is int else stream_handle(stream))
     if st:
         _native.check(st, "lso_adam_step")
+
+
+def adam_step_noalloc(table: BlockTable, stream=None) -> None:
+    """adam_step for callers that cannot allocate device memory: the same
+    update, with the block table kept in the library's fixed per-device
+    scratch array (at most LSO_NOALLOC_MAX_BLOCKS entries per call).  Calls
+    that overlap on one GPU race on that array."""
+    st = _native.lib().lso_adam_step_noalloc(table.ptr, len(table), stream_handle(stream))
+    if st:
+        _native.check(st, "lso_adam_step_noalloc")
 
 
 def norm_workspace_bytes(table: BlockTable) -> int:

@@ -20,6 +20,7 @@ LSO_TILE_ELEMS = 8192
 LSO_FILE_SYNC = 1
 LSO_FILE_SHADOW = 2
 LSO_SHADOW_HEADER_BYTES = 8192
+LSO_NOALLOC_MAX_BLOCKS = 4096
 LSO_COPY_SDMA_PAIR, LSO_COPY_DMA_IN, LSO_COPY_KERNELS, LSO_COPY_DMA = 0, 1, 2, 3
 COPY_MODE_NAMES = {LSO_COPY_SDMA_PAIR: "sdma-pair", LSO_COPY_DMA_IN: "dma-in", LSO_COPY_KERNELS: "kernel",
                    LSO_COPY_DMA: "dma"}
@@ -100,7 +101,7 @@ GRAD_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctype
                            ctypes.c_uint64, ctypes.c_void_p)
 
 # every symbol include/lso.h declares
-EXPORTS = ("lso_adam_step", "lso_norm_workspace_bytes", "lso_adam_step_norms", "lso_validate_blocks",
+EXPORTS = ("lso_adam_step", "lso_adam_step_noalloc", "lso_norm_workspace_bytes", "lso_adam_step_norms", "lso_validate_blocks",
            "lso_block_constants", "lso_kernel_launches", "lso_tiled_state_bytes",
            "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
            "lso_stream_files", "lso_shadow_format", "lso_shadow_state", "lso_shadow_commit",
@@ -128,6 +129,7 @@ def lib():
         L = ctypes.CDLL(path)
         vp, sz, u64, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint64, ctypes.c_int
         L.lso_adam_step.argtypes = [vp, sz, vp]
+        L.lso_adam_step_noalloc.argtypes = [vp, sz, vp]
         L.lso_norm_workspace_bytes.argtypes = [vp, sz]
         L.lso_norm_workspace_bytes.restype = u64
         L.lso_adam_step_norms.argtypes = [vp, sz, vp, vp, u64, vp]
@@ -157,7 +159,7 @@ def lib():
         L.lso_status_string.restype = ctypes.c_char_p
         L.lso_last_error.argtypes = []
         L.lso_last_error.restype = ctypes.c_char_p
-        for name in ("lso_adam_step", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants",
+        for name in ("lso_adam_step", "lso_adam_step_noalloc", "lso_adam_step_norms", "lso_validate_blocks", "lso_block_constants",
                      "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create",
                      "lso_stream_layers", "lso_stream_files", "lso_shadow_format", "lso_shadow_state",
                      "lso_shadow_commit", "lso_stream_destroy", "lso_host_alloc", "lso_host_free"):

@@ -25,7 +25,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 LINK = ["-lhsa-runtime64"]
 
 LIBS = {
-    "liblso.so": ["lso_adam.hip", "lso_copy.hip", "lso_tiled.hip", "lso_runtime.cpp",
+    "liblso.so": ["lso_adam.hip", "lso_copy.hip", "lso_tiled.hip", "lso_noalloc.hip", "lso_runtime.cpp",
                   "lso_stream.cpp", "lso_io.cpp", "lso_shadow.cpp", "lso_sdma.cpp"],
     "liblso_probes.so": ["lso_probes.hip", "lso_probe_io.cpp", "lso_sdma.cpp"],
 }

@@ -143,7 +143,8 @@ lso_status collect_geometry(const lso_block* blocks, size_t n, std::vector<Inter
 
 lso_status validate_geometry(const lso_block* blocks, size_t n)
 {
-    std::vector<Interval> iv;
+    thread_local std::vector<Interval> iv;   // reused: no allocation once grown
+    iv.clear();
     lso_status s = collect_geometry(blocks, n, iv);
     if (s != LSO_OK) return s;
     return check_overlap(iv);
@@ -394,8 +395,14 @@ uint64_t norm_workspace_bytes(const lso_block* blocks, size_t n)
     return chunks * kNormPartsPerChunk * sizeof(double);
 }
 
-lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked,
-                          const NormOut* norms)
+namespace {
+
+// The update of one call: one launch per (launch kind, 16 constant sets).
+// A launch's table of more than kInline blocks lives in a cached device
+// table (allocated on first sight), or with noalloc in the device's fixed
+// scratch array (written on the stream every call).
+lso_status enqueue_impl(const lso_block* blocks, size_t n, void* stream, bool geometry_checked,
+                        const NormOut* norms, bool noalloc)
 {
     if (n == 0) return LSO_OK;
     if (!blocks) return fail(LSO_E_INVALID, "blocks is NULL");
@@ -425,6 +432,34 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
     const size_t set_groups = (sets.size() + kMaxGroups - 1) / kMaxGroups;
     const size_t launches = set_groups * static_cast<size_t>(kinds);
     bool checked = geometry_checked;
+    DevBlock* scratch = nullptr;
+    size_t scratch_used = 0;
+    if (noalloc) {
+        // every table of the call must fit the scratch array; checked (with
+        // the addresses) before anything is enqueued
+        size_t need = 0;
+        for (int kind = 0; kind < 4; ++kind) {
+            if (!present[kind]) continue;
+            for (size_t L = 0; L < set_groups; ++L) {
+                size_t cnt = 0;
+                for (size_t i = 0; i < n; ++i)
+                    cnt += blocks[i].n != 0 && kind_of(blocks[i]) == kind && set_of[i] / kMaxGroups == L;
+                if (cnt > static_cast<size_t>(kInline)) need += cnt;
+            }
+        }
+        if (need > LSO_NOALLOC_MAX_BLOCKS)
+            return fail(LSO_E_INVALID, "%zu block-table entries exceed the %u of lso_adam_step_noalloc", need,
+                        static_cast<unsigned>(LSO_NOALLOC_MAX_BLOCKS));
+        if (!checked) {
+            lso_status s = validate_geometry(blocks, n);
+            if (s != LSO_OK) return s;
+            checked = true;
+        }
+        if (need > 0) {
+            lso_status s = noalloc_scratch(&scratch);
+            if (s != LSO_OK) return s;
+        }
+    }
     if (launches > 1 && !checked) {
         // overlaps across the launches of one call are checked up front, so
         // an error never follows a launch already enqueued
@@ -490,6 +525,12 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
                     last_ok_n = tab.size();
                 }
                 for (size_t j = 0; j < tab.size(); ++j) args.inl[j] = tab[j];
+            } else if (noalloc) {
+                lso_status s = noalloc_write_table(scratch + scratch_used, tab.data(), tab.size(), stream);
+                if (s != LSO_OK) return s;
+                args.blocks = scratch + scratch_used;
+                args.chunk_block = nullptr;   // the kernel searches the table
+                scratch_used += tab.size();
             } else {
                 lso_status s = device_table(blocks, n, checked, tab, chunks, unroll, stream, args);
                 if (s != LSO_OK) return s;
@@ -506,6 +547,19 @@ lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool 
         }
     }
     return LSO_OK;
+}
+
+}  // namespace
+
+lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked,
+                          const NormOut* norms)
+{
+    return enqueue_impl(blocks, n, stream, geometry_checked, norms, false);
+}
+
+lso_status enqueue_update_noalloc(const lso_block* blocks, size_t n, void* stream)
+{
+    return enqueue_impl(blocks, n, stream, false, nullptr, true);
 }
 
 }  // namespace lso

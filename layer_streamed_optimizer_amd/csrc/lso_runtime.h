@@ -43,4 +43,19 @@ lso_status validate_norm_buffers(const lso_block* blocks, size_t n, const NormOu
 lso_status enqueue_update(const lso_block* blocks, size_t n, void* stream, bool geometry_checked,
                           const NormOut* norms = nullptr);
 
+struct DevBlock;
+
+// The current device's fixed scratch array of LSO_NOALLOC_MAX_BLOCKS
+// DevBlocks (lso_noalloc.hip); its address is looked up once per device.
+lso_status noalloc_scratch(DevBlock** out);
+
+// Enqueue on stream the writes of count table entries to dst (inside the
+// scratch array), carried in kernel arguments.
+lso_status noalloc_write_table(DevBlock* dst, const DevBlock* tab, size_t count, void* stream);
+
+// lso_adam_step_noalloc: validate every call, and keep the block tables of
+// the call's launches in the device's fixed scratch array instead of
+// allocated, cached device tables (no allocation of any kind).
+lso_status enqueue_update_noalloc(const lso_block* blocks, size_t n, void* stream);
+
 }  // namespace lso

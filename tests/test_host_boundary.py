@@ -88,7 +88,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define\s+(LSO_[A-Z0-9_]+)\s+(\d+)u?\b", text))
     for name in ("LSO_COPY_SDMA_PAIR", "LSO_COPY_DMA_IN", "LSO_COPY_KERNELS", "LSO_COPY_DMA",
-                 "LSO_FILE_SYNC", "LSO_FILE_SHADOW", "LSO_SHADOW_HEADER_BYTES", "LSO_TILE_ELEMS"):
+                 "LSO_FILE_SYNC", "LSO_FILE_SHADOW", "LSO_SHADOW_HEADER_BYTES", "LSO_TILE_ELEMS",
+                 "LSO_NOALLOC_MAX_BLOCKS"):
         assert int(defs[name]) == getattr(_native, name), name
     codes = [getattr(_native, n) for n in ("LSO_COPY_SDMA_PAIR", "LSO_COPY_DMA_IN", "LSO_COPY_KERNELS",
                                            "LSO_COPY_DMA")]
@@ -225,6 +226,25 @@ def test_adam_step_rejects_before_touching_the_device():
 
 def test_empty_adam_step_is_a_no_op():
     lso.adam_step(table([]), stream=0)
+    lso.adam_step_noalloc(table([]), stream=0)
+
+
+def test_noalloc_rejects_tables_beyond_its_scratch_before_touching_the_device():
+    """lso_adam_step_noalloc: a call whose launches need more table entries
+    than the fixed scratch array holds is refused with a clear error before
+    any HIP call (this runs without a GPU); so are the usual invalid tables."""
+    rows = [row(k, n=16) for k in range(_native.LSO_NOALLOC_MAX_BLOCKS + 1)]
+    with pytest.raises(lso.LsoError) as e:
+        lso.adam_step_noalloc(table(rows), stream=0)
+    assert e.value.status == _native.LSO_E_INVALID and "exceed" in str(e.value)
+    r = row(0)
+    r["master"] += 4
+    with pytest.raises(lso.LsoError) as e:
+        lso.adam_step_noalloc(table([r]), stream=0)
+    assert e.value.status == _native.LSO_E_ALIGN
+    with pytest.raises(lso.LsoError) as e:
+        lso.adam_step_noalloc(table([row(0), row(0)] + [row(k) for k in range(2, 7)]), stream=0)
+    assert e.value.status == _native.LSO_E_OVERLAP
 
 
 # ----------------------------------------------------------------- constants
