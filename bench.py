@@ -399,6 +399,55 @@ def shaped_ceiling(torch, dev, tiled: bool, n: int = 134_283 * 8192) -> float:
     return 28 * n / (ms * 1e-3) / 1e9
 
 
+def hbm_probe(nbytes: int = 8 << 30, reps: int = 6) -> dict:
+    """The HBM ceiling for the update's 1:1 read/write traffic: every shape
+    of lso_probe_copy_variant over nbytes, best-of-`reps` GB/s counting the
+    bytes read plus the bytes written, each copy checked bit for bit."""
+    import torch
+
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    dev = torch.device("cuda:0")
+    hs = torch.cuda.current_stream().cuda_stream
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    keep = src.clone()
+    cases = [("base: 1 vector per lane, nt", 0, 0)]
+    cases += [(f"direct-to-LDS read phase then write phase, {kb} KB per workgroup", 1, kb)
+              for kb in (4, 8, 16, 32, 64)]
+    cases += [(f"{p} vectors per lane in registers", 2, p) for p in (1, 2, 4, 8)]
+    names = ["none", "nt", "sc1", "nt sc1", "sc0 sc1", "sc0 sc1 nt"]
+    cases += [(f"cache policy: load {names[l]}, store {names[st]}", 3, l + 8 * st)
+              for l in range(6) for st in range(6)]
+    cases += [("in place (read and write the same addresses)", 4, 0), ("read only", 5, 0),
+              ("write only", 6, 0)]
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = []
+    for name, var, param in cases:
+        dst.zero_()
+        times = []
+        for r in range(reps + 2):   # an even count: in place ends where it began
+            s.record()
+            rc = P.lso_probe_copy_variant(var, param, src.data_ptr(), dst.data_ptr(), nbytes, hs)
+            e.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"lso_probe_copy_variant({var}, {param}) failed ({rc})")
+            if r >= 2:
+                times.append(s.elapsed_time(e))
+        moved = nbytes if var in (5, 6) else 2 * nbytes
+        ok = None
+        if var in (0, 1, 2, 3):
+            ok = bool(torch.equal(src, dst))
+        elif var == 4:
+            ok = bool(torch.equal(src, keep))
+        gbps = moved / (min(times) * 1e-3) / 1e9
+        rows.append(dict(shape=name, variant=var, param=param, GBps=gbps, exact=ok))
+        progress(f"hbm probe: {name}: {gbps:.0f} GB/s{'' if ok is not False else ' WRONG'}")
+    del src, dst, keep
+    return dict(hbm_probe=rows, bytes=nbytes, best_of=reps, unit="GB/s (read + write)")
+
+
 # ------------------------------------------------------------ streamed path
 
 def link_peak(nbytes=4 << 30):
@@ -808,6 +857,9 @@ def main():
                     help="only the host-link microbenchmark: 256 MiB to 10 GiB page-locked "
                          "buffers, each direction alone and both at once, best of 10, for every "
                          "engine choice; one JSON line")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only the HBM ceiling sweep: every shape of the 1:1 read/write copy "
+                         "probe over 8 GiB, best of 6; one JSON line")
     ap.add_argument("--host-memory", choices=["pageable", "pinned", "file"], default="pageable",
                     help="c4: authoritative blocks in pageable memory (staged through pinned "
                          "buffers), page-locked (direct; limited by the host's page-locked "
@@ -843,6 +895,14 @@ def main():
         torch.cuda.set_device(0)
         print(json.dumps(dict(link_probe=link_probe_sweep(), unit="GB/s", best_of=10,
                               environment=environment())), flush=True)
+        return
+    if args.hbm_probe:
+        import torch
+
+        torch.cuda.set_device(0)
+        out = hbm_probe()
+        out["environment"] = environment()
+        print(json.dumps(out), flush=True)
         return
     from layer_streamed_optimizer_amd import configs
     w = configs.get(args.config)

@@ -178,6 +178,8 @@ def probes():
         vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
         P.lso_probe_copy.argtypes = [vp, vp, u64, ctypes.c_uint, vp]
         P.lso_probe_copy.restype = ctypes.c_int
+        P.lso_probe_copy_variant.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, u64, vp]
+        P.lso_probe_copy_variant.restype = ctypes.c_int
         P.lso_probe_copy_shaped.argtypes = [vp, vp, vp, u64, ctypes.c_int, vp]
         P.lso_probe_copy_shaped.restype = ctypes.c_int
         P.lso_probe_link_sdma.argtypes = [u64, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32),

@@ -8,6 +8,12 @@
 //                      written, in the planar or tiled state layout, one
 //                      1,024-element chunk per workgroup -- the ceiling of
 //                      the update's own traffic shape.
+//  lso_probe_copy_variant  other shapes of the same 1:1 read/write
+//                      stream (direct-to-LDS loads with a read phase and a
+//                      write phase per workgroup, several vectors in flight
+//                      per lane, cache-policy bits, in-place, read-only and
+//                      write-only streams), to find the part's ceiling for
+//                      the update's traffic
 //  lso_probe_link_mode / lso_probe_link_sdma  host-link rates, each
 //                      direction alone and both at once, per copy engine
 //  lso_probe_bf16_rne  the fused kernel's BF16 rounding applied to a range
@@ -100,6 +106,108 @@ shaped_copy_kernel(float* __restrict__ state, const uint16_t* __restrict__ grad,
     st_nt<u32x2>(weight + e0 + i, w);
 }
 
+// ---- copy variants (lso_probe_copy_variant) ----
+
+#define LSO_LDS __attribute__((address_space(3)))
+
+// Read phase then write phase per workgroup: the workgroup's KB kilobytes
+// are loaded straight into LDS (global_load_lds_dwordx4: no VGPRs held by
+// the loads, so all of them are in flight at once), then written out from
+// LDS.  Lane t of wave w's load k lands at LDS vector k*256 + w*64 + t.
+template <int KB>
+__global__ void __launch_bounds__(256)
+copy_lds_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst)
+{
+    constexpr int kVec = KB * 1024 / 16;   // vectors per workgroup
+    constexpr int kPer = kVec / 256;       // per lane
+    __shared__ u32x4 buf[kVec];
+    const uint64_t base = static_cast<uint64_t>(blockIdx.x) * kVec;
+    const int wave0 = threadIdx.x & ~63;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const u32x4* s = src + base + k * 256 + threadIdx.x;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const LSO_GLOBAL void*>(reinterpret_cast<uintptr_t>(s)),
+                                         (LSO_LDS void*)(&buf[k * 256 + wave0]), 16, 0, 2 /* nt */);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        st_nt<u32x4>(dst + base + k * 256 + threadIdx.x, buf[k * 256 + threadIdx.x]);
+}
+
+// P vectors per lane: all P loads, then all P stores (a workgroup covers
+// 256 * P consecutive vectors, lane-interleaved).
+template <int P>
+__global__ void __launch_bounds__(256)
+copy_regs_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst)
+{
+    const uint64_t base = static_cast<uint64_t>(blockIdx.x) * 256 * P;
+    u32x4 x[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) x[k] = ld_nt<u32x4>(src + base + k * 256 + threadIdx.x);
+#pragma unroll
+    for (int k = 0; k < P; ++k) st_nt<u32x4>(dst + base + k * 256 + threadIdx.x, x[k]);
+}
+
+// One vector per lane with the cache-policy bits of the load (L) and the
+// store (S): 0 none, 1 nt, 2 sc1, 3 nt sc1, 4 sc0 sc1, 5 sc0 sc1 nt.
+#define LSO_CPOL_LOAD(ms) \
+    asm volatile("global_load_dwordx4 %0, %1, off " ms "\n\ts_waitcnt vmcnt(0)" : "=v"(x) : "v"(s) : "memory")
+#define LSO_CPOL_STORE(ms) asm volatile("global_store_dwordx4 %0, %1, off " ms : : "v"(d), "v"(x) : "memory")
+
+template <int L, int S>
+__global__ void __launch_bounds__(256)
+copy_cpol_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst)
+{
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const LSO_GLOBAL u32x4* s = reinterpret_cast<const LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(src + i));
+    LSO_GLOBAL u32x4* d = reinterpret_cast<LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(dst + i));
+    u32x4 x;
+    if (L == 0) LSO_CPOL_LOAD("");
+    else if (L == 1) LSO_CPOL_LOAD("nt");
+    else if (L == 2) LSO_CPOL_LOAD("sc1");
+    else if (L == 3) LSO_CPOL_LOAD("nt sc1");
+    else if (L == 4) LSO_CPOL_LOAD("sc0 sc1");
+    else LSO_CPOL_LOAD("sc0 sc1 nt");
+    if (S == 0) LSO_CPOL_STORE("");
+    else if (S == 1) LSO_CPOL_STORE("nt");
+    else if (S == 2) LSO_CPOL_STORE("sc1");
+    else if (S == 3) LSO_CPOL_STORE("nt sc1");
+    else if (S == 4) LSO_CPOL_STORE("sc0 sc1");
+    else LSO_CPOL_STORE("sc0 sc1 nt");
+}
+
+// In place: every vector read and written back to the same address (bits
+// flipped), as the update does with its state.
+__global__ void __launch_bounds__(256)
+inplace_kernel(u32x4* __restrict__ buf)
+{
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const u32x4 x = ld_nt<u32x4>(buf + i);
+    st_nt<u32x4>(buf + i, ~x);
+}
+
+// Read-only: every vector read; one word per workgroup written so the
+// loads stay.
+__global__ void __launch_bounds__(256)
+read_only_kernel(const u32x4* __restrict__ src, uint32_t* __restrict__ sink)
+{
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const u32x4 x = ld_nt<u32x4>(src + i);
+    const uint32_t r = x.x ^ x.y ^ x.z ^ x.w;
+    if (r == 0x9E3779B9u) sink[blockIdx.x] = r;   // practically never
+}
+
+// Write-only: every vector written.
+__global__ void __launch_bounds__(256)
+write_only_kernel(u32x4* __restrict__ dst)
+{
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const uint32_t v = static_cast<uint32_t>(i);
+    st_nt<u32x4>(dst + i, u32x4{v, v, v, v});
+}
+
 __global__ void __launch_bounds__(256)
 bf16_probe_kernel(uint32_t first, uint64_t count, uint16_t* __restrict__ out)
 {
@@ -154,6 +262,73 @@ int lso_probe_copy_shaped(void* state, const void* grad, void* weight, uint64_t 
     else
         hipLaunchKernelGGL(shaped_copy_kernel<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
                            st, g, w, n);
+    return static_cast<int>(hipGetLastError());
+}
+
+// One variant of the device copy of lso_probe_copy over `bytes` (a multiple
+// of 64 KiB; src and dst 16-byte aligned, not overlapping, at most 2^36
+// bytes), one chunk per workgroup, no grid loop:
+//   0  one vector per lane, nt load and store (lso_probe_copy's shape)
+//   1  direct-to-LDS read phase, then write phase; param = KB per workgroup
+//      (4, 8, 16, 32 or 64)
+//   2  param vectors per lane in registers (1, 2, 4 or 8)
+//   3  cache-policy bits: param = load policy + 8 * store policy (0..5 each,
+//      see copy_cpol_kernel)
+//   4  in place over src (dst unused): read and write the same addresses
+//   5  read-only over src (dst receives at most a few words)
+//   6  write-only over dst
+// Returns a hipError_t (hipErrorInvalidValue for a bad variant, param or
+// size).
+int lso_probe_copy_variant(int variant, int param, const void* src, void* dst, uint64_t bytes, void* stream)
+{
+    if (bytes == 0 || bytes % (64 << 10) != 0 || bytes > (uint64_t(1) << 36) || !src || !dst ||
+        reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+        return static_cast<int>(hipErrorInvalidValue);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const auto* s = static_cast<const u32x4*>(src);
+    auto* d = static_cast<u32x4*>(dst);
+    const uint64_t n16 = bytes / 16;
+    const dim3 t(256);
+    const unsigned g1 = static_cast<unsigned>(n16 / 256);   // one vector per lane
+    switch (variant) {
+    case 0: hipLaunchKernelGGL(copy_kernel, dim3(g1), t, 0, st, s, d, n16); break;
+    case 1:
+        switch (param) {
+        case 4: hipLaunchKernelGGL(copy_lds_kernel<4>, dim3(bytes / (4 << 10)), t, 0, st, s, d); break;
+        case 8: hipLaunchKernelGGL(copy_lds_kernel<8>, dim3(bytes / (8 << 10)), t, 0, st, s, d); break;
+        case 16: hipLaunchKernelGGL(copy_lds_kernel<16>, dim3(bytes / (16 << 10)), t, 0, st, s, d); break;
+        case 32: hipLaunchKernelGGL(copy_lds_kernel<32>, dim3(bytes / (32 << 10)), t, 0, st, s, d); break;
+        case 64: hipLaunchKernelGGL(copy_lds_kernel<64>, dim3(bytes / (64 << 10)), t, 0, st, s, d); break;
+        default: return static_cast<int>(hipErrorInvalidValue);
+        }
+        break;
+    case 2:
+        switch (param) {
+        case 1: hipLaunchKernelGGL(copy_regs_kernel<1>, dim3(g1), t, 0, st, s, d); break;
+        case 2: hipLaunchKernelGGL(copy_regs_kernel<2>, dim3(g1 / 2), t, 0, st, s, d); break;
+        case 4: hipLaunchKernelGGL(copy_regs_kernel<4>, dim3(g1 / 4), t, 0, st, s, d); break;
+        case 8: hipLaunchKernelGGL(copy_regs_kernel<8>, dim3(g1 / 8), t, 0, st, s, d); break;
+        default: return static_cast<int>(hipErrorInvalidValue);
+        }
+        break;
+    case 3: {
+        const int L = param % 8, S = param / 8;
+        if (L > 5 || S > 5 || param < 0) return static_cast<int>(hipErrorInvalidValue);
+#define LSO_CPOL_CASE(l, s_) \
+    if (L == l && S == s_) hipLaunchKernelGGL((copy_cpol_kernel<l, s_>), dim3(g1), t, 0, st, s, d)
+#define LSO_CPOL_ROW(l) \
+    LSO_CPOL_CASE(l, 0); LSO_CPOL_CASE(l, 1); LSO_CPOL_CASE(l, 2); LSO_CPOL_CASE(l, 3); LSO_CPOL_CASE(l, 4); \
+    LSO_CPOL_CASE(l, 5)
+        LSO_CPOL_ROW(0); LSO_CPOL_ROW(1); LSO_CPOL_ROW(2); LSO_CPOL_ROW(3); LSO_CPOL_ROW(4); LSO_CPOL_ROW(5);
+#undef LSO_CPOL_ROW
+#undef LSO_CPOL_CASE
+        break;
+    }
+    case 4: hipLaunchKernelGGL(inplace_kernel, dim3(g1), t, 0, st, const_cast<u32x4*>(s)); break;
+    case 5: hipLaunchKernelGGL(read_only_kernel, dim3(g1), t, 0, st, s, static_cast<uint32_t*>(dst)); break;
+    case 6: hipLaunchKernelGGL(write_only_kernel, dim3(g1), t, 0, st, d); break;
+    default: return static_cast<int>(hipErrorInvalidValue);
+    }
     return static_cast<int>(hipGetLastError());
 }
 
