@@ -92,6 +92,16 @@ int main()
     // argument checks ahead of any device call
     EXPECT(lso_adam_step(tab.data(), 0, nullptr) == LSO_OK);
     EXPECT(lso_adam_step(nullptr, 1, nullptr) != LSO_OK);
+    // the allocation-free variant: its refusals come before any device call
+    EXPECT(lso_adam_step_noalloc(tab.data(), 0, nullptr) == LSO_OK);
+    EXPECT(lso_adam_step_noalloc(nullptr, 1, nullptr) != LSO_OK);
+    std::vector<lso_block> many;
+    for (uint64_t i = 0; i <= LSO_NOALLOC_MAX_BLOCKS; ++i) many.push_back(block(A + (i << 26), 16));
+    EXPECT(lso_adam_step_noalloc(many.data(), many.size(), nullptr) == LSO_E_INVALID);
+    EXPECT(lso_adam_step_noalloc(bad.data(), bad.size(), nullptr) != LSO_OK);
+    const uint64_t launches = lso_kernel_launches();
+    EXPECT(lso_kernel_launches() == launches);
+
     lso_stream_ctx* ctx = reinterpret_cast<lso_stream_ctx*>(1);
     EXPECT(lso_stream_create(0, 1, nullptr, nullptr, 0, &ctx) == LSO_E_INVALID && ctx == nullptr);
     EXPECT(lso_stream_copy_mode(nullptr, nullptr, nullptr) == -1);

@@ -39,8 +39,8 @@ def test_oracle_under_address_and_undefined_sanitizers(tmp_path):
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
 def test_host_runtime_under_address_and_undefined_sanitizers(tmp_path):
     exe = str(tmp_path / "runtime_driver")
-    srcs = [os.path.join(CSRC, f) for f in ("lso_adam.hip", "lso_copy.hip", "lso_tiled.hip", "lso_runtime.cpp",
-                                            "lso_stream.cpp", "lso_io.cpp", "lso_shadow.cpp", "lso_sdma.cpp")]
+    from layer_streamed_optimizer_amd import build
+    srcs = [os.path.join(CSRC, f) for f in build.LIBS["liblso.so"]]   # the library's own source list
     # each sanitizer flag applies to the host pass only
     host_san = ["-Xarch_host", "-fsanitize=address",
                 "-Xarch_host", "-fsanitize=undefined",
