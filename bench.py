@@ -601,7 +601,7 @@ def streamed(args, w):
         L[b]["layout"] = lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR
         L[b]["lr"], L[b]["beta1"], L[b]["beta2"], L[b]["eps"] = (configs.LR, configs.BETA1,
                                                                  configs.BETA2, configs.EPS)
-    step_s = []
+    step_s, stats = [], []
     for j in range(1, args.warmup + args.steps + 1):
         prm.step = j
         L["t"] = j
@@ -612,8 +612,43 @@ def streamed(args, w):
         progress(f"step {j}: {dt:.3f} s")
         if j > args.warmup:
             step_s.append(dt)
+            stats.append(ls.stats())
     copy_mode = ls.copy_mode()
     ls.close()
+    j_next = args.warmup + args.steps + 1
+    compared = {}
+    for label, env in getattr(args, "compare_modes", ()):
+        # the same layers (their state carries on, t continues) through a
+        # context made with other LSO_STREAM_* settings: 1 untimed step, then
+        # the timed ones
+        old = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
+        try:
+            other = lso.LayerStream(nbytes, n, fn, ctypes.addressof(prm))
+        finally:
+            for k, v in old.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        times, st = [], None
+        for k in range(1 + args.compare_steps):
+            prm.step = j_next
+            L["t"] = j_next
+            j_next += 1
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            other.stream_layers(L)
+            dt = time.perf_counter() - t0
+            if k > 0:
+                times.append(dt)
+                st = other.stats()
+        compared[label] = dict(env=env, copy_mode=other.copy_mode(), ms_per_step=1e3 * sum(times) / len(times),
+                               steps=len(times), host_waits_per_piece=st["host_waits"] / max(1, st["pieces"]),
+                               chained=st["chained"])
+        other.close()
+        progress(f"{label}: {compared[label]['ms_per_step']:.0f} ms per step, "
+                 f"{compared[label]['host_waits_per_piece']:.1f} host wake-ups per piece")
     for hb in hosts:
         if pinned:
             hb.close()
@@ -633,6 +668,10 @@ def streamed(args, w):
         # against a one-way hipMemcpyAsync of page-locked memory (nothing in
         # the other direction): a looser reference than the duplex peak
         frac_of_hipmemcpy_one_way=per_dir / min(peak["dma"]["h2d"], peak["dma"]["d2h"]),
+        pieces_per_step=stats[-1]["pieces"],
+        host_waits_per_piece=sum(x["host_waits"] for x in stats) / max(1, sum(x["pieces"] for x in stats)),
+        h2d_chained_on_engine=stats[-1]["chained"],
+        other_modes=compared or None,
         config=dict(workload=f"{w.key}: {w.title}", layers=n_layers, layers_in_config=len(w.blocks),
                     params=params, host_memory="pinned" if pinned else "pageable+staged",
                     state_layout=args.layout,
@@ -934,6 +973,12 @@ def main():
         sa = argparse.Namespace(**vars(args))
         sa.layers, sa.host_memory, sa.layout, sa.grad_dtype = 0, "pageable", "tiled", "bf16"
         sa.warmup, sa.steps = 1, max(1, args.streamed_steps)
+        # beside the default: the host carrying buffer-free, and the three
+        # HIP streams tied by hipEvents (DMA H2D, copy-kernel D2H)
+        sa.compare_modes = (("host-gated H2D (LSO_STREAM_CHAIN=0)", {"LSO_STREAM_CHAIN": "0"}),
+                            ("three HIP streams tied by hipEvents (LSO_STREAM_COPY=dma-in)",
+                             {"LSO_STREAM_COPY": "dma-in"}))
+        sa.compare_steps = 1
         progress(f"streamed record: c4, {sa.warmup} untimed + {sa.steps} timed steps")
         r = streamed(sa, configs.get("c4"))
         out["streamed"] = dict(metric=r.pop("metric"), value=r.pop("value"), unit=r.pop("unit"),

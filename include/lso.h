@@ -240,9 +240,10 @@ lso_status lso_tiled_unpack(const void* state, float* master, float* m, float* v
  * buffering): a slot's H2D waits until its previous block has been copied
  * back (buffer-free), the update waits for the H2D (weights-ready), the
  * D2H waits for the update (step-done).  By default the two copies run on
- * two SDMA engines the library names and the host loop carries these
- * dependencies; in the fallback modes (lso_stream_copy_mode) they are
- * events between three HIP streams.
+ * two SDMA engines the library names: each H2D is queued on its engine with
+ * the slot's previous D2H as a dependency the engine waits for itself, and
+ * the host loop carries weights-ready and step-done; in the fallback modes
+ * (lso_stream_copy_mode) all three are events between three HIP streams.
  * Host blocks may be pinned (lso_host_alloc, or any page-locked HIP host
  * allocation): the copies then read and write them directly.  Or they may
  * be ordinary pageable memory (for state larger than the page-locked
@@ -435,6 +436,14 @@ void* lso_stream_slot_weight(lso_stream_ctx* ctx, int slot);
  * each device slot with NaN once its piece has been copied back, before
  * the next piece may come in (a slot-reuse race then shows as NaN). */
 int lso_stream_copy_mode(const lso_stream_ctx* ctx, uint32_t* h2d_engine, uint32_t* d2h_engine);
+
+/* Counters of the most recent lso_stream_layers / lso_stream_files call on
+ * ctx: out[0] pieces moved, out[1] times the host loop slept waiting for a
+ * completion (its wake-ups), out[2] 1 if each H2D was chained on the copy
+ * engine to the slot's previous D2H (the default with named engines;
+ * LSO_STREAM_CHAIN=0 or LSO_STREAM_POISON=1 at lso_stream_create turn it
+ * off), else 0.  Returns 0, or -1 if ctx or out is NULL. */
+int lso_stream_stats(const lso_stream_ctx* ctx, uint64_t out[3]);
 
 /* Waits for outstanding work, frees slots, events and streams. */
 lso_status lso_stream_destroy(lso_stream_ctx* ctx);

@@ -311,6 +311,14 @@ class LayerStream:
         return dict(mode=_native.COPY_MODE_NAMES.get(code, code), code=code, h2d_engine=h.value,
                     d2h_engine=d.value)
 
+    def stats(self) -> dict:
+        """lso_stream_stats: pieces moved by the last call, the host loop's
+        wake-ups during it, and whether each H2D was chained on the engine."""
+        out = (ctypes.c_uint64 * 3)()
+        if _native.lib().lso_stream_stats(self.ctx, out) != 0:
+            raise RuntimeError("lso_stream_stats failed")
+        return dict(pieces=int(out[0]), host_waits=int(out[1]), chained=bool(out[2]))
+
     def close(self) -> None:
         if self.ctx:
             _native.lib().lso_stream_destroy(self.ctx)

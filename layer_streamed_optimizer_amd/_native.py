@@ -105,7 +105,7 @@ EXPORTS = ("lso_adam_step", "lso_adam_step_noalloc", "lso_norm_workspace_bytes",
            "lso_block_constants", "lso_kernel_launches", "lso_tiled_state_bytes",
            "lso_tiled_pack", "lso_tiled_unpack", "lso_stream_create", "lso_stream_layers",
            "lso_stream_files", "lso_shadow_format", "lso_shadow_state", "lso_shadow_commit",
-           "lso_stream_copy_mode", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc",
+           "lso_stream_copy_mode", "lso_stream_stats", "lso_stream_slot_weight", "lso_stream_destroy", "lso_host_alloc",
            "lso_host_free", "lso_status_string", "lso_last_error")
 
 _lib = None
@@ -150,6 +150,8 @@ def lib():
         L.lso_shadow_commit.argtypes = [i32, u64, u64, u64, u64]
         L.lso_stream_copy_mode.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
         L.lso_stream_copy_mode.restype = i32
+        L.lso_stream_stats.argtypes = [vp, ctypes.POINTER(u64)]
+        L.lso_stream_stats.restype = i32
         L.lso_stream_slot_weight.argtypes = [vp, i32]
         L.lso_stream_slot_weight.restype = vp
         L.lso_stream_destroy.argtypes = [vp]

@@ -91,8 +91,9 @@ void do_part(IoRequest* r, uint64_t lo, uint64_t hi)
 
 }  // namespace
 
-IoPool::IoPool(unsigned threads, std::mutex* note_mu, std::condition_variable* note_cv)
-    : n_(threads ? threads : 1), note_mu_(note_mu), note_cv_(note_cv)
+IoPool::IoPool(unsigned threads, std::mutex* note_mu, std::condition_variable* note_cv,
+               std::atomic<uint64_t>* note_gen)
+    : n_(threads ? threads : 1), note_mu_(note_mu), note_cv_(note_cv), note_gen_(note_gen)
 {
     for (unsigned k = 0; k < n_; ++k) workers_.emplace_back([this] { run(); });
 }
@@ -152,6 +153,7 @@ void IoPool::run()
             {
                 std::lock_guard<std::mutex> l(*note_mu_);
                 r->done.store(true);
+                note_gen_->fetch_add(1);
             }
             note_cv_->notify_all();
         }

@@ -43,9 +43,10 @@ struct IoRequest {
 
 class IoPool {
 public:
-    // threads workers; *note_cv is notified (under *note_mu) whenever a
-    // request completes.
-    IoPool(unsigned threads, std::mutex* note_mu, std::condition_variable* note_cv);
+    // threads workers; whenever a request completes, *note_gen is
+    // incremented under *note_mu and *note_cv notified.
+    IoPool(unsigned threads, std::mutex* note_mu, std::condition_variable* note_cv,
+           std::atomic<uint64_t>* note_gen);
     ~IoPool();   // joins the threads; no request may be in flight
 
     // Parts of 4 KB multiples, about 4 per thread, 4-256 MB each.  r must
@@ -63,6 +64,7 @@ private:
     unsigned n_;
     std::mutex* note_mu_;
     std::condition_variable* note_cv_;
+    std::atomic<uint64_t>* note_gen_;
     std::vector<std::thread> workers_;
     std::mutex mu_;
     std::condition_variable cv_;

@@ -26,11 +26,17 @@
 // Every wait refers to an event recorded earlier in host order.  Each copy
 // is one burst over a piece.  By default both directions run on two SDMA
 // engines the library names (lso_sdma.h: H2D on one engine of a pair, D2H
-// on its partner), and the host loop carries the dependencies itself: it
-// issues a piece's H2D once the slot's previous piece has been copied back,
-// enqueues its update once the H2D has ended (the layer's gradient
-// producer is queued ahead, at the H2D), and issues the D2H once the update
-// has ended; no shader core moves a byte over the link.  Where the engines
+// on its partner).  The buffer-free dependency is carried by the engines
+// themselves: a piece's H2D is queued on the H2D engine as soon as the
+// slot's previous D2H has been issued, with that D2H's completion signal as
+// its dependency, so the engine starts it the moment the slot is copied
+// back.  The host loop carries the other two: it enqueues a piece's update
+// once the H2D has ended (the layer's gradient producer is queued ahead, at
+// the H2D) and issues the D2H once the update has ended (HIP streams cannot
+// wait on a ROCr signal, nor a ROCr copy on a HIP event).  No shader core
+// moves a byte over the link.  LSO_STREAM_CHAIN=0 at context creation has
+// the host carry buffer-free too (it issues the H2D once it has seen the
+// slot's D2H end), as does the slot-poisoning debug mode below.  Where the engines
 // cannot be named, H2D runs on a runtime-chosen DMA engine and D2H by a copy
 // kernel, tied by the events above.  LSO_STREAM_COPY=kernel uses copy
 // kernels both ways, LSO_STREAM_COPY=dma runtime-chosen DMA engines both
@@ -102,6 +108,11 @@ constexpr uint64_t kShadowHeaderCopy = lso::kShadowCopy;
 
 constexpr int kMaxSlots = 4;
 constexpr int kMaxStaging = 8;
+// D2H completion signals, one per piece in flight: piece i uses
+// i % (nslots + nstaging), so a signal is re-armed only after the host has
+// seen the end of the piece that used it before (at most nstaging pieces
+// are between their stage-in and their write-out's end)
+constexpr int kMaxRing = kMaxSlots + kMaxStaging;
 
 // Which engine moves each direction of a layer block.
 // the LSO_COPY_* codes of lso.h
@@ -133,12 +144,22 @@ struct lso_stream_ctx {
     size_t norm_cap = 0;
     double* norm_ws = nullptr;     // chunk sums of the layer being updated
     uint64_t norm_ws_bytes = 0;
-    std::mutex note_mu;          // signalled when a request completes
+    // The host loop sleeps on note_cv until note_gen moves: worker pools
+    // bump it when a stage-in or write-out completes and, with named
+    // engines, ROCr's signal handlers when a copy ends and a host function
+    // on the compute stream when an update ends.  `callbacks` counts those
+    // handlers and host functions not yet run.
+    std::mutex note_mu;
     std::condition_variable note_cv;
+    std::atomic<uint64_t> note_gen{0};
+    std::atomic<int> callbacks{0};
     int copy_mode = kCopyDmaIn;
     lso::SdmaLink sdma;                       // kCopyEngines: the two engines
     hsa_signal_t h2d_sig[kMaxSlots] = {};     // kCopyEngines: per slot, its H2D ended
-    hsa_signal_t d2h_sig[kMaxSlots] = {};     // kCopyEngines: per slot, its D2H ended
+    hsa_signal_t d2h_sig[kMaxRing] = {};      // kCopyEngines: per piece in flight, its D2H ended
+    bool chain = true;                        // kCopyEngines: H2D waits for the slot's D2H on the engine
+    uint64_t stat_pieces = 0;                 // the last call's pieces
+    uint64_t stat_waits = 0;                  // the last call's host-loop sleeps
     hipEvent_t grad_ready[kMaxSlots] = {};    // kCopyEngines: a layer's producer ended (per parity)
     bool poison = false;                      // debug: NaN-fill each slot once copied back
     hipEvent_t poison_done[kMaxSlots] = {};   // kCopyEngines: the slot's fill ended
@@ -153,6 +174,43 @@ namespace {
 
 uint64_t round16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
 
+// Wake the host loop (see note_gen).
+void notify(lso_stream_ctx* c)
+{
+    {
+        std::lock_guard<std::mutex> l(c->note_mu);
+        c->note_gen.fetch_add(1);
+    }
+    c->note_cv.notify_all();
+}
+
+// ROCr calls this on its own thread once a watched copy's signal drops
+// below 1 (the copy ended, or failed); it runs once.
+bool on_copy_end(hsa_signal_value_t, void* arg)
+{
+    auto* c = static_cast<lso_stream_ctx*>(arg);
+    notify(c);
+    c->callbacks.fetch_sub(1);
+    return false;
+}
+
+// Host function on the compute stream after a piece's update.
+void on_update_end(void* arg)
+{
+    auto* c = static_cast<lso_stream_ctx*>(arg);
+    notify(c);
+    c->callbacks.fetch_sub(1);
+}
+
+// Have the loop woken when the copy behind sig ends.  If ROCr refuses, the
+// loop still sees the end at its next periodic look.
+void watch_copy(lso_stream_ctx* c, hsa_signal_t sig)
+{
+    c->callbacks.fetch_add(1);
+    if (hsa_amd_signal_async_handler(sig, HSA_SIGNAL_CONDITION_LT, 1, on_copy_end, c) != HSA_STATUS_SUCCESS)
+        c->callbacks.fetch_sub(1);
+}
+
 void release(lso_stream_ctx* c)
 {
     if (!c) return;
@@ -161,6 +219,8 @@ void release(lso_stream_ctx* c)
     (void)hipSetDevice(c->device);
     for (hipStream_t s : {c->h2d, c->compute, c->d2h})
         if (s) (void)hipStreamSynchronize(s);
+    // every copy and update has ended; their handlers may still be running
+    for (int k = 0; k < 200000 && c->callbacks.load() > 0; ++k) std::this_thread::sleep_for(std::chrono::microseconds(50));
     delete c->reader;   // joins its threads; no request is in flight between calls
     delete c->writer;
     if (c->dev_norms) (void)hipFree(c->dev_norms);
@@ -182,8 +242,9 @@ void release(lso_stream_ctx* c)
     for (hipStream_t s : {c->h2d, c->compute, c->d2h})
         if (s) (void)hipStreamDestroy(s);
     for (int s = 0; s < kMaxSlots; ++s)
-        for (hsa_signal_t sig : {c->h2d_sig[s], c->d2h_sig[s]})
-            if (sig.handle) (void)hsa_signal_destroy(sig);
+        if (c->h2d_sig[s].handle) (void)hsa_signal_destroy(c->h2d_sig[s]);
+    for (int s = 0; s < kMaxRing; ++s)
+        if (c->d2h_sig[s].handle) (void)hsa_signal_destroy(c->d2h_sig[s]);
     lso::sdma_close(&c->sdma);
     (void)hipSetDevice(prev);
     delete c;
@@ -355,8 +416,8 @@ lso_status ensure_staging(lso_stream_ctx* c, uint64_t need)
                              static_cast<unsigned long long>(c->staging_bytes));
         }
     }
-    if (!c->reader) c->reader = new (std::nothrow) IoPool(io_threads(), &c->note_mu, &c->note_cv);
-    if (!c->writer) c->writer = new (std::nothrow) IoPool(io_threads(), &c->note_mu, &c->note_cv);
+    if (!c->reader) c->reader = new (std::nothrow) IoPool(io_threads(), &c->note_mu, &c->note_cv, &c->note_gen);
+    if (!c->writer) c->writer = new (std::nothrow) IoPool(io_threads(), &c->note_mu, &c->note_cv, &c->note_gen);
     if (!c->reader || !c->writer) return lso::fail(LSO_E_NOMEM, "worker pools");
     return LSO_OK;
 }
@@ -472,8 +533,17 @@ lso_status enqueue_piece_update(lso_stream_ctx* c, const Unit& U, size_t i, bool
         return lso::fail(LSO_E_INVALID, "layer %zu: norm workspace too small", h.index);
     lso_status st = lso::enqueue_update(&b, 1, c->compute, false, h.sq_norm ? &o : nullptr);
     if (st != LSO_OK) return st;
-    const hipError_t err = hipEventRecord(c->step_done[s], c->compute);
+    hipError_t err = hipEventRecord(c->step_done[s], c->compute);
     if (err != hipSuccess) return lso::hip_fail(err, "hipEventRecord(step-done)");
+    if (wait_grads && !c->poison) {
+        // named engines: the host loop issues the D2H once it is woken here
+        c->callbacks.fetch_add(1);
+        err = hipLaunchHostFunc(c->compute, on_update_end, c);
+        if (err != hipSuccess) {
+            c->callbacks.fetch_sub(1);
+            return lso::hip_fail(err, "hipLaunchHostFunc(step-done)");
+        }
+    }
     return LSO_OK;
 }
 
@@ -515,11 +585,14 @@ lso_status issue_unit(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
 // first piece) the gradient producer, on the otherwise idle h2d stream with
 // grad_ready recorded after it -- so the previous layer's updates on the
 // compute stream never wait behind it -- then the H2D on the link's H2D
-// engine.  The loop calls it only once the piece that used the slot before
-// (nslots pieces ago) has been copied back, so the slot, the piece's
-// completion signals and the gradient buffer of its parity (last read by
-// layer - nslots, whose pieces all came earlier) are free.
-lso_status issue_h2d_engine(lso_stream_ctx* c, const Unit& U, size_t i, const void* buf)
+// engine.  The loop calls it once the piece that used the slot before
+// (nslots pieces ago) has had its D2H issued -- which it does only after
+// that piece's update has ended, and the updates end in order -- so the
+// gradient buffer of the piece's parity (last read by layer - nslots, whose
+// pieces all came earlier) and the slot's H2D signal are free; dep (that
+// D2H's completion signal, or NULL once the host has seen it end) holds
+// the copy on the engine until the slot has been copied back.
+lso_status issue_h2d_engine(lso_stream_ctx* c, const Unit& U, size_t i, const void* buf, const hsa_signal_t* dep)
 {
     const int s = static_cast<int>(i % c->nslots);
     lso_status st = enqueue_producer(c, U, c->h2d);
@@ -528,26 +601,28 @@ lso_status issue_h2d_engine(lso_stream_ctx* c, const Unit& U, size_t i, const vo
         const hipError_t err = hipEventRecord(c->grad_ready[U.layer % c->nslots], c->h2d);
         if (err != hipSuccess) return lso::hip_fail(err, "hipEventRecord(gradients ready)");
     }
-    const hsa_status_t hs = lso::sdma_copy(c->sdma, c->slot_state[s], buf, U.bytes, true, nullptr, c->h2d_sig[s]);
+    const hsa_status_t hs = lso::sdma_copy(c->sdma, c->slot_state[s], buf, U.bytes, true, dep, c->h2d_sig[s]);
     if (hs != HSA_STATUS_SUCCESS) {
         hsa_signal_store_screlease(c->h2d_sig[s], 0);
         return lso::fail(LSO_E_HIP, "SDMA H2D copy of %llu bytes not accepted (status %d)",
                          static_cast<unsigned long long>(U.bytes), static_cast<int>(hs));
     }
+    watch_copy(c, c->h2d_sig[s]);
     return LSO_OK;
 }
 
 // SDMA-pair mode, last stage: the piece's D2H on the link's D2H engine,
-// once its update has completed.
-lso_status issue_d2h_engine(lso_stream_ctx* c, const Unit& U, size_t i, void* buf)
+// once its update has completed; its completion is d2h_sig[sig].
+lso_status issue_d2h_engine(lso_stream_ctx* c, const Unit& U, size_t i, void* buf, size_t sig)
 {
     const int s = static_cast<int>(i % c->nslots);
-    const hsa_status_t hs = lso::sdma_copy(c->sdma, buf, c->slot_state[s], U.bytes, false, nullptr, c->d2h_sig[s]);
+    const hsa_status_t hs = lso::sdma_copy(c->sdma, buf, c->slot_state[s], U.bytes, false, nullptr, c->d2h_sig[sig]);
     if (hs != HSA_STATUS_SUCCESS) {
-        hsa_signal_store_screlease(c->d2h_sig[s], 0);
+        hsa_signal_store_screlease(c->d2h_sig[sig], 0);
         return lso::fail(LSO_E_HIP, "SDMA D2H copy of %llu bytes not accepted (status %d)",
                          static_cast<unsigned long long>(U.bytes), static_cast<int>(hs));
     }
+    watch_copy(c, c->d2h_sig[sig]);
     return LSO_OK;
 }
 
@@ -654,7 +729,10 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
         if (result == LSO_OK) result = s;
     };
     const bool engines = c->copy_mode == kCopyEngines;
+    const bool chain = engines && c->chain && !c->poison;
     const size_t S = static_cast<size_t>(c->nslots);
+    const size_t R = S + K;   // D2H completion signals in the ring
+    uint64_t waits = 0;
     size_t next_read = 0;     // next piece to stage in
     size_t next_issue = 0;    // next piece to enqueue on the GPU (SDMA-pair mode: its H2D)
     size_t next_update = 0;   // SDMA-pair mode: next piece whose H2D completion is awaited
@@ -677,7 +755,11 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
             if (!read_complete(i)) return true;
         return false;
     };
+    // with named engines (no slot poisoning) every completion the loop
+    // waits for wakes it; otherwise it looks every 50 / 200 us
+    const bool woken = engines && !c->poison;
     for (;;) {
+        const uint64_t seen = c->note_gen.load();
         bool progress = false;
         // 1. stage in while a buffer is free
         while (next_read < stop_at && next_read < next_done + K) {
@@ -705,9 +787,11 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
             progress = true;
         }
         // 2. issue staged pieces in order (SDMA-pair mode: once the piece
-        //    that used the slot before has been copied back)
+        //    that used the slot before has had its D2H issued -- the H2D
+        //    engine then waits for that D2H itself -- or, unchained, once
+        //    the host has seen that D2H end)
         while (next_issue < next_read && next_issue < stop_at && read_complete(next_issue) &&
-               (!engines || next_issue < next_retire + S)) {
+               (!engines || next_issue < (chain ? next_offload : next_retire) + S)) {
             const Unit& U = units[next_issue];
             const Job& j = *U.job;
             if (engines && c->poison && next_issue >= S) {
@@ -729,7 +813,10 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
                 }
             }
             trace.mark(trace.issue, next_issue);
-            const lso_status s = engines ? issue_h2d_engine(c, U, next_issue, buf_of(next_issue))
+            // the slot's previous D2H, unless the host has already seen it end
+            const hsa_signal_t* dep =
+                chain && next_issue >= S && next_issue - S >= next_retire ? &c->d2h_sig[(next_issue - S) % R] : nullptr;
+            const lso_status s = engines ? issue_h2d_engine(c, U, next_issue, buf_of(next_issue), dep)
                                          : issue_unit(c, U, next_issue, buf_of(next_issue));
             if (s != LSO_OK) {
                 record(s);
@@ -767,7 +854,7 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
                 const hipError_t q = hipEventQuery(c->step_done[i % S]);
                 if (q == hipErrorNotReady) break;
                 const lso_status s = q != hipSuccess ? lso::hip_fail(q, "update completion")
-                                                     : issue_d2h_engine(c, units[i], i, buf_of(i));
+                                                     : issue_d2h_engine(c, units[i], i, buf_of(i), i % R);
                 if (s != LSO_OK) {
                     record(s);
                     gpu_ok = false;
@@ -782,12 +869,15 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
         //    untouched)
         while (next_retire < (engines ? next_offload : next_issue) && next_done == next_retire) {
             if (engines) {
-                const int64_t st = gpu_ok ? lso::sdma_state(c->d2h_sig[next_retire % S]) : 0;
+                const int64_t st = gpu_ok ? lso::sdma_state(c->d2h_sig[next_retire % R]) : 0;
                 if (st > 0) break;
                 if (st < 0) {
                     record(lso::fail(LSO_E_HIP, "SDMA D2H copy of layer %zu failed", units[next_retire].job->index));
                     gpu_ok = false;
                     stop_at = std::min(stop_at, next_issue);
+                    // an H2D chained to this copy waits for the signal to
+                    // reach 0: release it (nothing of it is written back)
+                    hsa_signal_store_screlease(c->d2h_sig[next_retire % R], 0);
                 }
                 if (gpu_ok && c->poison) {
                     const size_t s = next_retire % S;
@@ -864,19 +954,32 @@ lso_status run_pipeline(lso_stream_ctx* c, const Job* J, size_t nj)
         const size_t last = std::min(stop_at, n);
         if (next_done == next_issue && next_issue >= last && !reads_in_flight()) break;
         if (!progress) {
-            // SDMA-pair mode: the loop itself moves each piece from copy to
-            // update to copy, so it looks more often
+            ++waits;
             std::unique_lock<std::mutex> l(c->note_mu);
-            c->note_cv.wait_for(l, std::chrono::microseconds(engines ? 50 : 200));
+            if (woken) {
+                // until something completes (the time limit only bounds a
+                // missed notification)
+                c->note_cv.wait_for(l, std::chrono::milliseconds(20), [&] { return c->note_gen.load() != seen; });
+            } else {
+                // SDMA-pair mode with poisoning: the loop itself moves each
+                // piece from copy to update to copy, so it looks more often
+                c->note_cv.wait_for(l, std::chrono::microseconds(engines ? 50 : 200));
+            }
         }
     }
     // Every enqueued stage finishes before return (on error too, so no copy
-    // into a block is still running when the caller looks at it).
+    // into a block is still running when the caller looks at it).  A failed
+    // D2H's signal is released, so an H2D chained to it can end too.
     if (engines) {
+        for (size_t s = 0; s < R; ++s) {
+            while (lso::sdma_state(c->d2h_sig[s]) > 0) std::this_thread::sleep_for(std::chrono::microseconds(50));
+            if (lso::sdma_state(c->d2h_sig[s]) < 0) hsa_signal_store_screlease(c->d2h_sig[s], 0);
+        }
         for (size_t s = 0; s < S; ++s)
-            while (lso::sdma_state(c->h2d_sig[s]) > 0 || lso::sdma_state(c->d2h_sig[s]) > 0)
-                std::this_thread::sleep_for(std::chrono::microseconds(50));
+            while (lso::sdma_state(c->h2d_sig[s]) > 0) std::this_thread::sleep_for(std::chrono::microseconds(50));
     }
+    c->stat_pieces = n;
+    c->stat_waits = waits;
     for (hipStream_t st : {c->h2d, c->compute, c->d2h}) {
         const hipError_t err = hipStreamSynchronize(st);
         if (err != hipSuccess) record(lso::hip_fail(err, "hipStreamSynchronize"));
@@ -999,14 +1102,17 @@ lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params
     c->copy_mode = want == kCopyEngines ? kCopyDmaIn : want;
     if (want == kCopyEngines && lso::sdma_open(device, &c->sdma)) {
         bool ok = true;
-        for (int s = 0; s < c->nslots && ok; ++s)
-            for (hsa_signal_t* sig : {&c->h2d_sig[s], &c->d2h_sig[s]})
-                if (ok && hsa_signal_create(0, 0, nullptr, sig) != HSA_STATUS_SUCCESS) {
-                    sig->handle = 0;
-                    ok = false;
-                }
+        auto make = [&ok](hsa_signal_t* sig) {
+            if (ok && hsa_signal_create(0, 0, nullptr, sig) != HSA_STATUS_SUCCESS) {
+                sig->handle = 0;
+                ok = false;
+            }
+        };
+        for (int s = 0; s < c->nslots; ++s) make(&c->h2d_sig[s]);
+        for (int s = 0; s < c->nslots + c->nstaging; ++s) make(&c->d2h_sig[s]);
         if (ok) c->copy_mode = kCopyEngines;
     }
+    if (const char* e = std::getenv("LSO_STREAM_CHAIN")) c->chain = std::strcmp(e, "0") != 0;
     // chunk sums of one layer at the smallest chunk size (any layout)
     const uint64_t min_chunk = lso::chunk_elems(lso::kUnrollSmall);
     const uint64_t max_chunks = ((max_layer_params ? max_layer_params : 1) + min_chunk - 1) / min_chunk;
@@ -1118,6 +1224,15 @@ int lso_stream_copy_mode(const lso_stream_ctx* c, uint32_t* h2d_engine, uint32_t
     if (h2d_engine) *h2d_engine = eng ? c->sdma.h2d_engine : 0;
     if (d2h_engine) *d2h_engine = eng ? c->sdma.d2h_engine : 0;
     return c->copy_mode;
+}
+
+int lso_stream_stats(const lso_stream_ctx* c, uint64_t out[3])
+{
+    if (!c || !out) return -1;
+    out[0] = c->stat_pieces;
+    out[1] = c->stat_waits;
+    out[2] = (c->copy_mode == kCopyEngines && c->chain && !c->poison) ? 1 : 0;
+    return 0;
 }
 
 void* lso_stream_slot_weight(lso_stream_ctx* c, int slot)

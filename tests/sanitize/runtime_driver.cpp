@@ -101,7 +101,8 @@ int main()
     EXPECT(lso_adam_step_noalloc(bad.data(), bad.size(), nullptr) != LSO_OK);
     const uint64_t launches = lso_kernel_launches();
     EXPECT(lso_kernel_launches() == launches);
-
+    uint64_t stats[3] = {1, 1, 1};
+    EXPECT(lso_stream_stats(nullptr, stats) == -1 && stats[0] == 1);
     lso_stream_ctx* ctx = reinterpret_cast<lso_stream_ctx*>(1);
     EXPECT(lso_stream_create(0, 1, nullptr, nullptr, 0, &ctx) == LSO_E_INVALID && ctx == nullptr);
     EXPECT(lso_stream_copy_mode(nullptr, nullptr, nullptr) == -1);

@@ -332,12 +332,15 @@ def test_every_copy_mode_gives_the_same_bits(pageable):
 def test_named_engines_many_small_pieces_any_slot_count(slots):
     """Forty layers, tiled ones cut into one-tile pieces and small planar
     ones, pinned and pageable mixed: the named-engine pipeline, with 2, 3 or
-    4 device slots (the host loop reuses each slot's signals every `slots`
-    pieces, and a layer's producer is queued ahead at its first H2D), gives
-    the bits of copy kernels with two slots -- state, weights and norms.
-    The named-engine and dma-in runs fill every slot with NaN once its piece
-    is copied back (LSO_STREAM_POISON), so an update that ran before its H2D
-    had landed would leave NaN in the results."""
+    4 device slots (each H2D chained on the engine to the slot's previous
+    D2H, whose completion signals rotate over slots + staging buffers; a
+    layer's producer is queued ahead at its first H2D), gives the bits of
+    copy kernels with two slots -- state, weights and norms.  An H2D that
+    overtook the slot's D2H, or an update that ran before its H2D had
+    landed, would mix two pieces' data.  The unchained named-engine run and
+    the dma-in run also fill every slot with NaN once its piece is copied
+    back (LSO_STREAM_POISON).  Each context reports its pieces and whether it
+    chained."""
     T = torch()
     rng = np.random.default_rng(7)
     sizes_t = [int(x) for x in rng.integers(1, 3 * 8192 + 5, 24)]
@@ -347,8 +350,11 @@ def test_named_engines_many_small_pieces_any_slot_count(slots):
     mb = max([configs.host_layer_layout(n, tiled=True)[3] for n in sizes_t] +
              [configs.host_layer_layout(n)[3] for n in sizes_p])
     runs = {}
-    for mode, k, poison in (("sdma-pair", slots, 1), ("dma-in", slots, 1), ("kernel", 2, 0)):
-        log("many pieces", mode, "slots", k, "poison", poison)
+    # the named engines with each H2D chained on the engine to the slot's
+    # previous D2H (the default), and unchained with slot poisoning
+    for name, mode, k, poison in (("chained", "sdma-pair", slots, 0), ("sdma-pair", "sdma-pair", slots, 1),
+                                  ("dma-in", "dma-in", slots, 1), ("kernel", "kernel", 2, 0)):
+        log("many pieces", name, "slots", k, "poison", poison)
         ht = HostLayers(sizes_t, sid, tiled=True, pageable=lambda b: b % 3 == 1)
         hp = HostLayers(sizes_p, sid + 1, pageable=lambda b: b % 2 == 0)
         with stream_pieces(1), stream_env(COPY=mode, SLOTS=k, POISON=poison):
@@ -363,11 +369,15 @@ def test_named_engines_many_small_pieces_any_slot_count(slots):
             L["sq_norm"] = [norms.ctypes.data + 8 * i for i in range(len(sizes))]
             ls.stream_layers(L)
         T.cuda.synchronize()
+        st = ls.stats()
+        pieces = sum((n + 8191) // 8192 for n in sizes_t) + len(sizes_p)
+        assert st["pieces"] == pieces and st["chained"] == (name == "chained"), st
+        log("many pieces", name, st)
         raw = [ht.raw(b) for b in range(len(sizes_t))] + [hp.raw(b) for b in range(len(sizes_p))]
-        runs[mode] = (raw, [x.cpu().numpy() for x in w], norms.copy())
+        runs[name] = (raw, [x.cpu().numpy() for x in w], norms.copy())
         ls.close()
     b = runs["kernel"]
-    for mode in ("sdma-pair", "dma-in"):
+    for mode in ("chained", "sdma-pair", "dma-in"):
         a = runs[mode]
         for i in range(len(sizes)):
             assert np.array_equal(a[0][i], b[0][i]), (mode, i)
