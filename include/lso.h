@@ -136,7 +136,14 @@ typedef struct lso_block {
 /*
  * lso_adam_step: one update of n device-resident blocks, enqueued on
  * stream as ONE kernel launch (a ragged multi-tensor launch: hundreds of
- * small tensors cost one launch).  More than 16 distinct
+ * small tensors cost one launch).
+ * Defined by: "Training 70B Models on Consumer Hardware (If You're Willing
+ * to Wait)", section "The Math" (the moments, the bias correction with the
+ * step t, the update added to the stored weights); the Cloudera community
+ * training-memory article, line item "Optimizer states" (the FP32 master is
+ * updated and cast back down to the BF16 weight); the LoRA fine-tuning
+ * memory article of the same site (adapters on seven projections of every
+ * layer: the hundreds of small tensors one call takes).  More than 16 distinct
  * (opt, t, lr, beta1, beta2, eps) sets in one call, or blocks of different
  * layouts or gradient dtypes mixed in one call, split it into one launch
  * per (layout, gradient dtype) and per 16 sets.
@@ -293,7 +300,12 @@ typedef int (*lso_grad_fn)(void* user, size_t layer, void* dev_grad, uint64_t n,
 
 typedef struct lso_stream_ctx lso_stream_ctx;
 
-/* Create a streaming context on `device`: its streams, two device slots
+/* Defined by: the MegaTrain summary on blog.hotdry.top, section on
+ * streaming execution and the double-buffered pipeline (two sets of
+ * staging buffers, a weight-transfer, a compute and a write-back stream
+ * tied by weights-ready / backward-done / buffer-free events) and section
+ * on key engineering parameters (each buffer holds the largest layer).
+ * Create a streaming context on `device`: its streams, two device slots
  * of max_layer_bytes (rounded up to 4 KB) of state plus max_layer_params
  * BF16 gradients and BF16 weights each, the events, and the copy mode (see
  * lso_stream_copy_mode; the three pinned staging buffers of that size and
@@ -304,7 +316,15 @@ typedef struct lso_stream_ctx lso_stream_ctx;
 lso_status lso_stream_create(uint64_t max_layer_bytes, uint64_t max_layer_params,
                              lso_grad_fn fn, void* user, int device, lso_stream_ctx** out);
 
-/* Stream n_layers layers through the pipeline, in order.  Synchronous with
+/* Defined by: the MegaTrain summary, section on the system architecture
+ * (host memory holds the authoritative parameters and optimizer state, the
+ * GPU only computes on what is streamed in) and section on streaming
+ * execution (one contiguous, page-aligned block per layer moved by one
+ * burst; ping-pong buffers; the three events); "Training 70B Models on
+ * Consumer Hardware", section "The Math" (the stored weights take
+ * += delta) and section "Training Loop" (each layer loaded, updated and
+ * written back in turn).
+ * Stream n_layers layers through the pipeline, in order.  Synchronous with
  * respect to host memory: on LSO_OK every host block holds its updated
  * state, and each layer's sq_norm (if not NULL) its gradient's sum of g^2
  * (as lso_adam_step_norms).  A layer with n == 0 is skipped entirely -- no
@@ -445,11 +465,18 @@ int lso_stream_copy_mode(const lso_stream_ctx* ctx, uint32_t* h2d_engine, uint32
  * off), else 0.  Returns 0, or -1 if ctx or out is NULL. */
 int lso_stream_stats(const lso_stream_ctx* ctx, uint64_t out[3]);
 
-/* Waits for outstanding work, frees slots, events and streams. */
+/* The end of a context made by lso_stream_create (same sections of the
+ * MegaTrain summary): waits for outstanding work, frees slots, events and
+ * streams.  NULL is a no-op.  Always LSO_OK. */
 lso_status lso_stream_destroy(lso_stream_ctx* ctx);
 
-/* Pinned host memory for layer blocks (page aligned, so 4 KB aligned).
- * Errors: INVALID (bytes == 0 or out NULL), NOMEM. */
+/* Defined by: the MegaTrain summary, section on streaming execution
+ * (layer blocks aligned to 4 KB pages, for pinned staging) and section on
+ * key engineering parameters (pinned buffers of the largest layer).
+ * Pinned host memory for layer blocks (page aligned, so 4 KB aligned):
+ * hipHostMalloc, owned by the caller until lso_host_free.  Errors: INVALID
+ * (bytes == 0 or out NULL), NOMEM; *out is NULL on error.  lso_host_free:
+ * NULL is a no-op; HIP on a pointer the runtime does not know. */
 lso_status lso_host_alloc(uint64_t bytes, void** out);
 lso_status lso_host_free(void* p);
 
