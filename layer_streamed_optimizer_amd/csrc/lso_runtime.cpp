@@ -241,15 +241,18 @@ HyperKey key_of(const lso_block& b)
 // Device copies of block tables of more than kInline blocks (plus their
 // per-chunk block index), cached by content so a training loop that passes
 // the same blocks every step uploads its table once.  Per device; at most
-// kCacheCap entries.  The least recently used entry is evicted after a
-// device synchronisation, because queued kernels on any stream may still
-// read it; a loop that cycles through more than kCacheCap distinct tables
-// pays that synchronisation on every new one.
+// kCacheCap entries and kCacheBytes of device memory.  Uploads go through
+// one page-locked staging buffer per device, reused (a new table waits
+// until the previous upload has read it), so the cache holds no host
+// memory.  Least recently used entries are evicted after a device
+// synchronisation, because queued kernels on any stream may still read
+// them; a loop that cycles through more tables than the cache holds pays
+// that synchronisation on every new one.
 struct TableEntry {
     std::vector<DevBlock> key;
     int unroll = 0;
     void* dev = nullptr;          // [DevBlock x n | uint32 index x chunks]
-    void* pinned = nullptr;       // host staging of the upload
+    size_t bytes = 0;
     hipEvent_t ready = nullptr;   // recorded after the upload
     bool ready_seen = false;
     void* upload_stream = nullptr;
@@ -258,10 +261,16 @@ struct TableEntry {
 };
 
 constexpr size_t kCacheCap = 256;
+constexpr size_t kCacheBytes = 512ull << 20;
 
 struct DeviceTables {
     std::vector<TableEntry> entries;
     uint64_t tick = 0;
+    size_t bytes = 0;                    // device bytes of all entries
+    void* staging = nullptr;             // page-locked upload buffer
+    size_t staging_bytes = 0;
+    hipEvent_t staging_read = nullptr;   // the last upload from it has been read
+    bool staging_busy = false;
 };
 
 std::mutex g_mu;
@@ -270,9 +279,36 @@ std::unordered_map<int, DeviceTables> g_tables;
 void free_entry(TableEntry& e)
 {
     if (e.dev) (void)hipFree(e.dev);
-    if (e.pinned) (void)hipHostFree(e.pinned);
     if (e.ready) (void)hipEventDestroy(e.ready);
     e = TableEntry{};
+}
+
+// The device's staging buffer, at least `bytes` large and no longer read by
+// an earlier upload.
+lso_status staging_for(DeviceTables& dt, size_t bytes)
+{
+    hipError_t err;
+    if (!dt.staging_read) {
+        err = hipEventCreateWithFlags(&dt.staging_read, hipEventDisableTiming);
+        if (err != hipSuccess) { dt.staging_read = nullptr; return hip_fail(err, "hipEventCreateWithFlags"); }
+    }
+    if (dt.staging_busy) {
+        err = hipEventSynchronize(dt.staging_read);
+        if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize (table staging)");
+        dt.staging_busy = false;
+    }
+    if (dt.staging_bytes < bytes) {
+        if (dt.staging) (void)hipHostFree(dt.staging);
+        dt.staging = nullptr;
+        dt.staging_bytes = 0;
+        const size_t want = (bytes + (1u << 20) - 1) & ~size_t((1u << 20) - 1);
+        if (hipHostMalloc(&dt.staging, want, hipHostMallocDefault) != hipSuccess) {
+            dt.staging = nullptr;
+            return fail(LSO_E_NOMEM, "hipHostMalloc of a %zu-byte table staging buffer failed", want);
+        }
+        dt.staging_bytes = want;
+    }
+    return LSO_OK;
 }
 
 bool same_table(const TableEntry& e, const std::vector<DevBlock>& tab, int unroll)
@@ -315,33 +351,36 @@ lso_status device_table(const lso_block* blocks, size_t n, bool geometry_checked
         lso_status s = validate_geometry(blocks, n);
         if (s != LSO_OK) return s;
     }
-    if (dt.entries.size() >= kCacheCap) {
-        auto lru = std::min_element(dt.entries.begin(), dt.entries.end(),
-                                    [](const TableEntry& a, const TableEntry& b) { return a.tick < b.tick; });
+    const bool has_index = total_chunks <= kMaxIndexChunks;
+    const size_t tab_bytes = tab.size() * sizeof(DevBlock);
+    const size_t bytes = tab_bytes + (has_index ? total_chunks * sizeof(uint32_t) : 0);
+    if (dt.entries.size() >= kCacheCap || (!dt.entries.empty() && dt.bytes + bytes > kCacheBytes)) {
         err = hipDeviceSynchronize();
         if (err != hipSuccess) return hip_fail(err, "hipDeviceSynchronize (table eviction)");
-        free_entry(*lru);
-        dt.entries.erase(lru);
+        while (!dt.entries.empty() && (dt.entries.size() >= kCacheCap || dt.bytes + bytes > kCacheBytes)) {
+            auto lru = std::min_element(dt.entries.begin(), dt.entries.end(),
+                                        [](const TableEntry& a, const TableEntry& b) { return a.tick < b.tick; });
+            dt.bytes -= lru->bytes;
+            free_entry(*lru);
+            dt.entries.erase(lru);
+        }
     }
+    lso_status st = staging_for(dt, bytes);
+    if (st != LSO_OK) return st;
     TableEntry e;
     e.key = tab;
     e.unroll = unroll;
     e.tick = dt.tick;
     e.upload_stream = stream;
-    e.has_index = total_chunks <= kMaxIndexChunks;
-    const size_t tab_bytes = tab.size() * sizeof(DevBlock);
-    const size_t bytes = tab_bytes + (e.has_index ? total_chunks * sizeof(uint32_t) : 0);
+    e.has_index = has_index;
+    e.bytes = bytes;
     if (hipMalloc(&e.dev, bytes) != hipSuccess) {
         free_entry(e);
         return fail(LSO_E_NOMEM, "hipMalloc of a %zu-byte block table failed", bytes);
     }
-    if (hipHostMalloc(&e.pinned, bytes, hipHostMallocDefault) != hipSuccess) {
-        free_entry(e);
-        return fail(LSO_E_NOMEM, "hipHostMalloc of a %zu-byte block table failed", bytes);
-    }
-    std::memcpy(e.pinned, tab.data(), tab_bytes);
+    std::memcpy(dt.staging, tab.data(), tab_bytes);
     if (e.has_index) {
-        uint32_t* idx = reinterpret_cast<uint32_t*>(static_cast<char*>(e.pinned) + tab_bytes);
+        uint32_t* idx = reinterpret_cast<uint32_t*>(static_cast<char*>(dt.staging) + tab_bytes);
         for (size_t k = 0; k < tab.size(); ++k) {
             const uint64_t end = k + 1 < tab.size() ? tab[k + 1].chunk0 : total_chunks;
             for (uint64_t c = tab[k].chunk0; c < end; ++c) idx[c] = static_cast<uint32_t>(k);
@@ -349,10 +388,13 @@ lso_status device_table(const lso_block* blocks, size_t n, bool geometry_checked
     }
     err = hipEventCreateWithFlags(&e.ready, hipEventDisableTiming);
     if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipEventCreateWithFlags"); }
-    err = hipMemcpyAsync(e.dev, e.pinned, bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    err = hipMemcpyAsync(e.dev, dt.staging, bytes, hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipMemcpyAsync (block table)"); }
     err = hipEventRecord(e.ready, static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) err = hipEventRecord(dt.staging_read, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipEventRecord"); }
+    dt.staging_busy = true;
+    dt.bytes += bytes;
     args.blocks = static_cast<const DevBlock*>(e.dev);
     args.chunk_block = e.has_index
         ? reinterpret_cast<const uint32_t*>(static_cast<const char*>(e.dev) + tab_bytes)

@@ -584,3 +584,36 @@ def test_mixed_gradient_dtypes_and_layouts_in_one_call():
         for i in range(len(refs[k])):
             assert_parity(read_arena(arenas[k], i), refs[k][i], TOL10, f"kind {k} block {i}", scale)
         assert arenas[k].canaries_intact()
+
+
+def test_table_cache_past_its_capacity_equals_per_block_launches():
+    """More distinct tables than the device-table cache holds (256): 300
+    different 5-block subsets of 12 blocks, then the first 20 again (evicted
+    and uploaded anew), against the same updates as single-block launches
+    (which travel by value and use no cache), bit for bit."""
+    import itertools
+    T = torch()
+    sizes = [1000 + 97 * i for i in range(12)]
+    ref = host_inputs(sizes, 97)
+    a, b = Arena(sizes), Arena(sizes)
+    load_arena(a, ref)
+    load_arena(b, ref)
+    for i, g in enumerate(grads(sizes, 97, 1)):
+        a.put(i, "grad", g)
+        b.put(i, "grad", g)
+    rows_a, rows_b = a.rows(), b.rows()
+    subsets = list(itertools.islice(itertools.combinations(range(12), 5), 300))
+    steps = [0] * 12
+    log("table cache: 320 calls over 300 distinct tables")
+    for sub in subsets + subsets[:20]:
+        for i in sub:
+            steps[i] += 1
+            rows_a[i]["t"] = rows_b[i]["t"] = steps[i]
+        lso.adam_step(lso.BlockTable.from_rows([rows_a[i] for i in sub]))
+        for i in sub:
+            lso.adam_step(lso.BlockTable.from_rows([rows_b[i]]))
+    T.cuda.synchronize()
+    for i in range(12):
+        for q in ("master", "m", "v", "weight"):
+            assert np.array_equal(a.get(i, q).view(np.uint8), b.get(i, q).view(np.uint8)), (i, q)
+    assert a.canaries_intact() and b.canaries_intact()
