@@ -448,6 +448,67 @@ def hbm_probe(nbytes: int = 8 << 30, reps: int = 6) -> dict:
     return dict(hbm_probe=rows, bytes=nbytes, best_of=reps, unit="GB/s (read + write)")
 
 
+def launch_floor() -> dict:
+    """The floors of the launch-bound workloads (c0, c2): an empty
+    one-workgroup launch, and at each workload's size the update's traffic
+    shape with no arithmetic (lso_probe_copy_shaped, planar, the same
+    1,024-element chunks) and a plain copy of the same bytes -- each warm
+    (median of isolated launches), with 512 MB written before every launch,
+    and back to back (100-200 launches between two events)."""
+    import torch
+
+    import synth
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    dev = torch.device("cuda:0")
+    hs = torch.cuda.current_stream().cuda_stream
+
+    def isolated(fn, reps, flush=None):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for s, e in ev:
+            if flush is not None:
+                synth.device_fill_zero(flush.data_ptr(), flush.numel(), hs)
+            s.record()
+            if fn() != 0:
+                raise RuntimeError("probe launch failed")
+            e.record()
+        torch.cuda.synchronize()
+        d = sorted(s.elapsed_time(e) * 1e3 for s, e in ev)
+        return dict(median_us=d[len(d) // 2], min_us=d[0])
+
+    def back_to_back(fn, k):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(k):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / k
+
+    a = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    b = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    empty = lambda: P.lso_probe_copy(a.data_ptr(), b.data_ptr(), 16, 0, hs)
+    out = dict(one_workgroup_launch=dict(isolated=isolated(empty, 200), back_to_back_us=back_to_back(empty, 2000)))
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for name, n in (("c0", 1 << 20), ("c2", 6307840)):
+        state = torch.zeros(12 * n, dtype=torch.uint8, device=dev)
+        grad = torch.zeros(2 * n, dtype=torch.uint8, device=dev)
+        w = torch.empty(2 * n, dtype=torch.uint8, device=dev)
+        shaped = lambda: P.lso_probe_copy_shaped(state.data_ptr(), grad.data_ptr(), w.data_ptr(), n, 0, hs)
+        out[f"shaped_{name}"] = dict(params=n, workgroups=n // 1024, warm=isolated(shaped, 100),
+                                     flushed=isolated(shaped, 50, flush), back_to_back_us=back_to_back(shaped, 200))
+        src = torch.zeros(14 * n, dtype=torch.uint8, device=dev)
+        dst = torch.zeros(14 * n, dtype=torch.uint8, device=dev)
+        copy = lambda: P.lso_probe_copy(src.data_ptr(), dst.data_ptr(), 14 * n, 0, hs)
+        out[f"copy_{name}"] = dict(bytes_each_way=14 * n, warm=isolated(copy, 100),
+                                   flushed=isolated(copy, 50, flush), back_to_back_us=back_to_back(copy, 200))
+        progress(f"launch floor {name}: shaped {out[f'shaped_{name}']}, copy {out[f'copy_{name}']}")
+        del state, grad, w, src, dst
+    return dict(launch_floor=out, unit="us")
+
+
 # ------------------------------------------------------------ streamed path
 
 def link_peak(nbytes=4 << 30):
@@ -899,6 +960,9 @@ def main():
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only the HBM ceiling sweep: every shape of the 1:1 read/write copy "
                          "probe over 8 GiB, best of 6; one JSON line")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="only the floors of the launch-bound workloads (c0, c2 sizes): an empty "
+                         "launch, the update-shaped copy and a plain copy; one JSON line")
     ap.add_argument("--host-memory", choices=["pageable", "pinned", "file"], default="pageable",
                     help="c4: authoritative blocks in pageable memory (staged through pinned "
                          "buffers), page-locked (direct; limited by the host's page-locked "
@@ -934,6 +998,14 @@ def main():
         torch.cuda.set_device(0)
         print(json.dumps(dict(link_probe=link_probe_sweep(), unit="GB/s", best_of=10,
                               environment=environment())), flush=True)
+        return
+    if args.launch_floor:
+        import torch
+
+        torch.cuda.set_device(0)
+        out = launch_floor()
+        out["environment"] = environment()
+        print(json.dumps(out), flush=True)
         return
     if args.hbm_probe:
         import torch
