@@ -287,21 +287,27 @@ __device__ __forceinline__ uint32_t search_block(const LSO_CONST DevBlock* block
     return lo;
 }
 
-// Same for the few blocks passed by value: fully unrolled selects.
-__device__ __forceinline__ DevBlock find_inline(const KernelArgs& a, uint64_t chunk)
+// Same for the few blocks passed by value, with their constants (block k
+// of a by-value launch uses coef[k]): the blocks' first chunks load in one
+// round from fixed places in the kernel arguments, the pick is a few scalar
+// selects, and the picked block and its constants load in a second round --
+// a one-round grid (a small call) reaches its data after two rounds of
+// scalar loads instead of a chain of them.
+__device__ __forceinline__ void find_inline(const KernelArgs& a, uint64_t chunk, DevBlock& b, Coef& c)
 {
-    DevBlock b = a.inl[0];
+    uint32_t sel = 0;
 #pragma unroll
     for (int k = 1; k < kInline; ++k)
-        if (static_cast<uint32_t>(k) < a.nblocks && a.inl[k].chunk0 <= chunk) b = a.inl[k];
-    return b;
+        sel = (static_cast<uint32_t>(k) < a.nblocks && a.inl[k].chunk0 <= chunk) ? static_cast<uint32_t>(k) : sel;
+    c = a.coef[sel];
+    b = a.inl[sel];
 }
 
 template <int U, bool kTiled, bool kG32, bool kNorm>
-__device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const DevBlock& b, uint64_t chunk)
+__device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const DevBlock& b, const Coef& c,
+                                                uint64_t chunk)
 {
     constexpr uint64_t kChunkU = static_cast<uint64_t>(kThreads) * kQuad * U;
-    const Coef c = args.coef[b.group];
     const uint64_t k = chunk - b.chunk0;   // chunk index inside the block
     const uint64_t e0 = k * kChunkU;       // its first element
     const uint64_t left = b.n - e0;
@@ -333,21 +339,37 @@ __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const De
     }
 }
 
-template <int U, bool kTiled, bool kG32, bool kNorm>
+// kTable: the blocks are in a device table (found by the per-chunk index or
+// by a binary search), else in the kernel arguments.  The grid never
+// exceeds the chunk count, so every workgroup has a first chunk: the loop
+// only tests the count for grids smaller than the call (very large calls).
+template <int U, bool kTiled, bool kG32, bool kNorm, bool kTable>
 __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs args)
 {
-    if (args.blocks) {
+    uint64_t chunk = blockIdx.x;
+    if (kTable) {
         const LSO_CONST DevBlock* table =
             reinterpret_cast<const LSO_CONST DevBlock*>(reinterpret_cast<uintptr_t>(args.blocks));
         const LSO_CONST uint32_t* index =
             reinterpret_cast<const LSO_CONST uint32_t*>(reinterpret_cast<uintptr_t>(args.chunk_block));
-        for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x) {
+        // one constant set for the whole launch (the usual case): its load
+        // does not wait for the block's
+        const Coef c0 = args.coef[0];
+        do {
             const uint32_t bi = index ? index[chunk] : search_block(table, args.nblocks, chunk);
-            run_block_chunk<U, kTiled, kG32, kNorm>(args, load_block(table + bi), chunk);
-        }
+            const DevBlock b = load_block(table + bi);
+            const Coef c = args.ngroups == 1 ? c0 : args.coef[b.group];
+            run_block_chunk<U, kTiled, kG32, kNorm>(args, b, c, chunk);
+            chunk += gridDim.x;
+        } while (chunk < args.total_chunks);
     } else {
-        for (uint64_t chunk = blockIdx.x; chunk < args.total_chunks; chunk += gridDim.x)
-            run_block_chunk<U, kTiled, kG32, kNorm>(args, find_inline(args, chunk), chunk);
+        do {
+            DevBlock b;
+            Coef c;
+            find_inline(args, chunk, b, c);
+            run_block_chunk<U, kTiled, kG32, kNorm>(args, b, c, chunk);
+            chunk += gridDim.x;
+        } while (chunk < args.total_chunks);
     }
 }
 
@@ -396,8 +418,13 @@ template <int U, bool kTiled, bool kG32>
 void launch_variant(const KernelArgs& args, dim3 g, hipStream_t s)
 {
     const dim3 t(kThreads);
-    if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true>), g, t, 0, s, args);
-    else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false>), g, t, 0, s, args);
+    if (args.blocks) {
+        if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true, true>), g, t, 0, s, args);
+        else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false, true>), g, t, 0, s, args);
+    } else {
+        if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true, false>), g, t, 0, s, args);
+        else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false, false>), g, t, 0, s, args);
+    }
 }
 
 }  // namespace

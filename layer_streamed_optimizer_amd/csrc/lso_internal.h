@@ -68,8 +68,8 @@ struct KernelArgs {
     double* partials;              // norm variant: sum of g^2 per wave and chunk of this launch
     uint64_t total_chunks;
     uint32_t nblocks;
-    uint32_t pad;
-    Coef coef[kMaxGroups];
+    uint32_t ngroups;              // constant sets in coef[] (table launches)
+    Coef coef[kMaxGroups];         // by-value launches: coef[k] is inl[k]'s
     DevBlock inl[kInline];
 };
 

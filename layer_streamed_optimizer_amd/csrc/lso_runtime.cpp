@@ -546,6 +546,7 @@ lso_status enqueue_impl(const lso_block* blocks, size_t n, void* stream, bool ge
                 const HyperKey& k = sets[j];
                 args.coef[j % kMaxGroups] = make_coef(k.opt, k.t, k.lr, k.beta1, k.beta2, k.eps);
             }
+            args.ngroups = static_cast<uint32_t>(std::min<size_t>(kMaxGroups, sets.size() - L * kMaxGroups));
             if (tab.empty()) continue;
             args.total_chunks = chunks;
             args.nblocks = static_cast<uint32_t>(tab.size());
@@ -566,7 +567,14 @@ lso_status enqueue_impl(const lso_block* blocks, size_t n, void* stream, bool ge
                     std::memcpy(last_ok, tab.data(), tab.size() * sizeof(DevBlock));
                     last_ok_n = tab.size();
                 }
-                for (size_t j = 0; j < tab.size(); ++j) args.inl[j] = tab[j];
+                // by value, block j carries its constants in coef[j]
+                Coef mine[kInline];
+                for (size_t j = 0; j < tab.size(); ++j) mine[j] = args.coef[tab[j].group];
+                for (size_t j = 0; j < tab.size(); ++j) {
+                    args.inl[j] = tab[j];
+                    args.inl[j].group = static_cast<uint32_t>(j);
+                    args.coef[j] = mine[j];
+                }
             } else if (noalloc) {
                 lso_status s = noalloc_write_table(scratch + scratch_used, tab.data(), tab.size(), stream);
                 if (s != LSO_OK) return s;
