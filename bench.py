@@ -173,6 +173,8 @@ def resident(args, w):
     free, _total = torch.cuda.mem_get_info()
     budget = free - lay.state_bytes - lay.weight_bytes - (8 << 30)
     n_sets = max(1, min(total_steps, budget // max(lay.grad_bytes, 1)))
+    if args.grad_sets:
+        n_sets = max(1, min(n_sets, args.grad_sets))
     progress(f"{w.key}: {len(sizes)} blocks, {params:,} params, {args.layout} state "
              f"{lay.state_bytes / 1e9:.1f} GB, {n_sets} {args.grad_dtype} gradient sets of "
              f"{lay.grad_bytes / 1e9:.2f} GB")
@@ -983,6 +985,9 @@ def main():
     ap.add_argument("--norms", action="store_true",
                     help="resident workloads: the update with per-block gradient norms "
                          "(progressive layer locking)")
+    ap.add_argument("--grad-sets", type=int, default=0,
+                    help="resident workloads: at most this many gradient sets rotate over the steps "
+                         "(0: as many as fit, up to one per step)")
     ap.add_argument("--grad-dtype", choices=["bf16", "f32"], default="bf16",
                     help="gradient dtype (f32: the LoRA article's FP32 adapter gradients; for c4 "
                          "the device producer writes FP32)")
