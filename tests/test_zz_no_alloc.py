@@ -144,3 +144,44 @@ def test_noalloc_too_many_entries_rejected_and_nothing_written():
     assert "exceed" in lso.last_error()
     T.cuda.synchronize()
     assert T.equal(before, a.buf)
+
+
+def test_noalloc_steps_captured_in_a_hip_graph_replay_like_eager():
+    """The callers this entry point is for: three steps of the 308 LoRA
+    tensors captured into one HIP graph (the table writes and the updates,
+    no allocation inside the capture), replayed four times with new
+    gradients copied in eagerly and a synchronisation between replays; after
+    every replay the state equals three eager lso_adam_step calls, bit for
+    bit."""
+    T = torch()
+    w = configs.get("c2")
+    sizes = [b.n for b in w.blocks]
+    init = [b.init for b in w.blocks]
+    sid = configs.STREAM_ID["c2"]
+    ga, ea, warm = Arena(sizes), Arena(sizes), Arena(sizes)
+    fill([ga, ea, warm], sizes, sid, init, 1)
+    # one call outside the capture: the scratch array's address is looked up
+    lso.adam_step_noalloc(warm.table())
+    T.cuda.synchronize()
+    tg, te = ga.table(), ea.table()
+    graph = T.cuda.CUDAGraph()
+    cap = T.cuda.Stream()
+    log("no-alloc: capturing three steps of 308 tensors")
+    with T.cuda.graph(graph, stream=cap):
+        for t in range(1, 4):
+            tg.set_step(t)
+            lso.adam_step_noalloc(tg, T.cuda.current_stream())
+    T.cuda.synchronize()
+    for r in range(4):
+        fill([ga, ea], sizes, sid, init, 10 + r)   # new gradients, eagerly
+        T.cuda.synchronize()
+        graph.replay()
+        for t in range(1, 4):
+            te.set_step(t)
+            lso.adam_step(te)
+        T.cuda.synchronize()
+        for i in range(len(sizes)):
+            for q in QUANTITIES:
+                assert np.array_equal(ga.get(i, q).view(np.uint8), ea.get(i, q).view(np.uint8)), (r, i, q)
+        log(f"no-alloc graph replay {r}: equal to the eager steps")
+    assert ga.canaries_intact() and ea.canaries_intact()
