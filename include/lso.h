@@ -173,7 +173,11 @@ lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream);
  * LSO_E_INVALID with nothing enqueued.  Every call on one GPU shares that
  * GPU's array and leaves its table there: calls that overlap on one GPU
  * (different streams, or unordered threads) race on it and must not be
- * issued.  Errors: as lso_adam_step (NOMEM cannot occur).
+ * issued.  The array's device address is looked up once per device, by
+ * the first call that needs it (or by the first lso_adam_step on that
+ * device); that first lookup must not happen under stream capture -- such
+ * a call returns LSO_E_INVALID with nothing enqueued -- so make one call
+ * before capturing.  Errors: as lso_adam_step (NOMEM cannot occur).
  */
 #define LSO_NOALLOC_MAX_BLOCKS 4096u
 lso_status lso_adam_step_noalloc(const lso_block* blocks, size_t n, void* stream);

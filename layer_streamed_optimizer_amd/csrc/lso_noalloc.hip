@@ -54,13 +54,23 @@ DevBlock* g_scratch[kMaxDevices] = {};   // device address of `scratch`, per dev
 
 }  // namespace
 
-lso_status noalloc_scratch(DevBlock** out)
+lso_status noalloc_scratch(DevBlock** out, void* stream)
 {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
     if (dev < 0 || dev >= kMaxDevices) return fail(LSO_E_INVALID, "device %d out of range", dev);
     std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_scratch[dev] && stream) {
+        // the address is looked up once per device, outside any capture (the
+        // lookup may load the code object, which a capture cannot hold)
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        err = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs);
+        if (err != hipSuccess) return hip_fail(err, "hipStreamIsCapturing");
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(LSO_E_INVALID, "the first lso_adam_step_noalloc call on device %d is under stream capture: "
+                        "make one call (any table of more than 4 blocks, or lso_adam_step) before capturing", dev);
+    }
     if (!g_scratch[dev]) {
         // once per device, with that device current
         void* p = nullptr;

@@ -498,7 +498,7 @@ lso_status enqueue_impl(const lso_block* blocks, size_t n, void* stream, bool ge
             checked = true;
         }
         if (need > 0) {
-            lso_status s = noalloc_scratch(&scratch);
+            lso_status s = noalloc_scratch(&scratch, stream);
             if (s != LSO_OK) return s;
         }
     }
@@ -621,7 +621,19 @@ extern "C" {
 lso_status lso_adam_step(const lso_block* blocks, size_t n, void* stream)
 {
     lso::clear_error();
-    return lso::enqueue_update(blocks, n, stream, false);
+    lso_status s = lso::enqueue_update(blocks, n, stream, false);
+    if (s == LSO_OK && n > 0) {
+        // so a caller that captures lso_adam_step_noalloc later finds the
+        // allocation-free path's array already looked up on this device
+        thread_local int looked_up = -1;
+        int dev = -1;
+        if (hipGetDevice(&dev) == hipSuccess && dev != looked_up) {
+            lso::DevBlock* p = nullptr;
+            if (lso::noalloc_scratch(&p, stream) == LSO_OK) looked_up = dev;
+            lso::clear_error();
+        }
+    }
+    return s;
 }
 
 uint64_t lso_norm_workspace_bytes(const lso_block* blocks, size_t n)

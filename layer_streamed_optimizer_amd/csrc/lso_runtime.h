@@ -47,7 +47,9 @@ struct DevBlock;
 
 // The current device's fixed scratch array of LSO_NOALLOC_MAX_BLOCKS
 // DevBlocks (lso_noalloc.hip); its address is looked up once per device.
-lso_status noalloc_scratch(DevBlock** out);
+// stream: the call's stream, checked for capture before the first lookup
+// (NULL skips the check).
+lso_status noalloc_scratch(DevBlock** out, void* stream);
 
 // Enqueue on stream the writes of count table entries to dst (inside the
 // scratch array), carried in kernel arguments.

@@ -185,3 +185,19 @@ def test_noalloc_steps_captured_in_a_hip_graph_replay_like_eager():
                 assert np.array_equal(ga.get(i, q).view(np.uint8), ea.get(i, q).view(np.uint8)), (r, i, q)
         log(f"no-alloc graph replay {r}: equal to the eager steps")
     assert ga.canaries_intact() and ea.canaries_intact()
+
+
+def test_noalloc_first_call_under_capture_is_refused_in_a_fresh_process():
+    """The array's address is looked up once per device, outside any capture:
+    in a fresh process the first call made under capture returns
+    LSO_E_INVALID and writes nothing; after one call outside, captured calls
+    replay like eager ones (tests/noalloc_capture_child.py)."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    log("no-alloc: capture rule in a child process")
+    r = subprocess.run([sys.executable, os.path.join(here, "noalloc_capture_child.py")],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "capture rule ok" in r.stdout
