@@ -486,6 +486,28 @@ def hbm_probe(nbytes: int = 8 << 30, reps: int = 6) -> dict:
         rows.append(dict(shape=name, variant=var, param=param, GBps=gbps, exact=ok))
         progress(f"hbm probe: {name}: {gbps:.0f} GB/s{'' if ok is not False else ' WRONG'}")
     del src, dst, keep
+    # the update's own tiled traffic shape (14 B read, 14 B written per
+    # element, in place) with each store policy
+    n = 134_283 * 8192
+    state = torch.zeros(12 * n, dtype=torch.uint8, device=dev)
+    grad = torch.zeros(2 * n, dtype=torch.uint8, device=dev)
+    weight = torch.empty(2 * n, dtype=torch.uint8, device=dev)
+    for st_pol in range(6):
+        times = []
+        for r in range(reps + 2):
+            s.record()
+            rc = P.lso_probe_copy_shaped_cpol(state.data_ptr(), grad.data_ptr(), weight.data_ptr(), n, st_pol, hs)
+            e.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"lso_probe_copy_shaped_cpol({st_pol}) failed ({rc})")
+            if r >= 2:
+                times.append(s.elapsed_time(e))
+        gbps = 28 * n / (min(times) * 1e-3) / 1e9
+        name = f"update-shaped (tiled, in place), stores {names[st_pol]}"
+        rows.append(dict(shape=name, variant="shaped", param=st_pol, GBps=gbps, exact=None))
+        progress(f"hbm probe: {name}: {gbps:.0f} GB/s")
+    del state, grad, weight
     return dict(hbm_probe=rows, bytes=nbytes, best_of=reps, unit="GB/s (read + write)")
 
 

@@ -182,6 +182,8 @@ def probes():
         P.lso_probe_copy.restype = ctypes.c_int
         P.lso_probe_copy_variant.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, u64, vp]
         P.lso_probe_copy_variant.restype = ctypes.c_int
+        P.lso_probe_copy_shaped_cpol.argtypes = [vp, vp, vp, u64, ctypes.c_int, vp]
+        P.lso_probe_copy_shaped_cpol.restype = ctypes.c_int
         P.lso_probe_copy_shaped.argtypes = [vp, vp, vp, u64, ctypes.c_int, vp]
         P.lso_probe_copy_shaped.restype = ctypes.c_int
         P.lso_probe_link_sdma.argtypes = [u64, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32),

@@ -65,6 +65,28 @@ __device__ __forceinline__ void st_nt(void* p, T v)
     __builtin_nontemporal_store(v, reinterpret_cast<LSO_GLOBAL T*>(reinterpret_cast<uintptr_t>(p)));
 }
 
+// Stores of a tiled chunk carry the cache-policy bits nt (streaming) and
+// sc1 (device scope).  Measured on this part, alternating libraries on one
+// box: c3 (LLaMA-7B, tiled) 28.75 ms against 29.71 ms with nt alone over
+// six runs each, c1 tiled 4.75 against 4.87 ms; planar chunks (four quads
+// per lane) were 3% slower with them, so they keep plain nt stores.  No
+// compiler builtin sets sc1 on a global store, hence the inline assembly.
+// The compiler does not count these stores in its waits; on this
+// architecture vector-memory operations complete in order and share one
+// counter, and every lane issues them after all its loads of the chunk, so
+// each wait the compiler emits only becomes longer, never shorter.
+__device__ __forceinline__ void st_nt_sc1(const void* p, f32x4 v)
+{
+    const LSO_GLOBAL f32x4* a = reinterpret_cast<const LSO_GLOBAL f32x4*>(reinterpret_cast<uintptr_t>(p));
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1" : : "v"(a), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void st_nt_sc1(const void* p, u32x2 v)
+{
+    const LSO_GLOBAL u32x2* a = reinterpret_cast<const LSO_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(p));
+    asm volatile("global_store_dwordx2 %0, %1, off nt sc1" : : "v"(a), "v"(v) : "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T ld(const void* p)
 {
@@ -162,9 +184,18 @@ __device__ __forceinline__ u32x2 compute_quad(const Coef& c, Quad& x, float& sq)
     return w;
 }
 
-template <bool kSgd>
+template <bool kSgd, bool kSc1>
 __device__ __forceinline__ void store_quad(const Chunk& ch, uint32_t e, const Quad& x, u32x2 w, bool has_w)
 {
+    if (kSc1) {
+        st_nt_sc1(ch.p + e, x.p);
+        if (!kSgd) {
+            st_nt_sc1(ch.m + e, x.m);
+            st_nt_sc1(ch.v + e, x.v);
+        }
+        if (has_w) st_nt_sc1(ch.w + e, w);
+        return;
+    }
     st_nt<f32x4>(ch.p + e, x.p);
     if (!kSgd) {
         st_nt<f32x4>(ch.m + e, x.m);
@@ -196,7 +227,7 @@ __device__ void tail_elems(const Chunk& ch, const Coef& c, uint32_t e, uint32_t 
 
 // One chunk of kThreads * kQuad * U elements.  Returns this lane's sum of
 // g^2 (norm variant; 0 otherwise).
-template <int U, bool kSgd, bool kG32, bool kNorm>
+template <int U, bool kSgd, bool kG32, bool kNorm, bool kSc1>
 __device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool has_w)
 {
     constexpr uint32_t kChunkU = static_cast<uint32_t>(kThreads) * kQuad * U;
@@ -209,7 +240,7 @@ __device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const u32x2 w = compute_quad<kSgd, kG32, kNorm>(c, x[u], sq);
-            store_quad<kSgd>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u], w, has_w);
+            store_quad<kSgd, kSc1>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u], w, has_w);
         }
         return sq;
     }
@@ -220,7 +251,7 @@ __device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool 
             Quad x;
             load_quad<kSgd, kG32>(ch, e, x);
             const u32x2 w = compute_quad<kSgd, kG32, kNorm>(c, x, sq);
-            store_quad<kSgd>(ch, e, x, w, has_w);
+            store_quad<kSgd, kSc1>(ch, e, x, w, has_w);
         } else if (e < ch.n) {
             tail_elems<kSgd, kG32, kNorm>(ch, c, e, ch.n, has_w, sq);
         }
@@ -329,8 +360,8 @@ __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const De
         ch.v = b.v ? b.v + e0 : nullptr;
     }
     const bool has_w = (b.flags & kFlagWeight) != 0;
-    const float sq = (!kTiled && (b.flags & kFlagSgd)) ? run_chunk<U, true, kG32, kNorm>(ch, c, has_w)
-                                                       : run_chunk<U, false, kG32, kNorm>(ch, c, has_w);
+    const float sq = (!kTiled && (b.flags & kFlagSgd)) ? run_chunk<U, true, kG32, kNorm, false>(ch, c, has_w)
+                                                       : run_chunk<U, false, kG32, kNorm, kTiled>(ch, c, has_w);
     if (kNorm) {
         // one sum per wave (no barrier in the update kernel); the reduce
         // kernel adds a block's wave sums in order

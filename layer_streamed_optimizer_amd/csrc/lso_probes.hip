@@ -178,6 +178,56 @@ copy_cpol_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst)
     else LSO_CPOL_STORE("sc0 sc1 nt");
 }
 
+// The update's tiled traffic shape (shaped_copy_kernel<true>) with the
+// cache-policy bits S of its stores (as copy_cpol_kernel's).
+#define LSO_CPOL_ST16(ms, addr, val) asm volatile("global_store_dwordx4 %0, %1, off " ms : : "v"(addr), "v"(val) : "memory")
+#define LSO_CPOL_ST8(ms, addr, val) asm volatile("global_store_dwordx2 %0, %1, off " ms : : "v"(addr), "v"(val) : "memory")
+
+template <int S>
+__device__ __forceinline__ void st16_cpol(float* p, f32x4 x)
+{
+    LSO_GLOBAL f32x4* a = reinterpret_cast<LSO_GLOBAL f32x4*>(reinterpret_cast<uintptr_t>(p));
+    if (S == 0) LSO_CPOL_ST16("", a, x);
+    else if (S == 1) LSO_CPOL_ST16("nt", a, x);
+    else if (S == 2) LSO_CPOL_ST16("sc1", a, x);
+    else if (S == 3) LSO_CPOL_ST16("nt sc1", a, x);
+    else if (S == 4) LSO_CPOL_ST16("sc0 sc1", a, x);
+    else LSO_CPOL_ST16("sc0 sc1 nt", a, x);
+}
+
+template <int S>
+__device__ __forceinline__ void st8_cpol(uint16_t* p, u32x2 x)
+{
+    LSO_GLOBAL u32x2* a = reinterpret_cast<LSO_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(p));
+    if (S == 0) LSO_CPOL_ST8("", a, x);
+    else if (S == 1) LSO_CPOL_ST8("nt", a, x);
+    else if (S == 2) LSO_CPOL_ST8("sc1", a, x);
+    else if (S == 3) LSO_CPOL_ST8("nt sc1", a, x);
+    else if (S == 4) LSO_CPOL_ST8("sc0 sc1", a, x);
+    else LSO_CPOL_ST8("sc0 sc1 nt", a, x);
+}
+
+template <int S>
+__global__ void __launch_bounds__(256)
+shaped_cpol_kernel(float* __restrict__ state, const uint16_t* __restrict__ grad, uint16_t* __restrict__ weight)
+{
+    const uint64_t e0 = static_cast<uint64_t>(blockIdx.x) * kShapedChunk;
+    float* p = state + 3 * (e0 / kShapedTile) * kShapedTile + e0 % kShapedTile;
+    float* m = p + kShapedTile;
+    float* v = m + kShapedTile;
+    const uint32_t i = threadIdx.x * 4;
+    const u32x2 g = ld_nt<u32x2>(grad + e0 + i);
+    f32x4 a = ld_nt<f32x4>(p + i), b = ld_nt<f32x4>(m + i), c = ld_nt<f32x4>(v + i);
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    u32x4v ai = __builtin_bit_cast(u32x4v, a) ^ g.x, bi = __builtin_bit_cast(u32x4v, b) ^ g.y;
+    u32x4v ci = __builtin_bit_cast(u32x4v, c) ^ (g.x + g.y);
+    st16_cpol<S>(p + i, __builtin_bit_cast(f32x4, ai));
+    st16_cpol<S>(m + i, __builtin_bit_cast(f32x4, bi));
+    st16_cpol<S>(v + i, __builtin_bit_cast(f32x4, ci));
+    const u32x2 w = {(ai.x >> 16) | (ai.y & 0xFFFF0000u), (ai.z >> 16) | (ai.w & 0xFFFF0000u)};
+    st8_cpol<S>(weight + e0 + i, w);
+}
+
 // In place: every vector read and written back to the same address (bits
 // flipped), as the update does with its state.
 __global__ void __launch_bounds__(256)
@@ -328,6 +378,33 @@ int lso_probe_copy_variant(int variant, int param, const void* src, void* dst, u
     case 5: hipLaunchKernelGGL(read_only_kernel, dim3(g1), t, 0, st, s, static_cast<uint32_t*>(dst)); break;
     case 6: hipLaunchKernelGGL(write_only_kernel, dim3(g1), t, 0, st, d); break;
     default: return static_cast<int>(hipErrorInvalidValue);
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+// The tiled update-shaped copy of lso_probe_copy_shaped with the store
+// cache-policy bits `store_cpol` (0 none, 1 nt, 2 sc1, 3 nt sc1, 4 sc0 sc1,
+// 5 sc0 sc1 nt); same buffer rules.  Returns a hipError_t.
+int lso_probe_copy_shaped_cpol(void* state, const void* grad, void* weight, uint64_t n, int store_cpol,
+                               void* stream)
+{
+    if (n % kShapedTile != 0 || n > (uint64_t(1) << 34) || !state || !grad || !weight || store_cpol < 0 ||
+        store_cpol > 5 || reinterpret_cast<uintptr_t>(state) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(grad) % 16 != 0 || reinterpret_cast<uintptr_t>(weight) % 16 != 0)
+        return static_cast<int>(hipErrorInvalidValue);
+    if (n == 0) return 0;
+    const dim3 grid(static_cast<unsigned>(n / kShapedChunk));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto* sp = static_cast<float*>(state);
+    auto* g = static_cast<const uint16_t*>(grad);
+    auto* w = static_cast<uint16_t*>(weight);
+    switch (store_cpol) {
+    case 0: hipLaunchKernelGGL(shaped_cpol_kernel<0>, grid, dim3(256), 0, st, sp, g, w); break;
+    case 1: hipLaunchKernelGGL(shaped_cpol_kernel<1>, grid, dim3(256), 0, st, sp, g, w); break;
+    case 2: hipLaunchKernelGGL(shaped_cpol_kernel<2>, grid, dim3(256), 0, st, sp, g, w); break;
+    case 3: hipLaunchKernelGGL(shaped_cpol_kernel<3>, grid, dim3(256), 0, st, sp, g, w); break;
+    case 4: hipLaunchKernelGGL(shaped_cpol_kernel<4>, grid, dim3(256), 0, st, sp, g, w); break;
+    default: hipLaunchKernelGGL(shaped_cpol_kernel<5>, grid, dim3(256), 0, st, sp, g, w); break;
     }
     return static_cast<int>(hipGetLastError());
 }
