@@ -374,6 +374,7 @@ def resident(args, w):
         kernel_median_us=sorted(kernel_ms)[len(kernel_ms) // 2] * 1e3,
         kernel_first_step_us=cold * 1e3 if cold is not None else None,
         hbm_copy_ceiling_GBps=ceiling,
+        frac_of_copy_ceiling=achieved / ceiling,
         hbm_update_shaped_copy_GBps=shaped,
         config=dict(workload=f"{w.key}: {w.title}", blocks=len(sizes), params=params,
                     state_layout=args.layout, grad_dtype=args.grad_dtype, bytes_per_param=bpp,
@@ -1122,6 +1123,9 @@ def main():
         out["streamed"] = dict(metric=r.pop("metric"), value=r.pop("value"), unit=r.pop("unit"),
                                steps=sa.steps, warmup=sa.warmup, ms_per_step=r.pop("ms_per_step"),
                                config=r.pop("config"), roofline=r.pop("roofline"), **r)
+        if not args.no_cpu_baseline:
+            progress("timing the oracle on one 70B-shaped layer")
+            out["streamed"]["cpu_baseline"] = cpu_baseline(configs.get("c4"), budget_s=8.0)
     out["environment"] = environment()
     print(json.dumps(out), flush=True)
 
