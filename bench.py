@@ -1006,6 +1006,95 @@ def cpu_baseline(w, budget_s=12.0):
 
 # ---------------------------------------------------------------------- main
 
+def placement_scan(positions: int = 12, reps: int = 4) -> dict:
+    """The c3 update's rate against where its arrays sit in HBM: one pool of
+    all free memory but 8 GiB, the whole working set (tiled state, weights,
+    one gradient set, laid out as in the resident bench) placed at
+    `positions` offsets spread over it, and at each the update, its traffic
+    shape with no arithmetic (lso_probe_copy_shaped_cpol, the update's
+    stores) and a plain 8 GiB copy inside the state region, each the average
+    of `reps` launches after one."""
+    import torch
+
+    import layer_streamed_optimizer_amd as lso
+    import synth
+    from layer_streamed_optimizer_amd import _native, configs
+    P = _native.probes()
+    dev = torch.device("cuda:0")
+    hs = torch.cuda.current_stream().cuda_stream
+    w = configs.get("c3")
+    sid = configs.STREAM_ID["c3"]
+    sizes = [b.n for b in w.blocks]
+    lay = configs.ResidentLayout(sizes, tiled=True, grad_f32=False)
+    m2 = 2 << 20
+
+    def up(x):
+        return (x + m2 - 1) // m2 * m2
+
+    off_w = up(lay.state_bytes)
+    off_g = off_w + up(lay.weight_bytes)
+    span_bytes = off_g + up(lay.grad_bytes)
+    n_shaped = w.params // 8192 * 8192
+    copy_bytes = 8 << 30
+    free, _ = torch.cuda.mem_get_info()
+    total = (free - (8 << 30)) // m2 * m2
+    if total < span_bytes + m2:
+        raise RuntimeError("not enough device memory for the c3 working set")
+    pool = torch.empty(total, dtype=torch.uint8, device=dev)
+    base = int(pool.data_ptr())
+    scratch = torch.empty(max(sizes), dtype=torch.float32, device=dev)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+
+    rows, step = [], [0]
+    for k in range(positions):
+        off = (total - span_bytes) * k // max(1, positions - 1) // m2 * m2
+        sb, wb, gb = base + off, base + off + off_w, base + off + off_g
+        for b, spec in enumerate(w.blocks):
+            synth.device_fill_normal_f32(int(scratch.data_ptr()), spec.n, stream=sid, block=b,
+                                         purpose=synth.PURPOSE_MASTER, step=0, sigma=configs.MASTER_SIGMA,
+                                         hip_stream=hs)
+            lso.tiled_pack(sb + lay.off_master[b], int(scratch.data_ptr()), None, None, n=spec.n, stream=hs)
+            synth.device_fill_normal_bf16(gb + lay.off_grad[b], spec.n, stream=sid, block=b,
+                                          purpose=synth.PURPOSE_GRAD, step=1, sigma=configs.GRAD_SIGMA,
+                                          hip_stream=hs)
+        tab = lso.BlockTable.from_rows(
+            dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
+                 grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], t=1, lr=configs.LR,
+                 beta1=configs.BETA1, beta2=configs.BETA2, eps=configs.EPS, layout=lso.LSO_LAYOUT_TILED,
+                 grad_dtype=lso.LSO_DT_BF16) for b, n in enumerate(sizes))
+
+        def update():
+            step[0] += 1
+            tab.set_step(step[0])
+            lso.adam_step(tab, hs)
+
+        t_update = timed(update)
+        t_copy = timed(lambda: check(P.lso_probe_copy(sb, sb + copy_bytes, copy_bytes, 0, hs), "copy"))
+        # last: it overwrites the state with mixed bits
+        t_shaped = timed(lambda: check(P.lso_probe_copy_shaped_cpol(sb, gb, wb, n_shaped, 3, hs), "shaped copy"))
+        row = dict(offset_GB=off / 1e9, update_ms=t_update, update_GBps=28 * w.params / (t_update * 1e-3) / 1e9,
+                   shaped_GBps=28 * n_shaped / (t_shaped * 1e-3) / 1e9,
+                   copy_GBps=2 * copy_bytes / (t_copy * 1e-3) / 1e9)
+        rows.append(row)
+        progress(f"placement +{row['offset_GB']:.1f} GB: update {t_update:.3f} ms ({row['update_GBps']:.0f} GB/s), "
+                 f"shaped copy {row['shaped_GBps']:.0f} GB/s, plain copy {row['copy_GBps']:.0f} GB/s")
+    del pool, scratch
+    return dict(placement_scan=rows, pool_GB=total / 1e9, working_set_GB=span_bytes / 1e9, reps=reps)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1027,6 +1116,9 @@ def main():
     ap.add_argument("--launch-floor", action="store_true",
                     help="only the floors of the launch-bound workloads (c0, c2 sizes): an empty "
                          "launch, the update-shaped copy and a plain copy; one JSON line")
+    ap.add_argument("--placement-scan", action="store_true",
+                    help="only the placement scan: the c3 update, its traffic shape and a plain "
+                         "copy with the working set at 12 offsets in one pool; one JSON line")
     ap.add_argument("--host-memory", choices=["pageable", "pinned", "file"], default="pageable",
                     help="c4: authoritative blocks in pageable memory (staged through pinned "
                          "buffers), page-locked (direct; limited by the host's page-locked "
@@ -1071,6 +1163,14 @@ def main():
 
         torch.cuda.set_device(0)
         out = launch_floor()
+        out["environment"] = environment()
+        print(json.dumps(out), flush=True)
+        return
+    if args.placement_scan:
+        import torch
+
+        torch.cuda.set_device(0)
+        out = placement_scan()
         out["environment"] = environment()
         print(json.dumps(out), flush=True)
         return
