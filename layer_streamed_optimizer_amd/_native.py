@@ -191,6 +191,8 @@ def probes():
         P.lso_probe_link_sdma.restype = ctypes.c_int
         P.lso_probe_bf16_rne.argtypes = [u32, u64, vp, vp]
         P.lso_probe_bf16_rne.restype = ctypes.c_int
+        P.lso_probe_sqrt.argtypes = [u32, u64, vp, vp]
+        P.lso_probe_sqrt.restype = ctypes.c_int
         P.lso_probe_link.argtypes = [u64, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
         P.lso_probe_link.restype = ctypes.c_int
         P.lso_probe_link_mode.argtypes = [u64, ctypes.c_int, ctypes.c_int, ctypes.c_uint,

@@ -16,9 +16,12 @@ INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: FMAs are spelled out in the kernel; nothing else fuses.
+# -fhip-fp32-correctly-rounded-divide-sqrt: FP32 division and sqrtf round
+# correctly (stated here rather than left to the compiler's default).
 # Packed FP32 instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-         "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 # ROCr, for copies on named SDMA engines (lso_sdma.cpp)

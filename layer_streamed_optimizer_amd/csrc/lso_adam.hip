@@ -34,6 +34,9 @@
 //
 // Built with -ffp-contract=off: every FMA below is an explicit fmaf and every
 // other operator rounds once, so the SGD path is exactly fl(W + fl(-(lr*g))).
+// Built with -fhip-fp32-correctly-rounded-divide-sqrt: FP32 division and
+// sqrtf are correctly rounded (HIP's __fsqrt_rn is the hardware's 1-ulp root
+// unless the rounded-operation library is selected, so it is not used).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -103,8 +106,8 @@ __device__ __forceinline__ void adam_elem(const Coef& c, float g, float& master,
 {
     const float m1 = fmaf(c.b1, m, c.c1 * g);
     const float v1 = fmaf(c.b2, v, c.c2 * (g * g));   // g*g is exact for BF16 g (8 significant bits)
-    const float den = fmaf(__fsqrt_rn(v1), c.r, c.e);  // sqrt(v_hat) + eps, v_hat = v1 * r^2
-    const float delta = -__fdiv_rn(c.s * m1, den);
+    const float den = fmaf(__builtin_sqrtf(v1), c.r, c.e);  // sqrt(v_hat) + eps, v_hat = v1 * r^2
+    const float delta = -((c.s * m1) / den);
     master = master + delta;
     m = m1;
     v = v1;
@@ -290,19 +293,13 @@ __device__ __forceinline__ double workgroup_sum(double v)
     return s;
 }
 
+// A table entry in one 64-byte scalar load (fields loaded one by one let
+// the compiler fetch the constant-set index first and wait for it).
 __device__ __forceinline__ DevBlock load_block(const LSO_CONST DevBlock* p)
 {
-    DevBlock b;
-    b.master = p->master;
-    b.m = p->m;
-    b.v = p->v;
-    b.g = p->g;
-    b.w = p->w;
-    b.n = p->n;
-    b.chunk0 = p->chunk0;
-    b.group = p->group;
-    b.flags = p->flags;
-    return b;
+    typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+    const u32x16 raw = *reinterpret_cast<const LSO_CONST u32x16*>(p);
+    return __builtin_bit_cast(DevBlock, raw);
 }
 
 // The last block whose chunk0 <= chunk (uniform across the workgroup).
@@ -371,10 +368,12 @@ __device__ __forceinline__ void run_block_chunk(const KernelArgs& args, const De
 }
 
 // kTable: the blocks are in a device table (found by the per-chunk index or
-// by a binary search), else in the kernel arguments.  The grid never
-// exceeds the chunk count, so every workgroup has a first chunk: the loop
-// only tests the count for grids smaller than the call (very large calls).
-template <int U, bool kTiled, bool kG32, bool kNorm, bool kTable>
+// by a binary search), else in the kernel arguments; kOne: a by-value call
+// of one block, whose fields and constants load in a single round with no
+// pick.  The grid never exceeds the chunk count, so every workgroup has a
+// first chunk: the loop only tests the count for grids smaller than the
+// call (very large calls).
+template <int U, bool kTiled, bool kG32, bool kNorm, bool kTable, bool kOne>
 __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs args)
 {
     uint64_t chunk = blockIdx.x;
@@ -389,9 +388,17 @@ __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs a
         do {
             const uint32_t bi = index ? index[chunk] : search_block(table, args.nblocks, chunk);
             const DevBlock b = load_block(table + bi);
-            const Coef c = args.ngroups == 1 ? c0 : args.coef[b.group];
+            Coef c = c0;
+            if (args.ngroups != 1) c = args.coef[b.group];
             run_block_chunk<U, kTiled, kG32, kNorm>(args, b, c, chunk);
-            chunk += gridDim.x;
+            chunk += args.grid;
+        } while (chunk < args.total_chunks);
+    } else if (kOne) {
+        const DevBlock b = args.inl[0];
+        const Coef c = args.coef[0];
+        do {
+            run_block_chunk<U, kTiled, kG32, kNorm>(args, b, c, chunk);
+            chunk += args.grid;
         } while (chunk < args.total_chunks);
     } else {
         do {
@@ -399,7 +406,7 @@ __global__ void __launch_bounds__(kThreads) fused_adam_kernel(const KernelArgs a
             Coef c;
             find_inline(args, chunk, b, c);
             run_block_chunk<U, kTiled, kG32, kNorm>(args, b, c, chunk);
-            chunk += gridDim.x;
+            chunk += args.grid;
         } while (chunk < args.total_chunks);
     }
 }
@@ -450,11 +457,14 @@ void launch_variant(const KernelArgs& args, dim3 g, hipStream_t s)
 {
     const dim3 t(kThreads);
     if (args.blocks) {
-        if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true, true>), g, t, 0, s, args);
-        else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false, true>), g, t, 0, s, args);
+        if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true, true, false>), g, t, 0, s, args);
+        else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false, true, false>), g, t, 0, s, args);
+    } else if (args.nblocks == 1) {
+        if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true, false, true>), g, t, 0, s, args);
+        else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false, false, true>), g, t, 0, s, args);
     } else {
-        if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true, false>), g, t, 0, s, args);
-        else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false, false>), g, t, 0, s, args);
+        if (args.partials) hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, true, false, false>), g, t, 0, s, args);
+        else hipLaunchKernelGGL((fused_adam_kernel<U, kTiled, kG32, false, false, false>), g, t, 0, s, args);
     }
 }
 
@@ -463,18 +473,21 @@ void launch_variant(const KernelArgs& args, dim3 g, hipStream_t s)
 int launch_fused_adam(const KernelArgs& args, int unroll, bool tiled, bool grad_f32, void* stream)
 {
     if (args.total_chunks == 0) return 0;
-    // one chunk per workgroup; a call too large for one grid loops
-    const uint64_t grid = args.total_chunks < kMaxGrid ? args.total_chunks : kMaxGrid;
+    // one chunk per workgroup; a call too large for one grid loops.  The
+    // stride travels as an ordinary argument: it then loads with the rest
+    // of the first round, where the grid size would be a second one.
+    KernelArgs a = args;
+    a.grid = args.total_chunks < kMaxGrid ? args.total_chunks : kMaxGrid;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 g(static_cast<unsigned>(grid));
+    const dim3 g(static_cast<unsigned>(a.grid));
     if (grad_f32) {
-        if (tiled) launch_variant<kUnrollTiled, true, true>(args, g, s);
-        else if (unroll == kUnrollLarge) launch_variant<kUnrollLarge, false, true>(args, g, s);
-        else launch_variant<kUnrollSmall, false, true>(args, g, s);
+        if (tiled) launch_variant<kUnrollTiled, true, true>(a, g, s);
+        else if (unroll == kUnrollLarge) launch_variant<kUnrollLarge, false, true>(a, g, s);
+        else launch_variant<kUnrollSmall, false, true>(a, g, s);
     } else {
-        if (tiled) launch_variant<kUnrollTiled, true, false>(args, g, s);
-        else if (unroll == kUnrollLarge) launch_variant<kUnrollLarge, false, false>(args, g, s);
-        else launch_variant<kUnrollSmall, false, false>(args, g, s);
+        if (tiled) launch_variant<kUnrollTiled, true, false>(a, g, s);
+        else if (unroll == kUnrollLarge) launch_variant<kUnrollLarge, false, false>(a, g, s);
+        else launch_variant<kUnrollSmall, false, false>(a, g, s);
     }
     return static_cast<int>(hipGetLastError());
 }

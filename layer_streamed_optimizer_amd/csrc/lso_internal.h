@@ -67,6 +67,7 @@ struct KernelArgs {
     const uint32_t* chunk_block;   // block index per chunk, or nullptr: search
     double* partials;              // norm variant: sum of g^2 per wave and chunk of this launch
     uint64_t total_chunks;
+    uint64_t grid;                 // workgroups of the launch (set by launch_fused_adam)
     uint32_t nblocks;
     uint32_t ngroups;              // constant sets in coef[] (table launches)
     Coef coef[kMaxGroups];         // by-value launches: coef[k] is inl[k]'s

@@ -19,6 +19,9 @@
 //  lso_probe_bf16_rne  the fused kernel's BF16 rounding applied to a range
 //                      of FP32 bit patterns, so a test can compare it with
 //                      the host definition over all 2^32 patterns.
+//  lso_probe_sqrt      the fused kernel's FP32 square root (__builtin_sqrtf
+//                      under the same build flags) over a range of bit
+//                      patterns, for an exhaustive check of its rounding.
 #include <hip/hip_runtime.h>
 
 #include <chrono>
@@ -268,6 +271,14 @@ bf16_probe_kernel(uint32_t first, uint64_t count, uint16_t* __restrict__ out)
     }
 }
 
+__global__ void __launch_bounds__(256)
+sqrt_probe_kernel(uint32_t first, uint64_t count, float* __restrict__ out)
+{
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride)
+        out[i] = __builtin_sqrtf(__uint_as_float(first + static_cast<uint32_t>(i)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -417,6 +428,18 @@ int lso_probe_bf16_rne(uint32_t first, uint64_t count, uint16_t* out, void* stre
     if (static_cast<uint64_t>(first) + count > (uint64_t(1) << 32) || !out)
         return static_cast<int>(hipErrorInvalidValue);
     hipLaunchKernelGGL(bf16_probe_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       first, count, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+// out[i] = FP32 square root of the pattern first + i, for i < count
+// (first + count <= 2^32).  Returns a hipError_t.
+int lso_probe_sqrt(uint32_t first, uint64_t count, float* out, void* stream)
+{
+    if (count == 0) return 0;
+    if (static_cast<uint64_t>(first) + count > (uint64_t(1) << 32) || !out)
+        return static_cast<int>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(sqrt_probe_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
                        first, count, out);
     return static_cast<int>(hipGetLastError());
 }

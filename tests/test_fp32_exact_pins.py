@@ -1,0 +1,143 @@
+"""Pins of the exact binary32 emulator (tests/fp32_exact.py) against
+independent IEEE implementations: numpy's float32 arithmetic and
+float64-to-float32 conversion (round to nearest even in hardware), torch's
+BF16 cast, and hand-worked ties, underflow and fused-versus-unfused cases."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import fp32_exact as fx
+
+
+def bits(x) -> int:
+    return int(np.float32(x).view(np.uint32))
+
+
+def same(a, b) -> bool:
+    return bits(a) == bits(b)
+
+
+def random_f32(rng, n, lo=-30, hi=30):
+    """Finite float32 values over a wide exponent range, both signs."""
+    mant = rng.uniform(1.0, 2.0, n)
+    exp = rng.integers(lo, hi, n)
+    sign = rng.choice([-1.0, 1.0], n)
+    return (sign * np.ldexp(mant, exp)).astype(np.float32)
+
+
+def test_round32_matches_hardware_conversion_from_float64():
+    rng = np.random.default_rng(1)
+    xs = np.concatenate([rng.normal(0, 1, 4000) * np.ldexp(1.0, rng.integers(-160, 120, 4000)),
+                         rng.uniform(-1, 1, 1000) * 2.0 ** -140,        # subnormal range
+                         rng.uniform(-1, 1, 200) * 2.0 ** 128])         # overflow range
+    with np.errstate(over="ignore"):
+        want = xs.astype(np.float32)
+    for x, w in zip(xs, want):
+        assert same(fx.round32(Fraction(float(x))), w), x
+
+
+@pytest.mark.parametrize("q,want", [
+    (Fraction(1) + Fraction(1, 2 ** 24), 1.0),                      # tie, even below
+    (Fraction(1) + Fraction(3, 2 ** 24), 1.0 + 2.0 ** -22),         # tie, even above
+    (-(Fraction(1) + Fraction(1, 2 ** 24)), -1.0),
+    (Fraction(1, 2 ** 150), 0.0),                                   # half the least subnormal: to 0
+    (Fraction(3, 2 ** 150), 2.0 ** -148),                           # tie between subnormals
+    (-Fraction(1, 2 ** 151), -0.0),                                 # underflow keeps the sign
+    (Fraction((1 << 24) - 1) * 2 ** 104 + Fraction(2 ** 103), float("inf")),   # max + half ulp
+    (Fraction((1 << 24) - 1) * 2 ** 104 + Fraction(2 ** 102), float(np.finfo(np.float32).max)),
+])
+def test_round32_ties_underflow_overflow(q, want):
+    assert same(fx.round32(q), np.float32(want))
+
+
+def test_add_mul_div_match_numpy_float32():
+    rng = np.random.default_rng(2)
+    a = random_f32(rng, 3000)
+    b = random_f32(rng, 3000)
+    with np.errstate(all="ignore"):
+        s, p, d = a + b, a * b, a / b
+    for i in range(a.size):
+        assert same(fx.add(a[i], b[i]), s[i])
+        assert same(fx.mul(a[i], b[i]), p[i])
+        assert same(fx.div(a[i], b[i]), d[i])
+    # cancellation and zero signs
+    assert same(fx.add(np.float32(1.5), np.float32(-1.5)), np.float32(0.0))
+    assert same(fx.add(np.float32(-0.0), np.float32(-0.0)), np.float32(-0.0))
+    assert same(fx.mul(np.float32(-0.0), np.float32(3.0)), np.float32(-0.0))
+
+
+def test_sqrt_matches_numpy_float32():
+    rng = np.random.default_rng(3)
+    xs = np.abs(random_f32(rng, 4000, -149, 127))
+    xs = np.concatenate([xs, np.array([0.0, 2.0 ** -149, 2.0 ** -126, 4.0, 2.0, 3.0,
+                                       float(np.finfo(np.float32).max)], np.float32)])
+    want = np.sqrt(xs)
+    for x, w in zip(xs, want):
+        assert same(fx.sqrt(x), w), x
+    assert same(fx.sqrt(np.float32(-0.0)), np.float32(-0.0))
+
+
+def test_fma_rounds_once():
+    # (1 + 2^-12)^2 - 1 = 2^-11 + 2^-24 exactly (representable); a separate
+    # product would first round 1 + 2^-11 + 2^-24 to 1 + 2^-11 (a tie to even)
+    a = np.float32(1.0 + 2.0 ** -12)
+    assert same(fx.fma(a, a, np.float32(-1.0)), np.float32(2.0 ** -11 + 2.0 ** -24))
+    assert same(fx.add(fx.mul(a, a), np.float32(-1.0)), np.float32(2.0 ** -11))
+    # reductions to the single operations
+    rng = np.random.default_rng(4)
+    x, y, z = random_f32(rng, 500), random_f32(rng, 500), random_f32(rng, 500)
+    for i in range(500):
+        assert same(fx.fma(x[i], y[i], np.float32(0.0)), fx.mul(x[i], y[i])) or fx.mul(x[i], y[i]) == 0
+        assert same(fx.fma(x[i], np.float32(1.0), z[i]), fx.add(x[i], z[i]))
+    # zero signs: (+0)(-1) + (-0) = -0; 1*1 + (-1) = +0
+    assert same(fx.fma(np.float32(0.0), np.float32(-1.0), np.float32(-0.0)), np.float32(-0.0))
+    assert same(fx.fma(np.float32(1.0), np.float32(1.0), np.float32(-1.0)), np.float32(0.0))
+
+
+def test_bf16_rne_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([random_f32(rng, 5000, -130, 127),
+                         np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),
+                                   float(np.finfo(np.float32).max)], np.float32)])
+    want = torch.from_numpy(xs).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    for x, w in zip(xs, want):
+        assert fx.bf16_rne_bits(x) == int(w), x
+
+
+def test_adam_binary32_agrees_with_the_fp64_oracle():
+    """The binary32 sequence the kernel follows stays within the parity
+    tolerance of the FP64 definition (1e-6 of each quantity's RMS, BF16
+    weights within one spacing or that bound), three steps in a row: a
+    dropped term, a wrong sign or a misplaced constant in the emulation
+    would not."""
+    oracle = pytest.importorskip("oracle")
+    import synth
+    n = 3000
+    rng_master = synth.normal_f32(n, stream=96, block=0, purpose=synth.PURPOSE_MASTER, step=0, sigma=0.02)
+    rng_master[::2] = 0.0
+    emu = [rng_master.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    ref = [rng_master.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    w_ref = np.zeros(n, np.uint16)
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    for t in range(1, 4):
+        g = synth.normal_bf16(n, stream=96, block=0, purpose=synth.PURPOSE_GRAD, step=t, sigma=1e-3)
+        p, m, v, w = fx.adam_binary32(*emu, g, fx.adam_constants(t, lr, b1, b2, eps))
+        emu = [p, m, v]
+        oracle.adam_step(ref[0], ref[1], ref[2], g, w_ref, t, lr, b1, b2, eps)
+        for got, want in zip(emu, ref):
+            floor = float(np.sqrt(np.mean(want.astype(np.float64) ** 2)))
+            err = np.abs(got.astype(np.float64) - want) / np.maximum(np.abs(want.astype(np.float64)), floor)
+            assert float(err.max()) <= 1e-6
+        # weights: one BF16 spacing, or the FP32 bound where the master is
+        # near 0 (as the GPU parity tests judge them)
+        wv = fx_bf16(w).astype(np.float64)
+        rv = fx_bf16(w_ref).astype(np.float64)
+        spacing = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(rv), 2.0 ** -126))) - 7)
+        bound = np.maximum(spacing, 1e-6 * float(np.sqrt(np.mean(ref[0].astype(np.float64) ** 2))))
+        assert np.all(np.abs(wv - rv) <= bound)
+
+
+def fx_bf16(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)

@@ -420,6 +420,29 @@ def test_bf16_cast_exhaustive_all_fp32_patterns():
         assert bad.size == 0, f"segment {s}: {bad.size} mismatches, first {hex(int(bits[bad[0]]))}"
 
 
+def test_sqrt_exhaustive_all_positive_fp32():
+    """The kernel's FP32 square root (the same expression and build flags,
+    through the probe library) is correctly rounded for every positive
+    finite FP32 pattern and +inf: equal bit for bit to numpy's IEEE float32
+    root."""
+    T = torch()
+    from layer_streamed_optimizer_amd import _native
+    P = _native.probes()
+    end = 0x7F800001                     # up to and including +inf
+    seg = 1 << 27
+    out = T.empty(seg, dtype=T.float32, device="cuda")
+    for first in range(0, end, seg):
+        n = min(seg, end - first)
+        log("sqrt exhaustive from", hex(first))
+        rc = P.lso_probe_sqrt(first, n, out.data_ptr(), T.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        got = out[:n].cpu().numpy().view(np.uint32)
+        x = np.arange(first, first + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        want = np.sqrt(x).view(np.uint32)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"{bad.size} mismatches from {hex(first)}, first input {hex(first + int(bad[0]))}"
+
+
 # ------------------------------------------------------------- tiled layout
 
 def test_tiled_ragged_sizes_match_oracle():
