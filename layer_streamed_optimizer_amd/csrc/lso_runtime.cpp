@@ -392,7 +392,12 @@ lso_status device_table(const lso_block* blocks, size_t n, bool geometry_checked
     if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipMemcpyAsync (block table)"); }
     err = hipEventRecord(e.ready, static_cast<hipStream_t>(stream));
     if (err == hipSuccess) err = hipEventRecord(dt.staging_read, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) { free_entry(e); return hip_fail(err, "hipEventRecord"); }
+    if (err != hipSuccess) {
+        // the copy is queued: let it finish before its buffers go
+        (void)hipStreamSynchronize(static_cast<hipStream_t>(stream));
+        free_entry(e);
+        return hip_fail(err, "hipEventRecord");
+    }
     dt.staging_busy = true;
     dt.bytes += bytes;
     args.blocks = static_cast<const DevBlock*>(e.dev);

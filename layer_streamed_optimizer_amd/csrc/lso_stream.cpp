@@ -221,6 +221,7 @@ void release(lso_stream_ctx* c)
         if (s) (void)hipStreamSynchronize(s);
     // every copy and update has ended; their handlers may still be running
     for (int k = 0; k < 200000 && c->callbacks.load() > 0; ++k) std::this_thread::sleep_for(std::chrono::microseconds(50));
+    const bool handlers_pending = c->callbacks.load() > 0;
     delete c->reader;   // joins its threads; no request is in flight between calls
     delete c->writer;
     if (c->dev_norms) (void)hipFree(c->dev_norms);
@@ -241,6 +242,15 @@ void release(lso_stream_ctx* c)
     }
     for (hipStream_t s : {c->h2d, c->compute, c->d2h})
         if (s) (void)hipStreamDestroy(s);
+    if (handlers_pending) {
+        // a copy engine never signalled the end of a watched copy in 10 s:
+        // its handler still holds the context and the signal, so both stay
+        // (a leak, not a use after free)
+        std::fprintf(stderr, "lso_stream_destroy: %d completion handler(s) never ran; keeping the context\n",
+                     c->callbacks.load());
+        (void)hipSetDevice(prev);
+        return;
+    }
     for (int s = 0; s < kMaxSlots; ++s)
         if (c->h2d_sig[s].handle) (void)hsa_signal_destroy(c->h2d_sig[s]);
     for (int s = 0; s < kMaxRing; ++s)
