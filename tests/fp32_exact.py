@@ -142,12 +142,15 @@ def adam_binary32(master, m, v, g_bits, c):
     """One Adam step of every element as the kernel orders it in binary32:
     m' = fma(b1, m, (1-b1) g); v' = fma(b2, v, (1-b2)(g g));
     den = fma(sqrt(v'), r, eps); master' = master + -((s m') / den); the
-    BF16 weight is master' rounded to nearest even.  Returns new arrays."""
+    BF16 weight is master' rounded to nearest even.  g_bits: BF16 patterns
+    (uint16) or FP32 gradients (float32; then g*g rounds).  Returns new
+    arrays."""
     b1, c1, b2, c2, s, r, e = (np.float32(x) for x in c[:7])
     out_p, out_m, out_v = master.copy(), m.copy(), v.copy()
     out_w = np.zeros(master.size, np.uint16)
+    f32_grads = np.asarray(g_bits).dtype == np.float32
     for i in range(master.size):
-        g = bf16_to_f32(g_bits[i])
+        g = np.float32(g_bits[i]) if f32_grads else bf16_to_f32(g_bits[i])
         m1 = fma(b1, m[i], mul(c1, g))
         v1 = fma(b2, v[i], mul(c2, mul(g, g)))
         den = fma(sqrt(v1), r, e)

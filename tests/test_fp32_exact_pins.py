@@ -106,7 +106,8 @@ def test_bf16_rne_matches_torch_cast():
         assert fx.bf16_rne_bits(x) == int(w), x
 
 
-def test_adam_binary32_agrees_with_the_fp64_oracle():
+@pytest.mark.parametrize("f32_grads", [False, True], ids=["bf16_grads", "f32_grads"])
+def test_adam_binary32_agrees_with_the_fp64_oracle(f32_grads):
     """The binary32 sequence the kernel follows stays within the parity
     tolerance of the FP64 definition (1e-6 of each quantity's RMS, BF16
     weights within one spacing or that bound), three steps in a row: a
@@ -122,7 +123,8 @@ def test_adam_binary32_agrees_with_the_fp64_oracle():
     w_ref = np.zeros(n, np.uint16)
     lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
     for t in range(1, 4):
-        g = synth.normal_bf16(n, stream=96, block=0, purpose=synth.PURPOSE_GRAD, step=t, sigma=1e-3)
+        draw = synth.normal_f32 if f32_grads else synth.normal_bf16
+        g = draw(n, stream=96, block=0, purpose=synth.PURPOSE_GRAD, step=t, sigma=1e-3)
         p, m, v, w = fx.adam_binary32(*emu, g, fx.adam_constants(t, lr, b1, b2, eps))
         emu = [p, m, v]
         oracle.adam_step(ref[0], ref[1], ref[2], g, w_ref, t, lr, b1, b2, eps)

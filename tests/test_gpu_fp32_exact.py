@@ -9,7 +9,8 @@ lso_block_constants).  tests/fp32_exact.py carries out the same sequence in
 exact rational arithmetic rounded once per operation, so every output bit
 is fixed: this test compares master, m, v and the BF16 weight exactly,
 three steps in a row, for planar and tiled state, blocks passed by value
-(one block, and a few) and through a device table.  Half of the masters
+(one block, and a few) and through a device table, with BF16 and with FP32
+gradients.  Half of the masters
 start at 0, so the first step writes each element's step itself (any
 rounding difference in the root or the division shows in those bits).
 
@@ -31,12 +32,14 @@ STREAM = 95
 STEPS = 3
 
 CASES = [
-    # sizes, tiled, (lr, beta1, beta2, eps)
-    ([3001], False, (1e-3, 0.9, 0.999, 1e-8)),                       # one block by value
-    ([5, 1029, 2000], False, (1e-3, 0.9, 0.999, 1e-8)),              # a few by value
-    ([1, 7, 1024, 1500, 33, 2049], False, (2e-3, 0.8, 0.99, 1e-3)),  # device table, large eps
-    ([8195], True, (1e-3, 0.9, 0.999, 1e-8)),                        # tiled, one block
-    ([5, 1030, 8192, 300, 17], True, (1e-3, 0.9, 0.95, 1e-6)),       # tiled, device table
+    # sizes, tiled, FP32 gradients, (lr, beta1, beta2, eps)
+    ([3001], False, False, (1e-3, 0.9, 0.999, 1e-8)),                       # one block by value
+    ([5, 1029, 2000], False, False, (1e-3, 0.9, 0.999, 1e-8)),              # a few by value
+    ([1, 7, 1024, 1500, 33, 2049], False, False, (2e-3, 0.8, 0.99, 1e-3)),  # device table, large eps
+    ([8195], True, False, (1e-3, 0.9, 0.999, 1e-8)),                        # tiled, one block
+    ([5, 1030, 8192, 300, 17], True, False, (1e-3, 0.9, 0.95, 1e-6)),       # tiled, device table
+    ([2500, 9, 700], False, True, (1e-3, 0.9, 0.999, 1e-8)),                # FP32 gradients, by value
+    ([8200, 5, 1030, 64, 300], True, True, (1e-3, 0.9, 0.999, 1e-8)),       # FP32 gradients, tiled table
 ]
 
 
@@ -55,13 +58,14 @@ def first_diff(got, want):
     return idx.size, (int(idx[0]), hex(int(gb[idx[0]])), hex(int(wb[idx[0]]))) if idx.size else None
 
 
-@pytest.mark.parametrize("sizes,tiled,hyper", CASES,
-                         ids=["one_block", "by_value", "table", "tiled_one_block", "tiled_table"])
-def test_update_bit_exact_against_binary32_emulation(sizes, tiled, hyper):
+@pytest.mark.parametrize("sizes,tiled,f32,hyper", CASES,
+                         ids=["one_block", "by_value", "table", "tiled_one_block", "tiled_table",
+                              "f32_grads_by_value", "f32_grads_tiled_table"])
+def test_update_bit_exact_against_binary32_emulation(sizes, tiled, f32, hyper):
     lr, b1, b2, eps = hyper
-    log("fp32 exact", f"sizes={sizes} tiled={tiled} hyper={hyper}")
+    log("fp32 exact", f"sizes={sizes} tiled={tiled} f32_grads={f32} hyper={hyper}")
     T = torch()
-    arena = Arena(sizes, tiled=tiled)
+    arena = Arena(sizes, tiled=tiled, grad_f32=f32)
     state = []
     for i, n in enumerate(sizes):
         master = synth.normal_f32(n, stream=STREAM, block=i, purpose=synth.PURPOSE_MASTER, step=0, sigma=0.02)
@@ -76,7 +80,8 @@ def test_update_bit_exact_against_binary32_emulation(sizes, tiled, hyper):
     table = arena.table(lr=lr, beta1=b1, beta2=b2, eps=eps)
     for t in range(1, STEPS + 1):
         c = constants(t, lr, b1, b2, eps)
-        gs = [synth.normal_bf16(n, stream=STREAM, block=i, purpose=synth.PURPOSE_GRAD, step=t, sigma=1e-3)
+        draw = synth.normal_f32 if f32 else synth.normal_bf16
+        gs = [draw(n, stream=STREAM, block=i, purpose=synth.PURPOSE_GRAD, step=t, sigma=1e-3)
               for i, n in enumerate(sizes)]
         for i, g in enumerate(gs):
             arena.put(i, "grad", g)
