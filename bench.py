@@ -167,23 +167,25 @@ def resident(args, w):
     tiled = args.layout == "tiled"
     g32 = args.grad_dtype == "f32"
     bpp = BYTES_PER_PARAM[args.grad_dtype]
-    lay = configs.ResidentLayout(sizes, tiled=tiled, grad_f32=g32)
+    one = configs.BlockArena(sizes, tiled=tiled, grad_f32=g32)
     params = w.params
     total_steps = args.warmup + args.steps
     free, _total = torch.cuda.mem_get_info()
-    budget = free - lay.state_bytes - lay.weight_bytes - (8 << 30)
-    n_sets = max(1, min(total_steps, budget // max(lay.grad_bytes, 1)))
+    scratch_bytes = 4 * max(sizes) if tiled else 0
+    budget = free - one.state_bytes - one.weight_bytes - scratch_bytes - (8 << 30)
+    n_sets = max(1, min(total_steps, budget // max(one.grad_bytes, 1)))
     if args.grad_sets:
         n_sets = max(1, min(n_sets, args.grad_sets))
+    # one arena, block after block [state | weights | gradient sets]: the
+    # arrays a block's update streams together sit next to each other
+    lay = configs.BlockArena(sizes, tiled=tiled, grad_f32=g32, grad_sets=n_sets)
     progress(f"{w.key}: {len(sizes)} blocks, {params:,} params, {args.layout} state "
              f"{lay.state_bytes / 1e9:.1f} GB, {n_sets} {args.grad_dtype} gradient sets of "
-             f"{lay.grad_bytes / 1e9:.2f} GB")
+             f"{lay.grad_bytes / 1e9:.2f} GB, one arena of {lay.total_bytes / 1e9:.1f} GB")
     stream = torch.cuda.current_stream()
     hs = int(stream.cuda_stream)
-    state = torch.empty(lay.state_bytes, dtype=torch.uint8, device=dev)
-    weight = torch.empty(lay.weight_bytes, dtype=torch.uint8, device=dev)
-    grads = [torch.empty(lay.grad_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
-    sb, wb = int(state.data_ptr()), int(weight.data_ptr())
+    arena = torch.empty(lay.total_bytes, dtype=torch.uint8, device=dev)
+    sb = wb = int(arena.data_ptr())
     scratch = torch.empty(max(sizes), dtype=torch.float32, device=dev) if tiled else None
 
     def fill_master(dst, b, spec):
@@ -210,17 +212,16 @@ def resident(args, w):
                 synth.device_fill_zero(sb + lay.off_v[b], 4 * spec.n, hs)
 
     init_state()
+    gb = int(arena.data_ptr())
     for r in range(n_sets):
-        gb = int(grads[r].data_ptr())
         fill = synth.device_fill_normal_f32 if g32 else synth.device_fill_normal_bf16
         for b, n in enumerate(sizes):
-            fill(gb + lay.off_grad[b], n, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=r + 1,
+            fill(gb + lay.off_grad[r][b], n, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=r + 1,
                  sigma=configs.GRAD_SIGMA, hip_stream=hs)
     tables = []
     for r in range(n_sets):
-        gb = int(grads[r].data_ptr())
         rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
-                     grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], t=1,
+                     grad=gb + lay.off_grad[r][b], weight=wb + lay.off_weight[b], t=1,
                      lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2, eps=configs.EPS,
                      layout=lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR,
                      grad_dtype=lso.LSO_DT_F32 if g32 else lso.LSO_DT_BF16)
@@ -356,8 +357,8 @@ def resident(args, w):
                        note="512 MB written between steps; the main figures are cache-resident")
         del scratch_mall
     ev.close()
-    # the copy ceiling needs 16 GB: the gradient sets go first
-    grads.clear()
+    # the copy ceiling needs 16 GB: the arena goes first
+    del arena
     torch.cuda.empty_cache()
     ceiling = copy_ceiling(torch, dev)
     shaped = shaped_ceiling(torch, dev, tiled)
@@ -380,6 +381,7 @@ def resident(args, w):
                     state_layout=args.layout, grad_dtype=args.grad_dtype, bytes_per_param=bpp,
                     gradient_norms=bool(args.norms),
                     gradient_sets=n_sets,
+                    arena="one device arena, block after block [state | BF16 weights | gradient sets]",
                     hyper=dict(lr=configs.LR, beta1=configs.BETA1, beta2=configs.BETA2,
                                eps=configs.EPS)),
     )
@@ -389,7 +391,7 @@ def resident(args, w):
         result["cache_flushed"] = flushed
     if graph_rec:
         result["graph_replay"] = graph_rec
-    del state, weight, grads, scratch
+    del scratch
     return result
 
 
@@ -1009,11 +1011,15 @@ def cpu_baseline(w, budget_s=12.0):
 def placement_scan(positions: int = 12, reps: int = 4) -> dict:
     """The c3 update's rate against where its arrays sit in HBM: one pool of
     all free memory but 8 GiB, the whole working set (tiled state, weights,
-    one gradient set, laid out as in the resident bench) placed at
-    `positions` offsets spread over it, and at each the update, its traffic
-    shape with no arithmetic (lso_probe_copy_shaped_cpol, the update's
-    stores) and a plain 8 GiB copy inside the state region, each the average
-    of `reps` launches after one."""
+    one gradient set: 107.8 GB) placed at `positions` offsets spread over it.
+    At each offset, two arrangements of the same arrays: three regions (every
+    block's state, then every block's weights, then every block's gradients)
+    and one arena, block after block [state | weights | gradients] (the
+    resident bench's BlockArena, so the arrays streamed together are
+    adjacent); then the update's traffic shape with no arithmetic
+    (lso_probe_copy_shaped_cpol, the update's stores) over the regions and a
+    plain 8 GiB copy inside the state region.  Each figure is the average of
+    `reps` launches after one."""
     import torch
 
     import layer_streamed_optimizer_amd as lso
@@ -1031,9 +1037,15 @@ def placement_scan(positions: int = 12, reps: int = 4) -> dict:
     def up(x):
         return (x + m2 - 1) // m2 * m2
 
+    # three regions
     off_w = up(lay.state_bytes)
     off_g = off_w + up(lay.weight_bytes)
     span_bytes = off_g + up(lay.grad_bytes)
+    regions = [(lay.off_master[b], off_g + lay.off_grad[b], off_w + lay.off_weight[b]) for b in range(len(sizes))]
+    # one arena, block after block (the resident bench's arrangement)
+    one = configs.BlockArena(sizes, tiled=True)
+    per_block = [(one.off_master[b], one.off_grad[0][b], one.off_weight[b]) for b in range(len(sizes))]
+    assert one.total_bytes <= span_bytes
     n_shaped = w.params // 8192 * 8192
     copy_bytes = 8 << 30
     free, _ = torch.cuda.mem_get_info()
@@ -1058,39 +1070,48 @@ def placement_scan(positions: int = 12, reps: int = 4) -> dict:
         if rc != 0:
             raise RuntimeError(f"{what} failed ({rc})")
 
-    rows, step = [], [0]
-    for k in range(positions):
-        off = (total - span_bytes) * k // max(1, positions - 1) // m2 * m2
-        sb, wb, gb = base + off, base + off + off_w, base + off + off_g
+    step = [0]
+
+    def update_ms(origin, arrangement):
         for b, spec in enumerate(w.blocks):
+            so, go, _ = arrangement[b]
             synth.device_fill_normal_f32(int(scratch.data_ptr()), spec.n, stream=sid, block=b,
                                          purpose=synth.PURPOSE_MASTER, step=0, sigma=configs.MASTER_SIGMA,
                                          hip_stream=hs)
-            lso.tiled_pack(sb + lay.off_master[b], int(scratch.data_ptr()), None, None, n=spec.n, stream=hs)
-            synth.device_fill_normal_bf16(gb + lay.off_grad[b], spec.n, stream=sid, block=b,
-                                          purpose=synth.PURPOSE_GRAD, step=1, sigma=configs.GRAD_SIGMA,
-                                          hip_stream=hs)
+            lso.tiled_pack(origin + so, int(scratch.data_ptr()), None, None, n=spec.n, stream=hs)
+            synth.device_fill_normal_bf16(origin + go, spec.n, stream=sid, block=b, purpose=synth.PURPOSE_GRAD,
+                                          step=1, sigma=configs.GRAD_SIGMA, hip_stream=hs)
         tab = lso.BlockTable.from_rows(
-            dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
-                 grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], t=1, lr=configs.LR,
-                 beta1=configs.BETA1, beta2=configs.BETA2, eps=configs.EPS, layout=lso.LSO_LAYOUT_TILED,
-                 grad_dtype=lso.LSO_DT_BF16) for b, n in enumerate(sizes))
+            dict(n=n, master=origin + arrangement[b][0], grad=origin + arrangement[b][1],
+                 weight=origin + arrangement[b][2], t=1, lr=configs.LR, beta1=configs.BETA1,
+                 beta2=configs.BETA2, eps=configs.EPS, layout=lso.LSO_LAYOUT_TILED, grad_dtype=lso.LSO_DT_BF16)
+            for b, n in enumerate(sizes))
 
         def update():
             step[0] += 1
             tab.set_step(step[0])
             lso.adam_step(tab, hs)
 
-        t_update = timed(update)
+        return timed(update)
+
+    rows = []
+    for k in range(positions):
+        off = (total - span_bytes) * k // max(1, positions - 1) // m2 * m2
+        origin = base + off
+        t_regions = update_ms(origin, regions)
+        t_arena = update_ms(origin, per_block)
+        sb, wb, gb = origin, origin + off_w, origin + off_g
         t_copy = timed(lambda: check(P.lso_probe_copy(sb, sb + copy_bytes, copy_bytes, 0, hs), "copy"))
-        # last: it overwrites the state with mixed bits
         t_shaped = timed(lambda: check(P.lso_probe_copy_shaped_cpol(sb, gb, wb, n_shaped, 3, hs), "shaped copy"))
-        row = dict(offset_GB=off / 1e9, update_ms=t_update, update_GBps=28 * w.params / (t_update * 1e-3) / 1e9,
+        row = dict(offset_GB=off / 1e9, regions_ms=t_regions, regions_GBps=28 * w.params / (t_regions * 1e-3) / 1e9,
+                   block_arena_ms=t_arena,
+                   block_arena_GBps=28 * w.params / (t_arena * 1e-3) / 1e9,
                    shaped_GBps=28 * n_shaped / (t_shaped * 1e-3) / 1e9,
                    copy_GBps=2 * copy_bytes / (t_copy * 1e-3) / 1e9)
         rows.append(row)
-        progress(f"placement +{row['offset_GB']:.1f} GB: update {t_update:.3f} ms ({row['update_GBps']:.0f} GB/s), "
-                 f"shaped copy {row['shaped_GBps']:.0f} GB/s, plain copy {row['copy_GBps']:.0f} GB/s")
+        progress(f"placement +{row['offset_GB']:.1f} GB: three regions {t_regions:.3f} ms "
+                 f"({row['regions_GBps']:.0f} GB/s), block arena {t_arena:.3f} ms, shaped copy {row['shaped_GBps']:.0f} GB/s, "
+                 f"plain copy {row['copy_GBps']:.0f} GB/s")
     del pool, scratch
     return dict(placement_scan=rows, pool_GB=total / 1e9, working_set_GB=span_bytes / 1e9, reps=reps)
 

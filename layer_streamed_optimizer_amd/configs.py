@@ -179,6 +179,64 @@ class ResidentLayout:
         self.state_bytes, self.grad_bytes, self.weight_bytes = s, g, w
 
 
+@dataclass
+class BlockArena:
+    """Byte offsets of every array in one device arena, block after block:
+    [state | BF16 weights | gradient set 0 | ... | gradient set k-1], each
+    array 4 KB aligned (state as in ResidentLayout: tiled, or planar
+    [master | m | v]).
+
+    The arrays one block's update streams together sit next to each other.
+    Measured on MI355X (c3, LLaMA-7B), the update then runs at the same rate
+    wherever the arena lands in HBM (28.78-28.85 ms at 12 placements), where
+    three separate regions (all states, all weights, all gradients) run at
+    28.37-29.22 ms depending on placement.
+    """
+    sizes: list[int]
+    tiled: bool = False
+    grad_f32: bool = False
+    grad_sets: int = 1
+    off_master: list[int] = field(default_factory=list)
+    off_m: list[int] = field(default_factory=list)
+    off_v: list[int] = field(default_factory=list)
+    off_weight: list[int] = field(default_factory=list)
+    off_grad: list[list[int]] = field(default_factory=list)   # [set][block]
+    total_bytes: int = 0
+    state_bytes: int = 0     # sums over blocks (what each kind of array takes)
+    grad_bytes: int = 0      # one gradient set
+    weight_bytes: int = 0
+
+    def __post_init__(self):
+        if self.grad_sets < 1:
+            raise ValueError("grad_sets must be >= 1")
+        self.off_grad = [[] for _ in range(self.grad_sets)]
+        pos = 0
+        for n in self.sizes:
+            if self.tiled:
+                st = align(tiled_state_bytes(n))
+                self.off_master.append(pos)
+                self.off_m.append(pos)
+                self.off_v.append(pos)
+            else:
+                a = align(4 * n)
+                st = 3 * a
+                self.off_master.append(pos)
+                self.off_m.append(pos + a)
+                self.off_v.append(pos + 2 * a)
+            pos += st
+            self.state_bytes += st
+            wb = align(2 * n)
+            self.off_weight.append(pos)
+            pos += wb
+            self.weight_bytes += wb
+            gb = align((4 if self.grad_f32 else 2) * n)
+            for r in range(self.grad_sets):
+                self.off_grad[r].append(pos)
+                pos += gb
+            self.grad_bytes += gb
+        self.total_bytes = pos
+
+
 def host_layer_layout(n: int, tiled: bool = False) -> tuple[int, int, int, int]:
     """(off_master, off_m, off_v, bytes) of one streamed host block:
     [master | m | v] with 4 KB-aligned sub-arrays, or one tiled region."""

@@ -57,13 +57,12 @@ def run_resident_sampled(key, steps, tiled=True):
     w = configs.get(key)
     sid = configs.STREAM_ID[key]
     sizes = [b.n for b in w.blocks]
-    lay = configs.ResidentLayout(sizes, tiled=tiled)
+    lay = configs.BlockArena(sizes, tiled=tiled)   # the bench's arrangement
     log(f"{key}: {w.params:,} params, {len(sizes)} blocks, {steps} steps, tiled={tiled}")
     hs = T.cuda.current_stream().cuda_stream
-    state = T.empty(lay.state_bytes, dtype=T.uint8, device="cuda")
-    grad = T.empty(lay.grad_bytes, dtype=T.uint8, device="cuda")
-    weight = T.empty(lay.weight_bytes, dtype=T.uint8, device="cuda")
-    sb, gb, wb = int(state.data_ptr()), int(grad.data_ptr()), int(weight.data_ptr())
+    arena = T.empty(lay.total_bytes, dtype=T.uint8, device="cuda")
+    state = grad = weight = arena
+    sb = gb = wb = int(arena.data_ptr())
     scratch = T.empty(max(sizes), dtype=T.float32, device="cuda")
     for b, spec in enumerate(w.blocks):
         kind = init_kind(spec)
@@ -82,12 +81,12 @@ def run_resident_sampled(key, steps, tiled=True):
     del scratch
     layout = lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR
     rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
-                 grad=gb + lay.off_grad[b], weight=wb + lay.off_weight[b], layout=layout)
+                 grad=gb + lay.off_grad[0][b], weight=wb + lay.off_weight[b], layout=layout)
             for b, n in enumerate(sizes)]
     table = lso.BlockTable.from_rows(rows)
     for t in range(1, steps + 1):
         for b, n in enumerate(sizes):
-            synth.device_fill_normal_bf16(gb + lay.off_grad[b], n, stream=sid, block=b,
+            synth.device_fill_normal_bf16(gb + lay.off_grad[0][b], n, stream=sid, block=b,
                                           purpose=synth.PURPOSE_GRAD, step=t,
                                           sigma=configs.GRAD_SIGMA, hip_stream=hs)
         table.set_step(t)
@@ -128,7 +127,7 @@ def run_resident_sampled(key, steps, tiled=True):
     for ref, got, (b, off) in zip(refs, gots, where):
         worst.add(f"block {b} offset {off}", assert_parity(got, ref, 1e-6, f"{key} block {b} offset {off}"))
     log(f"{key} sampled worst errors after {steps} steps: {worst}")
-    del state, grad, weight
+    del state, grad, weight, arena
     T.cuda.empty_cache()
 
 

@@ -308,6 +308,36 @@ def test_resident_layout_is_page_aligned_and_disjoint():
     assert off[3] == 3 * configs.align(4 * 855_654_400) and off[3] % 4096 == 0
 
 
+@pytest.mark.parametrize("tiled", [False, True])
+def test_block_arena_is_page_aligned_disjoint_and_block_by_block(tiled):
+    sizes = [1000, 4096, 3, 65537, 8193]
+    a = configs.BlockArena(sizes, tiled=tiled, grad_sets=3)
+    spans = []
+    for b, n in enumerate(sizes):
+        st = configs.tiled_state_bytes(n) if tiled else 4 * n
+        if tiled:
+            assert a.off_m[b] == a.off_v[b] == a.off_master[b]
+            spans.append((a.off_master[b], st))
+        else:
+            spans += [(a.off_master[b], st), (a.off_m[b], st), (a.off_v[b], st)]
+        spans.append((a.off_weight[b], 2 * n))
+        spans += [(a.off_grad[r][b], 2 * n) for r in range(3)]
+        # a block's arrays lie between its state and the next block's state
+        nxt = a.off_master[b + 1] if b + 1 < len(sizes) else a.total_bytes
+        assert a.off_master[b] < a.off_weight[b] < a.off_grad[0][b] < a.off_grad[2][b] < nxt
+    for o, _ in spans:
+        assert o % configs.PAGE == 0
+    spans.sort()
+    for (x, lx), (y, _) in zip(spans, spans[1:]):
+        assert x + lx <= y
+    assert spans[-1][0] + spans[-1][1] <= a.total_bytes
+    one = configs.ResidentLayout(sizes, tiled=tiled)
+    assert (a.state_bytes, a.grad_bytes, a.weight_bytes) == (one.state_bytes, one.grad_bytes, one.weight_bytes)
+    assert a.total_bytes == a.state_bytes + a.weight_bytes + 3 * a.grad_bytes
+    with pytest.raises(ValueError):
+        configs.BlockArena(sizes, grad_sets=0)
+
+
 def test_tiled_state_region_validation():
     n = 3 * 8192 + 5
     rb = lso.tiled_state_bytes(n)
