@@ -190,7 +190,10 @@ class BlockArena:
     Measured on MI355X (c3, LLaMA-7B), the update then runs at the same rate
     wherever the arena lands in HBM (28.78-28.85 ms at 12 placements), where
     three separate regions (all states, all weights, all gradients) run at
-    28.37-29.22 ms depending on placement.
+    28.37-29.22 ms depending on placement.  It is for calls that stream HBM:
+    a cache-sized call (c2, 308 small tensors) spread over per-block groups
+    touches ten times the pages and ran slower (34.0 against 30.1 us) than
+    in compact regions (ResidentLayout).
     """
     sizes: list[int]
     tiled: bool = False
