@@ -150,6 +150,11 @@ typedef struct lso_block {
  * blocks: host array, read before return; the caller may reuse it at once.
  * Arrays: device memory owned by the caller; they must stay untouched until
  * stream passes the step.  Asynchronous: returns after enqueueing.
+ * Layout advice for calls that stream HBM (gigabytes per step): keep each
+ * block's state, gradients and weights next to each other (one arena, block
+ * after block).  Measured on MI355X, the update's rate then does not depend
+ * on where the arena lands; with all states, all gradients and all weights
+ * in three distant regions it varies by up to 3% with the placement.
  * n == 0 is a no-op.  Errors: INVALID, ALIGN, DTYPE, OVERLAP (nothing
  * enqueued), NOMEM, HIP.
  */
