@@ -1185,8 +1185,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the update is elementwise and would shard by "
-              "contiguous 1/N ranges with no exchange inside the step; multi-GPU runs are not "
-              "part of this build.", file=sys.stderr)
+              "contiguous 1/N ranges with no exchange inside the step; the library has no "
+              "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.link_probe:
         import torch
