@@ -70,7 +70,7 @@ __device__ __forceinline__ void st_nt(void* p, T v)
 
 // Stores of a tiled chunk carry the cache-policy bits nt (streaming) and
 // sc1 (device scope).  Measured on this part, alternating libraries on one
-// box: c3 (LLaMA-7B, tiled) 28.75 ms against 29.71 ms with nt alone over
+// machine: c3 (LLaMA-7B, tiled) 28.75 ms against 29.71 ms with nt alone over
 // six runs each, c1 tiled 4.75 against 4.87 ms; planar chunks (four quads
 // per lane) were 3% slower with them, so they keep plain nt stores.  No
 // compiler builtin sets sc1 on a global store, hence the inline assembly.

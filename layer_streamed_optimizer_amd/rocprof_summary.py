@@ -17,6 +17,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 import sys
 
@@ -24,11 +25,28 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("lso_adam.hip", "lso_internal.h", "lso_bf16.h")
 
 
-def kernel_hash() -> str:
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_of(text: str) -> str:
+    """Source text without comments, whitespace collapsed: what the
+    compiler sees of it."""
+    return " ".join(_COMMENTS.sub(" ", text).split())
+
+
+def kernel_hash(read=None) -> str:
+    """Hash of the update kernel's code (its sources without comments, and
+    the build flags): a profile taken with another hash measured another
+    kernel.  read(name) returns a source's text (default: the file here)."""
+    from . import build
+    if read is None:
+        def read(name):
+            with open(os.path.join(HERE, "csrc", name), encoding="utf-8") as f:
+                return f.read()
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(HERE, "csrc", name), "rb") as f:
-            h.update(f.read())
+        h.update(code_of(read(name)).encode())
+    h.update(" ".join(build.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
