@@ -159,3 +159,61 @@ def adam_binary32(master, m, v, g_bits, c):
         out_p[i], out_m[i], out_v[i] = p, m1, v1
         out_w[i] = bf16_rne_bits(p)
     return out_p, out_m, out_v, out_w
+
+
+# ------------------------------------------------- vectorised, for large samples
+#
+# numpy's float32 add, multiply, divide and sqrt are the IEEE binary32
+# operations (one rounding, to nearest even).  Only the FMA needs work: the
+# product of two binary32 values is exact in binary64, and TwoSum gives the
+# exact sum as s + e; s rounded to binary32 is the correct result except when
+# s lies exactly half-way between two binary32 values and e != 0, where the
+# sign of e decides.  Pinned against the rational functions above.
+
+def _two_sum(a, b):
+    s = a + b
+    bb = s - a
+    return s, (a - (s - bb)) + (b - bb)
+
+
+def fma_v(a, b, c):
+    """Correctly rounded a*b + c for binary32 arrays."""
+    a64, b64, c64 = (np.asarray(x, np.float32).astype(np.float64) for x in (a, b, c))
+    s, e = _two_sum(a64 * b64, c64)
+    with np.errstate(over="ignore"):
+        r = s.astype(np.float32)
+        r64 = r.astype(np.float64)
+        other = np.nextafter(r, np.where(s > r64, np.float32(np.inf), np.float32(-np.inf))).astype(np.float32)
+        mid = (r64 + other.astype(np.float64)) * 0.5
+    tie = (s != r64) & (s == mid) & (e != 0)
+    # at a tie the exact value lies beyond the midpoint on e's side
+    toward_other = tie & ((e > 0) == (other.astype(np.float64) > r64))
+    out = np.where(toward_other, other, r)
+    # an exact zero: -0 only when a*b and c are both zeros of sign -
+    zero = (s == 0) & (e == 0)
+    if np.any(zero):
+        pz = (a64 * b64 == 0) & (np.signbit(a64) != np.signbit(b64))
+        neg0 = zero & pz & (c64 == 0) & np.signbit(c64)
+        out = np.where(zero, np.where(neg0, np.float32(-0.0), np.float32(0.0)), out)
+    return out.astype(np.float32)
+
+
+def bf16_rne_bits_v(x):
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF).astype(np.uint16)
+
+
+def adam_binary32_v(master, m, v, g_bits, c):
+    """adam_binary32 on whole arrays (the same sequence of binary32
+    operations, vectorised)."""
+    b1, c1, b2, c2, s, r, e = (np.float32(x) for x in c[:7])
+    g = np.asarray(g_bits)
+    g = g.astype(np.float32) if g.dtype == np.float32 else (g.astype(np.uint32) << 16).view(np.float32)
+    f32 = lambda x: np.asarray(x, np.float32)
+    m1 = fma_v(b1, f32(m), c1 * g)
+    v1 = fma_v(b2, f32(v), c2 * (g * g))
+    den = fma_v(np.sqrt(v1), r, e)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        delta = -((s * m1) / den)
+    p = f32(master) + delta
+    return p.astype(np.float32), m1, v1, bf16_rne_bits_v(p)

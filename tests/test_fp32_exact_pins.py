@@ -143,3 +143,53 @@ def test_adam_binary32_agrees_with_the_fp64_oracle(f32_grads):
 
 def fx_bf16(bits):
     return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+
+def test_vectorised_fma_equals_the_rational_one():
+    """fma_v against fma over random operands of every scale, and over
+    constructed ties (a*b + c exactly half-way between two binary32 values,
+    nudged both ways by a tiny c) where binary64 rounding alone goes wrong."""
+    rng = np.random.default_rng(7)
+    a = random_f32(rng, 4000, -40, 40)
+    b = random_f32(rng, 4000, -40, 40)
+    c = random_f32(rng, 4000, -80, 80)
+    got = fx.fma_v(a, b, c)
+    for i in range(a.size):
+        assert same(got[i], fx.fma(a[i], b[i], c[i])), (a[i], b[i], c[i])
+    # ties: a = A * 2^-23 with A odd and b = 1.5 make a*b = 3A * 2^-24, a
+    # binary32 midpoint in [1.5, 2); c = +-2^-60 (lost in binary64) decides
+    ta, tb, tc = [], [], []
+    for A in range((1 << 23) + 1, (1 << 23) + 400, 2):
+        for cc in (2.0 ** -60, -2.0 ** -60, 0.0):
+            ta.append(A * 2.0 ** -23); tb.append(1.5); tc.append(cc)
+    ta, tb, tc = (np.array(q, np.float32) for q in (ta, tb, tc))
+    got = fx.fma_v(ta, tb, tc)
+    naive = (ta.astype(np.float64) * tb.astype(np.float64) + tc.astype(np.float64)).astype(np.float32)
+    assert np.count_nonzero(naive.view(np.uint32) != got.view(np.uint32)) > 100   # the case is live
+    for i in range(ta.size):
+        assert same(got[i], fx.fma(ta[i], tb[i], tc[i])), (ta[i], tb[i], tc[i])
+    zs = fx.fma_v(np.array([0.0, 1.0], np.float32), np.array([-1.0, 1.0], np.float32),
+                  np.array([-0.0, -1.0], np.float32))
+    assert same(zs[0], np.float32(-0.0)) and same(zs[1], np.float32(0.0))
+
+
+@pytest.mark.parametrize("f32_grads", [False, True], ids=["bf16_grads", "f32_grads"])
+def test_vectorised_adam_step_equals_the_rational_one(f32_grads):
+    import synth
+    n = 4000
+    master = synth.normal_f32(n, stream=97, block=0, purpose=synth.PURPOSE_MASTER, step=0, sigma=0.02)
+    master[::3] = 0.0
+    m = synth.normal_f32(n, stream=97, block=0, purpose=synth.PURPOSE_MASTER, step=1, sigma=1e-4)
+    v = np.abs(synth.normal_f32(n, stream=97, block=0, purpose=synth.PURPOSE_MASTER, step=2, sigma=1e-6))
+    a = [master, m, v]
+    b = [master.copy(), m.copy(), v.copy()]
+    for t in range(1, 4):
+        draw = synth.normal_f32 if f32_grads else synth.normal_bf16
+        g = draw(n, stream=97, block=0, purpose=synth.PURPOSE_GRAD, step=t, sigma=1e-3)
+        c = fx.adam_constants(t, 1e-3, 0.9, 0.999, 1e-8)
+        ra = fx.adam_binary32(*a, g, c)
+        rb = fx.adam_binary32_v(*b, g, c)
+        for x, y in zip(ra, rb):
+            dt = np.uint16 if x.dtype == np.uint16 else np.uint32
+            assert np.array_equal(np.asarray(x).view(dt), np.asarray(y).view(dt))
+        a, b = list(ra[:3]), list(rb[:3])

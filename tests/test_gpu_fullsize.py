@@ -6,7 +6,10 @@ gradients drawn on the device (device input generator); the oracle rebuilds
 just the sampled elements from the host input generator (same counter-based
 generator, bit-identical -- checked by test_gpu_stream) and runs the same
 steps on them.  Samples per block: 65,536 elements at offset 0, the last
-65,536 (ragged end), and six seeded 16-aligned offsets.
+65,536 (ragged end), and six seeded 16-aligned offsets.  Every sample is
+judged twice: against the FP64 oracle within the parity bound, and bit for
+bit against the binary32 emulation of the kernel's own arithmetic
+(tests/fp32_exact.py).
 """
 import numpy as np
 import pytest
@@ -14,6 +17,7 @@ import pytest
 import layer_streamed_optimizer_amd as lso
 import oracle
 import synth
+import fp32_exact as fx
 from layer_streamed_optimizer_amd import configs
 
 from gpu_util import TILE, Worst, assert_parity, log, torch
@@ -49,6 +53,35 @@ def init_kind(spec):
     if spec.init == "lora_a":
         return synth.PURPOSE_LORA_A, configs.LORA_A_SIGMA
     return synth.PURPOSE_MASTER, configs.MASTER_SIGMA
+
+
+def assert_bits(got, want, what):
+    """Every array of got (read back) equals want's (the binary32 emulation)
+    bit for bit."""
+    for q, arr in want.items():
+        if q not in got:
+            continue
+        g = np.ascontiguousarray(got[q])
+        dt = np.uint16 if arr.dtype == np.uint16 else np.uint32
+        bad = np.nonzero(g.view(dt) != np.ascontiguousarray(arr).view(dt))[0]
+        assert bad.size == 0, (f"{what}: {q} differs from the binary32 emulation at {bad.size} "
+                               f"elements, first at element {int(bad[0])} of the sample")
+
+
+def emulate(master, grads, steps, weights=True):
+    """The kernel's binary32 sequence over `steps` steps (vectorised; m = v =
+    0 at the start); grads(t) gives step t's BF16 gradients."""
+    p = np.asarray(master, np.float32).copy()
+    m = np.zeros(p.size, np.float32)
+    v = np.zeros(p.size, np.float32)
+    w = None
+    for t in range(1, steps + 1):
+        c = fx.adam_constants(t, configs.LR, configs.BETA1, configs.BETA2, configs.EPS)
+        p, m, v, w = fx.adam_binary32_v(p, m, v, grads(t), c)
+    out = dict(master=p, m=m, v=v)
+    if weights:
+        out["weight"] = w
+    return out
 
 
 def run_resident_sampled(key, steps, tiled=True):
@@ -93,7 +126,7 @@ def run_resident_sampled(key, steps, tiled=True):
         lso.adam_step(table, hs)
     T.cuda.synchronize()
     # oracle on the samples
-    refs, gots, where = [], [], []
+    refs, gots, where, exact = [], [], [], []
     for b, spec in enumerate(w.blocks):
         for off, ln in sample_offsets(spec.n, 1000 + b):
             kind = init_kind(spec)
@@ -102,13 +135,14 @@ def run_resident_sampled(key, steps, tiled=True):
             else:
                 master = synth.normal_f32(ln, stream=sid, block=b, purpose=kind[0], step=0,
                                           sigma=kind[1], start=off)
-            ref = dict(master=master, m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32),
+            ref = dict(master=master.copy(), m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32),
                        weight=np.zeros(ln, np.uint16))
+            gs = [synth.normal_bf16(ln, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=t,
+                                    sigma=configs.GRAD_SIGMA, start=off) for t in range(1, steps + 1)]
             for t in range(1, steps + 1):
-                g = synth.normal_bf16(ln, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=t,
-                                      sigma=configs.GRAD_SIGMA, start=off)
-                oracle.adam_step(ref["master"], ref["m"], ref["v"], g, ref["weight"], t,
+                oracle.adam_step(ref["master"], ref["m"], ref["v"], gs[t - 1], ref["weight"], t,
                                  configs.LR, configs.BETA1, configs.BETA2, configs.EPS)
+            exact.append(emulate(master, lambda t, gs=gs: gs[t - 1], steps))
 
             def rd(buf, byte_off, es, dt):
                 return buf[byte_off: byte_off + es * ln].cpu().numpy().view(dt)
@@ -124,9 +158,11 @@ def run_resident_sampled(key, steps, tiled=True):
             gots.append(got)
             where.append((b, off))
     worst = Worst()
-    for ref, got, (b, off) in zip(refs, gots, where):
+    for ref, got, (b, off), ex in zip(refs, gots, where, exact):
         worst.add(f"block {b} offset {off}", assert_parity(got, ref, 1e-6, f"{key} block {b} offset {off}"))
+        assert_bits(got, ex, f"{key} block {b} offset {off}")
     log(f"{key} sampled worst errors after {steps} steps: {worst}")
+    log(f"{key}: every sample equals the binary32 emulation bit for bit")
     del state, grad, weight, arena
     T.cuda.empty_cache()
 
@@ -209,21 +245,23 @@ def host_view(hb, pinned):
 
 def oracle_samples(sid, layer, spans, steps, weights=False):
     """The oracle's state after `steps` steps for each (offset, length)
-    span of a 70B-shaped layer, rebuilt from the host generator."""
-    out = []
+    span of a 70B-shaped layer, rebuilt from the host generator, and the
+    binary32 emulation's (what the kernel must hold bit for bit)."""
+    out, exact = [], []
     for off, ln in spans:
-        ref = dict(master=synth.normal_f32(ln, stream=sid, block=layer, purpose=synth.PURPOSE_MASTER,
-                                           step=0, sigma=configs.MASTER_SIGMA, start=off),
-                   m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32))
+        master = synth.normal_f32(ln, stream=sid, block=layer, purpose=synth.PURPOSE_MASTER,
+                                  step=0, sigma=configs.MASTER_SIGMA, start=off)
+        ref = dict(master=master.copy(), m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32))
         if weights:
             ref["weight"] = np.zeros(ln, np.uint16)
+        gs = [synth.normal_bf16(ln, stream=sid, block=layer, purpose=synth.PURPOSE_GRAD, step=t,
+                                sigma=configs.GRAD_SIGMA, start=off) for t in range(1, steps + 1)]
         for t in range(1, steps + 1):
-            g = synth.normal_bf16(ln, stream=sid, block=layer, purpose=synth.PURPOSE_GRAD, step=t,
-                                  sigma=configs.GRAD_SIGMA, start=off)
-            oracle.adam_step(ref["master"], ref["m"], ref["v"], g, ref.get("weight"), t, configs.LR,
+            oracle.adam_step(ref["master"], ref["m"], ref["v"], gs[t - 1], ref.get("weight"), t, configs.LR,
                              configs.BETA1, configs.BETA2, configs.EPS)
         out.append(ref)
-    return out
+        exact.append(emulate(master, lambda t, gs=gs: gs[t - 1], steps, weights))
+    return out, exact
 
 
 def read_host_sample(view, tiled, lay, off, ln):
@@ -279,16 +317,17 @@ def run_streamed_sampled(n_layers, tiled, pinned, steps=3, check_weights=False):
         spans = sample_offsets(n, 2000 + b)
         # just before and just after every piece boundary
         spans += [(p - SAMPLE // 2, SAMPLE) for p in bounds]
-        refs = oracle_samples(sid, b, spans, steps, weights=b in slot_w)
+        refs, exact = oracle_samples(sid, b, spans, steps, weights=b in slot_w)
         view = host_view(hosts[b], pinned)
-        for (off, ln), ref in zip(spans, refs):
+        for (off, ln), ref, ex in zip(spans, refs, exact):
             got = read_host_sample(view, tiled, lay, off, ln)
             if b in slot_w:
                 assert hip.hipMemcpy(int(wdev.data_ptr()), slot_w[b] + 2 * off, 2 * ln, 3) == 0
                 got["weight"] = wdev[:ln].cpu().numpy().view(np.uint16).copy()
             worst.add(f"layer {b} offset {off}",
                       assert_parity(got, ref, 1e-6, f"c4 layer {b} offset {off} (n={ln})"))
-        log(f"layer {b}: {len(spans)} samples checked")
+            assert_bits(got, ex, f"c4 layer {b} offset {off}")
+        log(f"layer {b}: {len(spans)} samples checked, each bit for bit")
     log(f"c4 {n_layers} layers, {steps} steps, worst errors: {worst}")
     ls.close()
     if pinned:
@@ -365,16 +404,17 @@ def test_block_of_more_than_2_32_elements_sampled(tiled):
         lso.adam_step(table, hs)
     T.cuda.synchronize()
     offs = [0, (1 << 31) - SAMPLE // 2, (1 << 32) - SAMPLE // 2, n - SAMPLE]
-    refs, gots = [], []
+    refs, gots, exact = [], [], []
     for off in offs:
-        ref = dict(master=synth.normal_f32(SAMPLE, stream=sid, block=0, purpose=0, step=0, sigma=0.02,
-                                           start=off),
-                   m=np.zeros(SAMPLE, np.float32), v=np.zeros(SAMPLE, np.float32),
+        master = synth.normal_f32(SAMPLE, stream=sid, block=0, purpose=0, step=0, sigma=0.02, start=off)
+        ref = dict(master=master.copy(), m=np.zeros(SAMPLE, np.float32), v=np.zeros(SAMPLE, np.float32),
                    weight=np.zeros(SAMPLE, np.uint16))
+        gs = [synth.normal_bf16(SAMPLE, stream=sid, block=0, purpose=2, step=t, sigma=1e-3, start=off)
+              for t in (1, 2)]
         for t in (1, 2):
-            g = synth.normal_bf16(SAMPLE, stream=sid, block=0, purpose=2, step=t, sigma=1e-3, start=off)
-            oracle.adam_step(ref["master"], ref["m"], ref["v"], g, ref["weight"], t, configs.LR,
+            oracle.adam_step(ref["master"], ref["m"], ref["v"], gs[t - 1], ref["weight"], t, configs.LR,
                              configs.BETA1, configs.BETA2, configs.EPS)
+        exact.append(emulate(master, lambda t, gs=gs: gs[t - 1], 2))
         if tiled:
             got = read_tiled(state, 0, off, SAMPLE)
         else:
@@ -383,7 +423,8 @@ def test_block_of_more_than_2_32_elements_sampled(tiled):
         got["weight"] = weight[2 * off: 2 * (off + SAMPLE)].cpu().numpy().view(np.uint16).copy()
         refs.append(ref)
         gots.append(got)
-    for off, ref, got in zip(offs, refs, gots):
+    for off, ref, got, ex in zip(offs, refs, gots, exact):
         assert_parity(got, ref, 1e-6, f"element offset {off}")
+        assert_bits(got, ex, f"element offset {off}")
     del state, grad, weight
     T.cuda.empty_cache()
