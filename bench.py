@@ -111,7 +111,7 @@ def measured_traffic(workload: str, grad_dtype: str = "bf16", norms: bool = Fals
     path = os.path.join(ROOT, "profiles", f"fused_adam_{tag}_pmc.md")
     if not os.path.exists(path):
         return None
-    text = open(path).read()
+    text = open(path, encoding="utf-8").read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():

@@ -46,8 +46,19 @@ def kernel_hash(read=None) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         h.update(code_of(read(name)).encode())
-    h.update(" ".join(build.FLAGS).encode())
+    h.update(" ".join(_portable(f, build.ROOT) for f in build.FLAGS).encode())
     return h.hexdigest()[:16]
+
+
+def _portable(flag: str, root: str) -> str:
+    """A build flag without the tree's own location: an include path inside
+    the tree counts relative to its root, so a copy of the tree elsewhere
+    has the same hash."""
+    if flag.startswith("-I"):
+        rel = os.path.relpath(flag[2:], root)
+        if rel != ".." and not rel.startswith(".." + os.sep):
+            return "-I" + rel.replace(os.sep, "/")
+    return flag
 
 
 def short(name: str, n: int = 70) -> str:

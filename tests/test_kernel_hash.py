@@ -39,11 +39,29 @@ def test_code_and_flags_move_the_hash():
     assert rs.kernel_hash() == base
 
 
+def test_hash_does_not_depend_on_where_the_tree_is():
+    """The build's include flags name the tree's absolute path; a copy of
+    the tree at another path (as a run elsewhere sees it) has the same hash."""
+    base = rs.kernel_hash()
+    saved = list(build.FLAGS)
+    saved_root = build.ROOT
+    try:
+        build.FLAGS[:] = [f.replace(saved_root, "/some/other/place/tree") for f in saved]
+        build.ROOT = "/some/other/place/tree"
+        assert rs.kernel_hash() == base
+        build.FLAGS.append("-I/usr/include/elsewhere")   # outside the tree: counts as written
+        assert rs.kernel_hash() != base
+    finally:
+        build.FLAGS[:] = saved
+        build.ROOT = saved_root
+    assert rs.kernel_hash() == base
+
+
 def test_committed_kernel_profiles_are_of_the_current_code():
     current = rs.kernel_hash()
     seen = 0
     for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
-        for h in re.findall(r"kernel_source_sha256: ([0-9a-f]{16})", open(path).read()):
+        for h in re.findall(r"kernel_source_sha256: ([0-9a-f]{16})", open(path, encoding="utf-8").read()):
             assert h == current, f"{os.path.basename(path)} was taken with kernel {h}, the code is {current}"
             seen += 1
     assert seen >= 8
