@@ -14,7 +14,8 @@ gradients).  A GPU test checks them against each other bit for bit.
 Recipe (all configs): key = (seed, stream) with seed 1234 and stream the
 workload number; counter = (index lo, index hi, block, purpose<<24 | step).
 Purposes: 0 FP32 master init, 1 LoRA-A init, 2 BF16 gradients (redrawn per
-step).  A normal deviate is the centred Irwin-Hall sum of the eight 16-bit
+step), 3 edge-case values (the raw Philox words mapped to subnormals, the
+smallest normals, signed zeros and ordinary values; host side only).  A normal deviate is the centred Irwin-Hall sum of the eight 16-bit
 halves of one Philox output times one FP32 scale; BF16 values are the
 truncated upper half of that FP32 pattern.
 """
@@ -32,6 +33,7 @@ SEED = 1234
 PURPOSE_MASTER = 0
 PURPOSE_LORA_A = 1
 PURPOSE_GRAD = 2
+PURPOSE_EDGE = 3   # values at the low end of the binary32 range (edge-case tests)
 
 # standard deviation of the sum of eight independent uniform 16-bit integers
 _IH8_SD = math.sqrt(8.0 * (65536.0 ** 2 - 1.0) / 12.0)
@@ -97,6 +99,8 @@ def _host_lib():
                 f = getattr(lib, name)
                 f.argtypes = [vp, vp, u64, u32, u32, u32, u32, u32, f32]
                 f.restype = None
+            lib.synth_philox_words.argtypes = [vp, u64, u64, u32, u32, u32, u32, u32]
+            lib.synth_philox_words.restype = None
             _host = lib
         return _host
 
@@ -141,6 +145,50 @@ def normal_bf16_at(idx: np.ndarray, *, stream: int, block: int, purpose: int, st
     _host_lib().synth_normal_bf16_at(out.ctypes.data, idx.ctypes.data, idx.size, seed, stream,
                                      block, purpose, step, scale_for(sigma))
     return out
+
+
+def philox_words(n: int, *, stream: int, block: int, purpose: int, step: int, start: int = 0,
+                 seed: int = SEED) -> np.ndarray:
+    """The raw Philox output of indices start .. start + n - 1: shape (n, 4)."""
+    out = np.empty((n, 4), dtype=np.uint32)
+    _host_lib().synth_philox_words(out.ctypes.data, start, n, seed, stream, block, purpose, step)
+    return out
+
+
+def edge_f32(n: int, *, stream: int, block: int, step: int, positive: bool = False,
+             seed: int = SEED) -> np.ndarray:
+    """FP32 values at the low end of the binary32 range.  By the first
+    Philox word of each element, mod 4: a subnormal (exponent field 0,
+    non-zero fraction), a value in one of the eight smallest normal binades
+    (exponent field 1..8), zero, or an ordinary value in [2^-8, 2^-5).  The
+    fraction comes from the second word, the sign from the third (none when
+    positive)."""
+    w = philox_words(n, stream=stream, block=block, purpose=PURPOSE_EDGE, step=step, seed=seed)
+    cls = w[:, 0] & 3
+    frac = w[:, 1] & 0x7FFFFF
+    frac = np.where(cls == 0, np.maximum(frac, 1), np.where(cls == 2, 0, frac))
+    w3 = w[:, 3].astype(np.int64)
+    exp = np.select([cls == 0, cls == 1, cls == 2], [0, 1 + (w3 & 7), 0], 119 + w3 % 3)
+    sign = np.zeros(n, np.uint32) if positive else w[:, 2] >> 31
+    bits = (sign << 31) | (exp.astype(np.uint32) << 23) | frac.astype(np.uint32)
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def edge_bf16(n: int, *, stream: int, block: int, step: int, seed: int = SEED) -> np.ndarray:
+    """BF16 gradient patterns at the low end of the range.  By the first
+    Philox word, mod 4: a BF16 subnormal (exponent field 0, non-zero
+    fraction), a normal whose square lies below the FP32 normal range
+    (exponent field 47..62: 2^-80 .. 2^-65), zero, or an ordinary gradient
+    (exponent field 115..118: 2^-12 .. 2^-9).  Fraction from the second
+    word, sign from the third."""
+    w = philox_words(n, stream=stream, block=block, purpose=PURPOSE_EDGE, step=step, seed=seed)
+    cls = w[:, 0] & 3
+    frac = w[:, 1] & 0x7F
+    frac = np.where(cls == 0, np.maximum(frac, 1), np.where(cls == 2, 0, frac))
+    w3 = w[:, 3].astype(np.int64)
+    exp = np.select([cls == 0, cls == 1, cls == 2], [0, 47 + (w3 & 15), 0], 115 + (w3 & 3))
+    bits = ((w[:, 2] >> 31) << 15) | (exp.astype(np.uint32) << 7) | frac.astype(np.uint32)
+    return bits.astype(np.uint16)
 
 
 # --------------------------------------------------------------- device side

@@ -100,3 +100,17 @@ void synth_normal_bf16_at(uint16_t* out, const uint64_t* idx, uint64_t n, uint32
         out[k] = (uint16_t)(u >> 16);
     }
 }
+
+/* The four raw Philox words of indices i0 .. i0 + n - 1 (out[4k .. 4k+3]),
+ * same counter and key as the deviates above. */
+void synth_philox_words(uint32_t* out, uint64_t i0, uint64_t n, uint32_t seed, uint32_t stream,
+                        uint32_t block, uint32_t purpose, uint32_t step)
+{
+    for (uint64_t k = 0; k < n; ++k) {
+        const uint64_t index = i0 + k;
+        uint32_t ctr[4] = { (uint32_t)index, (uint32_t)(index >> 32), block,
+                            (purpose << 24) | (step & 0x00FFFFFFu) };
+        uint32_t key[2] = { seed, stream };
+        synth_philox4x32_10(ctr, key, out + 4 * k);
+    }
+}

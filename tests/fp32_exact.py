@@ -161,6 +161,21 @@ def adam_binary32(master, m, v, g_bits, c):
     return out_p, out_m, out_v, out_w
 
 
+def sgd_binary32(master, g_bits, s):
+    """One SGD step as the kernel orders it in binary32: master' = master +
+    -(s g), a product and a sum each rounded once (nothing fused).  g_bits:
+    BF16 patterns or FP32 gradients.  Returns (master', BF16 weight bits)."""
+    s = np.float32(s)
+    out_p = np.asarray(master, np.float32).copy()
+    out_w = np.zeros(out_p.size, np.uint16)
+    f32_grads = np.asarray(g_bits).dtype == np.float32
+    for i in range(out_p.size):
+        g = np.float32(g_bits[i]) if f32_grads else bf16_to_f32(g_bits[i])
+        out_p[i] = add(out_p[i], neg(mul(s, g)))
+        out_w[i] = bf16_rne_bits(out_p[i])
+    return out_p, out_w
+
+
 # ------------------------------------------------- vectorised, for large samples
 #
 # numpy's float32 add, multiply, divide and sqrt are the IEEE binary32

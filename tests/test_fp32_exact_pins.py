@@ -193,3 +193,73 @@ def test_vectorised_adam_step_equals_the_rational_one(f32_grads):
             dt = np.uint16 if x.dtype == np.uint16 else np.uint32
             assert np.array_equal(np.asarray(x).view(dt), np.asarray(y).view(dt))
         a, b = list(ra[:3]), list(rb[:3])
+
+
+# Hyper-parameter sets for inputs at the bottom of the range: the usual ones
+# (a denominator of about eps); eps = 1 with dyadic betas (deltas of
+# subnormal moments are subnormal themselves); eps = 1e-30 (the root of a
+# subnormal v decides the denominator); a subnormal eps.
+EDGE_HYPER = [(1e-3, 0.9, 0.999, 1e-8), (1e-3, 0.5, 0.75, 1.0), (1e-3, 0.9, 0.999, 1e-30),
+              (1e-2, 0.9, 0.99, 1e-40)]
+EDGE_IDS = ["eps_1e-8", "eps_1", "eps_1e-30", "eps_subnormal"]
+
+
+def subnormal_count(x) -> int:
+    u = np.asarray(x, np.float32).view(np.uint32)
+    return int(np.count_nonzero(((u >> 23) & 0xFF) == 0) - np.count_nonzero((u & 0x7FFFFFFF) == 0))
+
+
+def test_edge_inputs_reach_the_bottom_of_the_range():
+    import synth
+    f = synth.edge_f32(4000, stream=98, block=0, step=0)
+    u = f.view(np.uint32)
+    assert 800 < subnormal_count(f) < 1200                      # a quarter subnormal
+    assert 800 < np.count_nonzero(((u >> 23) & 0xFF) - 1 < 8) < 1200   # smallest normal binades
+    assert np.count_nonzero(u == 0x80000000) > 300              # signed zeros both ways
+    assert np.all(synth.edge_f32(4000, stream=98, block=0, step=2, positive=True) >= 0)
+    g = synth.edge_bf16(4000, stream=98, block=0, step=1).astype(np.uint32)
+    gf = (g << 16).view(np.float32)
+    assert subnormal_count(gf) > 800                            # BF16 subnormals
+    sq = gf.astype(np.float64) ** 2
+    assert np.count_nonzero((sq > 0) & (sq < 2.0 ** -126)) > 400   # squares below the normal range
+    assert np.all(np.isfinite(gf))
+
+
+@pytest.mark.parametrize("hyper", EDGE_HYPER, ids=EDGE_IDS)
+@pytest.mark.parametrize("f32_grads", [False, True], ids=["bf16_grads", "f32_grads"])
+def test_vectorised_adam_step_equals_the_rational_one_at_the_bottom_of_the_range(hyper, f32_grads):
+    """Subnormal and tiny masters, moments and gradients (signed zeros
+    among them), three steps: the vectorised emulation, which the GPU tests
+    use, gives the rational one's bits, and subnormal results occur."""
+    import synth
+    n = 1500
+    a = [synth.edge_f32(n, stream=98, block=0, step=0), synth.edge_f32(n, stream=98, block=0, step=1),
+         synth.edge_f32(n, stream=98, block=0, step=2, positive=True)]
+    b = [x.copy() for x in a]
+    produced = 0
+    for t in range(1, 4):
+        g = (synth.edge_f32 if f32_grads else synth.edge_bf16)(n, stream=98, block=0, step=10 + t)
+        c = fx.adam_constants(t, *hyper)
+        ra = fx.adam_binary32(*a, g, c)
+        rb = fx.adam_binary32_v(*b, g, c)
+        for x, y in zip(ra, rb):
+            dt = np.uint16 if x.dtype == np.uint16 else np.uint32
+            assert np.array_equal(np.asarray(x).view(dt), np.asarray(y).view(dt))
+        assert all(np.all(np.isfinite(x)) for x in ra[:3])
+        produced += sum(subnormal_count(x) for x in ra[:3])
+        a, b = list(ra[:3]), list(rb[:3])
+    assert produced > 100, "no subnormal results: the inputs do not exercise the case"
+
+
+def test_sgd_emulation_equals_numpy_float32_at_the_bottom_of_the_range():
+    import synth
+    n = 3000
+    master = synth.edge_f32(n, stream=98, block=1, step=0)
+    for g in (synth.edge_bf16(n, stream=98, block=1, step=1), synth.edge_f32(n, stream=98, block=1, step=2)):
+        gf = g if g.dtype == np.float32 else (g.astype(np.uint32) << 16).view(np.float32)
+        s = np.float32(0.5)
+        p, w = fx.sgd_binary32(master, g, s)
+        want = master + (-(s * gf))
+        assert np.array_equal(p.view(np.uint32), want.view(np.uint32))
+        assert np.array_equal(w, fx.bf16_rne_bits_v(want))
+        assert subnormal_count(p) > 100

@@ -14,6 +14,12 @@ gradients.  Half of the masters
 start at 0, so the first step writes each element's step itself (any
 rounding difference in the root or the division shows in those bits).
 
+A second set of cases starts from values at the bottom of the binary32
+range (subnormal and tiny masters, moments and gradients, signed zeros, a
+subnormal eps, and SGD): the kernel keeps subnormals through every
+operation, so its bits still equal the emulation's, with hundreds of
+subnormal results per case.
+
 The FP64 oracle defines the update and is compared with a tolerance
 elsewhere; this is the check of the FP32 contract the kernel states.
 """
@@ -99,3 +105,101 @@ def test_update_bit_exact_against_binary32_emulation(sizes, tiled, f32, hyper):
             state[i] = [p, m, v]
     assert arena.canaries_intact(), "a write landed outside its array"
     log("fp32 exact", f"{sum(sizes)} elements x {STEPS} steps identical")
+
+
+# Inputs at the bottom of the binary32 range (synth.edge_f32 / edge_bf16: a
+# quarter subnormal, a quarter in the smallest normal binades or with squares
+# below them, a quarter signed zeros).  The kernel keeps subnormals (no flush
+# to zero in any operation), so its bits still equal the emulation's; the
+# vectorised emulation used here is pinned to the rational one on the same
+# kind of inputs.
+EDGE_STREAM = 94
+EDGE_CASES = [
+    # sizes, tiled, FP32 gradients, (lr, beta1, beta2, eps)
+    ([2085], False, False, (1e-3, 0.9, 0.999, 1e-8)),                       # one block by value
+    ([5, 1029, 600], False, False, (1e-3, 0.5, 0.75, 1.0)),                 # a few by value
+    ([1, 7, 1024, 1500, 33, 2049], False, False, (1e-2, 0.9, 0.99, 1e-40)), # table, subnormal eps
+    ([8195], True, False, (1e-3, 0.5, 0.75, 1.0)),                          # tiled, one block
+    ([5, 1030, 8192, 17], True, False, (1e-3, 0.9, 0.999, 1e-30)),          # tiled, table
+    ([2500, 9, 700], False, True, (1e-3, 0.9, 0.999, 1e-8)),                # FP32 gradients
+    ([8200, 5, 1030], True, True, (1e-2, 0.9, 0.99, 1e-40)),                # FP32 gradients, tiled
+]
+
+
+def subnormals(x) -> int:
+    u = np.asarray(x, np.float32).view(np.uint32)
+    return int(np.count_nonzero((((u >> 23) & 0xFF) == 0) & ((u & 0x7FFFFF) != 0)))
+
+
+@pytest.mark.parametrize("sizes,tiled,f32,hyper", EDGE_CASES,
+                         ids=["one_block", "by_value", "table_subnormal_eps", "tiled_one_block",
+                              "tiled_table", "f32_grads", "f32_grads_tiled_subnormal_eps"])
+def test_subnormal_and_tiny_values_bit_exact(sizes, tiled, f32, hyper):
+    lr, b1, b2, eps = hyper
+    log("fp32 edge", f"sizes={sizes} tiled={tiled} f32_grads={f32} hyper={hyper}")
+    T = torch()
+    arena = Arena(sizes, tiled=tiled, grad_f32=f32)
+    state = []
+    for i, n in enumerate(sizes):
+        st = [synth.edge_f32(n, stream=EDGE_STREAM, block=i, step=0),
+              synth.edge_f32(n, stream=EDGE_STREAM, block=i, step=1),
+              synth.edge_f32(n, stream=EDGE_STREAM, block=i, step=2, positive=True)]
+        state.append(st)
+        for name, x in zip(("master", "m", "v"), st):
+            arena.put(i, name, x)
+    table = arena.table(lr=lr, beta1=b1, beta2=b2, eps=eps)
+    produced = [0, 0, 0]   # subnormal results: master, m, v
+    for t in range(1, STEPS + 1):
+        c = constants(t, lr, b1, b2, eps)
+        draw = synth.edge_f32 if f32 else synth.edge_bf16
+        gs = [draw(n, stream=EDGE_STREAM, block=i, step=10 + t) for i, n in enumerate(sizes)]
+        for i, g in enumerate(gs):
+            arena.put(i, "grad", g)
+        table.set_step(t)
+        lso.adam_step(table, T.cuda.current_stream())
+        T.cuda.synchronize()
+        for i, n in enumerate(sizes):
+            p, m, v, w = fx.adam_binary32_v(*state[i], gs[i], c)
+            for name, want in (("master", p), ("m", m), ("v", v), ("weight", w)):
+                count, where = first_diff(arena.get(i, name), want)
+                assert count == 0, (f"step {t} block {i} (n={n}) {name}: {count} elements differ; "
+                                    f"first (index, got, emulated): {where}")
+            produced = [k + subnormals(x) for k, x in zip(produced, (p, m, v))]
+            state[i] = [p, m, v]
+    assert min(produced) > 100, f"too few subnormal results to exercise the case: {produced}"
+    assert arena.canaries_intact(), "a write landed outside its array"
+    log("fp32 edge", f"{sum(sizes)} elements x {STEPS} steps identical; {produced} subnormal results")
+
+
+def test_sgd_subnormal_and_tiny_values_bit_exact():
+    """SGD (master + -(s g), no fused operation) on the same kind of inputs,
+    BF16 and FP32 gradients: numpy's binary32 product and sum, which the
+    emulation's rational SGD step equals on such inputs."""
+    log("fp32 edge", "sgd")
+    T = torch()
+    sizes = [3001, 17, 1030]
+    for f32 in (False, True):
+        arena = Arena(sizes, adam=False, grad_f32=f32)
+        masters = [synth.edge_f32(n, stream=EDGE_STREAM, block=10 + i, step=0) for i, n in enumerate(sizes)]
+        for i, x in enumerate(masters):
+            arena.put(i, "master", x)
+        lib_s = lso.block_constants(t=1, lr=0.5, opt=lso.LSO_OPT_SGD)[4]
+        assert lib_s == np.float32(0.5)
+        table = arena.table(lr=0.5, opt=lso.LSO_OPT_SGD)
+        for t in range(1, STEPS + 1):
+            draw = synth.edge_f32 if f32 else synth.edge_bf16
+            gs = [draw(n, stream=EDGE_STREAM, block=10 + i, step=10 + t) for i, n in enumerate(sizes)]
+            for i, g in enumerate(gs):
+                arena.put(i, "grad", g)
+            table.set_step(t)
+            lso.adam_step(table, T.cuda.current_stream())
+            T.cuda.synchronize()
+            for i, g in enumerate(gs):
+                gf = g if f32 else (g.astype(np.uint32) << 16).view(np.float32)
+                want = masters[i] + (-(np.float32(0.5) * gf))
+                for name, ref in (("master", want), ("weight", fx.bf16_rne_bits_v(want))):
+                    count, where = first_diff(arena.get(i, name), ref)
+                    assert count == 0, f"f32={f32} step {t} block {i} {name}: {count} differ; first {where}"
+                masters[i] = want
+        assert sum(subnormals(x) for x in masters) > 0
+        assert arena.canaries_intact()

@@ -49,3 +49,13 @@ def test_moments():
     k = np.mean((x / x.std()) ** 4) - 3
     assert abs(k + 0.15) < 0.02
     assert np.max(np.abs(x)) <= np.sqrt(24.0) * 0.02 * 1.0001
+
+
+def test_raw_words_follow_the_same_counter():
+    """philox_words(n) is Philox4x32-10 at counter (index lo, index hi,
+    block, purpose << 24 | step), key (seed, stream), element by element."""
+    w = synth.philox_words(5, stream=7, block=3, purpose=synth.PURPOSE_EDGE, step=9, start=(1 << 32) - 2)
+    for k in range(5):
+        i = (1 << 32) - 2 + k
+        want = synth.philox4x32_10([i & 0xFFFFFFFF, i >> 32, 3, (synth.PURPOSE_EDGE << 24) | 9], [synth.SEED, 7])
+        assert list(w[k]) == want
