@@ -203,3 +203,88 @@ def test_sgd_subnormal_and_tiny_values_bit_exact():
                 masters[i] = want
         assert sum(subnormals(x) for x in masters) > 0
         assert arena.canaries_intact()
+
+
+WIDE_STREAM = 93
+
+
+def wide_grads(n, block, step, f32):
+    """Gradients over the upper exponent range, from the seeded Philox
+    words: a quarter with |g| in [2^64, 2^128) (g*g overflows binary32), the
+    rest with |g| in [1, 2^64); random signs and fractions.  Returns the
+    gradients (BF16 patterns or FP32) and the mask of the large ones."""
+    w = synth.philox_words(n, stream=WIDE_STREAM, block=block, purpose=synth.PURPOSE_EDGE, step=step)
+    w = w.astype(np.uint64)
+    big = (w[:, 0] & 3) == 0
+    e = np.where(big, 64 + w[:, 3] % 64, w[:, 3] % 64) + 127   # biased exponent field, at most 254
+    sign = w[:, 2] >> 31
+    if f32:
+        bits = (sign << 31) | (e << 23) | (w[:, 1] & 0x7FFFFF)
+        return bits.astype(np.uint32).view(np.float32), big
+    return ((sign << 15) | (e << 7) | (w[:, 1] & 0x7F)).astype(np.uint16), big
+
+
+@pytest.mark.parametrize("tiled,f32", [(False, False), (True, False), (False, True), (True, True)],
+                         ids=["planar", "tiled", "planar_f32_grads", "tiled_f32_grads"])
+def test_large_gradients_and_the_overflow_of_their_square(tiled, f32):
+    """Gradients from 1 to 2^128.  Below 2^64 every quantity stays finite:
+    the kernel equals the binary32 emulation bit for bit, and its masters and
+    weights are within the parity bound of the FP64 oracle.  From 2^64 up,
+    g*g overflows binary32 (the kernel forms c2 * (g*g), one rounding for a
+    BF16 g in range): v becomes +inf, the step -(s m')/inf is a zero, the
+    master keeps its bits and nothing turns NaN -- IEEE arithmetic on the
+    kernel's own operation order.  (The FP64 oracle keeps v finite until
+    c2 g^2 itself leaves the binary32 range, so there the two differ.)"""
+    import oracle
+    from gpu_util import assert_parity
+    sizes = [4101, 1030]
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    log("fp32 wide", f"sizes={sizes} tiled={tiled} f32_grads={f32}")
+    T = torch()
+    arena = Arena(sizes, tiled=tiled, grad_f32=f32)
+    state, ref, never_big = [], [], []
+    for i, n in enumerate(sizes):
+        master = synth.normal_f32(n, stream=WIDE_STREAM, block=i, purpose=synth.PURPOSE_MASTER, step=0, sigma=0.02)
+        st = [master, np.zeros(n, np.float32), np.zeros(n, np.float32)]
+        state.append(st)
+        ref.append([x.copy() for x in st] + [np.zeros(n, np.uint16)])
+        never_big.append(np.ones(n, bool))
+        for name, x in zip(("master", "m", "v"), st):
+            arena.put(i, name, x)
+    table = arena.table(lr=lr, beta1=b1, beta2=b2, eps=eps)
+    overflowed = 0
+    for t in range(1, STEPS + 1):
+        c = constants(t, lr, b1, b2, eps)
+        drawn = [wide_grads(n, i, t, f32) for i, n in enumerate(sizes)]
+        for i, (g, _) in enumerate(drawn):
+            arena.put(i, "grad", g)
+        table.set_step(t)
+        lso.adam_step(table, T.cuda.current_stream())
+        T.cuda.synchronize()
+        for i, n in enumerate(sizes):
+            g, big = drawn[i]
+            with np.errstate(all="ignore"):
+                p, m, v, w = fx.adam_binary32_v(*state[i], g, c)
+            got = {q: arena.get(i, q) for q in ("master", "m", "v", "weight")}
+            for name, want in (("master", p), ("m", m), ("v", v), ("weight", w)):
+                count, where = first_diff(got[name], want)
+                assert count == 0, (f"step {t} block {i} {name}: {count} elements differ; "
+                                    f"first (index, got, emulated): {where}")
+            # the overflow regime, stated directly
+            inf_v = np.isposinf(got["v"])
+            assert np.all(inf_v[big]), "a square that overflows leaves v finite"
+            assert np.array_equal(got["master"][inf_v].view(np.uint32), state[i][0][inf_v].view(np.uint32)), \
+                "a step taken where v is +inf"
+            assert not any(np.isnan(got[q]).any() for q in ("master", "m", "v")), "NaN appeared"
+            overflowed += int(np.count_nonzero(big))
+            # the FP64 oracle, where nothing has overflowed
+            never_big[i] &= ~big
+            ok = never_big[i]
+            r = ref[i]
+            oracle.adam_step(r[0], r[1], r[2], g, r[3], t, lr, b1, b2, eps)
+            assert_parity({"master": got["master"][ok], "weight": got["weight"][ok]},
+                          {"master": r[0][ok], "weight": r[3][ok]}, 1e-6, f"step {t} block {i} finite")
+            state[i] = [p, m, v]
+    assert overflowed > 1000
+    assert arena.canaries_intact(), "a write landed outside its array"
+    log("fp32 wide", f"identical; {overflowed} overflowing squares")
