@@ -278,12 +278,11 @@ class LayerStream:
         return np.zeros(n, HOST_LAYER_DTYPE)
 
     def stream_layers(self, host_layers: np.ndarray) -> None:
-        if host_layers.dtype != HOST_LAYER_DTYPE or not host_layers.flags.c_contiguous:
-            raise TypeError("host_layers must be a contiguous HOST_LAYER_DTYPE array")
-        st = _native.lib().lso_stream_layers(self.ctx, host_layers.ctypes.data, len(host_layers))
-        _native.check(st, "lso_stream_layers")
+        _native.check(self.stream_layers_status(host_layers), "lso_stream_layers")
 
     def stream_layers_status(self, host_layers: np.ndarray) -> int:
+        if host_layers.dtype != HOST_LAYER_DTYPE or not host_layers.flags.c_contiguous:
+            raise TypeError("host_layers must be a contiguous HOST_LAYER_DTYPE array")
         return _native.lib().lso_stream_layers(self.ctx, host_layers.ctypes.data, len(host_layers))
 
     @staticmethod

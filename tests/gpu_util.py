@@ -33,7 +33,7 @@ def to_dev(a: np.ndarray):
     return t.from_numpy(a.view(np.uint8).copy()).to("cuda")
 
 
-TILE = 8192
+TILE = configs.TILE   # elements per tile of the tiled state layout
 
 
 def tile_state(master, m, v):
