@@ -86,12 +86,14 @@ typedef enum lso_opt { LSO_OPT_ADAM = 0, LSO_OPT_SGD = 1 } lso_opt;
  *           +8*T, element j of the tile at index j of each.  The region is
  *           lso_tiled_state_bytes(n) = 12*T*ceil(n/T) bytes; the padding
  *           after element n-1 is never read or written.  Adam only.
- * The state is private to the optimizer, so its layout is free; the tiled
- * one keeps every workgroup of the update inside one contiguous run of
- * memory, which the HBM serves markedly faster than three separate
- * streams.  Gradients and weights are planar in both layouts (they are
- * shared with the forward and backward passes).  lso_tiled_pack and
- * lso_tiled_unpack convert between the two. */
+ * The state is private to the optimizer, so its layout is free; in the
+ * tiled one a workgroup of the update reads and writes three runs a fixed
+ * 32 KB apart inside one 96 KB tile, which the HBM serves markedly faster
+ * than three arrays far apart.  The tile size is a measured optimum on
+ * MI355X: tiles of 1,024 to 65,536 elements, powers of two and sizes
+ * between them, were all slower.  Gradients and weights are planar in
+ * both layouts (they are shared with the forward and backward passes).
+ * lso_tiled_pack and lso_tiled_unpack convert between the two. */
 typedef enum lso_layout { LSO_LAYOUT_PLANAR = 0, LSO_LAYOUT_TILED = 1 } lso_layout;
 #define LSO_TILE_ELEMS 8192u
 

@@ -22,7 +22,9 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("lso_adam.hip", "lso_internal.h", "lso_bf16.h")
+# the update kernel's sources and the public header they include (its tile
+# size and enum values are part of the kernel's code), relative to here
+KERNEL_SOURCES = ("csrc/lso_adam.hip", "csrc/lso_internal.h", "csrc/lso_bf16.h", "../include/lso.h")
 
 
 _COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
@@ -41,7 +43,7 @@ def kernel_hash(read=None) -> str:
     from . import build
     if read is None:
         def read(name):
-            with open(os.path.join(HERE, "csrc", name), encoding="utf-8") as f:
+            with open(os.path.join(HERE, name), encoding="utf-8") as f:
                 return f.read()
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _reader(edit=lambda name, text: text):
     def read(name):
-        with open(os.path.join(rs.HERE, "csrc", name), encoding="utf-8") as f:
+        with open(os.path.join(rs.HERE, name), encoding="utf-8") as f:
             return edit(name, f.read())
     return read
 
@@ -28,8 +28,11 @@ def test_comments_and_whitespace_do_not_move_the_hash():
 def test_code_and_flags_move_the_hash():
     base = rs.kernel_hash()
     changed = _reader(lambda n, t: t.replace("fmaf(c.b1, m, c.c1 * g)", "fmaf(c.b1, m, g)")
-                      if n == "lso_adam.hip" else t)
+                      if n.endswith("lso_adam.hip") else t)
     assert rs.kernel_hash(changed) != base
+    retiled = _reader(lambda n, t: t.replace("#define LSO_TILE_ELEMS 8192u", "#define LSO_TILE_ELEMS 16384u")
+                      if n.endswith("lso.h") else t)
+    assert rs.kernel_hash(retiled) != base   # the header's tile size is kernel code too
     saved = list(build.FLAGS)
     try:
         build.FLAGS.append("-DSOMETHING")
