@@ -481,6 +481,7 @@ def hbm_probe(nbytes: int = 8 << 30, reps: int = 6) -> dict:
               for l in range(6) for st in range(6)]
     cases += [("in place (read and write the same addresses)", 4, 0), ("read only", 5, 0),
               ("write only", 6, 0)]
+    cases += [(f"in place, load nt, store {names[st]}", 7, st) for st in range(6)]
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rows = []
     for name, var, param in cases:
@@ -499,7 +500,7 @@ def hbm_probe(nbytes: int = 8 << 30, reps: int = 6) -> dict:
         ok = None
         if var in (0, 1, 2, 3):
             ok = bool(torch.equal(src, dst))
-        elif var == 4:
+        elif var in (4, 7):
             ok = bool(torch.equal(src, keep))
         gbps = moved / (min(times) * 1e-3) / 1e9
         rows.append(dict(shape=name, variant=var, param=param, GBps=gbps, exact=ok))

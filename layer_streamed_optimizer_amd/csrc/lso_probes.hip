@@ -241,6 +241,27 @@ inplace_kernel(u32x4* __restrict__ buf)
     st_nt<u32x4>(buf + i, ~x);
 }
 
+// In place with nt loads and the store cache-policy bits S (as
+// copy_cpol_kernel's): the update's own state traffic, each vector read and
+// written back to its address (bits flipped).
+template <int S>
+__global__ void __launch_bounds__(256)
+inplace_cpol_kernel(u32x4* __restrict__ buf)
+{
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const LSO_GLOBAL u32x4* s = reinterpret_cast<const LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(buf + i));
+    LSO_GLOBAL u32x4* d = reinterpret_cast<LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(buf + i));
+    u32x4 x;
+    LSO_CPOL_LOAD("nt");
+    x = ~x;
+    if (S == 0) LSO_CPOL_STORE("");
+    else if (S == 1) LSO_CPOL_STORE("nt");
+    else if (S == 2) LSO_CPOL_STORE("sc1");
+    else if (S == 3) LSO_CPOL_STORE("nt sc1");
+    else if (S == 4) LSO_CPOL_STORE("sc0 sc1");
+    else LSO_CPOL_STORE("sc0 sc1 nt");
+}
+
 // Read-only: every vector read; one word per workgroup written so the
 // loads stay.
 __global__ void __launch_bounds__(256)
@@ -338,6 +359,8 @@ int lso_probe_copy_shaped(void* state, const void* grad, void* weight, uint64_t 
 //   4  in place over src (dst unused): read and write the same addresses
 //   5  read-only over src (dst receives at most a few words)
 //   6  write-only over dst
+//   7  in place over src with nt loads; param = store policy (0..5, see
+//      copy_cpol_kernel)
 // Returns a hipError_t (hipErrorInvalidValue for a bad variant, param or
 // size).
 int lso_probe_copy_variant(int variant, int param, const void* src, void* dst, uint64_t bytes, void* stream)
@@ -388,6 +411,19 @@ int lso_probe_copy_variant(int variant, int param, const void* src, void* dst, u
     case 4: hipLaunchKernelGGL(inplace_kernel, dim3(g1), t, 0, st, const_cast<u32x4*>(s)); break;
     case 5: hipLaunchKernelGGL(read_only_kernel, dim3(g1), t, 0, st, s, static_cast<uint32_t*>(dst)); break;
     case 6: hipLaunchKernelGGL(write_only_kernel, dim3(g1), t, 0, st, d); break;
+    case 7: {
+        auto* b = const_cast<u32x4*>(s);
+        switch (param) {
+        case 0: hipLaunchKernelGGL(inplace_cpol_kernel<0>, dim3(g1), t, 0, st, b); break;
+        case 1: hipLaunchKernelGGL(inplace_cpol_kernel<1>, dim3(g1), t, 0, st, b); break;
+        case 2: hipLaunchKernelGGL(inplace_cpol_kernel<2>, dim3(g1), t, 0, st, b); break;
+        case 3: hipLaunchKernelGGL(inplace_cpol_kernel<3>, dim3(g1), t, 0, st, b); break;
+        case 4: hipLaunchKernelGGL(inplace_cpol_kernel<4>, dim3(g1), t, 0, st, b); break;
+        case 5: hipLaunchKernelGGL(inplace_cpol_kernel<5>, dim3(g1), t, 0, st, b); break;
+        default: return static_cast<int>(hipErrorInvalidValue);
+        }
+        break;
+    }
     default: return static_cast<int>(hipErrorInvalidValue);
     }
     return static_cast<int>(hipGetLastError());
