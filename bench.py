@@ -482,6 +482,7 @@ def hbm_probe(nbytes: int = 8 << 30, reps: int = 6) -> dict:
     cases += [("in place (read and write the same addresses)", 4, 0), ("read only", 5, 0),
               ("write only", 6, 0)]
     cases += [(f"in place, load nt, store {names[st]}", 7, st) for st in range(6)]
+    cases += [(f"{w}-byte vector per lane, load nt, store nt sc1", 8, w) for w in (4, 8, 16)]
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rows = []
     for name, var, param in cases:
@@ -498,7 +499,7 @@ def hbm_probe(nbytes: int = 8 << 30, reps: int = 6) -> dict:
                 times.append(s.elapsed_time(e))
         moved = nbytes if var in (5, 6) else 2 * nbytes
         ok = None
-        if var in (0, 1, 2, 3):
+        if var in (0, 1, 2, 3, 8):
             ok = bool(torch.equal(src, dst))
         elif var in (4, 7):
             ok = bool(torch.equal(src, keep))

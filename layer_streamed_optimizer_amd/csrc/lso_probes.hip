@@ -262,6 +262,28 @@ inplace_cpol_kernel(u32x4* __restrict__ buf)
     else LSO_CPOL_STORE("sc0 sc1 nt");
 }
 
+// One W-byte vector per lane (W = 4, 8 or 16), nt loads and nt sc1 stores
+// (the update's bits): how the access width alone moves the stream.
+template <int W>
+__global__ void __launch_bounds__(256)
+copy_width_kernel(const char* __restrict__ src, char* __restrict__ dst)
+{
+    const uint64_t off = (static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x) * W;
+    if (W == 16) {
+        const u32x4 x = ld_nt<u32x4>(src + off);
+        LSO_GLOBAL u32x4* d = reinterpret_cast<LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(dst + off));
+        asm volatile("global_store_dwordx4 %0, %1, off nt sc1" : : "v"(d), "v"(x) : "memory");
+    } else if (W == 8) {
+        const u32x2 x = ld_nt<u32x2>(src + off);
+        LSO_GLOBAL u32x2* d = reinterpret_cast<LSO_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(dst + off));
+        asm volatile("global_store_dwordx2 %0, %1, off nt sc1" : : "v"(d), "v"(x) : "memory");
+    } else {
+        const uint32_t x = ld_nt<uint32_t>(src + off);
+        LSO_GLOBAL uint32_t* d = reinterpret_cast<LSO_GLOBAL uint32_t*>(reinterpret_cast<uintptr_t>(dst + off));
+        asm volatile("global_store_dword %0, %1, off nt sc1" : : "v"(d), "v"(x) : "memory");
+    }
+}
+
 // Read-only: every vector read; one word per workgroup written so the
 // loads stay.
 __global__ void __launch_bounds__(256)
@@ -361,6 +383,7 @@ int lso_probe_copy_shaped(void* state, const void* grad, void* weight, uint64_t 
 //   6  write-only over dst
 //   7  in place over src with nt loads; param = store policy (0..5, see
 //      copy_cpol_kernel)
+//   8  param bytes (4, 8 or 16) per lane, nt loads, nt sc1 stores
 // Returns a hipError_t (hipErrorInvalidValue for a bad variant, param or
 // size).
 int lso_probe_copy_variant(int variant, int param, const void* src, void* dst, uint64_t bytes, void* stream)
@@ -420,6 +443,17 @@ int lso_probe_copy_variant(int variant, int param, const void* src, void* dst, u
         case 3: hipLaunchKernelGGL(inplace_cpol_kernel<3>, dim3(g1), t, 0, st, b); break;
         case 4: hipLaunchKernelGGL(inplace_cpol_kernel<4>, dim3(g1), t, 0, st, b); break;
         case 5: hipLaunchKernelGGL(inplace_cpol_kernel<5>, dim3(g1), t, 0, st, b); break;
+        default: return static_cast<int>(hipErrorInvalidValue);
+        }
+        break;
+    }
+    case 8: {
+        const auto* cs = static_cast<const char*>(src);
+        auto* cd = static_cast<char*>(dst);
+        switch (param) {
+        case 4: hipLaunchKernelGGL(copy_width_kernel<4>, dim3(bytes / 1024), t, 0, st, cs, cd); break;
+        case 8: hipLaunchKernelGGL(copy_width_kernel<8>, dim3(bytes / 2048), t, 0, st, cs, cd); break;
+        case 16: hipLaunchKernelGGL(copy_width_kernel<16>, dim3(bytes / 4096), t, 0, st, cs, cd); break;
         default: return static_cast<int>(hipErrorInvalidValue);
         }
         break;
