@@ -154,10 +154,12 @@ copy_regs_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst)
 }
 
 // One vector per lane with the cache-policy bits of the load (L) and the
-// store (S): 0 none, 1 nt, 2 sc1, 3 nt sc1, 4 sc0 sc1, 5 sc0 sc1 nt.
+// store (S): 0 none, 1 nt, 2 sc1, 3 nt sc1, 4 sc0 sc1, 5 sc0 sc1 nt.  Every
+// inline-assembly store ends with s_nop 0: the compiler cannot see the wait
+// state a store's data registers need before a vector-ALU write to them.
 #define LSO_CPOL_LOAD(ms) \
     asm volatile("global_load_dwordx4 %0, %1, off " ms "\n\ts_waitcnt vmcnt(0)" : "=v"(x) : "v"(s) : "memory")
-#define LSO_CPOL_STORE(ms) asm volatile("global_store_dwordx4 %0, %1, off " ms : : "v"(d), "v"(x) : "memory")
+#define LSO_CPOL_STORE(ms) asm volatile("global_store_dwordx4 %0, %1, off " ms "\n\ts_nop 0" : : "v"(d), "v"(x) : "memory")
 
 template <int L, int S>
 __global__ void __launch_bounds__(256)
@@ -183,8 +185,8 @@ copy_cpol_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst)
 
 // The update's tiled traffic shape (shaped_copy_kernel<true>) with the
 // cache-policy bits S of its stores (as copy_cpol_kernel's).
-#define LSO_CPOL_ST16(ms, addr, val) asm volatile("global_store_dwordx4 %0, %1, off " ms : : "v"(addr), "v"(val) : "memory")
-#define LSO_CPOL_ST8(ms, addr, val) asm volatile("global_store_dwordx2 %0, %1, off " ms : : "v"(addr), "v"(val) : "memory")
+#define LSO_CPOL_ST16(ms, addr, val) asm volatile("global_store_dwordx4 %0, %1, off " ms "\n\ts_nop 0" : : "v"(addr), "v"(val) : "memory")
+#define LSO_CPOL_ST8(ms, addr, val) asm volatile("global_store_dwordx2 %0, %1, off " ms "\n\ts_nop 0" : : "v"(addr), "v"(val) : "memory")
 
 template <int S>
 __device__ __forceinline__ void st16_cpol(float* p, f32x4 x)
@@ -272,15 +274,15 @@ copy_width_kernel(const char* __restrict__ src, char* __restrict__ dst)
     if (W == 16) {
         const u32x4 x = ld_nt<u32x4>(src + off);
         LSO_GLOBAL u32x4* d = reinterpret_cast<LSO_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(dst + off));
-        asm volatile("global_store_dwordx4 %0, %1, off nt sc1" : : "v"(d), "v"(x) : "memory");
+        asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 0" : : "v"(d), "v"(x) : "memory");
     } else if (W == 8) {
         const u32x2 x = ld_nt<u32x2>(src + off);
         LSO_GLOBAL u32x2* d = reinterpret_cast<LSO_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(dst + off));
-        asm volatile("global_store_dwordx2 %0, %1, off nt sc1" : : "v"(d), "v"(x) : "memory");
+        asm volatile("global_store_dwordx2 %0, %1, off nt sc1\n\ts_nop 0" : : "v"(d), "v"(x) : "memory");
     } else {
         const uint32_t x = ld_nt<uint32_t>(src + off);
         LSO_GLOBAL uint32_t* d = reinterpret_cast<LSO_GLOBAL uint32_t*>(reinterpret_cast<uintptr_t>(dst + off));
-        asm volatile("global_store_dword %0, %1, off nt sc1" : : "v"(d), "v"(x) : "memory");
+        asm volatile("global_store_dword %0, %1, off nt sc1\n\ts_nop 0" : : "v"(d), "v"(x) : "memory");
     }
 }
 
