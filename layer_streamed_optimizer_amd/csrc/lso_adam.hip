@@ -268,14 +268,15 @@ __device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool 
 {
     constexpr uint32_t kChunkU = static_cast<uint32_t>(kThreads) * kQuad * U;
     float sq = 0.0f;
-    if (ch.n == kChunkU && kSc1 && !kG32 && !kSgd) {
-        // full tiled chunk, BF16 gradients: a wave's gradients and weights
-        // are each one 512-byte run, moved 16 bytes per lane by lanes 0-31
-        // and handed to the lanes of their quads by ds_bpermute (a lane's
-        // own quad is only 8 bytes of each).  Measured against 8-byte
-        // accesses: c3 28.71 against 28.89 ms, c1 4.681 against 4.699 ms
-        // (two alternating runs each).  Planar calls were slower with it (c0
-        // +5%, c2 +1.5%) and keep the 8-byte accesses below.
+    if (ch.n == kChunkU && kSc1 && !kSgd) {
+        // full tiled chunk: a wave's BF16 gradients and weights are each one
+        // 512-byte run, moved 16 bytes per lane by lanes 0-31 and handed to
+        // the lanes of their quads by ds_bpermute (a lane's own quad is only
+        // 8 bytes of each); FP32 gradients are 16 bytes per lane already and
+        // load as they are.  Measured against 8-byte accesses: c3 28.71
+        // against 28.89 ms, c1 4.681 against 4.699 ms, c1 with FP32
+        // gradients 5.041 against 5.048-5.127 ms (two alternating runs
+        // each).
         const uint32_t lane = threadIdx.x & 63u;
         Quad x[U];
         u32x4 gw[U];
@@ -283,11 +284,12 @@ __device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool 
         for (int u = 0; u < U; ++u) {
             const uint32_t we = (u * kThreads + (threadIdx.x & ~63u)) * kQuad;   // the wave's first element
             gw[u] = u32x4{0u, 0u, 0u, 0u};
-            if (lane < 32u) gw[u] = ld_nt<u32x4>(ch.g + we + 8u * lane);
+            if (kG32) x[u].gf = ld_nt<f32x4>(ch.gf + (u * kThreads + threadIdx.x) * kQuad);
+            else if (lane < 32u) gw[u] = ld_nt<u32x4>(ch.g + we + 8u * lane);
             load_state(ch, (u * kThreads + threadIdx.x) * kQuad, x[u]);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < U && !kG32; ++u) {
             // lane l's quad is the first or second half of lane l/2's load
             const int from = static_cast<int>(lane >> 1);
             const uint32_t a0 = lane_take(gw[u].x, from), a1 = lane_take(gw[u].y, from);
@@ -304,6 +306,56 @@ __device__ __forceinline__ float run_chunk(const Chunk& ch, const Coef& c, bool 
                 const u32x4 ww = {lane_take(w.x, s0), lane_take(w.y, s0), lane_take(w.x, s1), lane_take(w.y, s1)};
                 const uint32_t we = (u * kThreads + (threadIdx.x & ~63u)) * kQuad;
                 if (lane < 32u) st_nt_sc1(ch.w + we + 8u * lane, __builtin_bit_cast(f32x4, ww));
+            }
+        }
+        return sq;
+    }
+    if (ch.n == kChunkU && !kSc1 && U % 2 == 0 && !kG32 && !kSgd) {
+        // full planar chunk of a big call (four quads per lane), BF16
+        // gradients: rows are paired, lanes 0-31 moving row 2k's 512-byte
+        // gradient and weight runs and lanes 32-63 row 2k+1's, 16 bytes per
+        // lane, handed over by ds_bpermute.  Planar c3 33.96 against 34.21
+        // ms, c1 5.44 against 5.46-5.51 ms.  Small planar calls (one quad per
+        // lane, half of each wave moving) were slower with it (c0 +5%, c2
+        // +1.5%) and keep the 8-byte accesses below.
+        const uint32_t lane = threadIdx.x & 63u;
+        Quad x[U];
+        u32x4 gw[U / 2 > 0 ? U / 2 : 1];
+#pragma unroll
+        for (int k = 0; k < U / 2; ++k) {
+            const uint32_t r = 2u * k + (lane >> 5);   // lanes 0-31: row 2k, 32-63: row 2k+1
+            const uint32_t we = (r * kThreads + (threadIdx.x & ~63u)) * kQuad;
+            gw[k] = ld_nt<u32x4>(ch.g + we + 8u * (lane & 31u));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_state(ch, (u * kThreads + threadIdx.x) * kQuad, x[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int from = static_cast<int>((lane >> 1) + 32u * (u & 1));
+            const u32x4 g4 = gw[u / 2];
+            const uint32_t a0 = lane_take(g4.x, from), a1 = lane_take(g4.y, from);
+            const uint32_t a2 = lane_take(g4.z, from), a3 = lane_take(g4.w, from);
+            x[u].g = (lane & 1u) ? u32x2{a2, a3} : u32x2{a0, a1};
+        }
+        u32x2 wq[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wq[u] = compute_quad<kSgd, kG32, kNorm>(c, x[u], sq);
+            store_quad<kSgd, kSc1>(ch, (u * kThreads + threadIdx.x) * kQuad, x[u], wq[u], false);
+        }
+        if (has_w) {
+#pragma unroll
+            for (int k = 0; k < U / 2; ++k) {
+                // lane l stores 8 weights of row 2k + l/32: those of lanes
+                // 2(l%32) and 2(l%32) + 1
+                const int s0 = static_cast<int>(2u * (lane & 31u)), s1 = s0 + 1;
+                const u32x2 w0 = wq[2 * k], w1 = wq[2 * k + 1];
+                const uint32_t b0 = lane_take(w0.x, s0), b1 = lane_take(w0.y, s0), b2 = lane_take(w0.x, s1), b3 = lane_take(w0.y, s1);
+                const uint32_t c0 = lane_take(w1.x, s0), c1 = lane_take(w1.y, s0), c2 = lane_take(w1.x, s1), c3 = lane_take(w1.y, s1);
+                const u32x4 ww = (lane < 32u) ? u32x4{b0, b1, b2, b3} : u32x4{c0, c1, c2, c3};
+                const uint32_t r = 2u * k + (lane >> 5);
+                const uint32_t we = (r * kThreads + (threadIdx.x & ~63u)) * kQuad;
+                st_nt<u32x4>(ch.w + we + 8u * (lane & 31u), ww);
             }
         }
         return sq;
