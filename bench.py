@@ -186,6 +186,8 @@ def resident(args, w):
     # spread over per-block groups its few hundred MB touch ten times the
     # pages, and c2 measured 34.0 us instead of 30.1.
     use_arena = bpp * params > (1 << 30)
+    if args.arrangement != "auto":
+        use_arena = args.arrangement == "arena"
     if use_arena:
         lay = configs.BlockArena(sizes, tiled=tiled, grad_f32=g32, grad_sets=n_sets)
         keep = [torch.empty(lay.total_bytes, dtype=torch.uint8, device=dev)]
@@ -1173,6 +1175,9 @@ def main():
     ap.add_argument("--file-dir", default=None,
                     help="c4 with --host-memory file: where the layer files go "
                          "(default $LSO_FILE_DIR or /var/tmp)")
+    ap.add_argument("--arrangement", choices=["auto", "arena", "regions"], default="auto",
+                    help="resident arrays: one block-by-block arena, three regions (states, weights, "
+                         "gradient sets), or auto (the arena for steps of more than 1 GiB)")
     ap.add_argument("--layout", choices=["tiled", "planar"], default=None,
                     help="FP32 state layout (default: tiled for c1, c3, c4; planar for c0, c2)")
     ap.add_argument("--norms", action="store_true",
