@@ -288,3 +288,38 @@ def test_large_gradients_and_the_overflow_of_their_square(tiled, f32):
     assert overflowed > 1000
     assert arena.canaries_intact(), "a write landed outside its array"
     log("fp32 wide", f"identical; {overflowed} overflowing squares")
+
+
+NOWEIGHT_STREAM = 92
+
+
+@pytest.mark.parametrize("tiled,f32,n", [(True, False, 5 * 8192 + 3), (True, True, 5 * 8192 + 3),
+                                         (False, False, (32 << 20) + 4096 + 5)],
+                         ids=["tiled", "tiled_f32_grads", "planar_big_call"])
+def test_without_weights_bit_exact(tiled, f32, n):
+    """weight_dtype NONE on full chunks of every path that moves weights 16
+    bytes per lane (tiled chunks with BF16 and FP32 gradients, planar chunks
+    of a call above 32 M elements): master, m and v equal the emulation bit
+    for bit over two steps, and no byte outside the arrays is touched."""
+    log("fp32 no weights", f"n={n} tiled={tiled} f32_grads={f32}")
+    T = torch()
+    arena = Arena([n], tiled=tiled, grad_f32=f32, weight=False)
+    master = synth.normal_f32(n, stream=NOWEIGHT_STREAM, block=0, purpose=synth.PURPOSE_MASTER, step=0, sigma=0.02)
+    state = [master, np.zeros(n, np.float32), np.zeros(n, np.float32)]
+    for name, x in zip(("master", "m", "v"), state):
+        arena.put(0, name, x)
+    table = arena.table()
+    for t in (1, 2):
+        c = constants(t, 1e-3, 0.9, 0.999, 1e-8)
+        draw = synth.normal_f32 if f32 else synth.normal_bf16
+        g = draw(n, stream=NOWEIGHT_STREAM, block=0, purpose=synth.PURPOSE_GRAD, step=t, sigma=1e-3)
+        arena.put(0, "grad", g)
+        table.set_step(t)
+        lso.adam_step(table, T.cuda.current_stream())
+        T.cuda.synchronize()
+        p, m, v, _ = fx.adam_binary32_v(*state, g, c)
+        for name, want in (("master", p), ("m", m), ("v", v)):
+            count, where = first_diff(arena.get(0, name), want)
+            assert count == 0, f"step {t} {name}: {count} elements differ; first {where}"
+        state = [p, m, v]
+    assert arena.canaries_intact(), "a write landed outside the arrays (a weight store with no weights?)"
