@@ -13,10 +13,14 @@
 // order.
 //
 // Memory access: a lane owns groups of four consecutive elements, so every
-// FP32 access is one 128-bit load or store and every BF16 access one 64-bit
-// access, and each wave instruction covers one contiguous run (1 KB of FP32,
-// 512 B of BF16).  All state is touched exactly once, so loads and stores
-// are non-temporal (streamed past the caches).
+// FP32 access is one 128-bit load or store, and each wave instruction covers
+// one contiguous run (1 KB of FP32, 512 B of BF16).  A lane's own BF16
+// gradients and weights are 64 bits; on full tiled chunks and full planar
+// chunks of big calls they move 128 bits per lane instead (half of each
+// wave, or row pairs) and reach their lanes by ds_bpermute (run_chunk).  All
+// state is touched exactly once, so loads and stores are non-temporal
+// (streamed past the caches); tiled chunks store with device scope too
+// (inline assembly, each block of stores closed by a wait state).
 //
 // Two layouts of the FP32 state: planar (three arrays) or tiled (master, m
 // and v interleaved in tiles of LSO_TILE_ELEMS elements): in the tiled one
