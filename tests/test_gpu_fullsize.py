@@ -84,14 +84,15 @@ def emulate(master, grads, steps, weights=True):
     return out
 
 
-def run_resident_sampled(key, steps, tiled=True):
-    """The benchmark's configuration: tiled state for the large workloads."""
+def run_resident_sampled(key, steps, tiled=True, grad_f32=False):
+    """The benchmark's configuration: tiled state for the large workloads
+    (grad_f32: FP32 gradients instead of BF16)."""
     T = torch()
     w = configs.get(key)
     sid = configs.STREAM_ID[key]
     sizes = [b.n for b in w.blocks]
-    lay = configs.BlockArena(sizes, tiled=tiled)   # the bench's arrangement
-    log(f"{key}: {w.params:,} params, {len(sizes)} blocks, {steps} steps, tiled={tiled}")
+    lay = configs.BlockArena(sizes, tiled=tiled, grad_f32=grad_f32)   # the bench's arrangement
+    log(f"{key}: {w.params:,} params, {len(sizes)} blocks, {steps} steps, tiled={tiled}, f32 grads={grad_f32}")
     hs = T.cuda.current_stream().cuda_stream
     arena = T.empty(lay.total_bytes, dtype=T.uint8, device="cuda")
     state = grad = weight = arena
@@ -113,15 +114,17 @@ def run_resident_sampled(key, steps, tiled=True):
     T.cuda.synchronize()
     del scratch
     layout = lso.LSO_LAYOUT_TILED if tiled else lso.LSO_LAYOUT_PLANAR
+    gdt = lso.LSO_DT_F32 if grad_f32 else lso.LSO_DT_BF16
     rows = [dict(n=n, master=sb + lay.off_master[b], m=sb + lay.off_m[b], v=sb + lay.off_v[b],
-                 grad=gb + lay.off_grad[0][b], weight=wb + lay.off_weight[b], layout=layout)
+                 grad=gb + lay.off_grad[0][b], weight=wb + lay.off_weight[b], layout=layout, grad_dtype=gdt)
             for b, n in enumerate(sizes)]
+    fill_grad = synth.device_fill_normal_f32 if grad_f32 else synth.device_fill_normal_bf16
+    host_grad = synth.normal_f32 if grad_f32 else synth.normal_bf16
     table = lso.BlockTable.from_rows(rows)
     for t in range(1, steps + 1):
         for b, n in enumerate(sizes):
-            synth.device_fill_normal_bf16(gb + lay.off_grad[0][b], n, stream=sid, block=b,
-                                          purpose=synth.PURPOSE_GRAD, step=t,
-                                          sigma=configs.GRAD_SIGMA, hip_stream=hs)
+            fill_grad(gb + lay.off_grad[0][b], n, stream=sid, block=b, purpose=synth.PURPOSE_GRAD,
+                      step=t, sigma=configs.GRAD_SIGMA, hip_stream=hs)
         table.set_step(t)
         lso.adam_step(table, hs)
     T.cuda.synchronize()
@@ -137,8 +140,8 @@ def run_resident_sampled(key, steps, tiled=True):
                                           sigma=kind[1], start=off)
             ref = dict(master=master.copy(), m=np.zeros(ln, np.float32), v=np.zeros(ln, np.float32),
                        weight=np.zeros(ln, np.uint16))
-            gs = [synth.normal_bf16(ln, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=t,
-                                    sigma=configs.GRAD_SIGMA, start=off) for t in range(1, steps + 1)]
+            gs = [host_grad(ln, stream=sid, block=b, purpose=synth.PURPOSE_GRAD, step=t,
+                            sigma=configs.GRAD_SIGMA, start=off) for t in range(1, steps + 1)]
             for t in range(1, steps + 1):
                 oracle.adam_step(ref["master"], ref["m"], ref["v"], gs[t - 1], ref["weight"], t,
                                  configs.LR, configs.BETA1, configs.BETA2, configs.EPS)
@@ -173,6 +176,10 @@ def test_c1_tinyllama_full_size_sampled():
 
 def test_c1_tinyllama_full_size_sampled_planar():
     run_resident_sampled("c1", 10, tiled=False)
+
+
+def test_c1_tinyllama_full_size_sampled_f32_grads():
+    run_resident_sampled("c1", 10, grad_f32=True)
 
 
 def test_c3_llama7b_full_size_sampled():
