@@ -49,8 +49,9 @@ def assert_norms(got, gs, what):
 @pytest.mark.parametrize("tiled", [False, True], ids=["planar", "tiled"])
 @pytest.mark.parametrize("sizes", [[3 * 8192 + 17],
                                    [1, 7, 8193, 3 * 8192 + 17],
-                                   [1, 2, 3, 5, 1023, 1024, 1025, 4097, 12345, 100003]],
-                         ids=["one_block", "by_value", "table"])
+                                   [1, 2, 3, 5, 1023, 1024, 1025, 4097, 12345, 100003],
+                                   [(32 << 20) + 4101]],   # a big call: four quads per lane when planar
+                         ids=["one_block", "by_value", "table", "big_call"])
 def test_norms_match_oracle_and_leave_the_update_unchanged(sizes, tiled, f32):
     T = torch()
     sid = 80
